@@ -1,0 +1,158 @@
+"""ctypes binding of ``libdense_gemm.so`` (the C ABI in include/dense_gemm.h).
+
+Argument marshalling only: every step of the product runs in the library's
+HIP kernels.  Tensors are passed as raw device pointers with their leading
+dimensions, on the caller's current HIP stream (``torch.cuda`` is HIP on
+ROCm builds of PyTorch).  There is no fallback: if the library is missing or a
+call fails, a :class:`DenseGemmError` is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBNAME = "libdense_gemm.so"
+
+
+class Status(enum.IntEnum):
+    OK = 0
+    INVALID_DIM = 1
+    NULL_PTR = 2
+    BAD_LD = 3
+    MISALIGNED = 4
+    TOO_LARGE = 5
+    LAUNCH_FAILED = 6
+    NO_DEVICE = 7
+    BAD_ARG = 8
+
+
+class DenseGemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = Status(status) if status in Status._value2member_map_ else status
+        super().__init__("%s failed: %s (%d)" % (where, _status_string(status), int(status)))
+
+
+_lib = None
+
+# Every symbol the header declares, with its ctypes signature.
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+_vp = ctypes.c_void_p
+_GEMM_ARGS = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+SIGNATURES = {
+    "gemm_nt_f16": (_GEMM_ARGS, _i32),
+    "gemm_nn_bf16": (_GEMM_ARGS, _i32),
+    "gemm_nt_bf16": (_GEMM_ARGS, _i32),
+    "gemm_nn_f16": (_GEMM_ARGS, _i32),
+    "dense_gemm_status_string": ([_i32], ctypes.c_char_p),
+    "dense_gemm_validate": ([_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64], _i32),
+    "dense_gemm_tile_of_task": ([_i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_i64),
+                                 ctypes.POINTER(_i64)], _i32),
+    "dense_gemm_plan": ([_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_i64)], _i32),
+}
+
+
+def library_path() -> str:
+    return os.environ.get("DENSE_GEMM_LIB", os.path.join(_HERE, _LIBNAME))
+
+
+def load_library():
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            "HIP library %s is not built; run `python -c 'import __graft_entry__ as g; g.build()'`"
+            % path)
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return load_library().dense_gemm_status_string(int(status)).decode()
+    except Exception:  # library unavailable: fall back to the enum name
+        try:
+            return Status(status).name
+        except ValueError:
+            return "unknown status"
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check_tensor(t, dtype_name: str, what: str):
+    import torch
+    want = torch.float16 if dtype_name == "f16" else torch.bfloat16
+    if t.dtype != want:
+        raise TypeError("%s must be %s, got %s" % (what, want, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % what)
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("%s must be 2-D with unit column stride" % what)
+
+
+def _call(name: str, layout: str, fmt: str, A, B, D=None, stream=None):
+    """D = A @ B.T (layout "nt", B is N x K) or D = A @ B ("nn", B is K x N)."""
+    import torch
+    lib = load_library()
+    _check_tensor(A, fmt, "A")
+    _check_tensor(B, fmt, "B")
+    M, K = A.shape
+    if layout == "nt":
+        N, Kb = B.shape
+    else:
+        Kb, N = B.shape
+    if Kb != K:
+        raise ValueError("inner dimensions differ: A is %s, B is %s" % (tuple(A.shape), tuple(B.shape)))
+    if D is None:
+        D = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    else:
+        _check_tensor(D, fmt, "D")
+        if D.shape[0] != M or D.shape[1] != N:
+            raise ValueError("D has shape %s, expected (%d, %d)" % (tuple(D.shape), M, N))
+    st = getattr(lib, name)(M, N, K, A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0),
+                            D.data_ptr(), D.stride(0), _stream_handle(stream))
+    if st != Status.OK:
+        raise DenseGemmError(st, name)
+    return D
+
+
+def gemm_nt_f16(A, B, D=None, stream=None):
+    """D = A @ B.T in FP16 (FP32 accumulation); A is M x K, B is N x K."""
+    return _call("gemm_nt_f16", "nt", "f16", A, B, D, stream)
+
+
+def gemm_nn_bf16(A, B, D=None, stream=None):
+    """D = A @ B in BF16 (FP32 accumulation); A is M x K, B is K x N."""
+    return _call("gemm_nn_bf16", "nn", "bf16", A, B, D, stream)
+
+
+def gemm_nt_bf16(A, B, D=None, stream=None):
+    """D = A @ B.T in BF16 (FP32 accumulation); A is M x K, B is N x K."""
+    return _call("gemm_nt_bf16", "nt", "bf16", A, B, D, stream)
+
+
+def gemm_nn_f16(A, B, D=None, stream=None):
+    """D = A @ B in FP16 (FP32 accumulation); A is M x K, B is K x N."""
+    return _call("gemm_nn_f16", "nn", "f16", A, B, D, stream)
+
+
+def raw(name: str):
+    """The raw ctypes function ``name`` (for calls with explicit pointers)."""
+    return getattr(load_library(), name)
