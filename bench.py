@@ -1,0 +1,167 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X dense GEMM (one JSON line on stdout).
+
+A step is one call of the library's GEMM on the workload's operands, already
+resident in HBM: D = A @ B.T in FP16 at M = N = K = 4096 by default ("TIRx
+GEMM on Blackwell", "The short version").  ``--workload`` picks another of the
+seeded synthetic workloads in ``dense_gemm_08_amd/inputs.py``.
+
+Reported:
+* value: TFLOP/s = 2*M*N*K*steps / (wall time of the timed region);
+* roofline: the GEMM kernel against the dense FP16/BF16 MFMA peak, with its
+  average duration from HIP events recorded on the launch stream;
+* cpu_baseline: the CPU oracle (FP64, test infrastructure) timed on a bounded
+  row sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="square_nt")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, A, B, target_s: float):
+    """Time the oracle on a bounded sample: whole rows of D (all N columns)."""
+    import oracle
+    K, N = w.K, w.N
+    lda = K
+    ldb = K if w.layout == "nt" else N
+    oracle.gemm_entries(w.layout, w.fmt, A, B, K=K, lda=lda, ldb=ldb,
+                        rows=np.zeros(64, np.int64), cols=np.arange(64, dtype=np.int64) % N)
+    # calibrate on one row, then size the sample to the target time
+    t0 = time.perf_counter()
+    rows = np.zeros(N, np.int64)
+    cols = np.arange(N, dtype=np.int64)
+    oracle.gemm_entries(w.layout, w.fmt, A, B, K=K, lda=lda, ldb=ldb, rows=rows, cols=cols)
+    per_row = max(time.perf_counter() - t0, 1e-6)
+    nrows = int(max(1, min(w.M, target_s / per_row)))
+    rows = np.repeat(np.arange(nrows, dtype=np.int64), N)
+    cols = np.tile(np.arange(N, dtype=np.int64), nrows)
+    t0 = time.perf_counter()
+    oracle.gemm_entries(w.layout, w.fmt, A, B, K=K, lda=lda, ldb=ldb, rows=rows, cols=cols)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * nrows * N * K
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "%d full rows of D (%d x %d outputs, K=%d), FP64 accumulation, %.1f s"
+                      % (nrows, nrows, N, K, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this GEMM has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dense_gemm_08_amd import binding, inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    lib = binding.load_library()
+    entry = getattr(lib, {("nt", "f16"): "gemm_nt_f16", ("nn", "bf16"): "gemm_nn_bf16",
+                          ("nt", "bf16"): "gemm_nt_bf16", ("nn", "f16"): "gemm_nn_f16"}
+                    [(w.layout, w.fmt)])
+    A, B = inputs.make_operands(w)
+    dev = torch.device("cuda:0")
+    Ad = torch.from_numpy(A.view(np.int16)).to(dev)
+    Bd = torch.from_numpy(B.view(np.int16)).to(dev)
+    Dd = torch.empty((w.M, w.N), dtype=torch.int16, device=dev)
+    lda = w.K
+    ldb = w.K if w.layout == "nt" else w.N
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step():
+        st = entry(w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, Dd.data_ptr(), w.N, sh)
+        if st != 0:
+            raise binding.DenseGemmError(st, "gemm")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = ev0.elapsed_time(ev1) / args.steps
+
+    flops = float(w.flops)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.fmt]
+
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        rec = tj.get(w.name)
+        if rec and rec.get("kernel_source_sha") == source_sha():
+            traffic = rec["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+
+    out = {
+        "metric": "TFLOP/s and % of dense FP16 MFMA peak, D=A.B^T FP16 at M=N=K=4096"
+                  if w.name == "square_nt" else "TFLOP/s, %s" % w.name,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.fmt,
+        "data": "synthetic",
+        "config": {"workload": w.name, "layout": w.layout, "M": w.M, "N": w.N, "K": w.K,
+                   "dist": w.dist, "seed": w.seed},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "kernel_ms": kern_ms},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def source_sha() -> str:
+    import hashlib
+    p = os.path.join(ROOT, "dense_gemm_08_amd", "csrc", "dense_gemm.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

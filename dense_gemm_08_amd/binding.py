@@ -48,8 +48,9 @@ SIGNATURES = {
     "gemm_nn_f16": (_GEMM_ARGS, _i32),
     "dense_gemm_status_string": ([_i32], ctypes.c_char_p),
     "dense_gemm_validate": ([_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64], _i32),
-    "dense_gemm_tile_of_task": ([_i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_i64),
+    "dense_gemm_tile_of_task": ([_i64, _i64, _i64, _i64, ctypes.POINTER(_i64),
                                  ctypes.POINTER(_i64)], _i32),
+    "dense_gemm_xcd_slot": ([_i64, _i64, _i64], _i64),
     "dense_gemm_plan": ([_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_i64)], _i32),
 }
 

@@ -1,0 +1,574 @@
+// dense_gemm.hip -- tiled dense GEMM for the MI355X (gfx950) and its C ABI.
+//
+// The operation (D = A @ B.T in FP16, D = A @ B in BF16, FP32 accumulation,
+// one rounding to the output type) is defined in include/dense_gemm.h with
+// its citations.  This file holds the kernels and the host entry points.
+//
+// Kernel structure (one persistent workgroup per CU):
+//   * a persistent loop over output tiles in the grouped, XCD-aware order of
+//     tile_sched.h ("TIRx GEMM on Blackwell", V6: persistent CTAs pulling
+//     tiles; TileFoundry schedule tutorial, sections 2-3: persistent CTAs and
+//     the grouped traversal);
+//   * per K step, 16-byte buffer loads of the A and B tiles into registers,
+//     written into a two-stage LDS ring while the previous stage feeds the
+//     matrix cores ("TIRx GEMM on Blackwell", V5: two shared-memory stages so
+//     loading the next K tile overlaps the MMA of the current one);
+//   * an XOR swizzle of 16-byte chunks inside each LDS row, so both the
+//     row-wise tile writes and the column-wise MFMA fragment reads spread over
+//     all banks (the role of the 128-byte swizzle in the TIRx and TileFoundry
+//     shared-memory layouts);
+//   * v_mfma_f32_32x32x16_{f16,bf16} with FP32 accumulators; four waves each
+//     own a 128 x 128 quarter of a 256 x 256 tile and read the shared A and B
+//     stages ("TIRx GEMM on Blackwell", V8/V9: larger tiles and several
+//     consumers reusing one staged operand tile);
+//   * an epilogue that rounds to the output type, stages each wave's rows in
+//     LDS and writes whole 16-byte row chunks (TileFoundry tutorial, section 5:
+//     the output tile is staged in shared memory before the store);
+//   * ragged M, N and K handled by masking: out-of-range loads read zeros
+//     through the buffer descriptor's range check, out-of-range stores are
+//     skipped (the pages' shapes all divide the tiles; this is our reading).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "dense_gemm.h"
+#include "tile_sched.h"
+
+namespace dg {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+enum Layout { NT = 0, NN = 1 };
+
+// ---- tile configuration -------------------------------------------------
+constexpr int BM = 256;              // tile rows (M)
+constexpr int BN = 256;              // tile columns (N)
+constexpr int BK = 32;               // K depth of one LDS stage
+constexpr int STAGES = 4;            // LDS ring depth
+constexpr int WAVES = 4;             // 2 x 2 waves
+constexpr int THREADS = WAVES * 64;
+constexpr int WTM = 128;             // wave tile rows
+constexpr int WTN = 128;             // wave tile columns
+constexpr int MI = WTM / 32;         // 32 x 32 MFMA blocks per wave, M direction
+constexpr int NI = WTN / 32;         //                               N direction
+constexpr int A_BYTES = BM * BK * 2;           // 16 KiB: 256 rows x 64 B
+constexpr int B_BYTES = BN * BK * 2;           // 16 KiB
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES;  // 128 KiB of the 160 KiB per CU
+constexpr int DMA_PER_OPERAND = A_BYTES / (THREADS * 16);  // 16-byte loads per thread
+constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPERAND;
+constexpr uint32_t OOB = 0x80000000u;          // a buffer offset past every range
+
+static_assert(DMA_PER_OPERAND == 4, "each wave fills 4 KiB of each operand per stage");
+static_assert(BK == 32 && BM == 256 && BN == 256, "swizzles below assume these sizes");
+
+struct Params {
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* D;
+  int M, N, K;
+  int lda, ldb, ldd;
+  int tiles_m, tiles_n, group_m, num_tasks, num_xcds;
+  int d_vec;  // D rows are 16-byte aligned (16-byte stores allowed)
+};
+
+// LDS layouts.
+// K-contiguous tiles (A, and B for NT): row r holds 32 elements = four
+// 16-byte chunks; chunk c is stored at slot c ^ swz_k(r).  Eight consecutive
+// rows read at one chunk, or sixteen, land in distinct bank groups.
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 2) & 3) ^ (r & 2); }
+// N-contiguous B tile (NN): row k holds 256 elements = 32 chunks; chunk c is
+// stored at slot c ^ swz_n(k), so the four k rows read together by one
+// transposing load sit in different banks.
+__device__ __forceinline__ int swz_n(int k) { return (k & 3) << 2; }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)(a >> 32);  // stride 0
+  r[2] = (int)bytes;                // num_records: bytes in range
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16-byte global -> LDS copy for every lane of the wave: lane L's 16 bytes at
+// buffer offset `off` land at LDS address m0 + 16 L.  Offsets at or past the
+// descriptor's range write zeros.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(m0)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight and
+// its LDS reads are done, then synchronize the workgroup.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mfma<_Float16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma<__bf16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Round two floats to the output type (round-to-nearest-even) and pack them.
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  T l = (T)lo, h = (T)hi;
+  uint16_t lb = __builtin_bit_cast(uint16_t, l), hb = __builtin_bit_cast(uint16_t, h);
+  return (uint32_t)lb | ((uint32_t)hb << 16);
+}
+
+// Transposing LDS read: within each 16-lane block, lane i receives element
+// i % 4 of the 8 bytes addressed by lanes 4j + i / 4, for j = 0..3.
+__device__ __forceinline__ u32x2 read_tr(const char* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// threadIdx.x through an opaque move: values derived from it are recomputed
+// where they are used instead of being hoisted and kept live across the whole
+// persistent loop (where they would compete with the epilogue for registers).
+__device__ __forceinline__ int opaque_tid() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  return t;
+}
+
+struct Frags {
+  u32x4 a[MI];
+  u32x4 b[NI];
+};
+
+template <typename T, int LAYOUT>
+__global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  const uint32_t lds0 = lds_addr(smem);
+
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int wm = wave >> 1;  // wave tile row (0..1)
+  const int wn = wave & 1;   // wave tile column (0..1)
+
+  const int nk = (p.K + BK - 1) / BK;
+  const int slot0 = xcd_slot(blockIdx.x, gridDim.x, p.num_xcds);
+
+  for (int task = slot0; task < p.num_tasks; task += gridDim.x) {
+    int tm, tn;
+    tile_of_task(task, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int vm = min(BM, p.M - m0);  // valid rows of the A tile
+    const int vn = min(BN, p.N - n0);  // valid columns of D in this tile
+
+    const int lane = opaque_tid() & 63;
+    const int lr = lane & 31;
+    const int lh = lane >> 5;
+    // Loader roles.  K-contiguous tiles: each wave instruction fills 1 KiB =
+    // 16 rows; lane -> row lane/4 of the group, logical chunk by the swizzle.
+    const int kc_row = lane >> 2;
+    const int kc_chunk = (lane & 3) ^ swz_k(kc_row);
+    // NN B tile: each wave instruction fills 2 rows of 512 B.
+    const int nn_row_lo = lane >> 5;
+
+    // Fragment read offsets (bytes within a stage).
+    int fa[2], fb[2], fbn[NI];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      fa[s] = (wm * WTM + lr) * 64 + (((2 * s + lh) ^ swz_k(lr)) << 4);
+      fb[s] = A_BYTES + (wn * WTN + lr) * 64 + (((2 * s + lh) ^ swz_k(lr)) << 4);
+    }
+    {
+      // transposing reads: lane supplies row k = 8*lh + (lane%16)/4 and
+      // columns n = wn*128 + ni*32 + 16*((lane/16)%2) + 4*(lane%4)
+      const int klane = 8 * lh + ((lane & 15) >> 2);
+      const int low = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+      const int fl = (lane >> 2) & 3;  // == swz_n(klane + 4m) >> 2 for every m
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        fbn[ni] = A_BYTES + klane * 512 + ((wn * 16 + ((ni ^ fl) << 2) + low) << 4) + (lane & 1) * 8;
+    }
+
+    // Buffer descriptors for this tile; offsets past the last valid byte read
+    // zeros (rows beyond M for A, rows beyond N for the NT B tile).
+    const i32x4 rs_a = make_rsrc(p.A + (int64_t)m0 * p.lda,
+                                 p.K > 0 ? (uint32_t)(((int64_t)(vm - 1) * p.lda + p.K) * 2) : 0u);
+    i32x4 rs_b = rs_a;
+    uint32_t a_off[DMA_PER_OPERAND], b_off[DMA_PER_OPERAND];
+#pragma unroll
+    for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+      const int r = (4 * wave + i) * 16 + kc_row;
+      a_off[i] = r < vm ? (uint32_t)(r * p.lda * 2 + kc_chunk * 16) : OOB;
+    }
+    if (LAYOUT == NT) {
+      rs_b = make_rsrc(p.B + (int64_t)n0 * p.ldb,
+                       p.K > 0 ? (uint32_t)(((int64_t)(vn - 1) * p.ldb + p.K) * 2) : 0u);
+#pragma unroll
+      for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+        const int r = (4 * wave + i) * 16 + kc_row;
+        b_off[i] = r < vn ? (uint32_t)(r * p.ldb * 2 + kc_chunk * 16) : OOB;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+        const int k = 2 * (4 * wave + i) + nn_row_lo;
+        const int c = (lane & 31) ^ swz_n(k);
+        b_off[i] = (uint32_t)(k * p.ldb * 2 + c * 16);
+      }
+    }
+
+    // Issue the LDS-DMA loads of K step ks into ring slot `slot`.  Steps at
+    // or past nk load nothing (every offset is out of range, so the slot is
+    // zero-filled): the loop keeps a fixed number of loads in flight.
+    auto issue = [&](int ks, int slot) {
+      const int k0 = ks * BK;
+      const bool kin = k0 + (kc_chunk << 3) < p.K;
+      const uint32_t sa = lds0 + slot * STAGE_BYTES + (4 * wave) * 1024;
+#pragma unroll
+      for (int i = 0; i < DMA_PER_OPERAND; ++i)
+        dma16(rs_a, kin ? a_off[i] + (uint32_t)(k0 * 2) : OOB, sa + i * 1024);
+      const uint32_t sb = sa + A_BYTES;
+      if (LAYOUT == NT) {
+#pragma unroll
+        for (int i = 0; i < DMA_PER_OPERAND; ++i)
+          dma16(rs_b, kin ? b_off[i] + (uint32_t)(k0 * 2) : OOB, sb + i * 1024);
+      } else {
+        // rebase on this K step: rows past K, and row K-1 past N, read zeros
+        const int vk = min(BK, p.K - k0);
+        const i32x4 r = make_rsrc(
+            p.B + (vk > 0 ? (int64_t)k0 * p.ldb + n0 : 0),
+            vk > 0 ? (uint32_t)(((int64_t)(vk - 1) * p.ldb + (p.N - n0)) * 2) : 0u);
+#pragma unroll
+        for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+          const int k = 2 * (4 * wave + i) + nn_row_lo;
+          dma16(r, k < vk ? b_off[i] : OOB, sb + i * 1024);
+        }
+      }
+    };
+
+    auto read_frags = [&](int slot, int s, Frags& F) {
+      const char* base = smem + slot * STAGE_BYTES;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) F.a[i] = *(const u32x4*)(base + fa[s] + i * 2048);
+      if (LAYOUT == NT) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) F.b[j] = *(const u32x4*)(base + fb[s] + j * 2048);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const u32x2 lo = read_tr(base + fbn[j] + (s * 16) * 512);
+          const u32x2 hi = read_tr(base + fbn[j] + (s * 16 + 4) * 512);
+          F.b[j] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+    };
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) acc[i][j] = (f32x16){};
+
+    // Operand order (B fragment first) leaves each lane holding one row of D
+    // and four consecutive columns per register quad.
+    auto mfmas = [&](const Frags& F) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] = mfma<T>(F.b[j], F.a[i], acc[i][j]);
+    };
+    constexpr int READS = MI + (LAYOUT == NT ? NI : 2 * NI);
+    auto interleave = [&]() {
+      // one LDS read between MFMAs, the rest of the MFMAs after
+#pragma unroll
+      for (int i = 0; i < READS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, (MI * NI) / READS, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - READS * ((MI * NI) / READS), 0);
+    };
+
+    // The ring: stage ks lives in slot ks % STAGES.  At the top of step ks the
+    // loads of steps ks+1 .. ks+STAGES-2 may still be in flight, step ks has
+    // landed, and F0 holds the first half of stage ks.
+    Frags F0, F1;
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) issue(st, st);
+    wait_vm_barrier<(STAGES - 2) * DMA_PER_STAGE>();
+    read_frags(0, 0, F0);
+
+    for (int ks = 0; ks < nk; ++ks) {
+      const int slot = ks % STAGES;
+      // refill the slot every wave finished reading before the last barrier
+      issue(ks + STAGES - 1, (ks + STAGES - 1) % STAGES);
+      // first half of the stage: MFMAs on F0 while F1 is read
+      read_frags(slot, 1, F1);
+      mfmas(F0);
+      interleave();
+      // stage ks+1 has landed for every wave, and every wave has finished
+      // reading stage ks, so its slot may be refilled from the next step on
+      wait_vm_barrier<(STAGES - 2) * DMA_PER_STAGE>();
+      // second half: MFMAs on F1 while the first half of stage ks+1 is read
+      // (after the last step this reads a zero-filled slot, unused)
+      read_frags((ks + 1) % STAGES, 0, F0);
+      mfmas(F1);
+      interleave();
+    }
+
+    wait_vm_barrier<0>();  // every wave is done with the ring; reuse it for staging
+
+    // Epilogue: per 32-row block, round, stage 32 x 128 outputs of this wave
+    // in LDS (chunk-swizzled rows of 256 B), then store 16-byte row chunks.
+    char* stg = smem + wave * (32 * 256);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // lane holds row lr, columns j*32 + 8q + 4*lh + 0..3
+          u32x2 v;
+          v[0] = pack2<T>(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+          v[1] = pack2<T>(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          const int chunk = j * 4 + q;
+          *(u32x2*)(stg + lr * 256 + ((chunk ^ (lr & 15)) << 4) + lh * 8) = v;
+        }
+        // keep the conversions of one block together (bounded live registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int row0 = m0 + wm * WTM + i * 32;
+      const int col0 = n0 + wn * WTN;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int rr = t * 4 + (lane >> 4);
+        const int cc = lane & 15;
+        const u32x4 v = *(const u32x4*)(stg + rr * 256 + ((cc ^ (rr & 15)) << 4));
+        const int row = row0 + rr;
+        const int col = col0 + cc * 8;
+        if (row < p.M && col < p.N) {
+          uint16_t* dst = p.D + (int64_t)row * p.ldd + col;
+          if (p.d_vec && col + 8 <= p.N) {
+            *(u32x4*)dst = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (col + e < p.N) dst[e] = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm_barrier<0>();  // staging reads done before the next tile refills the ring
+  }
+}
+
+// ---- host side ----------------------------------------------------------
+
+struct DeviceInfo {
+  int cus = 0;
+  bool gfx950 = false;
+};
+
+static std::mutex g_mu;
+static DeviceInfo g_dev[64];
+static bool g_dev_ok[64];
+
+static dense_gemm_status device_info(DeviceInfo* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DENSE_GEMM_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_dev_ok[dev]) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DENSE_GEMM_NO_DEVICE;
+    g_dev[dev].cus = prop.multiProcessorCount;
+    g_dev[dev].gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev_ok[dev] = true;
+  }
+  *out = g_dev[dev];
+  return out->gfx950 && out->cus > 0 ? DENSE_GEMM_OK : DENSE_GEMM_NO_DEVICE;
+}
+
+static constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+static int choose_group_m(int64_t tiles_m, int64_t tiles_n, int64_t grid) {
+  // Workgroups resident together on one XCD form a block of tiles; an 8-row
+  // group makes that block close to square for the grids this library sees.
+  (void)tiles_n;
+  (void)grid;
+  return (int)(tiles_m < 8 ? tiles_m : 8);
+}
+
+}  // namespace dg
+
+using namespace dg;
+
+extern "C" {
+
+const char* dense_gemm_status_string(int status) {
+  switch (status) {
+    case DENSE_GEMM_OK: return "ok";
+    case DENSE_GEMM_INVALID_DIM: return "invalid dimension (negative M, N or K)";
+    case DENSE_GEMM_NULL_PTR: return "null pointer";
+    case DENSE_GEMM_BAD_LD: return "leading dimension below its minimum";
+    case DENSE_GEMM_MISALIGNED: return "misaligned pointer or K/ld/N not a multiple of 8";
+    case DENSE_GEMM_TOO_LARGE: return "problem too large for 32-bit tile offsets";
+    case DENSE_GEMM_LAUNCH_FAILED: return "kernel launch failed";
+    case DENSE_GEMM_NO_DEVICE: return "no gfx950 device current";
+    case DENSE_GEMM_BAD_ARG: return "bad argument";
+    default: return "unknown status";
+  }
+}
+
+dense_gemm_status dense_gemm_validate(int layout, int64_t M, int64_t N, int64_t K, const void* A,
+                                      int64_t lda, const void* B, int64_t ldb, const void* D,
+                                      int64_t ldd) {
+  if (layout != NT && layout != NN) return DENSE_GEMM_BAD_ARG;
+  if (M < 0 || N < 0 || K < 0) return DENSE_GEMM_INVALID_DIM;
+  if (M == 0 || N == 0) return DENSE_GEMM_OK;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return DENSE_GEMM_TOO_LARGE;
+  if (D == nullptr) return DENSE_GEMM_NULL_PTR;
+  if (K > 0 && (A == nullptr || B == nullptr)) return DENSE_GEMM_NULL_PTR;
+  if (ldd < N) return DENSE_GEMM_BAD_LD;
+  if (K > 0) {
+    if (lda < K) return DENSE_GEMM_BAD_LD;
+    if (layout == NT ? ldb < K : ldb < N) return DENSE_GEMM_BAD_LD;
+  }
+  if (((uintptr_t)D & 1) != 0) return DENSE_GEMM_MISALIGNED;
+  if (K > 0) {
+    if (((uintptr_t)A & 15) != 0 || ((uintptr_t)B & 15) != 0) return DENSE_GEMM_MISALIGNED;
+    if ((K & 7) != 0 || (lda & 7) != 0 || (ldb & 7) != 0) return DENSE_GEMM_MISALIGNED;
+    if (layout == NN && (N & 7) != 0) return DENSE_GEMM_MISALIGNED;
+    // 32-bit buffer offsets: the span one tile's descriptor covers.
+    const int64_t lim = ((int64_t)1 << 31) - 16;
+    if (((int64_t)(BM - 1) * lda + K) * 2 >= lim) return DENSE_GEMM_TOO_LARGE;
+    if (layout == NT && ((int64_t)(BN - 1) * ldb + K) * 2 >= lim) return DENSE_GEMM_TOO_LARGE;
+    if (layout == NN && ((int64_t)(BK - 1) * ldb + N) * 2 >= lim) return DENSE_GEMM_TOO_LARGE;
+  }
+  if (ldd >= kMaxDim || lda >= kMaxDim || ldb >= kMaxDim) return DENSE_GEMM_TOO_LARGE;
+  return DENSE_GEMM_OK;
+}
+
+dense_gemm_status dense_gemm_tile_of_task(int64_t task, int64_t tiles_m, int64_t tiles_n,
+                                          int64_t group_m, int64_t* tile_m, int64_t* tile_n) {
+  if (tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || task < 0 || task >= tiles_m * tiles_n ||
+      tiles_m * tiles_n >= kMaxDim || !tile_m || !tile_n)
+    return DENSE_GEMM_BAD_ARG;
+  int tm, tn;
+  tile_of_task((int)task, (int)tiles_m, (int)tiles_n, (int)group_m, &tm, &tn);
+  *tile_m = tm;
+  *tile_n = tn;
+  return DENSE_GEMM_OK;
+}
+
+int64_t dense_gemm_xcd_slot(int64_t b, int64_t grid, int64_t num_xcds) {
+  if (grid <= 0 || num_xcds <= 0 || b < 0 || b >= grid || grid >= kMaxDim) return -1;
+  return xcd_slot((int)b, (int)grid, (int)num_xcds);
+}
+
+dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t num_cus,
+                                  int64_t* out) {
+  if ((layout != NT && layout != NN) || M <= 0 || N <= 0 || K < 0 || num_cus <= 0 || !out)
+    return DENSE_GEMM_BAD_ARG;
+  const int64_t tiles_m = (M + BM - 1) / BM;
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t tasks = tiles_m * tiles_n;
+  const int64_t grid = tasks < num_cus ? tasks : num_cus;
+  out[0] = BM;
+  out[1] = BN;
+  out[2] = BK;
+  out[3] = tiles_m;
+  out[4] = tiles_n;
+  out[5] = grid;
+  out[6] = choose_group_m(tiles_m, tiles_n, grid);
+  out[7] = THREADS;
+  return DENSE_GEMM_OK;
+}
+
+}  // extern "C"
+
+namespace dg {
+
+template <typename T, int LAYOUT>
+static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                             const void* B, int64_t ldb, void* D, int64_t ldd,
+                             hipStream_t stream) {
+  dense_gemm_status st = dense_gemm_validate(LAYOUT, M, N, K, A, lda, B, ldb, D, ldd);
+  if (st != DENSE_GEMM_OK || M == 0 || N == 0) return st;
+  DeviceInfo info;
+  st = device_info(&info);
+  if (st != DENSE_GEMM_OK) return st;
+  int64_t plan[8];
+  st = dense_gemm_plan(LAYOUT, M, N, K, info.cus, plan);
+  if (st != DENSE_GEMM_OK) return st;
+  Params p;
+  p.A = (const uint16_t*)A;
+  p.B = (const uint16_t*)B;
+  p.D = (uint16_t*)D;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.lda = (int)lda;
+  p.ldb = (int)ldb;
+  p.ldd = (int)ldd;
+  p.tiles_m = (int)plan[3];
+  p.tiles_n = (int)plan[4];
+  p.group_m = (int)plan[6];
+  p.num_tasks = (int)(plan[3] * plan[4]);
+  p.num_xcds = 8;
+  p.d_vec = (((uintptr_t)D & 15) == 0 && (ldd & 7) == 0) ? 1 : 0;
+  hipLaunchKernelGGL((gemm_kernel<T, LAYOUT>), dim3((unsigned)plan[5]), dim3(THREADS), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return DENSE_GEMM_LAUNCH_FAILED;
+  return DENSE_GEMM_OK;
+}
+
+}  // namespace dg
+
+extern "C" {
+
+dense_gemm_status gemm_nt_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                              const void* B, int64_t ldb, void* D, int64_t ldd,
+                              hipStream_t stream) {
+  return run<_Float16, NT>(M, N, K, A, lda, B, ldb, D, ldd, stream);
+}
+
+dense_gemm_status gemm_nn_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, void* D, int64_t ldd,
+                               hipStream_t stream) {
+  return run<__bf16, NN>(M, N, K, A, lda, B, ldb, D, ldd, stream);
+}
+
+dense_gemm_status gemm_nt_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, void* D, int64_t ldd,
+                               hipStream_t stream) {
+  return run<__bf16, NT>(M, N, K, A, lda, B, ldb, D, ldd, stream);
+}
+
+dense_gemm_status gemm_nn_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                              const void* B, int64_t ldb, void* D, int64_t ldd,
+                              hipStream_t stream) {
+  return run<_Float16, NN>(M, N, K, A, lda, B, ldb, D, ldd, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+/*
+ * dense_gemm.h -- C ABI of the MI355X (gfx950) tiled dense GEMM library
+ * (libdense_gemm.so).
+ *
+ * Operation.  "TIRx GEMM on Blackwell", section "The short version", defines
+ * the product D = A @ B.T with FP16 inputs and output and FP32 accumulation.
+ * TileFoundry "Choosing schedules and instructions for a backend", section 1
+ * (the GRID HIR), defines D = a @ b with a (M, K) and b (K, N) in BF16: the
+ * accumulator starts at zero in f32, every K block adds its partial product,
+ * and the accumulator is cast to the output type once.  Section 6 of that
+ * page adds that the output need not be cleared before each tile overwrites
+ * it: D is overwritten, with no alpha, beta, bias or activation.
+ *
+ * Layout.  All matrices are row-major with an explicit leading dimension, as
+ * in the conventional layout rule of the CMU TIRx blog ("Conventional
+ * layouts": element (i, j) of a matrix with leading dimension ld sits at
+ * offset i * ld + j elements):
+ *   A  M x K, element (i, k) at A[i * lda + k]                  (lda >= K)
+ *   B  "nt": N x K, element (j, k) at B[j * ldb + k]            (ldb >= K)
+ *      "nn": K x N, element (k, j) at B[k * ldb + j]            (ldb >= N)
+ *   D  M x N, element (i, j) at D[i * ldd + j]                  (ldd >= N)
+ * Elements are 16-bit patterns (IEEE binary16 for *_f16, bfloat16 for
+ * *_bf16) passed as untyped device pointers.  Results are rounded from the
+ * FP32 accumulator to the output format with round-to-nearest-even.
+ *
+ * Semantics.  For 0 <= i < M, 0 <= j < N:
+ *     D[i][j] = round( sum_{k < K} A[i][k] * Bhat[k][j] )
+ * with the sum accumulated in FP32 in an order the library chooses (fixed per
+ * tile configuration, so repeated calls are bitwise reproducible).  Elements
+ * of D outside [0, M) x [0, N) -- including the columns between N and ldd --
+ * are never written.  K == 0 writes zeros; M == 0 or N == 0 does nothing.
+ *
+ * Alignment (operands move in 16-byte chunks): A and B must be 16-byte
+ * aligned and K, lda and ldb multiples of 8 elements; for the "nn" layout N
+ * must also be a multiple of 8.  D needs 2-byte alignment and any ldd >= N
+ * (16-byte stores are used where D's rows are 16-byte aligned).  Other
+ * arguments return DENSE_GEMM_MISALIGNED.  M and N are otherwise arbitrary
+ * (ragged edges are masked), and K need not be a multiple of the tile depth.
+ *
+ * Ownership and concurrency.  The caller owns every buffer and the stream.
+ * The library allocates no device memory, keeps no pointers after a call
+ * returns, and caches only per-device properties (thread-safe).  A, B and D
+ * must not overlap.  Calls are asynchronous and ordered on `stream` (0 is
+ * the null stream); the caller synchronizes.  Calls on different streams
+ * may run concurrently.
+ *
+ * Errors.  Every entry point validates its arguments before launching and
+ * returns a dense_gemm_status; on any error nothing is launched and D is
+ * untouched.  DENSE_GEMM_LAUNCH_FAILED reports an error from the HIP runtime
+ * at launch time (asynchronous faults surface at the caller's next
+ * synchronization, as for any HIP kernel).
+ */
+#ifndef DENSE_GEMM_H
+#define DENSE_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP runtime's stream handle (identical to its own declaration). */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum dense_gemm_status {
+  DENSE_GEMM_OK = 0,
+  DENSE_GEMM_INVALID_DIM = 1,   /* M, N or K negative */
+  DENSE_GEMM_NULL_PTR = 2,      /* D null with M*N > 0; A or B null with M*N*K > 0 */
+  DENSE_GEMM_BAD_LD = 3,        /* a leading dimension below its minimum */
+  DENSE_GEMM_MISALIGNED = 4,    /* A or B not 16-byte aligned, D odd, or K / lda / ldb / (nn) N not a multiple of 8 */
+  DENSE_GEMM_TOO_LARGE = 5,     /* a dimension >= 2^31, or a per-tile operand span >= 2^31 bytes */
+  DENSE_GEMM_LAUNCH_FAILED = 6, /* the HIP runtime rejected the launch */
+  DENSE_GEMM_NO_DEVICE = 7,     /* no current HIP device, or it is not a gfx950 */
+  DENSE_GEMM_BAD_ARG = 8        /* an argument of a helper below is out of its range */
+} dense_gemm_status;
+
+/* D = A @ B.T; FP16 in, FP32 accumulate, FP16 out.  A is M x K, B is N x K.
+ * The FP16 product of "TIRx GEMM on Blackwell", "The short version". */
+dense_gemm_status gemm_nt_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                              const void* B, int64_t ldb, void* D, int64_t ldd,
+                              hipStream_t stream);
+
+/* D = A @ B; BF16 in, FP32 accumulate, BF16 out.  A is M x K, B is K x N.
+ * The BF16 product of TileFoundry's schedule tutorial, section 1. */
+dense_gemm_status gemm_nn_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, void* D, int64_t ldd,
+                               hipStream_t stream);
+
+/* The other two combinations of the same operation (same kernels, other
+ * template arguments): D = A @ B.T in BF16 and D = A @ B in FP16. */
+dense_gemm_status gemm_nt_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, void* D, int64_t ldd,
+                               hipStream_t stream);
+dense_gemm_status gemm_nn_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                              const void* B, int64_t ldb, void* D, int64_t ldd,
+                              hipStream_t stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char* dense_gemm_status_string(int status);
+
+/* ---- host-only helpers (no device call; usable without a GPU) ---------- */
+
+/* The argument check every entry point runs first.  layout: 0 = "nt",
+ * 1 = "nn".  Pointers are only compared with NULL and tested for alignment. */
+dense_gemm_status dense_gemm_validate(int layout, int64_t M, int64_t N, int64_t K,
+                                      const void* A, int64_t lda, const void* B, int64_t ldb,
+                                      const void* D, int64_t ldd);
+
+/* The persistent tile scheduler's map from a workgroup's task index to the
+ * output tile it computes: tiles are visited in groups of group_m tile rows,
+ * column by column within a group (the grouped traversal of TileFoundry's
+ * schedule tutorial, section 3), the last group possibly shorter.  Writes the
+ * tile row and column.  Returns DENSE_GEMM_BAD_ARG if task is outside
+ * [0, tiles_m * tiles_n) or a size is not positive. */
+dense_gemm_status dense_gemm_tile_of_task(int64_t task, int64_t tiles_m, int64_t tiles_n,
+                                          int64_t group_m, int64_t* tile_m, int64_t* tile_n);
+
+/* The launch plan for a problem on a device with num_cus compute units.
+ * Writes 8 values to out: BM, BN, BK, tiles_m, tiles_n, grid (workgroups),
+ * group_m, threads per workgroup. */
+dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K,
+                                  int64_t num_cus, int64_t* out);
+
+/* The workgroup-to-task permutation of the persistent grid: workgroup b
+ * (dispatched to XCD b mod num_xcds) takes slot dense_gemm_xcd_slot(...) of
+ * the task order, so that workgroups that share an XCD's L2 take adjacent
+ * tasks.  A bijection of [0, grid).  Returns -1 on a bad argument. */
+int64_t dense_gemm_xcd_slot(int64_t b, int64_t grid, int64_t num_xcds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_GEMM_H */

@@ -1,0 +1,66 @@
+"""Helpers for the GPU tests: device buffers and raw C-ABI calls.
+
+torch provides device memory and the stream; every GEMM runs in the HIP
+library through its C entry points (``include/dense_gemm.h``).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from dense_gemm_08_amd import binding
+
+ENTRY = {("nt", "f16"): "gemm_nt_f16", ("nn", "bf16"): "gemm_nn_bf16",
+         ("nt", "bf16"): "gemm_nt_bf16", ("nn", "f16"): "gemm_nn_f16"}
+CANARY = 0x7E5A  # a NaN pattern in both formats: any write over it shows
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def to_dev(bits: np.ndarray, rows: int, cols: int, ld: int | None = None, fill: int = CANARY):
+    """A rows x ld int16 device buffer holding ``bits`` in its first cols
+    columns and ``fill`` in the padding.  Returns the tensor."""
+    t = torch()
+    ld = cols if ld is None else ld
+    host = np.full((rows, ld), fill, dtype=np.uint16)
+    if rows and cols:
+        host[:, :cols] = bits.reshape(rows, cols)
+    return t.from_numpy(host.view(np.int16)).to("cuda")
+
+
+def empty_out(rows: int, ld: int, fill: int = CANARY):
+    t = torch()
+    return t.full((max(rows, 1), max(ld, 1)), np.uint16(fill).view(np.int16).item(),
+                  dtype=t.int16, device="cuda")
+
+
+def from_dev(t_dev) -> np.ndarray:
+    return t_dev.cpu().numpy().view(np.uint16)
+
+
+def call(layout, fmt, M, N, K, A, lda, B, ldb, D, ldd, stream=None):
+    """Run the entry point for (layout, fmt) on device tensors; returns the status."""
+    t = torch()
+    fn = binding.raw(ENTRY[(layout, fmt)])
+    st = t.cuda.current_stream() if stream is None else stream
+    ptr = lambda x: 0 if x is None else x.data_ptr()  # noqa: E731
+    return binding.Status(fn(M, N, K, ptr(A), lda, ptr(B), ldb, ptr(D), ldd, st.cuda_stream))
+
+
+def gemm(layout, fmt, Abits, Bbits, M, N, K, lda=None, ldb=None, ldd=None, stream=None):
+    """Upload, run, download.  Returns (D bits M x ldd, status)."""
+    t = torch()
+    lda = K if lda is None else lda
+    ldb = (K if layout == "nt" else N) if ldb is None else ldb
+    ldd = N if ldd is None else ldd
+    A = to_dev(Abits, M, K, lda)
+    if layout == "nt":
+        B = to_dev(Bbits, N, K, ldb)
+    else:
+        B = to_dev(Bbits, K, N, ldb)
+    D = empty_out(M, ldd)
+    st = call(layout, fmt, M, N, K, A, lda, B, ldb, D, ldd, stream)
+    t.cuda.synchronize()
+    return from_dev(D)[:M], st

@@ -1,0 +1,176 @@
+"""Host-side tests of the C-ABI library (no GPU, no compute calls).
+
+The library must load, export every function ``include/dense_gemm.h``
+declares, reject bad arguments with the documented status codes, and its
+persistent tile scheduler must cover every tile exactly once in the grouped
+order of TileFoundry's schedule tutorial (sections 2, 3 and 5).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dense_gemm_08_amd import binding
+from tests.test_oracle import golden
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dense_gemm.h")
+NT, NN = 0, 1
+S = binding.Status
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_functions_are_exported(lib):
+    names = declared_functions()
+    assert {"gemm_nt_f16", "gemm_nn_bf16"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in binding.SIGNATURES, n
+
+
+def test_status_strings(lib):
+    for st in S:
+        s = lib.dense_gemm_status_string(int(st))
+        assert s and s.decode()
+    assert lib.dense_gemm_status_string(12345).decode() == "unknown status"
+
+
+def _v(layout, M, N, K, A=16, lda=None, B=16, ldb=None, D=16, ldd=None):
+    lib = binding.load_library()
+    lda = K if lda is None else lda
+    ldb = (K if layout == NT else N) if ldb is None else ldb
+    ldd = N if ldd is None else ldd
+    return S(lib.dense_gemm_validate(layout, M, N, K, A, lda, B, ldb, D, ldd))
+
+
+def test_validate_accepts_the_page_workloads():
+    assert _v(NT, 128, 128, 64) == S.OK
+    assert _v(NT, 128, 128, 4096) == S.OK
+    assert _v(NT, 4096, 4096, 4096) == S.OK
+    assert _v(NN, 8192, 17408, 5120) == S.OK
+    assert _v(NT, 3000, 5000, 4000) == S.OK
+
+
+def test_validate_error_codes():
+    assert _v(2, 8, 8, 8) == S.BAD_ARG
+    assert _v(NT, -1, 8, 8) == S.INVALID_DIM
+    assert _v(NT, 8, -1, 8) == S.INVALID_DIM
+    assert _v(NT, 8, 8, -8) == S.INVALID_DIM
+    # empty output: nothing to do, pointers not looked at
+    assert _v(NT, 0, 8, 8, A=0, B=0, D=0) == S.OK
+    assert _v(NN, 8, 0, 8, A=0, B=0, D=0) == S.OK
+    assert _v(NT, 8, 8, 8, D=0) == S.NULL_PTR
+    assert _v(NT, 8, 8, 8, A=0) == S.NULL_PTR
+    assert _v(NN, 8, 8, 8, B=0) == S.NULL_PTR
+    # K = 0: A and B are never read (D is set to zero)
+    assert _v(NT, 8, 8, 0, A=0, B=0) == S.OK
+    assert _v(NT, 8, 8, 16, lda=8) == S.BAD_LD
+    assert _v(NT, 8, 8, 16, ldb=8) == S.BAD_LD
+    assert _v(NN, 8, 16, 8, ldb=8) == S.BAD_LD
+    assert _v(NT, 8, 16, 8, ldd=8) == S.BAD_LD
+    assert _v(NT, 8, 8, 8, A=8) == S.MISALIGNED
+    assert _v(NT, 8, 8, 8, B=24) == S.MISALIGNED
+    assert _v(NT, 8, 8, 8, D=1) == S.MISALIGNED
+    assert _v(NT, 8, 8, 8, D=2) == S.OK  # D needs 2-byte alignment only
+    assert _v(NT, 8, 8, 12, lda=16, ldb=16) == S.MISALIGNED
+    assert _v(NT, 8, 8, 8, lda=12) == S.MISALIGNED
+    assert _v(NT, 8, 12, 8, ldd=12) == S.OK  # any ldd >= N
+    assert _v(NN, 8, 12, 8, ldb=16, ldd=16) == S.MISALIGNED
+    assert _v(NT, 8, 13, 8, ldd=16) == S.OK  # ragged N is fine for NT
+    assert _v(NT, 1 << 31, 8, 8) == S.TOO_LARGE
+    assert _v(NT, 8, 8, 8, lda=1 << 23) == S.TOO_LARGE
+    assert _v(NN, 8, 8, 8, ldb=1 << 26) == S.TOO_LARGE
+
+
+def tile_of(task, tm, tn, g):
+    lib = binding.load_library()
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    st = lib.dense_gemm_tile_of_task(task, tm, tn, g, ctypes.byref(a), ctypes.byref(b))
+    assert st == S.OK
+    return a.value, b.value
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n,g", [(1, 1, 8), (16, 16, 8), (16, 16, 16), (64, 68, 16),
+                                               (12, 20, 8), (13, 7, 4), (5, 9, 8), (32, 68, 8)])
+def test_scheduler_covers_every_tile_once(tiles_m, tiles_n, g):
+    seen = {tile_of(t, tiles_m, tiles_n, g) for t in range(tiles_m * tiles_n)}
+    assert seen == {(i, j) for i in range(tiles_m) for j in range(tiles_n)}
+
+
+def test_scheduler_matches_page_grouped_order():
+    # TileFoundry tutorial, section 5: task -> g = task // (GN*G), bn = (task//G) % GN,
+    # mi = task % G, tile = (g*G + mi, bn); the 64 x 68 tile grid with G = 16.
+    GM, GN, G = 64, 68, 16
+    gold = golden()
+    assert GM * GN == gold["tiles_8192x17408_128x256"]
+    for task in range(0, GM * GN, 7):
+        g, bn, mi = task // (GN * G), (task // G) % GN, task % G
+        assert tile_of(task, GM, GN, G) == (g * G + mi, bn)
+
+
+def test_page_persistent_assignment_covers_each_tile_once():
+    # TileFoundry tutorial, sections 2-3: 132 persistent CTAs; CTA p walks tasks
+    # p, p+132, ...; the grouped loops visit the same 4352 tiles exactly once,
+    # in 33 waves (the analyze output of section 1).
+    GM, GN, G, CTAS = 64, 68, 16, 132
+    gold = golden()
+    owners = {}
+    for p in range(CTAS):
+        for task in range(p, GM * GN, CTAS):
+            t = tile_of(task, GM, GN, G)
+            assert t not in owners
+            owners[t] = p
+    assert len(owners) == GM * GN
+    assert -(-GM * GN // CTAS) == gold["waves_4352_tiles_132_ctas"]
+    # the section-3 loop nest, written out, visits the same (m, n) per CTA
+    for p in (0, 1, 77, 131):
+        page = [((g * 16 + mi), bn) for g in range(64 // 16) for bn in range(68)
+                for mi in range((p - (g * 68 + bn) * 16) % 132, 16, 132)]
+        ours = [tile_of(task, GM, GN, G) for task in range(p, GM * GN, CTAS)]
+        assert page == ours
+
+
+def test_ragged_last_group():
+    # 13 tile rows in groups of 4: the last group holds one row
+    order = [tile_of(t, 13, 3, 4) for t in range(39)]
+    assert order[:4] == [(0, 0), (1, 0), (2, 0), (3, 0)]
+    assert order[-3:] == [(12, 0), (12, 1), (12, 2)]
+
+
+@pytest.mark.parametrize("grid", [1, 7, 8, 9, 64, 255, 256, 300])
+def test_xcd_slot_is_a_bijection(grid):
+    lib = binding.load_library()
+    slots = [lib.dense_gemm_xcd_slot(b, grid, 8) for b in range(grid)]
+    assert sorted(slots) == list(range(grid))
+    # the workgroups of one XCD hold consecutive slots
+    for x in range(min(8, grid)):
+        mine = sorted(s for b, s in enumerate(slots) if b % 8 == x)
+        assert mine == list(range(mine[0], mine[0] + len(mine)))
+    assert lib.dense_gemm_xcd_slot(grid, grid, 8) == -1
+
+
+def test_plan_for_the_workloads():
+    lib = binding.load_library()
+    out = (ctypes.c_int64 * 8)()
+    gold = golden()
+    assert lib.dense_gemm_plan(NT, 4096, 4096, 4096, 256, out) == S.OK
+    BM, BN, BK, tm, tn, grid, gm, threads = list(out)
+    assert tm * tn * BM * BN >= 4096 * 4096
+    assert grid == min(tm * tn, 256)
+    # the page's own tiling of this shape (128 x 128) gives 1024 tiles
+    assert (4096 // 128) ** 2 == gold["tiles_4096sq_128x128"]
+    assert gold["ksteps_5120_bk64"] == 5120 // 64
+    assert lib.dense_gemm_plan(NN, 8192, 17408, 5120, 256, out) == S.OK
+    assert out[5] <= 256
+    assert lib.dense_gemm_plan(NT, 0, 5, 5, 256, out) == S.BAD_ARG

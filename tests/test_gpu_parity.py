@@ -1,0 +1,274 @@
+"""GPU parity tests: the HIP path (through the C ABI) against the CPU oracle.
+
+Acceptance (per element): |d_gpu - d| <= ulp_out(|d|) + 2^-11 * sum_k |a*b|,
+with d the oracle's FP64 value.  Where the FP32 sum is exact (small-integer,
+identity and all-ones inputs) the result must equal the oracle's correctly
+rounded value bit for bit.  Shapes: every workload at a reduced size checked
+element by element (several tiles and a ragged tail in M, N and K), and at its
+full size in the launch configuration the benchmark times, on sampled entries.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_08_amd import inputs
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+S = None  # binding.Status, imported lazily
+
+
+def status():
+    from dense_gemm_08_amd.binding import Status
+    return Status
+
+
+def check_full(layout, fmt, A, B, M, N, K, D):
+    d, s = oracle.gemm(layout, fmt, A, B, M=M, N=N, K=K)
+    res = oracle.check(fmt, d, s, D[:, :N])
+    assert res.ok, (res, np.unravel_index(max(res.worst_idx, 0), (M, N)))
+    return d
+
+
+def check_sampled(layout, fmt, A, B, M, N, K, D, n=3000, seed=0):
+    rows, cols = inputs.sample_indices(M, N, n, seed)
+    ldb = K if layout == "nt" else N
+    d, s = oracle.gemm_entries(layout, fmt, A, B, K=K, lda=K, ldb=ldb, rows=rows, cols=cols)
+    res = oracle.check(fmt, d, s, D[rows, cols])
+    assert res.ok, (res, rows[max(res.worst_idx, 0)], cols[max(res.worst_idx, 0)])
+
+
+# --------------------------------------------------- workloads, reduced --
+
+REDUCED = [
+    # (workload, M, N, K): each spans several 256 x 256 tiles and a ragged tail
+    ("single_tile", 128, 128, 64),
+    ("k_loop", 128, 128, 4096),
+    ("square_nt", 600, 520, 712),
+    ("large_nn", 520, 776, 328),
+    ("ragged_nt", 300, 500, 400),
+]
+
+
+@pytest.mark.parametrize("name,M,N,K", REDUCED)
+def test_workload_reduced_full_check(name, M, N, K):
+    w = inputs.WORKLOADS[name]
+    A, B = inputs.make_operands(w, M=M, N=N, K=K)
+    D, st = _gpu.gemm(w.layout, w.fmt, A, B, M, N, K)
+    assert st == status().OK
+    check_full(w.layout, w.fmt, A, B, M, N, K, D)
+
+
+@pytest.mark.parametrize("layout,fmt", [("nt", "bf16"), ("nn", "f16")])
+def test_other_type_layout_pairs(layout, fmt):
+    w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 17)
+    M, N, K = 300, 264, 200
+    A, B = inputs.make_operands(w, M=M, N=N, K=K)
+    D, st = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    assert st == status().OK
+    check_full(layout, fmt, A, B, M, N, K, D)
+
+
+# ------------------------------------------------ workloads, full size --
+
+@pytest.mark.parametrize("name", ["single_tile", "k_loop", "square_nt", "large_nn", "ragged_nt"])
+def test_workload_full_size_sampled(name):
+    w = inputs.WORKLOADS[name]
+    A, B = inputs.make_operands(w)
+    D, st = _gpu.gemm(w.layout, w.fmt, A, B, w.M, w.N, w.K)
+    assert st == status().OK
+    if w.M * w.N * w.K <= 128 * 128 * 4096:
+        check_full(w.layout, w.fmt, A, B, w.M, w.N, w.K, D)
+    else:
+        check_sampled(w.layout, w.fmt, A, B, w.M, w.N, w.K, D, n=3000, seed=w.seed)
+        assert np.isfinite(oracle.decode(w.fmt, D[:: max(w.M // 64, 1), :: max(w.N // 64, 1)])).all()
+
+
+# ------------------------------------------------- bitwise special cases --
+
+@pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16"), ("nt", "bf16"), ("nn", "f16")])
+def test_small_integers_exact(layout, fmt):
+    # entries in {-3..3}: every FP32 partial sum is an exact integer, so the
+    # result is the exactly rounded integer sum (sums up to 9K exceed the
+    # FP16/BF16 integer range, so this pins round-to-nearest-even)
+    M, N, K = 264, 392, 1032
+    sa, sb = inputs.operand_shapes(layout, M, N, K)
+    A = inputs.small_integers(fmt, sa, seed=31)
+    B = inputs.small_integers(fmt, sb, seed=32)
+    D, st = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    assert st == status().OK
+    d, _ = oracle.gemm(layout, fmt, A, B)
+    want = oracle.round_to(fmt, d)
+    assert (D == want).all()
+
+
+@pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
+def test_identity_gives_a(layout, fmt):
+    w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 41)
+    M, K = 333, 264
+    A, _ = inputs.make_operands(w, M=M, N=8, K=K)
+    eye = inputs.identity(fmt, K)
+    D, st = _gpu.gemm(layout, fmt, A, eye, M, K, K)
+    assert st == status().OK
+    assert (oracle.decode(fmt, D) == oracle.decode(fmt, A)).all()
+
+
+@pytest.mark.parametrize("K", [64, 4096, 5120, 4000, 8])
+def test_all_ones_give_k(K):
+    for layout, fmt in (("nt", "f16"), ("nn", "bf16")):
+        M, N = 136, 264
+        sa, sb = inputs.operand_shapes(layout, M, N, K)
+        D, st = _gpu.gemm(layout, fmt, inputs.ones(fmt, sa), inputs.ones(fmt, sb), M, N, K)
+        assert st == status().OK
+        assert (D == oracle.round_to(fmt, np.array([float(K)]))[0]).all()
+
+
+def test_power_of_two_scaling():
+    w = inputs.WORKLOADS["square_nt"]
+    M, N, K = 300, 300, 256
+    A, B = inputs.make_operands(w, M=M, N=N, K=K)
+    D1, _ = _gpu.gemm("nt", "f16", A, B, M, N, K)
+    A4 = inputs.f16_bits(oracle.decode("f16", A) * 4.0)
+    D4, _ = _gpu.gemm("nt", "f16", A4, B, M, N, K)
+    d1 = oracle.decode("f16", D1)
+    d4 = oracle.decode("f16", D4)
+    # scaling one operand by 4 scales every product and partial sum exactly;
+    # only outputs in FP16's subnormal range round differently
+    normal = np.abs(d1) >= 2.0 ** -14
+    assert normal.mean() > 0.99
+    assert (d4[normal] == d1[normal] * 4.0).all()
+
+
+def test_k_tail_equals_zero_padding():
+    # K = 4000 (a partial last K step) against the same data zero-padded to 4096
+    w = inputs.WORKLOADS["ragged_nt"]
+    M, N, K, Kp = 272, 264, 4000, 4096
+    A, B = inputs.make_operands(w, M=M, N=N, K=K)
+    Ap = np.zeros((M, Kp), np.uint16)
+    Ap[:, :K] = A
+    Bp = np.zeros((N, Kp), np.uint16)
+    Bp[:, :K] = B
+    D1, _ = _gpu.gemm("nt", "f16", A, B, M, N, K)
+    D2, _ = _gpu.gemm("nt", "f16", Ap, Bp, M, N, Kp)
+    assert (D1 == D2).all()
+
+
+@pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
+def test_ragged_block_equals_padded_block(layout, fmt):
+    # a ragged M x N result is the top-left block of the zero-padded product
+    w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 51)
+    M, N, K, Mp, Np = 300, 504, 136, 512, 512
+    A, B = inputs.make_operands(w, M=M, N=N, K=K)
+    Ap = np.zeros((Mp, K), np.uint16)
+    Ap[:M] = A
+    if layout == "nt":
+        Bp = np.zeros((Np, K), np.uint16)
+        Bp[:N] = B
+    else:
+        Bp = np.zeros((K, Np), np.uint16)
+        Bp[:, :N] = B
+    D1, _ = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    D2, _ = _gpu.gemm(layout, fmt, Ap, Bp, Mp, Np, K)
+    assert (D1 == D2[:M, :N]).all()
+
+
+# ------------------------------------------------------------ edge paths --
+
+SWEEP = [1, 7, 8, 33, 65, 129, 255, 257]
+
+
+@pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
+def test_ragged_sweep(layout, fmt):
+    rng = np.random.default_rng(5)
+    w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 0)
+    for M in SWEEP:
+        for N in SWEEP:
+            if layout == "nn" and N % 8:
+                continue
+            K = int(rng.choice([8, 16, 56, 64, 72, 136]))
+            A, B = inputs.make_operands(w, seed=M * 1000 + N, M=M, N=N, K=K)
+            D, st = _gpu.gemm(layout, fmt, A, B, M, N, K)
+            assert st == status().OK, (M, N, K)
+            check_full(layout, fmt, A, B, M, N, K, D)
+
+
+@pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
+def test_leading_dimensions_and_untouched_padding(layout, fmt):
+    w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 61)
+    M, N, K = 280, 272, 200
+    lda, ldb, ldd = K + 24, (K if layout == "nt" else N) + 40, N + 16
+    A, B = inputs.make_operands(w, M=M, N=N, K=K)
+    D, st = _gpu.gemm(layout, fmt, A, B, M, N, K, lda=lda, ldb=ldb, ldd=ldd)
+    assert st == status().OK
+    assert (D[:, N:] == _gpu.CANARY).all()
+    check_full(layout, fmt, A, B, M, N, K, D)
+
+
+def test_zero_k_writes_zeros_and_empty_is_noop():
+    t = _gpu.torch()
+    D = _gpu.empty_out(40, 48)
+    st = _gpu.call("nt", "f16", 40, 48, 0, None, 0, None, 0, D, 48)
+    t.cuda.synchronize()
+    assert st == status().OK
+    assert (_gpu.from_dev(D) == 0).all()
+    D = _gpu.empty_out(40, 48)
+    A = _gpu.to_dev(np.zeros((40, 16), np.uint16), 40, 16)
+    B = _gpu.to_dev(np.zeros((16, 48), np.uint16), 16, 48)
+    assert _gpu.call("nn", "bf16", 0, 48, 16, A, 16, B, 48, D, 48) == status().OK
+    assert _gpu.call("nn", "bf16", 40, 0, 16, A, 16, B, 48, D, 48) == status().OK
+    t.cuda.synchronize()
+    assert (_gpu.from_dev(D) == _gpu.CANARY).all()
+
+
+def test_errors_launch_nothing():
+    t = _gpu.torch()
+    D = _gpu.empty_out(64, 64)
+    A = _gpu.to_dev(np.zeros((64, 64), np.uint16), 64, 64)
+    Sx = status()
+    assert _gpu.call("nt", "f16", 64, 64, 60, A, 64, A, 64, D, 64) == Sx.MISALIGNED
+    assert _gpu.call("nt", "f16", 64, 64, 64, A, 32, A, 64, D, 64) == Sx.BAD_LD
+    assert _gpu.call("nt", "f16", -1, 64, 64, A, 64, A, 64, D, 64) == Sx.INVALID_DIM
+    t.cuda.synchronize()
+    assert (_gpu.from_dev(D) == _gpu.CANARY).all()
+
+
+def test_deterministic_and_stream_ordered():
+    t = _gpu.torch()
+    w = inputs.WORKLOADS["square_nt"]
+    M = N = K = 1024
+    A, B = inputs.make_operands(w, M=M, N=N, K=K)
+    Ad, Bd = _gpu.to_dev(A, M, K), _gpu.to_dev(B, N, K)
+    outs = []
+    s = t.cuda.Stream()
+    for stream in (None, s, s):
+        D = _gpu.empty_out(M, N)
+        if stream is not None:
+            stream.wait_stream(t.cuda.current_stream())
+            with t.cuda.stream(stream):
+                assert _gpu.call("nt", "f16", M, N, K, Ad, K, Bd, K, D, N, stream) == status().OK
+            t.cuda.current_stream().wait_stream(stream)
+        else:
+            assert _gpu.call("nt", "f16", M, N, K, Ad, K, Bd, K, D, N) == status().OK
+        t.cuda.synchronize()
+        outs.append(_gpu.from_dev(D))
+    assert (outs[0] == outs[1]).all() and (outs[1] == outs[2]).all()
+
+
+def test_python_binding_roundtrip():
+    t = _gpu.torch()
+    import dense_gemm_08_amd as dg
+    a = t.randn(200, 136, device="cuda").half()
+    b = t.randn(72, 136, device="cuda").half()
+    d = dg.gemm_nt_f16(a, b)
+    t.cuda.synchronize()
+    A = a.cpu().numpy().view(np.uint16)
+    B = b.cpu().numpy().view(np.uint16)
+    check_full("nt", "f16", A, B, 200, 72, 136, d.cpu().numpy().view(np.uint16))
+    a2 = t.randn(64, 128, device="cuda").bfloat16()
+    b2 = t.randn(128, 96, device="cuda").bfloat16()
+    d2 = dg.gemm_nn_bf16(a2, b2)
+    t.cuda.synchronize()
+    check_full("nn", "bf16", a2.cpu().view(t.int16).numpy().view(np.uint16),
+               b2.cpu().view(t.int16).numpy().view(np.uint16), 64, 96, 128,
+               d2.cpu().view(t.int16).numpy().view(np.uint16))
