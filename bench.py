@@ -32,12 +32,18 @@ PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, published
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="square_nt")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ld-pad", type=int, default=0,
+                    help="extra elements on every leading dimension (lda, ldb, ldd)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the GEMM, time a plain device copy of this many MiB "
+                         "(the known-size reference for scaling the FETCH_SIZE/WRITE_SIZE "
+                         "counters of a rocprofv3 --pmc run)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
     return ap.parse_args()
@@ -80,6 +86,22 @@ def main():
     import torch
     from dense_gemm_08_amd import binding, inputs
 
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.ones(n // 2, dtype=torch.int16, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n,
+                          "GB_per_s": 2 * n / dt / 1e9}), flush=True)
+        return
+
     w = inputs.WORKLOADS[args.workload]
     lib = binding.load_library()
     entry = getattr(lib, {("nt", "f16"): "gemm_nt_f16", ("nn", "bf16"): "gemm_nn_bf16",
@@ -87,16 +109,20 @@ def main():
                     [(w.layout, w.fmt)])
     A, B = inputs.make_operands(w)
     dev = torch.device("cuda:0")
-    Ad = torch.from_numpy(A.view(np.int16)).to(dev)
-    Bd = torch.from_numpy(B.view(np.int16)).to(dev)
-    Dd = torch.empty((w.M, w.N), dtype=torch.int16, device=dev)
-    lda = w.K
-    ldb = w.K if w.layout == "nt" else w.N
+    pad = args.ld_pad
+    lda = w.K + pad
+    ldb = (w.K if w.layout == "nt" else w.N) + pad
+    ldd = w.N + pad
+    Ad = torch.zeros((A.shape[0], lda), dtype=torch.int16, device=dev)
+    Ad[:, :A.shape[1]] = torch.from_numpy(A.view(np.int16)).to(dev)
+    Bd = torch.zeros((B.shape[0], ldb), dtype=torch.int16, device=dev)
+    Bd[:, :B.shape[1]] = torch.from_numpy(B.view(np.int16)).to(dev)
+    Dd = torch.empty((w.M, ldd), dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
     def step():
-        st = entry(w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, Dd.data_ptr(), w.N, sh)
+        st = entry(w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, Dd.data_ptr(), ldd, sh)
         if st != 0:
             raise binding.DenseGemmError(st, "gemm")
 
@@ -146,7 +172,7 @@ def main():
         "dtype": w.fmt,
         "data": "synthetic",
         "config": {"workload": w.name, "layout": w.layout, "M": w.M, "N": w.N, "K": w.K,
-                   "dist": w.dist, "seed": w.seed},
+                   "lda": lda, "ldb": ldb, "ldd": ldd, "dist": w.dist, "seed": w.seed},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel_ms": kern_ms},

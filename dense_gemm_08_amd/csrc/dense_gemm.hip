@@ -52,24 +52,26 @@ enum Layout { NT = 0, NN = 1 };
 // ---- tile configuration -------------------------------------------------
 constexpr int BM = 256;              // tile rows (M)
 constexpr int BN = 256;              // tile columns (N)
-constexpr int BK = 32;               // K depth of one LDS stage
-constexpr int STAGES = 4;            // LDS ring depth
+constexpr int BK = 64;               // K depth of one LDS stage (128-byte rows)
+constexpr int STAGES = 2;            // LDS ring depth
+constexpr int SUB = BK / 16;         // MFMA k-substeps per stage
 constexpr int WAVES = 4;             // 2 x 2 waves
 constexpr int THREADS = WAVES * 64;
 constexpr int WTM = 128;             // wave tile rows
 constexpr int WTN = 128;             // wave tile columns
 constexpr int MI = WTM / 32;         // 32 x 32 MFMA blocks per wave, M direction
 constexpr int NI = WTN / 32;         //                               N direction
-constexpr int A_BYTES = BM * BK * 2;           // 16 KiB: 256 rows x 64 B
-constexpr int B_BYTES = BN * BK * 2;           // 16 KiB
+constexpr int A_BYTES = BM * BK * 2;           // 32 KiB: 256 rows x 128 B
+constexpr int B_BYTES = BN * BK * 2;           // 32 KiB
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;  // 128 KiB of the 160 KiB per CU
 constexpr int DMA_PER_OPERAND = A_BYTES / (THREADS * 16);  // 16-byte loads per thread
 constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPERAND;
 constexpr uint32_t OOB = 0x80000000u;          // a buffer offset past every range
 
-static_assert(DMA_PER_OPERAND == 4, "each wave fills 4 KiB of each operand per stage");
-static_assert(BK == 32 && BM == 256 && BN == 256, "swizzles below assume these sizes");
+static_assert(DMA_PER_OPERAND == 8, "each wave fills 8 KiB of each operand per stage");
+static_assert(BK == 64 && BM == 256 && BN == 256, "swizzles below assume these sizes");
+static_assert(MI * NI == 2 * DMA_PER_OPERAND, "one refill load per two MFMAs");
 
 struct Params {
   const uint16_t* A;
@@ -82,10 +84,11 @@ struct Params {
 };
 
 // LDS layouts.
-// K-contiguous tiles (A, and B for NT): row r holds 32 elements = four
-// 16-byte chunks; chunk c is stored at slot c ^ swz_k(r).  Eight consecutive
-// rows read at one chunk, or sixteen, land in distinct bank groups.
-__device__ __forceinline__ int swz_k(int r) { return ((r >> 2) & 3) ^ (r & 2); }
+// K-contiguous tiles (A, and B for NT): row r holds 64 elements = eight
+// 16-byte chunks (one 128-byte line of the source row); chunk c is stored at
+// slot c ^ swz_k(r).  Eight consecutive rows read at one chunk, or sixteen,
+// land in distinct bank groups.
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
 // N-contiguous B tile (NN): row k holds 256 elements = 32 chunks; chunk c is
 // stored at slot c ^ swz_n(k), so the four k rows read together by one
 // transposing load sit in different banks.
@@ -114,6 +117,9 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t off, uint32_t m0) {
                : "v"(off), "s"(rsrc), "s"(m0)
                : "memory", "m0");
 }
+
+// Scheduling fence: the compiler may move no instruction across it.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Wait until at most N vector-memory operations of this wave are in flight and
 // its LDS reads are done, then synchronize the workgroup.
@@ -186,19 +192,20 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     const int lane = opaque_tid() & 63;
     const int lr = lane & 31;
     const int lh = lane >> 5;
+
     // Loader roles.  K-contiguous tiles: each wave instruction fills 1 KiB =
-    // 16 rows; lane -> row lane/4 of the group, logical chunk by the swizzle.
-    const int kc_row = lane >> 2;
-    const int kc_chunk = (lane & 3) ^ swz_k(kc_row);
-    // NN B tile: each wave instruction fills 2 rows of 512 B.
+    // 8 rows of 128 B; wave w's instruction i covers rows (8w + i) * 8 ...
+    // +7, lane -> row lane/8 of the group and a logical chunk by the swizzle
+    // (which depends on the row's low four bits, i.e. on i's parity).
+    // NN B tile: each wave instruction fills 2 k rows of 512 B.
     const int nn_row_lo = lane >> 5;
 
     // Fragment read offsets (bytes within a stage).
-    int fa[2], fb[2], fbn[NI];
+    int fa[SUB], fb[SUB], fbn[NI];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      fa[s] = (wm * WTM + lr) * 64 + (((2 * s + lh) ^ swz_k(lr)) << 4);
-      fb[s] = A_BYTES + (wn * WTN + lr) * 64 + (((2 * s + lh) ^ swz_k(lr)) << 4);
+    for (int s = 0; s < SUB; ++s) {
+      fa[s] = (wm * WTM + lr) * 128 + (((2 * s + lh) ^ swz_k(lr)) << 4);
+      fb[s] = A_BYTES + (wn * WTN + lr) * 128 + (((2 * s + lh) ^ swz_k(lr)) << 4);
     }
     {
       // transposing reads: lane supplies row k = 8*lh + (lane%16)/4 and
@@ -217,43 +224,48 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
                                  p.K > 0 ? (uint32_t)(((int64_t)(vm - 1) * p.lda + p.K) * 2) : 0u);
     i32x4 rs_b = rs_a;
     uint32_t a_off[DMA_PER_OPERAND], b_off[DMA_PER_OPERAND];
+    int kc[2];  // logical chunk of this lane for even / odd instruction index
+#pragma unroll
+    for (int h = 0; h < 2; ++h) kc[h] = (lane & 7) ^ swz_k(h * 8 + (lane >> 3));
 #pragma unroll
     for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-      const int r = (4 * wave + i) * 16 + kc_row;
-      a_off[i] = r < vm ? (uint32_t)(r * p.lda * 2 + kc_chunk * 16) : OOB;
+      const int r = (8 * wave + i) * 8 + (lane >> 3);
+      a_off[i] = r < vm ? (uint32_t)(r * p.lda * 2 + kc[i & 1] * 16) : OOB;
     }
     if (LAYOUT == NT) {
       rs_b = make_rsrc(p.B + (int64_t)n0 * p.ldb,
                        p.K > 0 ? (uint32_t)(((int64_t)(vn - 1) * p.ldb + p.K) * 2) : 0u);
 #pragma unroll
       for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-        const int r = (4 * wave + i) * 16 + kc_row;
-        b_off[i] = r < vn ? (uint32_t)(r * p.ldb * 2 + kc_chunk * 16) : OOB;
+        const int r = (8 * wave + i) * 8 + (lane >> 3);
+        b_off[i] = r < vn ? (uint32_t)(r * p.ldb * 2 + kc[i & 1] * 16) : OOB;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-        const int k = 2 * (4 * wave + i) + nn_row_lo;
+        const int k = 2 * (8 * wave + i) + nn_row_lo;
         const int c = (lane & 31) ^ swz_n(k);
         b_off[i] = (uint32_t)(k * p.ldb * 2 + c * 16);
       }
     }
 
-    // Issue the LDS-DMA loads of K step ks into ring slot `slot`.  Steps at
-    // or past nk load nothing (every offset is out of range, so the slot is
-    // zero-filled): the loop keeps a fixed number of loads in flight.
-    auto issue = [&](int ks, int slot) {
+    // LDS-DMA loads of K step ks into ring slot `slot`: the A tile (half 0)
+    // or the B tile (half 1).  Steps at or past nk load nothing (every offset
+    // is out of range, so the slot is zero-filled): the loop keeps a fixed
+    // pattern of loads in flight.  `between(t)` runs before load t.
+    auto refill = [&](int ks, int slot, int half, auto&& between) {
       const int k0 = ks * BK;
-      const bool kin = k0 + (kc_chunk << 3) < p.K;
-      const uint32_t sa = lds0 + slot * STAGE_BYTES + (4 * wave) * 1024;
+      const uint32_t base = lds0 + slot * STAGE_BYTES + half * A_BYTES + (8 * wave) * 1024;
+      if (half == 0 || LAYOUT == NT) {
+        const i32x4 r = half == 0 ? rs_a : rs_b;
 #pragma unroll
-      for (int i = 0; i < DMA_PER_OPERAND; ++i)
-        dma16(rs_a, kin ? a_off[i] + (uint32_t)(k0 * 2) : OOB, sa + i * 1024);
-      const uint32_t sb = sa + A_BYTES;
-      if (LAYOUT == NT) {
-#pragma unroll
-        for (int i = 0; i < DMA_PER_OPERAND; ++i)
-          dma16(rs_b, kin ? b_off[i] + (uint32_t)(k0 * 2) : OOB, sb + i * 1024);
+        for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+          between(i);
+          const bool kin = k0 + (kc[i & 1] << 3) < p.K;
+          const uint32_t off = half == 0 ? a_off[i] : b_off[i];
+          dma16(r, kin ? off + (uint32_t)(k0 * 2) : OOB, base + i * 1024);
+          fence();
+        }
       } else {
         // rebase on this K step: rows past K, and row K-1 past N, read zeros
         const int vk = min(BK, p.K - k0);
@@ -262,19 +274,22 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
             vk > 0 ? (uint32_t)(((int64_t)(vk - 1) * p.ldb + (p.N - n0)) * 2) : 0u);
 #pragma unroll
         for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-          const int k = 2 * (4 * wave + i) + nn_row_lo;
-          dma16(r, k < vk ? b_off[i] : OOB, sb + i * 1024);
+          between(i);
+          const int k = 2 * (8 * wave + i) + nn_row_lo;
+          dma16(r, k < vk ? b_off[i] : OOB, base + i * 1024);
+          fence();
         }
       }
     };
+    auto nothing = [](int) {};
 
     auto read_frags = [&](int slot, int s, Frags& F) {
       const char* base = smem + slot * STAGE_BYTES;
 #pragma unroll
-      for (int i = 0; i < MI; ++i) F.a[i] = *(const u32x4*)(base + fa[s] + i * 2048);
+      for (int i = 0; i < MI; ++i) F.a[i] = *(const u32x4*)(base + fa[s] + i * 4096);
       if (LAYOUT == NT) {
 #pragma unroll
-        for (int j = 0; j < NI; ++j) F.b[j] = *(const u32x4*)(base + fb[s] + j * 2048);
+        for (int j = 0; j < NI; ++j) F.b[j] = *(const u32x4*)(base + fb[s] + j * 4096);
       } else {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
@@ -293,48 +308,60 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
 
     // Operand order (B fragment first) leaves each lane holding one row of D
     // and four consecutive columns per register quad.
+    auto mfma_at = [&](const Frags& F, int t) {
+      acc[t / NI][t % NI] = mfma<T>(F.b[t % NI], F.a[t / NI], acc[t / NI][t % NI]);
+    };
     auto mfmas = [&](const Frags& F) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = mfma<T>(F.b[j], F.a[i], acc[i][j]);
+      for (int t = 0; t < MI * NI; ++t) mfma_at(F, t);
     };
-    constexpr int READS = MI + (LAYOUT == NT ? NI : 2 * NI);
-    auto interleave = [&]() {
-      // one LDS read between MFMAs, the rest of the MFMAs after
-#pragma unroll
-      for (int i = 0; i < READS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, (MI * NI) / READS, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - READS * ((MI * NI) / READS), 0);
+    // MFMAs on F with the 8 loads of one refill half between pairs of them
+    auto mfmas_with_refill = [&](const Frags& F, int ks, int slot, int half) {
+      refill(ks, slot, half, [&](int i) {
+        mfma_at(F, 2 * i);
+        mfma_at(F, 2 * i + 1);
+        fence();
+      });
     };
 
-    // The ring: stage ks lives in slot ks % STAGES.  At the top of step ks the
-    // loads of steps ks+1 .. ks+STAGES-2 may still be in flight, step ks has
-    // landed, and F0 holds the first half of stage ks.
+    // The ring: stage ks lives in slot ks % 2.  Entering step ks, stage ks has
+    // landed, the B half of stage ks+1 is still to be issued, and F0 holds
+    // substep 0 of stage ks.  Substeps 0..2 read the next substep's fragments
+    // up front and then run the MFMAs; the barrier sits before substep 3, once
+    // every read of stage ks is done, so stage ks's slot can be refilled
+    // (with stage ks+2) while substep 3 and the next step's substep 0 run.
     Frags F0, F1;
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st) issue(st, st);
-    wait_vm_barrier<(STAGES - 2) * DMA_PER_STAGE>();
+    refill(0, 0, 0, nothing);
+    refill(0, 0, 1, nothing);
+    refill(1, 1, 0, nothing);
+    wait_vm_barrier<DMA_PER_OPERAND>();
     read_frags(0, 0, F0);
 
     for (int ks = 0; ks < nk; ++ks) {
-      const int slot = ks % STAGES;
-      // refill the slot every wave finished reading before the last barrier
-      issue(ks + STAGES - 1, (ks + STAGES - 1) % STAGES);
-      // first half of the stage: MFMAs on F0 while F1 is read
+      const int slot = ks & 1;
+      // substep 0 (+ the B half of stage ks+1)
       read_frags(slot, 1, F1);
-      mfmas(F0);
-      interleave();
-      // stage ks+1 has landed for every wave, and every wave has finished
-      // reading stage ks, so its slot may be refilled from the next step on
-      wait_vm_barrier<(STAGES - 2) * DMA_PER_STAGE>();
-      // second half: MFMAs on F1 while the first half of stage ks+1 is read
-      // (after the last step this reads a zero-filled slot, unused)
-      read_frags((ks + 1) % STAGES, 0, F0);
+      fence();
+      mfmas_with_refill(F0, ks + 1, slot ^ 1, 1);
+      // substep 1
+      read_frags(slot, 2, F0);
+      fence();
       mfmas(F1);
-      interleave();
+      fence();
+      // substep 2
+      read_frags(slot, 3, F1);
+      fence();
+      mfmas(F0);
+      fence();
+      // stage ks+1 has landed for every wave, and every wave has finished
+      // reading stage ks
+      wait_vm_barrier<0>();
+      fence();
+      // substep 3 (+ the A half of stage ks+2 into the freed slot); past the
+      // last step this reads and loads zero-filled data, unused
+      read_frags(slot ^ 1, 0, F0);
+      fence();
+      mfmas_with_refill(F1, ks + 2, slot, 0);
     }
 
     wait_vm_barrier<0>();  // every wave is done with the ring; reuse it for staging
