@@ -158,7 +158,7 @@ def main():
         traffic = None
 
     out = {
-        "metric": "TFLOP/s and % of dense FP16 MFMA peak, D=A.B^T FP16 at M=N=K=4096"
+        "metric": "TFLOP/s and % of dense FP16 MFMA peak, D=A\u00b7B\u1d40 FP16 at M=N=K=4096"
                   if w.name == "square_nt" else "TFLOP/s, %s" % w.name,
         "value": round(value, 2),
         "unit": "TFLOP/s",
