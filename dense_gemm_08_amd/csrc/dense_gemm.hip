@@ -282,22 +282,68 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       }
     };
     auto nothing = [](int) {};
-
-    auto read_frags = [&](int slot, int s, Frags& F) {
-      const char* base = smem + slot * STAGE_BYTES;
-#pragma unroll
-      for (int i = 0; i < MI; ++i) F.a[i] = *(const u32x4*)(base + fa[s] + i * 4096);
-      if (LAYOUT == NT) {
-#pragma unroll
-        for (int j = 0; j < NI; ++j) F.b[j] = *(const u32x4*)(base + fb[s] + j * 4096);
+    // One refill half issued load by load (for interleaving with MFMAs): the
+    // descriptor and masks are set up once, then load(i) issues load i.
+    struct Half {
+      i32x4 r;
+      uint32_t base;
+      int k0, vk;
+    };
+    auto half_setup = [&](int ks, int slot, int half) {
+      Half h;
+      h.k0 = ks * BK;
+      h.base = lds0 + slot * STAGE_BYTES + half * A_BYTES + (8 * wave) * 1024;
+      h.vk = 0;
+      if (half == 0) {
+        h.r = rs_a;
+      } else if (LAYOUT == NT) {
+        h.r = rs_b;
       } else {
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          const u32x2 lo = read_tr(base + fbn[j] + (s * 16) * 512);
-          const u32x2 hi = read_tr(base + fbn[j] + (s * 16 + 4) * 512);
-          F.b[j] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
-        }
+        // rebase on this K step: rows past K, and row K-1 past N, read zeros
+        h.vk = min(BK, p.K - h.k0);
+        h.r = make_rsrc(p.B + (h.vk > 0 ? (int64_t)h.k0 * p.ldb + n0 : 0),
+                        h.vk > 0 ? (uint32_t)(((int64_t)(h.vk - 1) * p.ldb + (p.N - n0)) * 2) : 0u);
       }
+      return h;
+    };
+    auto refill_one = [&](const Half& h, int half, int i) {
+      if (half == 0 || LAYOUT == NT) {
+        const bool kin = h.k0 + (kc[i & 1] << 3) < p.K;
+        const uint32_t off = half == 0 ? a_off[i] : b_off[i];
+        dma16(h.r, kin ? off + (uint32_t)(h.k0 * 2) : OOB, h.base + i * 1024);
+      } else {
+        const int k = 2 * (8 * wave + i) + nn_row_lo;
+        dma16(h.r, k < h.vk ? b_off[i] : OOB, h.base + i * 1024);
+      }
+      fence();
+    };
+
+    // Fragment reads of k-substep s of the stage in slot `slot`, one LDS
+    // instruction at a time: item f < MI reads A fragment f; the rest read the
+    // B fragments (NT: one ds_read_b128 each; NN: two transposing reads each).
+    constexpr int READS = MI + (LAYOUT == NT ? NI : 2 * NI);
+    auto read_item = [&](int slot, int s, Frags& F, int f) {
+      const char* base = smem + slot * STAGE_BYTES;
+      if (f < MI) {
+        F.a[f] = *(const u32x4*)(base + fa[s] + f * 4096);
+      } else if (LAYOUT == NT) {
+        const int j = f - MI;
+        F.b[j] = *(const u32x4*)(base + fb[s] + j * 4096);
+      } else {
+        const int j = (f - MI) >> 1, h = (f - MI) & 1;
+        const u32x2 v = read_tr(base + fbn[j] + (s * 16 + 4 * h) * 512);
+        F.b[j][2 * h] = v[0];
+        F.b[j][2 * h + 1] = v[1];
+      }
+    };
+    auto read_frags = [&](int slot, int s, Frags& F) {
+#pragma unroll
+      for (int f = 0; f < READS; ++f) read_item(slot, s, F, f);
+    };
+    // the reads to issue before MFMA pair q (of 8), spread evenly
+    auto reads_before_pair = [&](int slot, int s, Frags& F, int q) {
+#pragma unroll
+      for (int f = (q * READS) / 8; f < ((q + 1) * READS) / 8; ++f) read_item(slot, s, F, f);
     };
 
     f32x16 acc[MI][NI];
@@ -307,29 +353,61 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       for (int j = 0; j < NI; ++j) acc[i][j] = (f32x16){};
 
     // Operand order (B fragment first) leaves each lane holding one row of D
-    // and four consecutive columns per register quad.
+    // and four consecutive columns per register quad.  Consecutive MFMAs
+    // share a B fragment (A.B^T) or an A fragment (A.B): the faster order of
+    // each, measured.
     auto mfma_at = [&](const Frags& F, int t) {
-      acc[t / NI][t % NI] = mfma<T>(F.b[t % NI], F.a[t / NI], acc[t / NI][t % NI]);
+      const int i = LAYOUT == NT ? t % MI : t / NI;
+      const int j = LAYOUT == NT ? t / MI : t % NI;
+      acc[i][j] = mfma<T>(F.b[j], F.a[i], acc[i][j]);
     };
-    auto mfmas = [&](const Frags& F) {
+    // One substep: the 16 MFMAs on F in pairs; before each pair, its share
+    // of the next substep's reads into G (slot gslot, substep gs) and, when a
+    // refill is given, one LDS-DMA load of it.  `upfront` issues all of G's
+    // reads before the first pair instead (measured faster for the A.B layout
+    // in the substeps that also carry refill loads, whose twelve transposing
+    // and plain reads per substep then stay clear of the loads).
+    auto substep = [&](const Frags& F, Frags& G, int gslot, int gs, bool upfront, auto&& dma) {
+      if (upfront) {
+        read_frags(gslot, gs, G);
+        fence();
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (!upfront) reads_before_pair(gslot, gs, G, q);
+        mfma_at(F, 2 * q);
+        mfma_at(F, 2 * q + 1);
+        fence();
+        dma(q);
+      }
+    };
+    // A substep without refill loads for the A.B layout: the reads and MFMAs
+    // form one scheduling region whose order is set by sched_group_barrier
+    // (a read, then two MFMAs and a read, seven times, then two MFMAs; the
+    // remaining reads are placed by the compiler).
+    auto substep_nn = [&](const Frags& F, Frags& G, int gslot, int gs) {
+      read_frags(gslot, gs, G);
 #pragma unroll
       for (int t = 0; t < MI * NI; ++t) mfma_at(F, t);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int u = 0; u < 7; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      fence();
     };
-    // MFMAs on F with the 8 loads of one refill half between pairs of them
-    auto mfmas_with_refill = [&](const Frags& F, int ks, int slot, int half) {
-      refill(ks, slot, half, [&](int i) {
-        mfma_at(F, 2 * i);
-        mfma_at(F, 2 * i + 1);
-        fence();
-      });
-    };
+    auto no_dma = [](int) {};
+    constexpr bool kUpfront = LAYOUT == NN;
 
     // The ring: stage ks lives in slot ks % 2.  Entering step ks, stage ks has
     // landed, the B half of stage ks+1 is still to be issued, and F0 holds
-    // substep 0 of stage ks.  Substeps 0..2 read the next substep's fragments
-    // up front and then run the MFMAs; the barrier sits before substep 3, once
-    // every read of stage ks is done, so stage ks's slot can be refilled
-    // (with stage ks+2) while substep 3 and the next step's substep 0 run.
+    // substep 0 of stage ks.  In each substep the LDS reads of the next
+    // substep's fragments are spread between the MFMA pairs.  The barrier sits
+    // before substep 3, once every read of stage ks is done, so stage ks's
+    // slot can be refilled (with stage ks+2) while substep 3 and the next
+    // step's substep 0 run; the refill loads also sit between MFMA pairs.
     Frags F0, F1;
     refill(0, 0, 0, nothing);
     refill(0, 0, 1, nothing);
@@ -340,28 +418,24 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     for (int ks = 0; ks < nk; ++ks) {
       const int slot = ks & 1;
       // substep 0 (+ the B half of stage ks+1)
-      read_frags(slot, 1, F1);
-      fence();
-      mfmas_with_refill(F0, ks + 1, slot ^ 1, 1);
-      // substep 1
-      read_frags(slot, 2, F0);
-      fence();
-      mfmas(F1);
-      fence();
-      // substep 2
-      read_frags(slot, 3, F1);
-      fence();
-      mfmas(F0);
-      fence();
+      const Half hb = half_setup(ks + 1, slot ^ 1, 1);
+      substep(F0, F1, slot, 1, kUpfront, [&](int q) { refill_one(hb, 1, q); });
+      // substeps 1 and 2
+      if (LAYOUT == NT) {
+        substep(F1, F0, slot, 2, false, no_dma);
+        substep(F0, F1, slot, 3, false, no_dma);
+      } else {
+        substep_nn(F1, F0, slot, 2);
+        substep_nn(F0, F1, slot, 3);
+      }
       // stage ks+1 has landed for every wave, and every wave has finished
       // reading stage ks
       wait_vm_barrier<0>();
       fence();
       // substep 3 (+ the A half of stage ks+2 into the freed slot); past the
       // last step this reads and loads zero-filled data, unused
-      read_frags(slot ^ 1, 0, F0);
-      fence();
-      mfmas_with_refill(F1, ks + 2, slot, 0);
+      const Half ha = half_setup(ks + 2, slot, 0);
+      substep(F1, F0, slot ^ 1, 0, kUpfront, [&](int q) { refill_one(ha, 0, q); });
     }
 
     wait_vm_barrier<0>();  // every wave is done with the ring; reuse it for staging
