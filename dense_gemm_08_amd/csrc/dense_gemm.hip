@@ -140,12 +140,20 @@ __device__ __forceinline__ f32x16 mfma<__bf16>(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Round two floats to the output type (round-to-nearest-even) and pack them.
+// Round two floats to the output type (round-to-nearest-even) and pack them
+// (one v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <typename T>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  T l = (T)lo, h = (T)hi;
-  uint16_t lb = __builtin_bit_cast(uint16_t, l), hb = __builtin_bit_cast(uint16_t, h);
-  return (uint32_t)lb | ((uint32_t)hb << 16);
+__device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <>
+__device__ __forceinline__ uint32_t pack2<_Float16>(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<__bf16>(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Transposing LDS read: within each 16-lane block, lane i receives element
@@ -443,6 +451,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     // Epilogue: per 32-row block, round, stage 32 x 128 outputs of this wave
     // in LDS (chunk-swizzled rows of 256 B), then store 16-byte row chunks.
     char* stg = smem + wave * (32 * 256);
+    const bool interior = p.d_vec && vm == BM && vn == BN;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -461,21 +470,32 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       }
       const int row0 = m0 + wm * WTM + i * 32;
       const int col0 = n0 + wn * WTN;
+      if (interior) {
+        // the whole tile is inside D and its rows are 16-byte aligned
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int rr = t * 4 + (lane >> 4);
-        const int cc = lane & 15;
-        const u32x4 v = *(const u32x4*)(stg + rr * 256 + ((cc ^ (rr & 15)) << 4));
-        const int row = row0 + rr;
-        const int col = col0 + cc * 8;
-        if (row < p.M && col < p.N) {
-          uint16_t* dst = p.D + (int64_t)row * p.ldd + col;
-          if (p.d_vec && col + 8 <= p.N) {
-            *(u32x4*)dst = v;
-          } else {
+        for (int t = 0; t < 8; ++t) {
+          const int rr = t * 4 + (lane >> 4);
+          const int cc = lane & 15;
+          const u32x4 v = *(const u32x4*)(stg + rr * 256 + ((cc ^ (rr & 15)) << 4));
+          *(u32x4*)(p.D + (int64_t)(row0 + rr) * p.ldd + col0 + cc * 8) = v;
+        }
+      } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (col + e < p.N) dst[e] = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
+        for (int t = 0; t < 8; ++t) {
+          const int rr = t * 4 + (lane >> 4);
+          const int cc = lane & 15;
+          const u32x4 v = *(const u32x4*)(stg + rr * 256 + ((cc ^ (rr & 15)) << 4));
+          const int row = row0 + rr;
+          const int col = col0 + cc * 8;
+          if (row < p.M && col < p.N) {
+            uint16_t* dst = p.D + (int64_t)row * p.ldd + col;
+            if (p.d_vec && col + 8 <= p.N) {
+              *(u32x4*)dst = v;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (col + e < p.N) dst[e] = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
+            }
           }
         }
       }
