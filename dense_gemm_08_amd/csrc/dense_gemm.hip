@@ -29,6 +29,7 @@
 //     skipped (the pages' shapes all divide the tiles; this is our reading).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -81,6 +82,12 @@ struct Params {
   int lda, ldb, ldd;
   int tiles_m, tiles_n, group_m, num_tasks, num_xcds;
   int d_vec;  // D rows are 16-byte aligned (16-byte stores allowed)
+  // split-K: each task is (tile, split); the split covers K steps
+  // [split * split_steps, min(nk, (split + 1) * split_steps)) and writes its
+  // FP32 partial tile (row-major BM x BN) to ws at index split * tiles +
+  // tile_row * tiles_n + tile_col
+  int splits, split_steps, tiles;
+  float* ws;
 };
 
 // LDS layouts.
@@ -177,7 +184,7 @@ struct Frags {
   u32x4 b[NI];
 };
 
-template <typename T, int LAYOUT>
+template <typename T, int LAYOUT, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const uint32_t lds0 = lds_addr(smem);
@@ -191,7 +198,12 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
 
   for (int task = slot0; task < p.num_tasks; task += gridDim.x) {
     int tm, tn;
-    tile_of_task(task, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    const int tile = SPLIT ? task % p.tiles : task;
+    const int split = SPLIT ? task / p.tiles : 0;
+    tile_of_task(tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    // this task's K steps
+    const int kbeg = split * p.split_steps;
+    const int kend = SPLIT ? min(nk, kbeg + p.split_steps) : nk;
     const int m0 = tm * BM;
     const int n0 = tn * BN;
     const int vm = min(BM, p.M - m0);  // valid rows of the A tile
@@ -258,11 +270,11 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     }
 
     // LDS-DMA loads of K step ks into ring slot `slot`: the A tile (half 0)
-    // or the B tile (half 1).  Steps at or past nk load nothing (every offset
-    // is out of range, so the slot is zero-filled): the loop keeps a fixed
-    // pattern of loads in flight.  `between(t)` runs before load t.
+    // or the B tile (half 1).  Steps at or past kend load nothing (every
+    // offset is out of range, so the slot is zero-filled): the loop keeps a
+    // fixed pattern of loads in flight.  `between(t)` runs before load t.
     auto refill = [&](int ks, int slot, int half, auto&& between) {
-      const int k0 = ks * BK;
+      const int k0 = ks < kend ? ks * BK : p.K;
       const uint32_t base = lds0 + slot * STAGE_BYTES + half * A_BYTES + (8 * wave) * 1024;
       if (half == 0 || LAYOUT == NT) {
         const i32x4 r = half == 0 ? rs_a : rs_b;
@@ -299,7 +311,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     };
     auto half_setup = [&](int ks, int slot, int half) {
       Half h;
-      h.k0 = ks * BK;
+      h.k0 = ks < kend ? ks * BK : p.K;
       h.base = lds0 + slot * STAGE_BYTES + half * A_BYTES + (8 * wave) * 1024;
       h.vk = 0;
       if (half == 0) {
@@ -417,14 +429,14 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     // slot can be refilled (with stage ks+2) while substep 3 and the next
     // step's substep 0 run; the refill loads also sit between MFMA pairs.
     Frags F0, F1;
-    refill(0, 0, 0, nothing);
-    refill(0, 0, 1, nothing);
-    refill(1, 1, 0, nothing);
+    refill(kbeg, 0, 0, nothing);
+    refill(kbeg, 0, 1, nothing);
+    refill(kbeg + 1, 1, 0, nothing);
     wait_vm_barrier<DMA_PER_OPERAND>();
     read_frags(0, 0, F0);
 
-    for (int ks = 0; ks < nk; ++ks) {
-      const int slot = ks & 1;
+    for (int ks = kbeg; ks < kend; ++ks) {
+      const int slot = (ks - kbeg) & 1;
       // substep 0 (+ the B half of stage ks+1)
       const Half hb = half_setup(ks + 1, slot ^ 1, 1);
       substep(F0, F1, slot, 1, kUpfront, [&](int q) { refill_one(hb, 1, q); });
@@ -447,6 +459,27 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     }
 
     wait_vm_barrier<0>();  // every wave is done with the ring; reuse it for staging
+
+    if (SPLIT) {
+      // FP32 partial tile, row-major 256 x 256: lane holds row lr of each
+      // 32-row block and columns j*32 + 8q + 4*lh .. +3 (16 contiguous bytes)
+      float* w = p.ws + (size_t)(split * p.tiles + tm * p.tiles_n + tn) * (BM * BN) +
+                 (size_t)(wm * WTM + lr) * BN + wn * WTN + 4 * lh;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                         acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *(float4*)(w + i * 32 * BN + j * 32 + 8 * q) = v;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      continue;
+    }
 
     // Epilogue: per 32-row block, round, stage 32 x 128 outputs of this wave
     // in LDS (chunk-swizzled rows of 256 B), then store 16-byte row chunks.
@@ -502,6 +535,41 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vm_barrier<0>();  // staging reads done before the next tile refills the ring
+  }
+}
+
+// Sum of the split-K partials of every output element in split order 0, 1,
+// ... (a fixed order: results are reproducible), rounded once to the output
+// type.  One thread per 8 consecutive columns of a row.
+template <typename T>
+__global__ __launch_bounds__(256) void split_reduce(Params p) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int cols8 = (p.N + 7) / 8;
+  if (gid >= (int64_t)p.M * cols8) return;
+  const int row = (int)(gid / cols8);
+  const int col = (int)(gid % cols8) * 8;
+  const int tm = row / BM, tn = col / BN;
+  const int tile = tm * p.tiles_n + tn;  // partials are stored by tile position
+  const float* w = p.ws + (size_t)tile * (BM * BN) + (size_t)(row - tm * BM) * BN + (col - tn * BN);
+  float s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = 0.0f;
+  for (int k = 0; k < p.splits; ++k) {
+    const float4 a = *(const float4*)(w + (size_t)k * p.tiles * (BM * BN));
+    const float4 b = *(const float4*)(w + (size_t)k * p.tiles * (BM * BN) + 4);
+    s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+    s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+  }
+  u32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = pack2<T>(s[2 * e], s[2 * e + 1]);
+  uint16_t* dst = p.D + (int64_t)row * p.ldd + col;
+  if (p.d_vec && col + 8 <= p.N) {
+    *(u32x4*)dst = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (col + e < p.N) dst[e] = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
   }
 }
 
@@ -624,6 +692,21 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
   out[5] = grid;
   out[6] = choose_group_m(tiles_m, tiles_n, grid);
   out[7] = THREADS;
+  // split-K when the tiles would leave most CUs idle and K is long: at most
+  // one unit per CU, at least 4 K steps per unit
+  const int64_t nk = (K + BK - 1) / BK;
+  int64_t splits = 1, steps = nk;
+  if (tasks * 2 <= num_cus && nk >= 8) {
+    const int64_t by_cus = num_cus / tasks, by_k = nk / 4;
+    const int64_t sp = by_cus < by_k ? by_cus : by_k;
+    if (sp >= 2) {
+      steps = (nk + sp - 1) / sp;
+      splits = (nk + steps - 1) / steps;
+    }
+  }
+  out[8] = splits;
+  out[9] = steps;
+  if (splits > 1) out[5] = tasks * splits;
   return DENSE_GEMM_OK;
 }
 
@@ -640,9 +723,20 @@ static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int
   DeviceInfo info;
   st = device_info(&info);
   if (st != DENSE_GEMM_OK) return st;
-  int64_t plan[8];
+  int64_t plan[10];
   st = dense_gemm_plan(LAYOUT, M, N, K, info.cus, plan);
   if (st != DENSE_GEMM_OK) return st;
+  // DENSE_GEMM_SPLITK=off disables split-K; =<n> forces n splits (testing)
+  if (const char* e = getenv("DENSE_GEMM_SPLITK")) {
+    const int64_t nk = (K + BK - 1) / BK, tasks = plan[3] * plan[4];
+    int64_t want = strcmp(e, "off") == 0 ? 1 : atoll(e);
+    if (want >= 1 && nk >= 1) {
+      if (want > nk) want = nk;
+      plan[9] = (nk + want - 1) / want;
+      plan[8] = (nk + plan[9] - 1) / plan[9];
+      plan[5] = plan[8] > 1 ? tasks * plan[8] : (tasks < info.cus ? tasks : info.cus);
+    }
+  }
   Params p;
   p.A = (const uint16_t*)A;
   p.B = (const uint16_t*)B;
@@ -659,7 +753,32 @@ static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int
   p.num_tasks = (int)(plan[3] * plan[4]);
   p.num_xcds = 8;
   p.d_vec = (((uintptr_t)D & 15) == 0 && (ldd & 7) == 0) ? 1 : 0;
-  hipLaunchKernelGGL((gemm_kernel<T, LAYOUT>), dim3((unsigned)plan[5]), dim3(THREADS), 0, stream, p);
+  p.tiles = p.num_tasks;
+  p.splits = 1;
+  p.split_steps = 0;
+  p.ws = nullptr;
+  if (plan[8] > 1) {
+    // FP32 partials in a stream-ordered workspace, summed by a second kernel
+    const size_t bytes = (size_t)plan[8] * p.tiles * BM * BN * sizeof(float);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, bytes, stream) == hipSuccess && ws != nullptr) {
+      p.splits = (int)plan[8];
+      p.split_steps = (int)plan[9];
+      p.ws = (float*)ws;
+      p.num_tasks = p.tiles * p.splits;
+      hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>), dim3((unsigned)p.num_tasks), dim3(THREADS),
+                         0, stream, p);
+      const int64_t threads = (int64_t)p.M * ((p.N + 7) / 8);
+      hipLaunchKernelGGL((split_reduce<T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                         stream, p);
+      const hipError_t launch = hipGetLastError();
+      (void)hipFreeAsync(ws, stream);
+      return launch == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
+    }
+    (void)hipGetLastError();  // no workspace: run unsplit
+  }
+  hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false>), dim3((unsigned)(p.num_tasks < info.cus ? p.num_tasks : info.cus)),
+                     dim3(THREADS), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return DENSE_GEMM_LAUNCH_FAILED;
   return DENSE_GEMM_OK;
 }

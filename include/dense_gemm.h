@@ -37,12 +37,22 @@
  * arguments return DENSE_GEMM_MISALIGNED.  M and N are otherwise arbitrary
  * (ragged edges are masked), and K need not be a multiple of the tile depth.
  *
+ * Split-K.  When the output has too few tiles to occupy the GPU and K is
+ * long (see dense_gemm_plan), the K dimension is split: each part writes FP32
+ * partial tiles to a workspace and a second kernel sums them in a fixed order
+ * (results stay reproducible) and rounds once.  The workspace is taken with
+ * hipMallocAsync on `stream` and returned with hipFreeAsync on the same
+ * stream (stream-ordered, served by the device's default memory pool); if it
+ * cannot be had, the call runs unsplit.  The environment variable
+ * DENSE_GEMM_SPLITK=off disables split-K, DENSE_GEMM_SPLITK=<n> forces n
+ * parts (for testing and measurement).
+ *
  * Ownership and concurrency.  The caller owns every buffer and the stream.
- * The library allocates no device memory, keeps no pointers after a call
- * returns, and caches only per-device properties (thread-safe).  A, B and D
- * must not overlap.  Calls are asynchronous and ordered on `stream` (0 is
- * the null stream); the caller synchronizes.  Calls on different streams
- * may run concurrently.
+ * The library keeps no pointers after a call returns and caches only
+ * per-device properties (thread-safe); apart from the split-K workspace
+ * above it allocates no device memory.  A, B and D must not overlap.  Calls
+ * are asynchronous and ordered on `stream` (0 is the null stream); the caller
+ * synchronizes.  Calls on different streams may run concurrently.
  *
  * Errors.  Every entry point validates its arguments before launching and
  * returns a dense_gemm_status; on any error nothing is launched and D is
@@ -116,8 +126,11 @@ dense_gemm_status dense_gemm_tile_of_task(int64_t task, int64_t tiles_m, int64_t
                                           int64_t group_m, int64_t* tile_m, int64_t* tile_n);
 
 /* The launch plan for a problem on a device with num_cus compute units.
- * Writes 8 values to out: BM, BN, BK, tiles_m, tiles_n, grid (workgroups),
- * group_m, threads per workgroup. */
+ * Writes 10 values to out: BM, BN, BK, tiles_m, tiles_n, grid (workgroups of
+ * the GEMM kernel), group_m, threads per workgroup, the number of K splits
+ * (1: none) and the K steps (of BK) per split.  Split-K is chosen when
+ * 2 * tiles <= num_cus and K spans at least 8 steps: as many parts as keep
+ * one part per CU and at least 4 steps per part. */
 dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K,
                                   int64_t num_cus, int64_t* out);
 

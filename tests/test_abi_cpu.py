@@ -162,15 +162,43 @@ def test_xcd_slot_is_a_bijection(grid):
 
 def test_plan_for_the_workloads():
     lib = binding.load_library()
-    out = (ctypes.c_int64 * 8)()
+    out = (ctypes.c_int64 * 10)()
     gold = golden()
     assert lib.dense_gemm_plan(NT, 4096, 4096, 4096, 256, out) == S.OK
-    BM, BN, BK, tm, tn, grid, gm, threads = list(out)
+    BM, BN, BK, tm, tn, grid, gm, threads, splits, steps = list(out)
     assert tm * tn * BM * BN >= 4096 * 4096
     assert grid == min(tm * tn, 256)
+    assert splits == 1  # 256 tiles fill the GPU
     # the page's own tiling of this shape (128 x 128) gives 1024 tiles
     assert (4096 // 128) ** 2 == gold["tiles_4096sq_128x128"]
     assert gold["ksteps_5120_bk64"] == 5120 // 64
     assert lib.dense_gemm_plan(NN, 8192, 17408, 5120, 256, out) == S.OK
     assert out[5] <= 256
     assert lib.dense_gemm_plan(NT, 0, 5, 5, 256, out) == S.BAD_ARG
+
+
+def test_plan_split_k():
+    lib = binding.load_library()
+    out = (ctypes.c_int64 * 10)()
+    # one 128 x 128 tile with K = 4096 (64 steps of 64): 16 parts of 4 steps
+    assert lib.dense_gemm_plan(NT, 128, 128, 4096, 256, out) == S.OK
+    assert (out[8], out[9], out[5]) == (16, 4, 16)
+    # K too short to split
+    assert lib.dense_gemm_plan(NT, 128, 128, 448, 256, out) == S.OK
+    assert out[8] == 1
+    # 128 tiles leave half of 256 CUs idle: two parts
+    assert lib.dense_gemm_plan(NN, 2048, 4096, 8192, 256, out) == S.OK
+    assert (out[8], out[9], out[5]) == (2, 64, 256)
+    # more tiles than half the CUs: no split
+    assert lib.dense_gemm_plan(NN, 2304, 4096, 8192, 256, out) == S.OK
+    assert out[8] == 1
+    # 3000 x 5000 x 4000: 240 tiles, no split
+    assert lib.dense_gemm_plan(NT, 3000, 5000, 4000, 256, out) == S.OK
+    assert out[8] == 1
+    # every part covers whole steps and the parts cover K exactly once
+    for M, N, K in [(600, 520, 712), (128, 128, 4000), (1000, 1000, 8192), (256, 256, 5120)]:
+        assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK
+        tiles, nk, sp, st = out[3] * out[4], -(-K // 64), out[8], out[9]
+        if sp > 1:
+            assert (sp - 1) * st < nk <= sp * st and st >= 4 and tiles * sp <= 256
+            assert out[5] == tiles * sp

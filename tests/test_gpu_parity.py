@@ -51,8 +51,18 @@ REDUCED = [
 ]
 
 
+@pytest.fixture(params=["auto", "off"])
+def splitk(request, monkeypatch):
+    """Run with the library's own split-K choice, and with split-K disabled."""
+    if request.param == "off":
+        monkeypatch.setenv("DENSE_GEMM_SPLITK", "off")
+    else:
+        monkeypatch.delenv("DENSE_GEMM_SPLITK", raising=False)
+    return request.param
+
+
 @pytest.mark.parametrize("name,M,N,K", REDUCED)
-def test_workload_reduced_full_check(name, M, N, K):
+def test_workload_reduced_full_check(name, M, N, K, splitk):
     w = inputs.WORKLOADS[name]
     A, B = inputs.make_operands(w, M=M, N=N, K=K)
     D, st = _gpu.gemm(w.layout, w.fmt, A, B, M, N, K)
@@ -88,7 +98,7 @@ def test_workload_full_size_sampled(name):
 # ------------------------------------------------- bitwise special cases --
 
 @pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16"), ("nt", "bf16"), ("nn", "f16")])
-def test_small_integers_exact(layout, fmt):
+def test_small_integers_exact(layout, fmt, splitk):
     # entries in {-3..3}: every FP32 partial sum is an exact integer, so the
     # result is the exactly rounded integer sum (sums up to 9K exceed the
     # FP16/BF16 integer range, so this pins round-to-nearest-even)
@@ -140,8 +150,28 @@ def test_power_of_two_scaling():
     assert (d4[normal] == d1[normal] * 4.0).all()
 
 
-def test_k_tail_equals_zero_padding():
-    # K = 4000 (a partial last K step) against the same data zero-padded to 4096
+@pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
+@pytest.mark.parametrize("parts", ["2", "3", "7", "64"])
+def test_forced_split_k(layout, fmt, parts, monkeypatch):
+    # split-K forced on shapes of several tiles, a ragged K tail and parts of
+    # unequal length; the summation order is fixed, so a rerun is bitwise equal
+    monkeypatch.setenv("DENSE_GEMM_SPLITK", parts)
+    w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 71)
+    M, N, K = 300, 264, 1000
+    A, B = inputs.make_operands(w, M=M, N=N, K=K)
+    D, st = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    assert st == status().OK
+    check_full(layout, fmt, A, B, M, N, K, D)
+    D2, _ = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    assert (D == D2).all()
+
+
+@pytest.mark.parametrize("parts", ["off", "4"])
+def test_k_tail_equals_zero_padding(parts, monkeypatch):
+    # K = 4000 (a partial last K step) against the same data zero-padded to
+    # 4096, with the same accumulation structure (unsplit, or 4 parts of 16
+    # steps: the padded run's last part only adds zeros)
+    monkeypatch.setenv("DENSE_GEMM_SPLITK", parts)
     w = inputs.WORKLOADS["ragged_nt"]
     M, N, K, Kp = 272, 264, 4000, 4096
     A, B = inputs.make_operands(w, M=M, N=N, K=K)
