@@ -67,7 +67,6 @@ constexpr int B_BYTES = BN * BK * 2;           // 32 KiB
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;  // 128 KiB of the 160 KiB per CU
 constexpr int DMA_PER_OPERAND = A_BYTES / (THREADS * 16);  // 16-byte loads per thread
-constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPERAND;
 constexpr uint32_t OOB = 0x80000000u;          // a buffer offset past every range
 
 static_assert(DMA_PER_OPERAND == 8, "each wave fills 8 KiB of each operand per stage");
@@ -117,13 +116,18 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 
 // 16-byte global -> LDS copy for every lane of the wave: lane L's 16 bytes at
 // buffer offset `off` land at LDS address m0 + 16 L.  Offsets at or past the
-// descriptor's range write zeros.
+// descriptor's range write zeros.  The asm sets m0 itself; the clobber tells
+// the compiler, which warns that m0 is reserved (it keeps no value in m0
+// across these statements in this file's kernels), hence the pragma.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t off, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(off), "s"(rsrc), "s"(m0)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Scheduling fence: the compiler may move no instruction across it.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -133,6 +137,11 @@ __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+// Wait for this wave's LDS operations only, then synchronize the workgroup
+// (global stores still in flight keep going).
+__device__ __forceinline__ void wait_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 template <typename T>
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c);
@@ -463,12 +472,15 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     if (SPLIT) {
       // FP32 partial tile, row-major 256 x 256: lane holds row lr of each
       // 32-row block and columns j*32 + 8q + 4*lh .. +3 (16 contiguous bytes)
+      // (32 x 32 blocks wholly outside D are skipped: nothing reads them)
       float* w = p.ws + (size_t)(split * p.tiles + tm * p.tiles_n + tn) * (BM * BN) +
                  (size_t)(wm * WTM + lr) * BN + wn * WTN + 4 * lh;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
+        if (wm * WTM + i * 32 >= vm) break;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
+          if (wn * WTN + j * 32 >= vn) break;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
@@ -534,7 +546,9 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vm_barrier<0>();  // staging reads done before the next tile refills the ring
+    // staging reads done before the next tile refills the ring; the stores
+    // drain while the next tile's first loads are in flight
+    wait_lds_barrier();
   }
 }
 
@@ -551,14 +565,30 @@ __global__ __launch_bounds__(256) void split_reduce(Params p) {
   const int tm = row / BM, tn = col / BN;
   const int tile = tm * p.tiles_n + tn;  // partials are stored by tile position
   const float* w = p.ws + (size_t)tile * (BM * BN) + (size_t)(row - tm * BM) * BN + (col - tn * BN);
+  const size_t stride = (size_t)p.tiles * (BM * BN);  // between the partials of two splits
   float s[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.0f;
-  for (int k = 0; k < p.splits; ++k) {
-    const float4 a = *(const float4*)(w + (size_t)k * p.tiles * (BM * BN));
-    const float4 b = *(const float4*)(w + (size_t)k * p.tiles * (BM * BN) + 4);
-    s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
-    s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+  // eight splits' loads in flight at once, then added in split order
+  constexpr int U = 8;
+  for (int k0 = 0; k0 < p.splits; k0 += U) {
+    float4 a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k0 + u < p.splits) {
+        a[u] = *(const float4*)(w + (k0 + u) * stride);
+        b[u] = *(const float4*)(w + (k0 + u) * stride + 4);
+      } else {
+        a[u] = b[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k0 + u < p.splits) {
+        s[0] += a[u].x; s[1] += a[u].y; s[2] += a[u].z; s[3] += a[u].w;
+        s[4] += b[u].x; s[5] += b[u].y; s[6] += b[u].z; s[7] += b[u].w;
+      }
+    }
   }
   u32x4 v;
 #pragma unroll
