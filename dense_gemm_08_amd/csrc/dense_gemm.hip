@@ -383,52 +383,29 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
 
     // Operand order (B fragment first) leaves each lane holding one row of D
     // and four consecutive columns per register quad.  Consecutive MFMAs
-    // share a B fragment (A.B^T) or an A fragment (A.B): the faster order of
-    // each, measured.
+    // share a B fragment, so the next substep's reads (A fragments first, then
+    // B) arrive in the order its MFMAs need them.
     auto mfma_at = [&](const Frags& F, int t) {
-      const int i = LAYOUT == NT ? t % MI : t / NI;
-      const int j = LAYOUT == NT ? t / MI : t % NI;
+      const int i = t % MI;
+      const int j = t / MI;
       acc[i][j] = mfma<T>(F.b[j], F.a[i], acc[i][j]);
     };
     // One substep: the 16 MFMAs on F in pairs; before each pair, its share
-    // of the next substep's reads into G (slot gslot, substep gs) and, when a
-    // refill is given, one LDS-DMA load of it.  `upfront` issues all of G's
-    // reads before the first pair instead (measured faster for the A.B layout
-    // in the substeps that also carry refill loads, whose twelve transposing
-    // and plain reads per substep then stay clear of the loads).
-    auto substep = [&](const Frags& F, Frags& G, int gslot, int gs, bool upfront, auto&& dma) {
-      if (upfront) {
-        read_frags(gslot, gs, G);
-        fence();
-      }
+    // of the next substep's reads into G (slot gslot, substep gs) and, after
+    // it, one LDS-DMA load of a refill (`dma`).  Spreading the reads keeps
+    // the LDS command queue from filling (a burst of twelve reads per wave for
+    // the A.B layout stalls the MFMA issue behind it).
+    auto substep = [&](const Frags& F, Frags& G, int gslot, int gs, auto&& dma) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        if (!upfront) reads_before_pair(gslot, gs, G, q);
+        reads_before_pair(gslot, gs, G, q);
         mfma_at(F, 2 * q);
         mfma_at(F, 2 * q + 1);
         fence();
         dma(q);
       }
     };
-    // A substep without refill loads for the A.B layout: the reads and MFMAs
-    // form one scheduling region whose order is set by sched_group_barrier
-    // (a read, then two MFMAs and a read, seven times, then two MFMAs; the
-    // remaining reads are placed by the compiler).
-    auto substep_nn = [&](const Frags& F, Frags& G, int gslot, int gs) {
-      read_frags(gslot, gs, G);
-#pragma unroll
-      for (int t = 0; t < MI * NI; ++t) mfma_at(F, t);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-      for (int u = 0; u < 7; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      fence();
-    };
     auto no_dma = [](int) {};
-    constexpr bool kUpfront = LAYOUT == NN;
 
     // The ring: stage ks lives in slot ks % 2.  Entering step ks, stage ks has
     // landed, the B half of stage ks+1 is still to be issued, and F0 holds
@@ -448,15 +425,10 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       const int slot = (ks - kbeg) & 1;
       // substep 0 (+ the B half of stage ks+1)
       const Half hb = half_setup(ks + 1, slot ^ 1, 1);
-      substep(F0, F1, slot, 1, kUpfront, [&](int q) { refill_one(hb, 1, q); });
+      substep(F0, F1, slot, 1, [&](int q) { refill_one(hb, 1, q); });
       // substeps 1 and 2
-      if (LAYOUT == NT) {
-        substep(F1, F0, slot, 2, false, no_dma);
-        substep(F0, F1, slot, 3, false, no_dma);
-      } else {
-        substep_nn(F1, F0, slot, 2);
-        substep_nn(F0, F1, slot, 3);
-      }
+      substep(F1, F0, slot, 2, no_dma);
+      substep(F0, F1, slot, 3, no_dma);
       // stage ks+1 has landed for every wave, and every wave has finished
       // reading stage ks
       wait_vm_barrier<0>();
@@ -464,7 +436,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       // substep 3 (+ the A half of stage ks+2 into the freed slot); past the
       // last step this reads and loads zero-filled data, unused
       const Half ha = half_setup(ks + 2, slot, 0);
-      substep(F1, F0, slot ^ 1, 0, kUpfront, [&](int q) { refill_one(ha, 0, q); });
+      substep(F1, F0, slot ^ 1, 0, [&](int q) { refill_one(ha, 0, q); });
     }
 
     wait_vm_barrier<0>();  // every wave is done with the ring; reuse it for staging
