@@ -365,9 +365,16 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
         F.b[j][2 * h + 1] = v[1];
       }
     };
+    // All reads of a substep in item order.  The fences keep that order: the
+    // loop head then sees the same sequence of outstanding reads from the
+    // prologue as from the loop's back edge, and waits only for the ones the
+    // first MFMAs need.
     auto read_frags = [&](int slot, int s, Frags& F) {
 #pragma unroll
-      for (int f = 0; f < READS; ++f) read_item(slot, s, F, f);
+      for (int f = 0; f < READS; ++f) {
+        read_item(slot, s, F, f);
+        fence();
+      }
     };
     // the reads to issue before MFMA pair q (of 8), spread evenly
     auto reads_before_pair = [&](int slot, int s, Frags& F, int q) {
