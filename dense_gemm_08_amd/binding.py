@@ -26,6 +26,7 @@ class Status(enum.IntEnum):
     LAUNCH_FAILED = 6
     NO_DEVICE = 7
     BAD_ARG = 8
+    NO_MEMORY = 9
 
 
 class DenseGemmError(RuntimeError):

@@ -248,9 +248,12 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     }
 
     // Buffer descriptors for this tile; offsets past the last valid byte read
-    // zeros (rows beyond M for A, rows beyond N for the NT B tile).
+    // zeros (rows beyond M for A, rows beyond N for the NT B tile).  The range
+    // of the last row ends at a whole 8-element chunk: where K is not a
+    // multiple of 8 the operand is a zero-padded copy with ld >= K8.
+    const int K8 = (p.K + 7) & ~7;
     const i32x4 rs_a = make_rsrc(p.A + (int64_t)m0 * p.lda,
-                                 p.K > 0 ? (uint32_t)(((int64_t)(vm - 1) * p.lda + p.K) * 2) : 0u);
+                                 p.K > 0 ? (uint32_t)(((int64_t)(vm - 1) * p.lda + K8) * 2) : 0u);
     i32x4 rs_b = rs_a;
     uint32_t a_off[DMA_PER_OPERAND], b_off[DMA_PER_OPERAND];
     int kc[2];  // logical chunk of this lane for even / odd instruction index
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     }
     if (LAYOUT == NT) {
       rs_b = make_rsrc(p.B + (int64_t)n0 * p.ldb,
-                       p.K > 0 ? (uint32_t)(((int64_t)(vn - 1) * p.ldb + p.K) * 2) : 0u);
+                       p.K > 0 ? (uint32_t)(((int64_t)(vn - 1) * p.ldb + K8) * 2) : 0u);
 #pragma unroll
       for (int i = 0; i < DMA_PER_OPERAND; ++i) {
         const int r = (8 * wave + i) * 8 + (lane >> 3);
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
         const int vk = min(BK, p.K - k0);
         const i32x4 r = make_rsrc(
             p.B + (vk > 0 ? (int64_t)k0 * p.ldb + n0 : 0),
-            vk > 0 ? (uint32_t)(((int64_t)(vk - 1) * p.ldb + (p.N - n0)) * 2) : 0u);
+            vk > 0 ? (uint32_t)(((int64_t)(vk - 1) * p.ldb + ((p.N - n0 + 7) & ~7)) * 2) : 0u);
 #pragma unroll
         for (int i = 0; i < DMA_PER_OPERAND; ++i) {
           between(i);
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
         // rebase on this K step: rows past K, and row K-1 past N, read zeros
         h.vk = min(BK, p.K - h.k0);
         h.r = make_rsrc(p.B + (h.vk > 0 ? (int64_t)h.k0 * p.ldb + n0 : 0),
-                        h.vk > 0 ? (uint32_t)(((int64_t)(h.vk - 1) * p.ldb + (p.N - n0)) * 2) : 0u);
+                        h.vk > 0 ? (uint32_t)(((int64_t)(h.vk - 1) * p.ldb + ((p.N - n0 + 7) & ~7)) * 2) : 0u);
       }
       return h;
     };
@@ -582,6 +585,30 @@ __global__ __launch_bounds__(256) void split_reduce(Params p) {
   }
 }
 
+// Copy of a rows x cols matrix of 16-bit elements (any leading dimension,
+// 2-byte alignment) into a dense, 16-byte aligned rows x dcols matrix
+// (dcols = cols rounded up to 8), zero-filling columns cols .. dcols-1: the
+// layout the tiled kernel's 16-byte chunk loads need.  One thread per
+// 8-element chunk of the destination.
+__global__ __launch_bounds__(256) void repack(const uint16_t* __restrict__ src, int64_t rows,
+                                              int64_t cols, int64_t ld, uint16_t* __restrict__ dst,
+                                              int64_t dcols) {
+  const int64_t chunks = dcols / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * chunks) return;
+  const int64_t r = gid / chunks;
+  const int64_t c0 = (gid % chunks) * 8;
+  const uint16_t* s = src + r * ld + c0;
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t lo = c0 + 2 * e < cols ? s[2 * e] : 0u;
+    const uint32_t hi = c0 + 2 * e + 1 < cols ? s[2 * e + 1] : 0u;
+    w[e] = lo | (hi << 16);
+  }
+  *(u32x4*)(dst + r * dcols + c0) = (u32x4){w[0], w[1], w[2], w[3]};
+}
+
 // ---- host side ----------------------------------------------------------
 
 struct DeviceInfo {
@@ -630,11 +657,12 @@ const char* dense_gemm_status_string(int status) {
     case DENSE_GEMM_INVALID_DIM: return "invalid dimension (negative M, N or K)";
     case DENSE_GEMM_NULL_PTR: return "null pointer";
     case DENSE_GEMM_BAD_LD: return "leading dimension below its minimum";
-    case DENSE_GEMM_MISALIGNED: return "misaligned pointer or K/ld/N not a multiple of 8";
+    case DENSE_GEMM_MISALIGNED: return "operand pointer not aligned to its 2-byte elements";
     case DENSE_GEMM_TOO_LARGE: return "problem too large for 32-bit tile offsets";
     case DENSE_GEMM_LAUNCH_FAILED: return "kernel launch failed";
     case DENSE_GEMM_NO_DEVICE: return "no gfx950 device current";
     case DENSE_GEMM_BAD_ARG: return "bad argument";
+    case DENSE_GEMM_NO_MEMORY: return "no device memory for the operand repack workspace";
     default: return "unknown status";
   }
 }
@@ -655,14 +683,16 @@ dense_gemm_status dense_gemm_validate(int layout, int64_t M, int64_t N, int64_t 
   }
   if (((uintptr_t)D & 1) != 0) return DENSE_GEMM_MISALIGNED;
   if (K > 0) {
-    if (((uintptr_t)A & 15) != 0 || ((uintptr_t)B & 15) != 0) return DENSE_GEMM_MISALIGNED;
-    if ((K & 7) != 0 || (lda & 7) != 0 || (ldb & 7) != 0) return DENSE_GEMM_MISALIGNED;
-    if (layout == NN && (N & 7) != 0) return DENSE_GEMM_MISALIGNED;
-    // 32-bit buffer offsets: the span one tile's descriptor covers.
+    if (((uintptr_t)A & 1) != 0 || ((uintptr_t)B & 1) != 0) return DENSE_GEMM_MISALIGNED;
+    // 32-bit buffer offsets: the span one tile's descriptor covers, for the
+    // operand as given or as its repacked copy (leading dimension K8 or N8)
+    const int64_t K8 = (K + 7) & ~(int64_t)7, N8 = (N + 7) & ~(int64_t)7;
+    const int64_t lda_k = lda > K8 ? lda : K8;
+    const int64_t ldb_k = ldb > (layout == NT ? K8 : N8) ? ldb : (layout == NT ? K8 : N8);
     const int64_t lim = ((int64_t)1 << 31) - 16;
-    if (((int64_t)(BM - 1) * lda + K) * 2 >= lim) return DENSE_GEMM_TOO_LARGE;
-    if (layout == NT && ((int64_t)(BN - 1) * ldb + K) * 2 >= lim) return DENSE_GEMM_TOO_LARGE;
-    if (layout == NN && ((int64_t)(BK - 1) * ldb + N) * 2 >= lim) return DENSE_GEMM_TOO_LARGE;
+    if (((int64_t)(BM - 1) * lda_k + K8) * 2 >= lim) return DENSE_GEMM_TOO_LARGE;
+    if (layout == NT && ((int64_t)(BN - 1) * ldb_k + K8) * 2 >= lim) return DENSE_GEMM_TOO_LARGE;
+    if (layout == NN && ((int64_t)(BK - 1) * ldb_k + N8) * 2 >= lim) return DENSE_GEMM_TOO_LARGE;
   }
   if (ldd >= kMaxDim || lda >= kMaxDim || ldb >= kMaxDim) return DENSE_GEMM_TOO_LARGE;
   return DENSE_GEMM_OK;
@@ -766,30 +796,72 @@ static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int
   p.splits = 1;
   p.split_steps = 0;
   p.ws = nullptr;
-  if (plan[8] > 1) {
-    // FP32 partials in a stream-ordered workspace, summed by a second kernel
-    const size_t bytes = (size_t)plan[8] * p.tiles * BM * BN * sizeof(float);
-    void* ws = nullptr;
-    if (hipMallocAsync(&ws, bytes, stream) == hipSuccess && ws != nullptr) {
-      p.splits = (int)plan[8];
-      p.split_steps = (int)plan[9];
-      p.ws = (float*)ws;
-      p.num_tasks = p.tiles * p.splits;
-      hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>), dim3((unsigned)p.num_tasks), dim3(THREADS),
-                         0, stream, p);
-      const int64_t threads = (int64_t)p.M * ((p.N + 7) / 8);
-      hipLaunchKernelGGL((split_reduce<T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                         stream, p);
-      const hipError_t launch = hipGetLastError();
-      (void)hipFreeAsync(ws, stream);
-      return launch == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
+
+  // Operands the 16-byte chunk loader cannot read directly (a pointer not
+  // 16-byte aligned, a leading dimension or K -- or N for the A.B layout's
+  // B -- not a multiple of 8) are first copied into a dense, zero-padded
+  // layout (`repack`) in the workspace.
+  const int64_t K8 = (K + 7) & ~(int64_t)7, N8 = (N + 7) & ~(int64_t)7;
+  const bool a_direct = K == 0 || (((uintptr_t)A & 15) == 0 && (lda & 7) == 0 && (K & 7) == 0);
+  const bool b_direct = K == 0 || (((uintptr_t)B & 15) == 0 && (ldb & 7) == 0 &&
+                                   (LAYOUT == NT ? (K & 7) == 0 : (N & 7) == 0));
+  const int64_t b_rows = LAYOUT == NT ? N : K, b_cols = LAYOUT == NT ? K : N;
+  const int64_t b_dcols = LAYOUT == NT ? K8 : N8;
+  auto round256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t a_bytes = a_direct ? 0 : round256((size_t)M * K8 * 2);
+  const size_t b_bytes = b_direct ? 0 : round256((size_t)b_rows * b_dcols * 2);
+  const size_t split_bytes = plan[8] > 1 ? (size_t)plan[8] * p.tiles * BM * BN * sizeof(float) : 0;
+
+  // one stream-ordered workspace: [A copy | B copy | FP32 split-K partials]
+  char* ws = nullptr;
+  bool split = split_bytes > 0;
+  if (a_bytes + b_bytes + split_bytes > 0) {
+    if (hipMallocAsync((void**)&ws, a_bytes + b_bytes + split_bytes, stream) != hipSuccess) {
+      (void)hipGetLastError();
+      ws = nullptr;
+      split = false;  // retry without the partials: run unsplit
+      if (a_bytes + b_bytes > 0 &&
+          hipMallocAsync((void**)&ws, a_bytes + b_bytes, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return DENSE_GEMM_NO_MEMORY;
+      }
     }
-    (void)hipGetLastError();  // no workspace: run unsplit
   }
-  hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false>), dim3((unsigned)(p.num_tasks < info.cus ? p.num_tasks : info.cus)),
-                     dim3(THREADS), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return DENSE_GEMM_LAUNCH_FAILED;
-  return DENSE_GEMM_OK;
+  if (!a_direct) {
+    uint16_t* a2 = (uint16_t*)ws;
+    const int64_t threads = M * (K8 / 8);
+    hipLaunchKernelGGL(repack, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       (const uint16_t*)A, M, K, lda, a2, K8);
+    p.A = a2;
+    p.lda = (int)K8;
+  }
+  if (!b_direct) {
+    uint16_t* b2 = (uint16_t*)(ws + a_bytes);
+    const int64_t threads = b_rows * (b_dcols / 8);
+    hipLaunchKernelGGL(repack, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       (const uint16_t*)B, b_rows, b_cols, ldb, b2, b_dcols);
+    p.B = b2;
+    p.ldb = (int)b_dcols;
+  }
+  if (split) {
+    // FP32 partials, summed by a second kernel
+    p.splits = (int)plan[8];
+    p.split_steps = (int)plan[9];
+    p.ws = (float*)(ws + a_bytes + b_bytes);
+    p.num_tasks = p.tiles * p.splits;
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>), dim3((unsigned)p.num_tasks), dim3(THREADS),
+                       0, stream, p);
+    const int64_t threads = (int64_t)p.M * ((p.N + 7) / 8);
+    hipLaunchKernelGGL((split_reduce<T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false>),
+                       dim3((unsigned)(p.num_tasks < info.cus ? p.num_tasks : info.cus)),
+                       dim3(THREADS), 0, stream, p);
+  }
+  const hipError_t launch = hipGetLastError();
+  if (ws != nullptr) (void)hipFreeAsync(ws, stream);
+  return launch == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
 
 }  // namespace dg

@@ -30,27 +30,35 @@
  * of D outside [0, M) x [0, N) -- including the columns between N and ldd --
  * are never written.  K == 0 writes zeros; M == 0 or N == 0 does nothing.
  *
- * Alignment (operands move in 16-byte chunks): A and B must be 16-byte
- * aligned and K, lda and ldb multiples of 8 elements; for the "nn" layout N
- * must also be a multiple of 8.  D needs 2-byte alignment and any ldd >= N
- * (16-byte stores are used where D's rows are 16-byte aligned).  Other
- * arguments return DENSE_GEMM_MISALIGNED.  M and N are otherwise arbitrary
- * (ragged edges are masked), and K need not be a multiple of the tile depth.
+ * Alignment.  A, B and D need only the 2-byte alignment of their elements
+ * (an odd address returns DENSE_GEMM_MISALIGNED); M, N, K and the leading
+ * dimensions are otherwise arbitrary (ragged edges are masked, and K need not
+ * be a multiple of the tile depth).  The tiled kernel moves A and B in
+ * 16-byte chunks: it reads an operand in place when its pointer is 16-byte
+ * aligned and its leading dimension and row length (K; N for the "nn" B) are
+ * multiples of 8 elements.  Any other operand is first copied by a repack
+ * kernel into a dense, zero-padded copy in the workspace (one extra pass over
+ * that operand; the result is the same).  D is written with 16-byte stores
+ * where its rows are 16-byte aligned and element by element otherwise.
  *
  * Split-K.  When the output has too few tiles to occupy the GPU and K is
  * long (see dense_gemm_plan), the K dimension is split: each part writes FP32
- * partial tiles to a workspace and a second kernel sums them in a fixed order
- * (results stay reproducible) and rounds once.  The workspace is taken with
- * hipMallocAsync on `stream` and returned with hipFreeAsync on the same
- * stream (stream-ordered, served by the device's default memory pool); if it
- * cannot be had, the call runs unsplit.  The environment variable
- * DENSE_GEMM_SPLITK=off disables split-K, DENSE_GEMM_SPLITK=<n> forces n
- * parts (for testing and measurement).
+ * partial tiles to the workspace and a second kernel sums them in a fixed
+ * order (results stay reproducible) and rounds once.  The environment
+ * variable DENSE_GEMM_SPLITK=off disables split-K, DENSE_GEMM_SPLITK=<n>
+ * forces n parts (for testing and measurement).
+ *
+ * Workspace.  A call that repacks an operand or splits K takes one workspace
+ * with hipMallocAsync on `stream` and returns it with hipFreeAsync on the same
+ * stream (stream-ordered, served by the device's default memory pool).  If it
+ * cannot be had, a split call runs unsplit, and a call that needs a repack
+ * returns DENSE_GEMM_NO_MEMORY (nothing launched).  Aligned operands with
+ * enough output tiles need none.
  *
  * Ownership and concurrency.  The caller owns every buffer and the stream.
  * The library keeps no pointers after a call returns and caches only
- * per-device properties (thread-safe); apart from the split-K workspace
- * above it allocates no device memory.  A, B and D must not overlap.  Calls
+ * per-device properties (thread-safe); apart from the workspace above it
+ * allocates no device memory.  A, B and D must not overlap.  Calls
  * are asynchronous and ordered on `stream` (0 is the null stream); the caller
  * synchronizes.  Calls on different streams may run concurrently.
  *
@@ -77,11 +85,12 @@ typedef enum dense_gemm_status {
   DENSE_GEMM_INVALID_DIM = 1,   /* M, N or K negative */
   DENSE_GEMM_NULL_PTR = 2,      /* D null with M*N > 0; A or B null with M*N*K > 0 */
   DENSE_GEMM_BAD_LD = 3,        /* a leading dimension below its minimum */
-  DENSE_GEMM_MISALIGNED = 4,    /* A or B not 16-byte aligned, D odd, or K / lda / ldb / (nn) N not a multiple of 8 */
+  DENSE_GEMM_MISALIGNED = 4,    /* A, B or D at an odd address */
   DENSE_GEMM_TOO_LARGE = 5,     /* a dimension >= 2^31, or a per-tile operand span >= 2^31 bytes */
   DENSE_GEMM_LAUNCH_FAILED = 6, /* the HIP runtime rejected the launch */
   DENSE_GEMM_NO_DEVICE = 7,     /* no current HIP device, or it is not a gfx950 */
-  DENSE_GEMM_BAD_ARG = 8        /* an argument of a helper below is out of its range */
+  DENSE_GEMM_BAD_ARG = 8,       /* an argument of a helper below is out of its range */
+  DENSE_GEMM_NO_MEMORY = 9      /* no device memory for the repack workspace */
 } dense_gemm_status;
 
 /* D = A @ B.T; FP16 in, FP32 accumulate, FP16 out.  A is M x K, B is N x K.

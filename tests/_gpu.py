@@ -40,27 +40,44 @@ def from_dev(t_dev) -> np.ndarray:
     return t_dev.cpu().numpy().view(np.uint16)
 
 
-def call(layout, fmt, M, N, K, A, lda, B, ldb, D, ldd, stream=None):
-    """Run the entry point for (layout, fmt) on device tensors; returns the status."""
+def call(layout, fmt, M, N, K, A, lda, B, ldb, D, ldd, stream=None, offsets=(0, 0, 0)):
+    """Run the entry point for (layout, fmt) on device tensors; returns the
+    status.  ``offsets`` are byte offsets added to the A, B and D pointers."""
     t = torch()
     fn = binding.raw(ENTRY[(layout, fmt)])
     st = t.cuda.current_stream() if stream is None else stream
-    ptr = lambda x: 0 if x is None else x.data_ptr()  # noqa: E731
-    return binding.Status(fn(M, N, K, ptr(A), lda, ptr(B), ldb, ptr(D), ldd, st.cuda_stream))
+    ptr = lambda x, o: 0 if x is None else x.data_ptr() + o  # noqa: E731
+    oa, ob, od = offsets
+    return binding.Status(fn(M, N, K, ptr(A, oa), lda, ptr(B, ob), ldb, ptr(D, od), ldd,
+                             st.cuda_stream))
 
 
-def gemm(layout, fmt, Abits, Bbits, M, N, K, lda=None, ldb=None, ldd=None, stream=None):
-    """Upload, run, download.  Returns (D bits M x ldd, status)."""
+def to_dev_at(bits: np.ndarray, rows: int, cols: int, ld: int, off: int, fill: int = CANARY):
+    """Like to_dev, with the matrix starting ``off`` elements into the buffer."""
+    t = torch()
+    host = np.full(rows * ld + off + 8, fill, dtype=np.uint16)
+    if rows and cols:
+        host[off:off + rows * ld].reshape(rows, ld)[:, :cols] = bits.reshape(rows, cols)
+    return t.from_numpy(host.view(np.int16)).to("cuda")
+
+
+def gemm(layout, fmt, Abits, Bbits, M, N, K, lda=None, ldb=None, ldd=None, stream=None,
+         a_off=0, b_off=0, d_off=0):
+    """Upload, run, download.  Returns (D bits M x ldd, status).  ``*_off``
+    place a matrix that many elements into its buffer (misaligned pointers)."""
     t = torch()
     lda = K if lda is None else lda
     ldb = (K if layout == "nt" else N) if ldb is None else ldb
     ldd = N if ldd is None else ldd
-    A = to_dev(Abits, M, K, lda)
+    A = to_dev_at(Abits, M, K, lda, a_off)
     if layout == "nt":
-        B = to_dev(Bbits, N, K, ldb)
+        B = to_dev_at(Bbits, N, K, ldb, b_off)
     else:
-        B = to_dev(Bbits, K, N, ldb)
-    D = empty_out(M, ldd)
-    st = call(layout, fmt, M, N, K, A, lda, B, ldb, D, ldd, stream)
+        B = to_dev_at(Bbits, K, N, ldb, b_off)
+    D = to_dev_at(np.zeros(0, np.uint16), M, 0, ldd, d_off)
+    st = call(layout, fmt, M, N, K, A, lda, B, ldb, D, ldd, stream,
+              offsets=(2 * a_off, 2 * b_off, 2 * d_off))
     t.cuda.synchronize()
-    return from_dev(D)[:M], st
+    out = from_dev(D)[d_off:d_off + M * ldd].reshape(M, ldd) if M else np.zeros((0, ldd), np.uint16)
+    assert (from_dev(D)[:d_off] == CANARY).all() and (from_dev(D)[d_off + M * ldd:] == CANARY).all()
+    return out, st

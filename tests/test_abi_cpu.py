@@ -79,15 +79,22 @@ def test_validate_error_codes():
     assert _v(NT, 8, 8, 16, ldb=8) == S.BAD_LD
     assert _v(NN, 8, 16, 8, ldb=8) == S.BAD_LD
     assert _v(NT, 8, 16, 8, ldd=8) == S.BAD_LD
-    assert _v(NT, 8, 8, 8, A=8) == S.MISALIGNED
-    assert _v(NT, 8, 8, 8, B=24) == S.MISALIGNED
+    # every operand needs only its elements' 2-byte alignment; the rest is
+    # handled by repacking (not visible to the check)
+    assert _v(NT, 8, 8, 8, A=1) == S.MISALIGNED
+    assert _v(NN, 8, 8, 8, B=25) == S.MISALIGNED
     assert _v(NT, 8, 8, 8, D=1) == S.MISALIGNED
-    assert _v(NT, 8, 8, 8, D=2) == S.OK  # D needs 2-byte alignment only
-    assert _v(NT, 8, 8, 12, lda=16, ldb=16) == S.MISALIGNED
-    assert _v(NT, 8, 8, 8, lda=12) == S.MISALIGNED
+    assert _v(NT, 8, 8, 8, A=8) == S.OK
+    assert _v(NT, 8, 8, 8, B=24) == S.OK
+    assert _v(NT, 8, 8, 8, D=2) == S.OK
+    assert _v(NT, 8, 8, 12, lda=16, ldb=16) == S.OK
+    assert _v(NT, 8, 8, 7) == S.OK
+    assert _v(NT, 8, 8, 8, lda=13) == S.OK
     assert _v(NT, 8, 12, 8, ldd=12) == S.OK  # any ldd >= N
-    assert _v(NN, 8, 12, 8, ldb=16, ldd=16) == S.MISALIGNED
-    assert _v(NT, 8, 13, 8, ldd=16) == S.OK  # ragged N is fine for NT
+    assert _v(NN, 8, 12, 8, ldb=13, ldd=13) == S.OK
+    assert _v(NT, 8, 13, 8, ldd=16) == S.OK
+    # K = 0: A and B are never read, so their alignment does not matter
+    assert _v(NT, 8, 8, 0, A=1, B=3) == S.OK
     assert _v(NT, 1 << 31, 8, 8) == S.TOO_LARGE
     assert _v(NT, 8, 8, 8, lda=1 << 23) == S.TOO_LARGE
     assert _v(NN, 8, 8, 8, ldb=1 << 26) == S.TOO_LARGE
