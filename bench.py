@@ -46,7 +46,75 @@ def parse():
                          "counters of a rocprofv3 --pmc run)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of one workload, time D = A @ B.T (FP16) at M = 8192 over a grid "
+                         "of N and K (one JSON line per shape, torch.mm timed beside it)")
+    ap.add_argument("--seed", type=int, default=8192)
     return ap.parse_args()
+
+
+SWEEP_GRID = [1024, 2048, 4096, 8192, 16384]
+
+
+def sweep_shapes():
+    """M = 8192 with N and K over powers of two from 1024 to 16384, plus
+    ragged neighbours: N + 128 (a half-filled last tile column) at K = 4096
+    and K + 40 (a partial last K step) at N = 4096."""
+    shapes = [(8192, n, k) for n in SWEEP_GRID for k in SWEEP_GRID]
+    shapes += [(8192, n + 128, 4096) for n in SWEEP_GRID]
+    shapes += [(8192, 4096, k + 40) for k in SWEEP_GRID]
+    return shapes
+
+
+def run_sweep(args):
+    """Per shape: N(0,1)/8 FP16 operands from torch's seeded device generator
+    (timing only; tests check these shapes against the oracle on sampled
+    entries), warm-up, then HIP events around about 50 ms of back-to-back
+    calls on the launch stream."""
+    import torch
+    from dense_gemm_08_amd import binding
+    lib = binding.load_library()
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, steps, warm):
+        for _ in range(warm):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    for M, N, K in sweep_shapes():
+        A = (torch.randn(M, K, device=dev, generator=gen) * 0.125).half()
+        B = (torch.randn(N, K, device=dev, generator=gen) * 0.125).half()
+        D = torch.empty(M, N, dtype=torch.half, device=dev)
+        Dt = torch.empty(M, N, dtype=torch.half, device=dev)
+        flops = 2.0 * M * N * K
+        steps = max(5, min(200, int(0.05 / (flops / 1.2e15))))
+
+        def ours():
+            st = lib.gemm_nt_f16(M, N, K, A.data_ptr(), K, B.data_ptr(), K, D.data_ptr(), N,
+                                 stream.cuda_stream)
+            if st != 0:
+                raise binding.DenseGemmError(st, "gemm_nt_f16")
+
+        def ref():
+            torch.mm(A, B.t(), out=Dt)
+
+        ms = timed(ours, steps, max(3, steps // 4))
+        ms_ref = timed(ref, steps, max(3, steps // 4))
+        print(json.dumps({"mode": "sweep", "M": M, "N": N, "K": K, "steps": steps,
+                          "kernel_ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
+                          "torch_mm_ms": round(ms_ref, 5),
+                          "torch_mm_tflops": round(flops / ms_ref / 1e9, 1)}), flush=True)
+        del A, B, D, Dt
 
 
 def cpu_baseline(w, A, B, target_s: float):
@@ -85,6 +153,10 @@ def main():
 
     import torch
     from dense_gemm_08_amd import binding, inputs
+
+    if args.sweep:
+        run_sweep(args)
+        return
 
     if args.copy_mib:
         n = args.copy_mib << 20

@@ -41,7 +41,7 @@ namespace dg {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -55,23 +55,30 @@ constexpr int BM = 256;              // tile rows (M)
 constexpr int BN = 256;              // tile columns (N)
 constexpr int BK = 64;               // K depth of one LDS stage (128-byte rows)
 constexpr int STAGES = 2;            // LDS ring depth
-constexpr int SUB = BK / 16;         // MFMA k-substeps per stage
+constexpr int MK = 32;               // K depth of one MFMA (16 x 16 x 32)
+constexpr int SUB = BK / MK;         // MFMA k-substeps per stage
 constexpr int WAVES = 4;             // 2 x 2 waves
 constexpr int THREADS = WAVES * 64;
 constexpr int WTM = 128;             // wave tile rows
 constexpr int WTN = 128;             // wave tile columns
-constexpr int MI = WTM / 32;         // 32 x 32 MFMA blocks per wave, M direction
-constexpr int NI = WTN / 32;         //                               N direction
+constexpr int MI = WTM / 16;         // 16 x 16 MFMA blocks per wave, M direction
+constexpr int NI = WTN / 16;         //                               N direction
+constexpr int PAIRS = MI * NI / 2;   // MFMA pairs per substep
 constexpr int A_BYTES = BM * BK * 2;           // 32 KiB: 256 rows x 128 B
 constexpr int B_BYTES = BN * BK * 2;           // 32 KiB
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;  // 128 KiB of the 160 KiB per CU
 constexpr int DMA_PER_OPERAND = A_BYTES / (THREADS * 16);  // 16-byte loads per thread
+constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPERAND;
 constexpr uint32_t OOB = 0x80000000u;          // a buffer offset past every range
+// MFMA pairs of the last substep issued before its barrier: the reads of
+// that substep's fragments (issued during the previous substep) complete
+// meanwhile, so the barrier's LDS wait costs nothing
+constexpr int BAR_PAIR = 8;
 
 static_assert(DMA_PER_OPERAND == 8, "each wave fills 8 KiB of each operand per stage");
 static_assert(BK == 64 && BM == 256 && BN == 256, "swizzles below assume these sizes");
-static_assert(MI * NI == 2 * DMA_PER_OPERAND, "one refill load per two MFMAs");
+static_assert(SUB == 2, "the ring schedule below has two substeps per stage");
 
 struct Params {
   const uint16_t* A;
@@ -143,17 +150,24 @@ __device__ __forceinline__ void wait_vm_barrier() {
 __device__ __forceinline__ void wait_lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
+// c += a-rows x b-columns over 32 k: v_mfma_f32_16x16x32_{f16,bf16}, the
+// accumulator updated in place.  Written as asm: for this instruction the
+// compiler's builtin picks a form whose result may not overwrite its
+// accumulator input, and with all 256 accumulator registers live it then
+// copies accumulators through VGPRs around every MFMA.  The compiler does not
+// know these are MFMAs, so it adds no wait states for their results: the
+// kernel orders the accumulator reset and the reads of results itself.
+// (Measured alone on every CU, this MFMA shape sustains about 15% more
+// FLOP/s than 32 x 32 x 16 under the chip's power limit.)
 template <typename T>
-__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c);
+__device__ __forceinline__ void mfma16(f32x4& c, u32x4 a, u32x4 b);
 template <>
-__device__ __forceinline__ f32x16 mfma<_Float16>(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+__device__ __forceinline__ void mfma16<_Float16>(f32x4& c, u32x4 a, u32x4 b) {
+  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 template <>
-__device__ __forceinline__ f32x16 mfma<__bf16>(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+__device__ __forceinline__ void mfma16<__bf16>(f32x4& c, u32x4 a, u32x4 b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
 // Round two floats to the output type (round-to-nearest-even) and pack them
@@ -218,9 +232,20 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     const int vm = min(BM, p.M - m0);  // valid rows of the A tile
     const int vn = min(BN, p.N - n0);  // valid columns of D in this tile
 
+    // MFMA operand layout (16 x 16 x 32): lane l holds row l % 16 of a
+    // 16-row fragment and k = 8 (l / 16) .. +7 of the substep's 32
     const int lane = opaque_tid() & 63;
-    const int lr = lane & 31;
-    const int lh = lane >> 5;
+    const int l16 = lane & 15;
+    const int lq = lane >> 4;
+
+    // Accumulators, reset before the prologue so that many instructions
+    // separate the reset from the first MFMA that reads it.
+    f32x4 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) acc[i][j] = (f32x4){};
+    fence();
 
     // Loader roles.  K-contiguous tiles: each wave instruction fills 1 KiB =
     // 8 rows of 128 B; wave w's instruction i covers rows (8w + i) * 8 ...
@@ -229,22 +254,26 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     // NN B tile: each wave instruction fills 2 k rows of 512 B.
     const int nn_row_lo = lane >> 5;
 
-    // Fragment read offsets (bytes within a stage).
+    // Fragment read offsets (bytes within a stage).  Fragment f of a
+    // K-contiguous tile (16 rows) sits 16 * 128 bytes after fragment 0: the
+    // swizzle depends only on the row's low four bits.
     int fa[SUB], fb[SUB], fbn[NI];
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
-      fa[s] = (wm * WTM + lr) * 128 + (((2 * s + lh) ^ swz_k(lr)) << 4);
-      fb[s] = A_BYTES + (wn * WTN + lr) * 128 + (((2 * s + lh) ^ swz_k(lr)) << 4);
+      fa[s] = (wm * WTM + l16) * 128 + (((4 * s + lq) ^ swz_k(l16)) << 4);
+      fb[s] = A_BYTES + (wn * WTN + l16) * 128 + (((4 * s + lq) ^ swz_k(l16)) << 4);
     }
     {
-      // transposing reads: lane supplies row k = 8*lh + (lane%16)/4 and
-      // columns n = wn*128 + ni*32 + 16*((lane/16)%2) + 4*(lane%4)
-      const int klane = 8 * lh + ((lane & 15) >> 2);
-      const int low = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-      const int fl = (lane >> 2) & 3;  // == swz_n(klane + 4m) >> 2 for every m
+      // transposing reads (NN B): in 16-lane block lq, lane i supplies row
+      // k = 8 lq + i / 4 (+ 4 for the second read, + 32 per substep) and the
+      // four columns n = wn*128 + 16 j + 4 (i % 4) .. +3, so that it receives
+      // column 16 j + i at four consecutive k
+      const int klane = 8 * lq + (l16 >> 2);
+      const int fl = (lane >> 2) & 3;  // == k & 3 of every row this lane reads
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        fbn[ni] = A_BYTES + klane * 512 + ((wn * 16 + ((ni ^ fl) << 2) + low) << 4) + (lane & 1) * 8;
+      for (int j = 0; j < NI; ++j)
+        fbn[j] = A_BYTES + klane * 512 +
+                 ((wn * 16 + ((2 * j + ((lane & 3) >> 1)) ^ (fl << 2))) << 4) + (lane & 1) * 8;
     }
 
     // Buffer descriptors for this tile; offsets past the last valid byte read
@@ -282,40 +311,9 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     }
 
     // LDS-DMA loads of K step ks into ring slot `slot`: the A tile (half 0)
-    // or the B tile (half 1).  Steps at or past kend load nothing (every
-    // offset is out of range, so the slot is zero-filled): the loop keeps a
-    // fixed pattern of loads in flight.  `between(t)` runs before load t.
-    auto refill = [&](int ks, int slot, int half, auto&& between) {
-      const int k0 = ks < kend ? ks * BK : p.K;
-      const uint32_t base = lds0 + slot * STAGE_BYTES + half * A_BYTES + (8 * wave) * 1024;
-      if (half == 0 || LAYOUT == NT) {
-        const i32x4 r = half == 0 ? rs_a : rs_b;
-#pragma unroll
-        for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-          between(i);
-          const bool kin = k0 + (kc[i & 1] << 3) < p.K;
-          const uint32_t off = half == 0 ? a_off[i] : b_off[i];
-          dma16(r, kin ? off + (uint32_t)(k0 * 2) : OOB, base + i * 1024);
-          fence();
-        }
-      } else {
-        // rebase on this K step: rows past K, and row K-1 past N, read zeros
-        const int vk = min(BK, p.K - k0);
-        const i32x4 r = make_rsrc(
-            p.B + (vk > 0 ? (int64_t)k0 * p.ldb + n0 : 0),
-            vk > 0 ? (uint32_t)(((int64_t)(vk - 1) * p.ldb + ((p.N - n0 + 7) & ~7)) * 2) : 0u);
-#pragma unroll
-        for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-          between(i);
-          const int k = 2 * (8 * wave + i) + nn_row_lo;
-          dma16(r, k < vk ? b_off[i] : OOB, base + i * 1024);
-          fence();
-        }
-      }
-    };
-    auto nothing = [](int) {};
-    // One refill half issued load by load (for interleaving with MFMAs): the
-    // descriptor and masks are set up once, then load(i) issues load i.
+    // or the B tile (half 1), issued one load at a time.  Steps at or past
+    // kend load nothing (every offset is out of range, so the slot is
+    // zero-filled): the loop keeps a fixed pattern of loads in flight.
     struct Half {
       i32x4 r;
       uint32_t base;
@@ -349,6 +347,14 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       }
       fence();
     };
+    auto refill_stage = [&](int ks, int slot) {
+      const Half ha = half_setup(ks, slot, 0);
+      const Half hb = half_setup(ks, slot, 1);
+#pragma unroll
+      for (int i = 0; i < DMA_PER_OPERAND; ++i) refill_one(ha, 0, i);
+#pragma unroll
+      for (int i = 0; i < DMA_PER_OPERAND; ++i) refill_one(hb, 1, i);
+    };
 
     // Fragment reads of k-substep s of the stage in slot `slot`, one LDS
     // instruction at a time: item f < MI reads A fragment f; the rest read the
@@ -357,13 +363,13 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     auto read_item = [&](int slot, int s, Frags& F, int f) {
       const char* base = smem + slot * STAGE_BYTES;
       if (f < MI) {
-        F.a[f] = *(const u32x4*)(base + fa[s] + f * 4096);
+        F.a[f] = *(const u32x4*)(base + fa[s] + f * 2048);
       } else if (LAYOUT == NT) {
         const int j = f - MI;
-        F.b[j] = *(const u32x4*)(base + fb[s] + j * 4096);
+        F.b[j] = *(const u32x4*)(base + fb[s] + j * 2048);
       } else {
         const int j = (f - MI) >> 1, h = (f - MI) & 1;
-        const u32x2 v = read_tr(base + fbn[j] + (s * 16 + 4 * h) * 512);
+        const u32x2 v = read_tr(base + fbn[j] + (s * 32 + 4 * h) * 512);
         F.b[j][2 * h] = v[0];
         F.b[j][2 * h + 1] = v[1];
       }
@@ -379,123 +385,114 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
         fence();
       }
     };
-    // the reads to issue before MFMA pair q (of 8), spread evenly
-    auto reads_before_pair = [&](int slot, int s, Frags& F, int q) {
+    // the share of `total` items due before step q of `steps`, spread evenly
+    auto share = [](int q, int steps, int total, auto&& item) {
 #pragma unroll
-      for (int f = (q * READS) / 8; f < ((q + 1) * READS) / 8; ++f) read_item(slot, s, F, f);
+      for (int f = (q * total) / steps; f < ((q + 1) * total) / steps; ++f) item(f);
     };
-
-    f32x16 acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j) acc[i][j] = (f32x16){};
 
     // Operand order (B fragment first) leaves each lane holding one row of D
-    // and four consecutive columns per register quad.  Consecutive MFMAs
-    // share a B fragment, so the next substep's reads (A fragments first, then
-    // B) arrive in the order its MFMAs need them.
-    auto mfma_at = [&](const Frags& F, int t) {
-      const int i = t % MI;
-      const int j = t / MI;
-      acc[i][j] = mfma<T>(F.b[j], F.a[i], acc[i][j]);
-    };
-    // One substep: the 16 MFMAs on F in pairs; before each pair, its share
-    // of the next substep's reads into G (slot gslot, substep gs) and, after
-    // it, one LDS-DMA load of a refill (`dma`).  Spreading the reads keeps
-    // the LDS command queue from filling (a burst of twelve reads per wave for
-    // the A.B layout stalls the MFMA issue behind it).
-    auto substep = [&](const Frags& F, Frags& G, int gslot, int gs, auto&& dma) {
+    // and four consecutive columns.  Consecutive MFMAs share a B fragment, so
+    // the next substep's reads (A fragments first, then B) arrive in the
+    // order its MFMAs need them.
+    auto mfma_pair = [&](const Frags& F, int q) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        reads_before_pair(gslot, gs, G, q);
-        mfma_at(F, 2 * q);
-        mfma_at(F, 2 * q + 1);
-        fence();
-        dma(q);
-      }
+      for (int t = 2 * q; t < 2 * q + 2; ++t) mfma16<T>(acc[t % MI][t / MI], F.b[t / MI], F.a[t % MI]);
     };
-    auto no_dma = [](int) {};
 
-    // The ring: stage ks lives in slot ks % 2.  Entering step ks, stage ks has
-    // landed, the B half of stage ks+1 is still to be issued, and F0 holds
-    // substep 0 of stage ks.  In each substep the LDS reads of the next
-    // substep's fragments are spread between the MFMA pairs.  The barrier sits
-    // before substep 3, once every read of stage ks is done, so stage ks's
-    // slot can be refilled (with stage ks+2) while substep 3 and the next
-    // step's substep 0 run; the refill loads also sit between MFMA pairs.
+    // The ring: stage ks lives in slot ks % 2.  Entering step ks, stage ks
+    // has landed, stage ks+1 is in flight, and F0 holds substep 0 of stage
+    // ks.  Substep 0 runs its 64 MFMAs in pairs with the reads of substep 1
+    // spread between them (spread, not bunched: a burst of reads fills the
+    // LDS command queue and stalls the MFMA issue behind it).  Substep 1 runs
+    // BAR_PAIR pairs, then the barrier: stage ks+1 has landed for every wave
+    // and every wave is done reading stage ks, so the rest of substep 1
+    // interleaves the reads of stage ks+1's first substep with the refill of
+    // stage ks's slot by stage ks+2.
     Frags F0, F1;
-    refill(kbeg, 0, 0, nothing);
-    refill(kbeg, 0, 1, nothing);
-    refill(kbeg + 1, 1, 0, nothing);
-    wait_vm_barrier<DMA_PER_OPERAND>();
+    refill_stage(kbeg, 0);
+    refill_stage(kbeg + 1, 1);
+    wait_vm_barrier<DMA_PER_STAGE>();
     read_frags(0, 0, F0);
 
     for (int ks = kbeg; ks < kend; ++ks) {
       const int slot = (ks - kbeg) & 1;
-      // substep 0 (+ the B half of stage ks+1)
-      const Half hb = half_setup(ks + 1, slot ^ 1, 1);
-      substep(F0, F1, slot, 1, [&](int q) { refill_one(hb, 1, q); });
-      // substeps 1 and 2
-      substep(F1, F0, slot, 2, no_dma);
-      substep(F0, F1, slot, 3, no_dma);
-      // stage ks+1 has landed for every wave, and every wave has finished
-      // reading stage ks
-      wait_vm_barrier<0>();
-      fence();
-      // substep 3 (+ the A half of stage ks+2 into the freed slot); past the
-      // last step this reads and loads zero-filled data, unused
+#pragma unroll
+      for (int q = 0; q < PAIRS; ++q) {
+        share(q, PAIRS, READS, [&](int f) { read_item(slot, 1, F1, f); });
+        mfma_pair(F0, q);
+        fence();
+      }
       const Half ha = half_setup(ks + 2, slot, 0);
-      substep(F1, F0, slot ^ 1, 0, [&](int q) { refill_one(ha, 0, q); });
+      const Half hb = half_setup(ks + 2, slot, 1);
+#pragma unroll
+      for (int q = 0; q < PAIRS; ++q) {
+        if (q == BAR_PAIR) {
+          wait_vm_barrier<0>();
+          fence();
+        }
+        if (q >= BAR_PAIR)
+          share(q - BAR_PAIR, PAIRS - BAR_PAIR, READS, [&](int f) { read_item(slot ^ 1, 0, F0, f); });
+        mfma_pair(F1, q);
+        fence();
+        if (q >= BAR_PAIR)
+          share(q - BAR_PAIR, PAIRS - BAR_PAIR, DMA_PER_STAGE, [&](int i) {
+            if (i < DMA_PER_OPERAND) refill_one(ha, 0, i);
+            else refill_one(hb, 1, i - DMA_PER_OPERAND);
+          });
+      }
     }
 
     wait_vm_barrier<0>();  // every wave is done with the ring; reuse it for staging
+    // wait states between the last MFMAs and the first reads of their results
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    fence();
 
     if (SPLIT) {
-      // FP32 partial tile, row-major 256 x 256: lane holds row lr of each
-      // 32-row block and columns j*32 + 8q + 4*lh .. +3 (16 contiguous bytes)
-      // (32 x 32 blocks wholly outside D are skipped: nothing reads them)
+      // FP32 partial tile, row-major 256 x 256: lane holds row l16 of each
+      // 16-row block and columns j*16 + 4*lq .. +3 (16 contiguous bytes);
+      // 16 x 16 blocks wholly outside D are skipped (nothing reads them)
       float* w = p.ws + (size_t)(split * p.tiles + tm * p.tiles_n + tn) * (BM * BN) +
-                 (size_t)(wm * WTM + lr) * BN + wn * WTN + 4 * lh;
+                 (size_t)(wm * WTM + l16) * BN + wn * WTN + 4 * lq;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        if (wm * WTM + i * 32 >= vm) break;
+        if (wm * WTM + i * 16 >= vm) break;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-          if (wn * WTN + j * 32 >= vn) break;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                         acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            *(float4*)(w + i * 32 * BN + j * 32 + 8 * q) = v;
-          }
+          if (wn * WTN + j * 16 >= vn) break;
+          *(float4*)(w + i * 16 * BN + j * 16) =
+              make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       continue;
     }
 
-    // Epilogue: per 32-row block, round, stage 32 x 128 outputs of this wave
-    // in LDS (chunk-swizzled rows of 256 B), then store 16-byte row chunks.
+    // Epilogue: per 32-row band (two 16-row blocks), round, stage the band's
+    // 32 x 128 outputs of this wave in LDS (chunk-swizzled rows of 256 B),
+    // then store 16-byte row chunks.
     char* stg = smem + wave * (32 * 256);
     const bool interior = p.d_vec && vm == BM && vn == BN;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+    for (int band = 0; band < MI / 2; ++band) {
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
+      for (int half = 0; half < 2; ++half) {
+        const int i = 2 * band + half;
+        const int row = half * 16 + l16;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          // lane holds row lr, columns j*32 + 8q + 4*lh + 0..3
+        for (int j = 0; j < NI; ++j) {
+          // lane holds row `row` of the band, columns j*16 + 4*lq + 0..3:
+          // 16-byte chunk 2j + lq/2, its lower or upper 8 bytes
           u32x2 v;
-          v[0] = pack2<T>(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-          v[1] = pack2<T>(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          const int chunk = j * 4 + q;
-          *(u32x2*)(stg + lr * 256 + ((chunk ^ (lr & 15)) << 4) + lh * 8) = v;
+          v[0] = pack2<T>(acc[i][j][0], acc[i][j][1]);
+          v[1] = pack2<T>(acc[i][j][2], acc[i][j][3]);
+          const int chunk = 2 * j + (lq >> 1);
+          *(u32x2*)(stg + row * 256 + ((chunk ^ (row & 15)) << 4) + (lq & 1) * 8) = v;
         }
         // keep the conversions of one block together (bounded live registers)
         __builtin_amdgcn_sched_barrier(0);
       }
-      const int row0 = m0 + wm * WTM + i * 32;
+      const int row0 = m0 + wm * WTM + band * 32;
       const int col0 = n0 + wn * WTN;
       if (interior) {
         // the whole tile is inside D and its rows are 16-byte aligned

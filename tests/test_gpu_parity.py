@@ -97,6 +97,19 @@ def test_workload_full_size_sampled(name):
 
 # ------------------------------------------------- bitwise special cases --
 
+@pytest.mark.parametrize("M,N,K", [(8192, 16384 + 128, 4096), (8192, 4096, 16384 + 40),
+                                   (8192, 1024, 1024)])
+def test_m8192_sweep_shapes_sampled(M, N, K):
+    # extreme shapes of the benchmark's M = 8192 sweep (FP16 A.B^T, N(0,1)/8):
+    # the widest N with a ragged last tile column, the deepest K with a partial
+    # last step, and the smallest (split-K) shape; sampled against the oracle
+    w = inputs.WORKLOADS["square_nt"]
+    A, B = inputs.make_operands(w, seed=M + N + K, M=M, N=N, K=K)
+    D, st = _gpu.gemm("nt", "f16", A, B, M, N, K)
+    assert st == status().OK
+    check_sampled("nt", "f16", A, B, M, N, K, D, n=2000, seed=N + K)
+
+
 @pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16"), ("nt", "bf16"), ("nn", "f16")])
 def test_small_integers_exact(layout, fmt, splitk):
     # entries in {-3..3}: every FP32 partial sum is an exact integer, so the
