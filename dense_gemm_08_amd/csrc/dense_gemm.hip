@@ -276,14 +276,11 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
                  ((wn * 16 + ((2 * j + ((lane & 3) >> 1)) ^ (fl << 2))) << 4) + (lane & 1) * 8;
     }
 
-    // Buffer descriptors for this tile; offsets past the last valid byte read
-    // zeros (rows beyond M for A, rows beyond N for the NT B tile).  The range
-    // of the last row ends at a whole 8-element chunk: where K is not a
-    // multiple of 8 the operand is a zero-padded copy with ld >= K8.
+    // Per-lane load offsets, fixed for the tile; the buffer descriptor of
+    // each K step is rebased on that step (scalar work), so a load needs no
+    // vector arithmetic.  Rows beyond M (A) or N (NT B) get an offset past
+    // every range and read zeros.
     const int K8 = (p.K + 7) & ~7;
-    const i32x4 rs_a = make_rsrc(p.A + (int64_t)m0 * p.lda,
-                                 p.K > 0 ? (uint32_t)(((int64_t)(vm - 1) * p.lda + K8) * 2) : 0u);
-    i32x4 rs_b = rs_a;
     uint32_t a_off[DMA_PER_OPERAND], b_off[DMA_PER_OPERAND];
     int kc[2];  // logical chunk of this lane for even / odd instruction index
 #pragma unroll
@@ -294,8 +291,6 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       a_off[i] = r < vm ? (uint32_t)(r * p.lda * 2 + kc[i & 1] * 16) : OOB;
     }
     if (LAYOUT == NT) {
-      rs_b = make_rsrc(p.B + (int64_t)n0 * p.ldb,
-                       p.K > 0 ? (uint32_t)(((int64_t)(vn - 1) * p.ldb + K8) * 2) : 0u);
 #pragma unroll
       for (int i = 0; i < DMA_PER_OPERAND; ++i) {
         const int r = (8 * wave + i) * 8 + (lane >> 3);
@@ -311,39 +306,47 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     }
 
     // LDS-DMA loads of K step ks into ring slot `slot`: the A tile (half 0)
-    // or the B tile (half 1), issued one load at a time.  Steps at or past
-    // kend load nothing (every offset is out of range, so the slot is
-    // zero-filled): the loop keeps a fixed pattern of loads in flight.
+    // or the B tile (half 1), issued one load at a time.  The descriptor
+    // starts at the step's first column (K-contiguous tiles) or row (NN B)
+    // and ends with the tile's last valid row, rounded up to a whole 8-element
+    // chunk (where K or N is not a multiple of 8 the operand is a zero-padded
+    // copy).  Steps at or past kend get an empty range: the slot is
+    // zero-filled and the loop keeps a fixed pattern of loads in flight.
     struct Half {
       i32x4 r;
       uint32_t base;
-      int k0, vk;
+      int kvalid;   // K elements of this step inside [0, K): 0 .. BK
+      bool in[2];   // this lane's chunk is inside K (for even / odd loads)
     };
     auto half_setup = [&](int ks, int slot, int half) {
       Half h;
-      h.k0 = ks < kend ? ks * BK : p.K;
+      const int64_t k0 = (int64_t)ks * BK;
+      h.kvalid = ks < kend ? min(BK, p.K - (int)k0) : 0;
       h.base = lds0 + slot * STAGE_BYTES + half * A_BYTES + (8 * wave) * 1024;
-      h.vk = 0;
-      if (half == 0) {
-        h.r = rs_a;
-      } else if (LAYOUT == NT) {
-        h.r = rs_b;
+      h.in[0] = (kc[0] << 3) < h.kvalid;
+      h.in[1] = (kc[1] << 3) < h.kvalid;
+      if (half == 0 || LAYOUT == NT) {
+        const uint16_t* src = half == 0 ? p.A + (int64_t)m0 * p.lda : p.B + (int64_t)n0 * p.ldb;
+        const int64_t span = half == 0 ? (int64_t)(vm - 1) * p.lda : (int64_t)(vn - 1) * p.ldb;
+        h.r = make_rsrc(h.kvalid > 0 ? src + k0 : p.A, h.kvalid > 0 ? (uint32_t)((span + K8 - k0) * 2) : 0u);
       } else {
-        // rebase on this K step: rows past K, and row K-1 past N, read zeros
-        h.vk = min(BK, p.K - h.k0);
-        h.r = make_rsrc(p.B + (h.vk > 0 ? (int64_t)h.k0 * p.ldb + n0 : 0),
-                        h.vk > 0 ? (uint32_t)(((int64_t)(h.vk - 1) * p.ldb + ((p.N - n0 + 7) & ~7)) * 2) : 0u);
+        // rows k0 .. k0 + kvalid - 1 of B, columns n0 .. N (rounded up to 8)
+        h.r = make_rsrc(h.kvalid > 0 ? p.B + k0 * p.ldb + n0 : p.B,
+                        h.kvalid > 0 ? (uint32_t)(((int64_t)(h.kvalid - 1) * p.ldb + ((p.N - n0 + 7) & ~7)) * 2) : 0u);
       }
       return h;
     };
+    // Chunks of a K-contiguous tile at or past K (a partial last step) read
+    // zeros; rows of the NN B tile past K are outside the descriptor's range.
+    // (One select per load: a separate unmasked copy of the loop would put
+    // MFMAs on every accumulator in both arms of a branch, which the register
+    // allocator answers with copies and spills.)
     auto refill_one = [&](const Half& h, int half, int i) {
       if (half == 0 || LAYOUT == NT) {
-        const bool kin = h.k0 + (kc[i & 1] << 3) < p.K;
         const uint32_t off = half == 0 ? a_off[i] : b_off[i];
-        dma16(h.r, kin ? off + (uint32_t)(h.k0 * 2) : OOB, h.base + i * 1024);
+        dma16(h.r, h.in[i & 1] ? off : OOB, h.base + i * 1024);
       } else {
-        const int k = 2 * (8 * wave + i) + nn_row_lo;
-        dma16(h.r, k < h.vk ? b_off[i] : OOB, h.base + i * 1024);
+        dma16(h.r, b_off[i], h.base + i * 1024);
       }
       fence();
     };
