@@ -74,7 +74,7 @@ constexpr uint32_t OOB = 0x80000000u;          // a buffer offset past every ran
 // MFMA pairs of the last substep issued before its barrier: the reads of
 // that substep's fragments (issued during the previous substep) complete
 // meanwhile, so the barrier's LDS wait costs nothing
-constexpr int BAR_PAIR = 8;
+constexpr int BAR_PAIR = 2;
 
 static_assert(DMA_PER_OPERAND == 8, "each wave fills 8 KiB of each operand per stage");
 static_assert(BK == 64 && BM == 256 && BN == 256, "swizzles below assume these sizes");
@@ -111,8 +111,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void*)p;
 }
 
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
+__device__ __forceinline__ i32x4 make_rsrc(uint64_t a, uint32_t bytes) {
   i32x4 r;
   r[0] = (int)(uint32_t)a;
   r[1] = (int)(uint32_t)(a >> 32);  // stride 0
@@ -280,7 +279,15 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     // each K step is rebased on that step (scalar work), so a load needs no
     // vector arithmetic.  Rows beyond M (A) or N (NT B) get an offset past
     // every range and read zeros.
+    //
+    // K steps: step s covers k = s*BK - koff .. +BK-1.  koff pads the first
+    // step at its front so that the last one ends exactly at K8 (K rounded
+    // up to 8; where K8 > K the operand is a zero-padded copy, or for the NN
+    // B the descriptor ends at row K-1).  Only the first step reaches outside
+    // [0, K8) -- below 0 -- so only its loads, issued in the prologue, need
+    // per-lane masks.
     const int K8 = (p.K + 7) & ~7;
+    const int koff = (BK - (K8 & (BK - 1))) & (BK - 1);
     uint32_t a_off[DMA_PER_OPERAND], b_off[DMA_PER_OPERAND];
     int kc[2];  // logical chunk of this lane for even / odd instruction index
 #pragma unroll
@@ -315,38 +322,37 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     struct Half {
       i32x4 r;
       uint32_t base;
-      int kvalid;   // K elements of this step inside [0, K): 0 .. BK
-      bool in[2];   // this lane's chunk is inside K (for even / odd loads)
+      int k0;  // the step's first k (negative only for the first step)
     };
     auto half_setup = [&](int ks, int slot, int half) {
       Half h;
-      const int64_t k0 = (int64_t)ks * BK;
-      h.kvalid = ks < kend ? min(BK, p.K - (int)k0) : 0;
+      const int64_t k0 = (int64_t)ks * BK - koff;
+      const bool live = ks < kend;
+      h.k0 = (int)k0;
       h.base = lds0 + slot * STAGE_BYTES + half * A_BYTES + (8 * wave) * 1024;
-      h.in[0] = (kc[0] << 3) < h.kvalid;
-      h.in[1] = (kc[1] << 3) < h.kvalid;
       if (half == 0 || LAYOUT == NT) {
-        const uint16_t* src = half == 0 ? p.A + (int64_t)m0 * p.lda : p.B + (int64_t)n0 * p.ldb;
+        // columns k0 .. K8 of the tile's rows
+        const uint64_t src = half == 0 ? (uint64_t)(uintptr_t)(p.A + (int64_t)m0 * p.lda)
+                                       : (uint64_t)(uintptr_t)(p.B + (int64_t)n0 * p.ldb);
         const int64_t span = half == 0 ? (int64_t)(vm - 1) * p.lda : (int64_t)(vn - 1) * p.ldb;
-        h.r = make_rsrc(h.kvalid > 0 ? src + k0 : p.A, h.kvalid > 0 ? (uint32_t)((span + K8 - k0) * 2) : 0u);
+        h.r = make_rsrc(src + 2 * k0, live ? (uint32_t)((span + K8 - k0) * 2) : 0u);
       } else {
-        // rows k0 .. k0 + kvalid - 1 of B, columns n0 .. N (rounded up to 8)
-        h.r = make_rsrc(h.kvalid > 0 ? p.B + k0 * p.ldb + n0 : p.B,
-                        h.kvalid > 0 ? (uint32_t)(((int64_t)(h.kvalid - 1) * p.ldb + ((p.N - n0 + 7) & ~7)) * 2) : 0u);
+        // rows k0 .. min(k0 + BK, K) - 1 of B, columns n0 .. N (rounded up to 8)
+        const int64_t rows = min((int64_t)BK, (int64_t)p.K - k0);
+        h.r = make_rsrc((uint64_t)(uintptr_t)(p.B + n0) + 2 * k0 * p.ldb,
+                        live ? (uint32_t)(((rows - 1) * p.ldb + ((p.N - n0 + 7) & ~7)) * 2) : 0u);
       }
       return h;
     };
-    // Chunks of a K-contiguous tile at or past K (a partial last step) read
-    // zeros; rows of the NN B tile past K are outside the descriptor's range.
-    // (One select per load: a separate unmasked copy of the loop would put
-    // MFMAs on every accumulator in both arms of a branch, which the register
-    // allocator answers with copies and spills.)
-    auto refill_one = [&](const Half& h, int half, int i) {
+    // One load of a refill.  MASKED (prologue only): chunks or rows before
+    // k = 0 read zeros.
+    auto refill_one = [&](const Half& h, int half, int i, bool masked) {
       if (half == 0 || LAYOUT == NT) {
         const uint32_t off = half == 0 ? a_off[i] : b_off[i];
-        dma16(h.r, h.in[i & 1] ? off : OOB, h.base + i * 1024);
+        dma16(h.r, !masked || h.k0 + (kc[i & 1] << 3) >= 0 ? off : OOB, h.base + i * 1024);
       } else {
-        dma16(h.r, b_off[i], h.base + i * 1024);
+        const int k = 2 * (8 * wave + i) + nn_row_lo;
+        dma16(h.r, !masked || h.k0 + k >= 0 ? b_off[i] : OOB, h.base + i * 1024);
       }
       fence();
     };
@@ -354,9 +360,9 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       const Half ha = half_setup(ks, slot, 0);
       const Half hb = half_setup(ks, slot, 1);
 #pragma unroll
-      for (int i = 0; i < DMA_PER_OPERAND; ++i) refill_one(ha, 0, i);
+      for (int i = 0; i < DMA_PER_OPERAND; ++i) refill_one(ha, 0, i, true);
 #pragma unroll
-      for (int i = 0; i < DMA_PER_OPERAND; ++i) refill_one(hb, 1, i);
+      for (int i = 0; i < DMA_PER_OPERAND; ++i) refill_one(hb, 1, i, true);
     };
 
     // Fragment reads of k-substep s of the stage in slot `slot`, one LDS
@@ -440,8 +446,9 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
         fence();
         if (q >= BAR_PAIR)
           share(q - BAR_PAIR, PAIRS - BAR_PAIR, DMA_PER_STAGE, [&](int i) {
-            if (i < DMA_PER_OPERAND) refill_one(ha, 0, i);
-            else refill_one(hb, 1, i - DMA_PER_OPERAND);
+            // stages from the third on start at k >= 0: no masks
+            if (i < DMA_PER_OPERAND) refill_one(ha, 0, i, false);
+            else refill_one(hb, 1, i - DMA_PER_OPERAND, false);
           });
       }
     }

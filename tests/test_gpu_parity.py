@@ -179,22 +179,32 @@ def test_forced_split_k(layout, fmt, parts, monkeypatch):
     assert (D == D2).all()
 
 
+@pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
 @pytest.mark.parametrize("parts", ["off", "4"])
-def test_k_tail_equals_zero_padding(parts, monkeypatch):
-    # K = 4000 (a partial last K step) against the same data zero-padded to
-    # 4096, with the same accumulation structure (unsplit, or 4 parts of 16
-    # steps: the padded run's last part only adds zeros)
+def test_k_remainder_equals_leading_zero_padding(layout, fmt, parts, monkeypatch):
+    # K = 4000 is not a multiple of the 64-deep K step: the kernel pads its
+    # first step in front (k from -32), so the result must equal, bit for bit,
+    # the same data with 32 zero columns of A (and zero k-rows or columns of
+    # B) put in front, K = 4032, which has the same steps, unsplit or in 4
+    # parts of 16 steps
     monkeypatch.setenv("DENSE_GEMM_SPLITK", parts)
-    w = inputs.WORKLOADS["ragged_nt"]
-    M, N, K, Kp = 272, 264, 4000, 4096
+    w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 5)
+    M, N, K = 272, 264, 4000
+    pad = (64 - K % 64) % 64
+    Kp = K + pad
     A, B = inputs.make_operands(w, M=M, N=N, K=K)
     Ap = np.zeros((M, Kp), np.uint16)
-    Ap[:, :K] = A
-    Bp = np.zeros((N, Kp), np.uint16)
-    Bp[:, :K] = B
-    D1, _ = _gpu.gemm("nt", "f16", A, B, M, N, K)
-    D2, _ = _gpu.gemm("nt", "f16", Ap, Bp, M, N, Kp)
+    Ap[:, pad:] = A
+    if layout == "nt":
+        Bp = np.zeros((N, Kp), np.uint16)
+        Bp[:, pad:] = B
+    else:
+        Bp = np.zeros((Kp, N), np.uint16)
+        Bp[pad:] = B
+    D1, _ = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    D2, _ = _gpu.gemm(layout, fmt, Ap, Bp, M, N, Kp)
     assert (D1 == D2).all()
+    check_full(layout, fmt, A, B, M, N, K, D1)
 
 
 @pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
