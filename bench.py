@@ -50,6 +50,10 @@ def parse():
                     help="instead of one workload, time D = A @ B.T (FP16) at M = 8192 over a grid "
                          "of N and K (one JSON line per shape, torch.mm timed beside it)")
     ap.add_argument("--seed", type=int, default=8192)
+    ap.add_argument("--ladder", action="store_true",
+                    help="instead of one workload, time each optimisation-step kernel "
+                         "(gemm_nt_f16_ladder levels 1-6) on the 4096^3 FP16 workload "
+                         "(one JSON line per level)")
     return ap.parse_args()
 
 
@@ -64,6 +68,53 @@ def sweep_shapes():
     shapes += [(8192, n + 128, 4096) for n in SWEEP_GRID]
     shapes += [(8192, 4096, k + 40) for k in SWEEP_GRID]
     return shapes
+
+
+LADDER = {
+    1: "V3: 128x128 tiles, one workgroup each, thread copies, no overlap",
+    2: "V4: + LDS-DMA loads (the copy engine)",
+    3: "V5: + two LDS stages (loads overlap compute)",
+    4: "V6: + persistent grouped XCD-aware grid",
+    5: "V8/V9: + 256x256 tiles (staged tiles shared by two waves each)",
+    6: "library kernel: + fine-grained schedule",
+}
+
+
+def run_ladder(args):
+    """Each optimisation-step kernel on the 4096^3 FP16 A @ B.T workload
+    (operands resident in HBM): warm-up, then HIP events around back-to-back
+    calls on the launch stream."""
+    import torch
+    from dense_gemm_08_amd import binding, inputs
+    lib = binding.load_library()
+    w = inputs.WORKLOADS["square_nt"]
+    A, B = inputs.make_operands(w)
+    dev = torch.device("cuda:0")
+    Ad = torch.from_numpy(A.view(np.int16)).to(dev)
+    Bd = torch.from_numpy(B.view(np.int16)).to(dev)
+    Dd = torch.empty((w.M, w.N), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    for level, what in LADDER.items():
+        def step():
+            st = lib.gemm_nt_f16_ladder(level, w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(),
+                                        w.K, Dd.data_ptr(), w.N, stream.cuda_stream)
+            if st != 0:
+                raise binding.DenseGemmError(st, "gemm_nt_f16_ladder")
+        for _ in range(max(3, args.warmup // 10)):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        steps = max(5, args.steps // 5)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        print(json.dumps({"mode": "ladder", "level": level, "what": what, "M": w.M, "N": w.N,
+                          "K": w.K, "steps": steps, "kernel_ms": round(ms, 5),
+                          "tflops": round(w.flops / ms / 1e9, 1)}), flush=True)
 
 
 def run_sweep(args):
@@ -156,6 +207,9 @@ def main():
 
     if args.sweep:
         run_sweep(args)
+        return
+    if args.ladder:
+        run_ladder(args)
         return
 
     if args.copy_mib:

@@ -47,6 +47,7 @@ SIGNATURES = {
     "gemm_nn_bf16": (_GEMM_ARGS, _i32),
     "gemm_nt_bf16": (_GEMM_ARGS, _i32),
     "gemm_nn_f16": (_GEMM_ARGS, _i32),
+    "gemm_nt_f16_ladder": ([_i32] + _GEMM_ARGS, _i32),
     "dense_gemm_status_string": ([_i32], ctypes.c_char_p),
     "dense_gemm_validate": ([_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64], _i32),
     "dense_gemm_tile_of_task": ([_i64, _i64, _i64, _i64, ctypes.POINTER(_i64),

@@ -1,7 +1,8 @@
 """Build step for libdense_gemm.so (hipcc, gfx950 only).
 
-``python -m dense_gemm_08_amd.build`` compiles ``csrc/dense_gemm.hip`` into
-``dense_gemm_08_amd/libdense_gemm.so`` in place.
+``python -m dense_gemm_08_amd.build`` compiles ``csrc/dense_gemm.hip`` (the
+library's kernels and C ABI) and ``csrc/ladder.hip`` (the optimisation-step
+kernels) into ``dense_gemm_08_amd/libdense_gemm.so`` in place.
 """
 from __future__ import annotations
 
@@ -11,7 +12,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "dense_gemm.hip")
+SRCS = [os.path.join(HERE, "csrc", "dense_gemm.hip"), os.path.join(HERE, "csrc", "ladder.hip")]
 OUT = os.path.join(HERE, "libdense_gemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -32,7 +33,8 @@ def build(extra=None, out=OUT, verbose=False) -> str:
     cmd = [HIPCC] + FLAGS + list(extra or []) + [
         "-I", os.path.join(ROOT, "include"),
         "-I", os.path.join(HERE, "csrc"),
-        SRC, "-o", tmp,
+    ] + SRCS + [
+        "-o", tmp,
     ]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -1,0 +1,228 @@
+// ladder.hip -- the optimisation steps of "TIRx GEMM on Blackwell" (its
+// sections V3 to V9, "the journey"), rebuilt one idea at a time for gfx950,
+// to measure what each idea buys on this hardware.  D = A @ B.T in FP16 only
+// (the page's workload), on shapes that divide the tiles.  These kernels are
+// deliberately plain: each level adds one mechanism to the level before and
+// nothing else; the library's own kernel (dense_gemm.hip) is the last level.
+//
+//   level 1 (V3)  one 128 x 128 tile per workgroup, all tiles launched at
+//                 once; per K step the threads copy A and B through registers
+//                 into LDS, then compute (load and compute do not overlap)
+//   level 2 (V4)  the copy engine: LDS-DMA loads (buffer_load ... lds) move
+//                 the tiles instead of the threads (the role of TMA)
+//   level 3 (V5)  two LDS stages: the loads of step k+1 are in flight while
+//                 step k is computed
+//   level 4 (V6)  persistent workgroups, one per CU, walking the tiles in the
+//                 grouped order with the XCD remap (tile_sched.h)
+//   level 5 (V8/V9) a 256 x 256 tile per workgroup: each staged A and B tile
+//                 now feeds two wave rows / columns (the pages reach the same
+//                 reuse with a 2-CTA cluster and a second consumer)
+//   level 6       the library kernel: the same tile with the fine-grained
+//                 schedule (reads and loads spread between MFMA pairs, one
+//                 barrier per stage, descriptors rebased per step)
+//
+// The page's V7 (a producer warp feeding consumer warps) has no level: with
+// one wave per SIMD holding 256 accumulator registers there is no fifth wave
+// to dedicate to loads, and LDS-DMA loads are issued asynchronously by the
+// computing waves themselves.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cdna_ops.h"
+#include "dense_gemm.h"
+#include "tile_sched.h"
+
+namespace dg {
+
+// current device's CU count, checked to be a gfx950 (dense_gemm.hip)
+dense_gemm_status device_cus(int* cus);
+
+namespace ladder {
+
+constexpr int BK = 64;  // K depth of one stage (128-byte rows)
+
+struct LParams {
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* D;
+  int M, N, K;
+  int lda, ldb, ldd;
+  int tiles_m, tiles_n, num_tiles;
+};
+
+template <int TILE, bool DMA, int STAGES, bool PERSIST>
+__global__ __launch_bounds__(256) void ladder_kernel(LParams p) {
+  constexpr int W = TILE / 2;                 // wave tile (2 x 2 waves)
+  constexpr int MI = W / 16, NI = W / 16;     // 16 x 16 MFMA blocks per wave
+  constexpr int OPB = TILE * BK * 2;          // bytes of one operand tile per stage
+  constexpr int STB = 2 * OPB;                // A tile, then B tile
+  constexpr int LOADS = OPB / (256 * 16);     // 16-byte loads per thread per operand
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STB];
+  const uint32_t lds0 = lds_addr(smem);
+
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int nk = p.K / BK;
+
+  const int first = PERSIST ? xcd_slot(blockIdx.x, gridDim.x, 8) : blockIdx.x;
+  const int stride = PERSIST ? gridDim.x : p.num_tiles;
+  for (int t = first; t < p.num_tiles; t += stride) {
+    int tm, tn;
+    if (PERSIST) {
+      tile_of_task(t, p.tiles_m, p.tiles_n, p.tiles_m < 8 ? p.tiles_m : 8, &tm, &tn);
+    } else {
+      tm = t / p.tiles_n;
+      tn = t % p.tiles_n;
+    }
+    const uint16_t* a0 = p.A + (int64_t)tm * TILE * p.lda;
+    const uint16_t* b0 = p.B + (int64_t)tn * TILE * p.ldb;
+
+    f32x4 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) acc[i][j] = (f32x4){};
+    fence();
+
+    // Load i of this thread covers tile row r = (LOADS*wave + i)*8 + lane/8
+    // and the logical 16-byte chunk that the swizzle puts at physical chunk
+    // lane % 8, so each wave instruction fills 1 KiB of LDS contiguously.
+    auto row_of = [&](int i) { return (LOADS * wave + i) * 8 + (lane >> 3); };
+    auto chunk_of = [&](int i) { return (lane & 7) ^ swz_k(row_of(i)); };
+    const i32x4 ra = make_rsrc((uint64_t)(uintptr_t)a0, (uint32_t)(((int64_t)(TILE - 1) * p.lda + p.K) * 2));
+    const i32x4 rb = make_rsrc((uint64_t)(uintptr_t)b0, (uint32_t)(((int64_t)(TILE - 1) * p.ldb + p.K) * 2));
+    auto load = [&](int ks, int slot) {
+      const int k0 = ks * BK;
+      if (DMA) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          const int r = row_of(i), c = chunk_of(i);
+          const uint32_t m0 = lds0 + slot * STB + (LOADS * wave + i) * 1024;
+          dma16(ra, (uint32_t)((r * p.lda + k0 + c * 8) * 2), m0);
+          dma16(rb, (uint32_t)((r * p.ldb + k0 + c * 8) * 2), m0 + OPB);
+        }
+      } else {
+        u32x4 va[LOADS], vb[LOADS];
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          const int r = row_of(i), c = chunk_of(i);
+          va[i] = *(const u32x4*)(a0 + (int64_t)r * p.lda + k0 + c * 8);
+          vb[i] = *(const u32x4*)(b0 + (int64_t)r * p.ldb + k0 + c * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          char* dst = smem + slot * STB + (LOADS * wave + i) * 1024 + lane * 16;
+          *(u32x4*)dst = va[i];
+          *(u32x4*)(dst + OPB) = vb[i];
+        }
+      }
+    };
+    // Two 32-deep substeps: read the wave's A and B fragments, then its MFMAs.
+    auto compute = [&](int slot) {
+      const char* base = smem + slot * STB;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int off = (((4 * s + lq) ^ swz_k(l16)) << 4);
+        u32x4 a[MI], b[NI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) a[i] = *(const u32x4*)(base + (wm * W + i * 16 + l16) * 128 + off);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) b[j] = *(const u32x4*)(base + OPB + (wn * W + j * 16 + l16) * 128 + off);
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int i = 0; i < MI; ++i) mfma16<_Float16>(acc[i][j], b[j], a[i]);
+      }
+    };
+
+    if (STAGES == 1) {
+      for (int ks = 0; ks < nk; ++ks) {
+        load(ks, 0);
+        if (DMA)
+          wait_vm_barrier<0>();  // the DMA loads have landed
+        else
+          wait_lds_barrier();    // the threads' LDS writes are done
+        compute(0);
+        wait_lds_barrier();  // every wave is done reading before the next load
+      }
+    } else {
+      load(0, 0);
+      for (int ks = 0; ks < nk; ++ks) {
+        if (ks + 1 < nk) {
+          load(ks + 1, (ks + 1) & 1);
+          wait_vm_barrier<2 * LOADS>();  // step ks has landed; step ks+1 in flight
+        } else {
+          wait_vm_barrier<0>();
+        }
+        compute(ks & 1);
+        wait_lds_barrier();  // slot ks & 1 is refilled by the next iteration's load
+      }
+    }
+
+    // wait states between the last MFMAs and the reads of their results
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    fence();
+    // lane holds row l16 of each 16-row block and 4 consecutive columns
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int row = tm * TILE + wm * W + i * 16 + l16;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int col = tn * TILE + wn * W + j * 16 + 4 * lq;
+        u32x2 v;
+        v[0] = pack2<_Float16>(acc[i][j][0], acc[i][j][1]);
+        v[1] = pack2<_Float16>(acc[i][j][2], acc[i][j][3]);
+        *(u32x2*)(p.D + (int64_t)row * p.ldd + col) = v;
+      }
+    }
+  }
+}
+
+template <int TILE, bool DMA, int STAGES, bool PERSIST>
+static dense_gemm_status launch(const LParams& p0, int cus, hipStream_t stream) {
+  LParams p = p0;
+  p.tiles_m = p.M / TILE;
+  p.tiles_n = p.N / TILE;
+  p.num_tiles = p.tiles_m * p.tiles_n;
+  const int grid = PERSIST ? (p.num_tiles < cus ? p.num_tiles : cus) : p.num_tiles;
+  hipLaunchKernelGGL((ladder_kernel<TILE, DMA, STAGES, PERSIST>), dim3((unsigned)grid), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
+}
+
+}  // namespace ladder
+}  // namespace dg
+
+using namespace dg;
+
+extern "C" dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N, int64_t K,
+                                                const void* A, int64_t lda, const void* B,
+                                                int64_t ldb, void* D, int64_t ldd,
+                                                hipStream_t stream) {
+  if (level < 1 || level > 6) return DENSE_GEMM_BAD_ARG;
+  if (level == 6) return gemm_nt_f16(M, N, K, A, lda, B, ldb, D, ldd, stream);
+  const int64_t tile = level == 5 ? 256 : 128;
+  if (M <= 0 || N <= 0 || K <= 0 || M % tile || N % tile || K % ladder::BK) return DENSE_GEMM_BAD_ARG;
+  if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
+    return DENSE_GEMM_BAD_ARG;
+  if (!A || !B || !D) return DENSE_GEMM_NULL_PTR;
+  if (lda < K || ldb < K || ldd < N) return DENSE_GEMM_BAD_LD;
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)D) & 15 || (lda | ldb | ldd) & 7)
+    return DENSE_GEMM_MISALIGNED;
+  if (((tile - 1) * lda + K) * 2 >= ((int64_t)1 << 31) || ((tile - 1) * ldb + K) * 2 >= ((int64_t)1 << 31))
+    return DENSE_GEMM_TOO_LARGE;
+  int cus = 0;
+  const dense_gemm_status st = device_cus(&cus);
+  if (st != DENSE_GEMM_OK) return st;
+  ladder::LParams p{(const uint16_t*)A, (const uint16_t*)B, (uint16_t*)D, (int)M, (int)N, (int)K,
+                    (int)lda, (int)ldb, (int)ldd, 0, 0, 0};
+  switch (level) {
+    case 1: return ladder::launch<128, false, 1, false>(p, cus, stream);
+    case 2: return ladder::launch<128, true, 1, false>(p, cus, stream);
+    case 3: return ladder::launch<128, true, 2, false>(p, cus, stream);
+    case 4: return ladder::launch<128, true, 2, true>(p, cus, stream);
+    default: return ladder::launch<256, true, 2, true>(p, cus, stream);
+  }
+}

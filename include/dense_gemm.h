@@ -114,6 +114,27 @@ dense_gemm_status gemm_nn_f16(int64_t M, int64_t N, int64_t K, const void* A, in
                               const void* B, int64_t ldb, void* D, int64_t ldd,
                               hipStream_t stream);
 
+/* The optimisation steps of "TIRx GEMM on Blackwell" (sections V3 to V9)
+ * rebuilt one idea at a time, for measurement: D = A @ B.T in FP16 as
+ * gemm_nt_f16 computes it, by the kernel of `level`:
+ *   1  one 128 x 128 tile per workgroup, threads copy A and B into LDS, then
+ *      compute (no overlap)                                       (V3)
+ *   2  as 1, the tiles moved by LDS-DMA loads                      (V4)
+ *   3  as 2, two LDS stages (loads of step k+1 overlap step k)     (V5)
+ *   4  as 3, persistent workgroups in the grouped XCD-aware order  (V6)
+ *   5  as 4, 256 x 256 tiles (each staged tile feeds two waves)    (V8/V9)
+ *   6  gemm_nt_f16 itself
+ * Levels 1-5 take only shapes that divide their tile: M and N multiples of
+ * 128 (256 for level 5), K a positive multiple of 64, A, B and D 16-byte
+ * aligned with lda, ldb and ldd multiples of 8 (DENSE_GEMM_BAD_ARG,
+ * _BAD_LD, _MISALIGNED or _TOO_LARGE otherwise; a level outside 1..6 is
+ * DENSE_GEMM_BAD_ARG).  Same ownership, stream and error rules as the
+ * entry points above; the FP32 accumulation order differs between levels,
+ * so results agree within the rounding bound, not bit for bit. */
+dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N, int64_t K, const void* A,
+                                     int64_t lda, const void* B, int64_t ldb, void* D,
+                                     int64_t ldd, hipStream_t stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char* dense_gemm_status_string(int status);
 

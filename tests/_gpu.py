@@ -81,3 +81,17 @@ def gemm(layout, fmt, Abits, Bbits, M, N, K, lda=None, ldb=None, ldd=None, strea
     out = from_dev(D)[d_off:d_off + M * ldd].reshape(M, ldd) if M else np.zeros((0, ldd), np.uint16)
     assert (from_dev(D)[:d_off] == CANARY).all() and (from_dev(D)[d_off + M * ldd:] == CANARY).all()
     return out, st
+
+
+def ladder(level, Abits, Bbits, M, N, K):
+    """D = A @ B.T (FP16) by optimisation-step kernel `level` (tight leading
+    dimensions).  Returns (D bits M x N, status)."""
+    t = torch()
+    A = to_dev(Abits, M, K)
+    B = to_dev(Bbits, N, K)
+    D = empty_out(M, N)
+    fn = binding.raw("gemm_nt_f16_ladder")
+    st = binding.Status(fn(level, M, N, K, A.data_ptr(), K, B.data_ptr(), K, D.data_ptr(), N,
+                           t.cuda.current_stream().cuda_stream))
+    t.cuda.synchronize()
+    return from_dev(D)[:M], st

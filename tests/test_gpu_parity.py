@@ -371,3 +371,64 @@ def test_python_binding_roundtrip():
     check_full("nn", "bf16", a2.cpu().view(t.int16).numpy().view(np.uint16),
                b2.cpu().view(t.int16).numpy().view(np.uint16), 64, 96, 128,
                d2.cpu().view(t.int16).numpy().view(np.uint16))
+
+
+# ----------------------------------------------- optimisation-step kernels --
+
+LEVELS = [1, 2, 3, 4, 5, 6]
+
+
+@pytest.mark.parametrize("level", LEVELS)
+def test_ladder_level_full_check(level):
+    # each step of the optimisation ladder computes the same product (several
+    # tiles in M and N, 11 K steps; the shape divides every level's tile)
+    w = inputs.WORKLOADS["square_nt"]
+    M, N, K = 512, 768, 704
+    A, B = inputs.make_operands(w, seed=level, M=M, N=N, K=K)
+    D, st = _gpu.ladder(level, A, B, M, N, K)
+    assert st == status().OK
+    check_full("nt", "f16", A, B, M, N, K, D)
+
+
+@pytest.mark.parametrize("level", LEVELS)
+def test_ladder_level_4096_sampled(level):
+    # the benchmark's shape, in the configuration the ladder benchmark times
+    w = inputs.WORKLOADS["square_nt"]
+    A, B = inputs.make_operands(w)
+    D, st = _gpu.ladder(level, A, B, w.M, w.N, w.K)
+    assert st == status().OK
+    check_sampled("nt", "f16", A, B, w.M, w.N, w.K, D, n=2000, seed=level)
+
+
+def test_ladder_small_integers_exact():
+    # exact FP32 sums: every level must give the correctly rounded result
+    M, N, K = 256, 512, 256
+    A = inputs.small_integers("f16", (M, K), seed=3)
+    B = inputs.small_integers("f16", (N, K), seed=4)
+    d, _ = oracle.gemm("nt", "f16", A, B, M=M, N=N, K=K)
+    want = oracle.round_to("f16", d)
+    for level in LEVELS:
+        D, st = _gpu.ladder(level, A, B, M, N, K)
+        assert st == status().OK
+        assert (D == want).all(), level
+
+
+def test_ladder_rejects_shapes():
+    Sx = status()
+    A = _gpu.to_dev(np.zeros((512, 512), np.uint16), 512, 512)
+    D = _gpu.empty_out(512, 512)
+    fn = binding_raw("gemm_nt_f16_ladder")
+    s = _gpu.torch().cuda.current_stream().cuda_stream
+    p = A.data_ptr()
+    assert Sx(fn(0, 256, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
+    assert Sx(fn(7, 256, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
+    assert Sx(fn(5, 384, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
+    assert Sx(fn(1, 256, 256, 100, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
+    assert Sx(fn(2, 256, 256, 64, p + 2, 512, p, 512, D.data_ptr(), 512, s)) == Sx.MISALIGNED
+    _gpu.torch().cuda.synchronize()
+    assert (_gpu.from_dev(D) == _gpu.CANARY).all()
+
+
+def binding_raw(name):
+    from dense_gemm_08_amd import binding
+    return binding.raw(name)
