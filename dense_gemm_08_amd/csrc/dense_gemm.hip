@@ -210,23 +210,26 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       uint32_t base;
       int k0;  // the step's first k (negative only for the first step)
     };
+    // (Ranges are computed in 32 bits, which the argument check guarantees
+    // suffice; 64-bit forms made the compiler branch inside the loop.)
     auto half_setup = [&](int ks, int slot, int half) {
       Half h;
-      const int64_t k0 = (int64_t)ks * BK - koff;
+      const int k0 = ks * BK - koff;
       const bool live = ks < kend;
-      h.k0 = (int)k0;
+      h.k0 = k0;
       h.base = lds0 + slot * STAGE_BYTES + half * A_BYTES + (8 * wave) * 1024;
       if (half == 0 || LAYOUT == NT) {
         // columns k0 .. K8 of the tile's rows
         const uint64_t src = half == 0 ? (uint64_t)(uintptr_t)(p.A + (int64_t)m0 * p.lda)
                                        : (uint64_t)(uintptr_t)(p.B + (int64_t)n0 * p.ldb);
-        const int64_t span = half == 0 ? (int64_t)(vm - 1) * p.lda : (int64_t)(vn - 1) * p.ldb;
-        h.r = make_rsrc(src + 2 * k0, live ? (uint32_t)((span + K8 - k0) * 2) : 0u);
+        const int span = half == 0 ? (vm - 1) * p.lda : (vn - 1) * p.ldb;
+        const uint32_t bytes = (uint32_t)(span + K8 - k0) * 2u;
+        h.r = make_rsrc(src + 2 * (int64_t)k0, live ? bytes : 0u);
       } else {
         // rows k0 .. min(k0 + BK, K) - 1 of B, columns n0 .. N (rounded up to 8)
-        const int64_t rows = min((int64_t)BK, (int64_t)p.K - k0);
-        h.r = make_rsrc((uint64_t)(uintptr_t)(p.B + n0) + 2 * k0 * p.ldb,
-                        live ? (uint32_t)(((rows - 1) * p.ldb + ((p.N - n0 + 7) & ~7)) * 2) : 0u);
+        const int rows = min(BK, p.K - k0);
+        const uint32_t bytes = (uint32_t)((rows - 1) * p.ldb + ((p.N - n0 + 7) & ~7)) * 2u;
+        h.r = make_rsrc((uint64_t)(uintptr_t)(p.B + n0) + 2 * (int64_t)k0 * p.ldb, live ? bytes : 0u);
       }
       return h;
     };
