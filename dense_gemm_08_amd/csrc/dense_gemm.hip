@@ -79,11 +79,13 @@ struct Params {
   int lda, ldb, ldd;
   int tiles_m, tiles_n, group_m, num_tasks, num_xcds;
   int d_vec;  // D rows are 16-byte aligned (16-byte stores allowed)
-  // split-K: each task is (tile, split); the split covers K steps
-  // [split * split_steps, min(nk, (split + 1) * split_steps)) and writes its
-  // FP32 partial tile (row-major BM x BN) to ws at index split * tiles +
-  // tile_row * tiles_n + tile_col
-  int splits, split_steps, tiles;
+  // split-K (the SPLIT kernels): tasks below full_tasks are whole tiles;
+  // the rest are (tile, part) pairs over the last `tiles` tiles of the
+  // order.  Task full_tasks + u is part u / tiles of tile full_tasks +
+  // u % tiles; the part covers K steps [part * split_steps, min(nk, (part +
+  // 1) * split_steps)) and writes its FP32 partial tile (row-major BM x BN)
+  // to ws at index part * tiles + u % tiles
+  int full_tasks, splits, split_steps, tiles;
   float* ws;
 };
 
@@ -106,12 +108,14 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
 
   for (int task = slot0; task < p.num_tasks; task += gridDim.x) {
     int tm, tn;
-    const int tile = SPLIT ? task % p.tiles : task;
-    const int split = SPLIT ? task / p.tiles : 0;
+    const bool part = SPLIT && task >= p.full_tasks;
+    const int u = task - p.full_tasks;
+    const int tile = part ? p.full_tasks + u % p.tiles : task;
+    const int split = part ? u / p.tiles : 0;
     tile_of_task(tile, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     // this task's K steps
     const int kbeg = split * p.split_steps;
-    const int kend = SPLIT ? min(nk, kbeg + p.split_steps) : nk;
+    const int kend = part ? min(nk, kbeg + p.split_steps) : nk;
     const int m0 = tm * BM;
     const int n0 = tn * BN;
     const int vm = min(BM, p.M - m0);  // valid rows of the A tile
@@ -347,11 +351,11 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     fence();
 
-    if (SPLIT) {
+    if (part) {
       // FP32 partial tile, row-major 256 x 256: lane holds row l16 of each
       // 16-row block and columns j*16 + 4*lq .. +3 (16 contiguous bytes);
       // 16 x 16 blocks wholly outside D are skipped (nothing reads them)
-      float* w = p.ws + (size_t)(split * p.tiles + tm * p.tiles_n + tn) * (BM * BN) +
+      float* w = p.ws + (size_t)(split * p.tiles + u % p.tiles) * (BM * BN) +
                  (size_t)(wm * WTM + l16) * BN + wn * WTN + 4 * lq;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
@@ -430,19 +434,21 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
   }
 }
 
-// Sum of the split-K partials of every output element in split order 0, 1,
-// ... (a fixed order: results are reproducible), rounded once to the output
-// type.  One thread per 8 consecutive columns of a row.
+// Sum of the split-K partials of every output element of the split tiles in
+// part order 0, 1, ... (a fixed order: results are reproducible), rounded
+// once to the output type.  Workgroup b covers rows 8 (b % 32) .. +7 of
+// split tile b / 32; one thread per 8 consecutive columns of a row.
 template <typename T>
 __global__ __launch_bounds__(256) void split_reduce(Params p) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int cols8 = (p.N + 7) / 8;
-  if (gid >= (int64_t)p.M * cols8) return;
-  const int row = (int)(gid / cols8);
-  const int col = (int)(gid % cols8) * 8;
-  const int tm = row / BM, tn = col / BN;
-  const int tile = tm * p.tiles_n + tn;  // partials are stored by tile position
-  const float* w = p.ws + (size_t)tile * (BM * BN) + (size_t)(row - tm * BM) * BN + (col - tn * BN);
+  const int st = blockIdx.x >> 5;  // split tile (0 .. tiles-1)
+  int tm, tn;
+  tile_of_task(p.full_tasks + st, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+  const int r = (blockIdx.x & 31) * 8 + (threadIdx.x >> 5);
+  const int c = (threadIdx.x & 31) * 8;
+  const int row = tm * BM + r;
+  const int col = tn * BN + c;
+  if (row >= p.M || col >= p.N) return;
+  const float* w = p.ws + (size_t)st * (BM * BN) + (size_t)r * BN + c;
   const size_t stride = (size_t)p.tiles * (BM * BN);  // between the partials of two splits
   float s[8];
 #pragma unroll
@@ -634,12 +640,17 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
   out[5] = grid;
   out[6] = choose_group_m(tiles_m, tiles_n, grid);
   out[7] = THREADS;
-  // split-K when the tiles would leave most CUs idle and K is long: at most
-  // one unit per CU, at least 4 K steps per unit
+  // split-K for the tiles of the last, partial wave (all tiles when there
+  // are fewer than CUs) when K is long and they would leave at least half the
+  // CUs idle -- three quarters after full waves (measured: splitting a
+  // half-full last wave gains nothing, its partial sums and the reduce cost
+  // what the idle CUs would have saved): at most one part per idle CU, at
+  // least 4 K steps per part
   const int64_t nk = (K + BK - 1) / BK;
+  const int64_t rem = tasks % num_cus;
   int64_t splits = 1, steps = nk;
-  if (tasks * 2 <= num_cus && nk >= 8) {
-    const int64_t by_cus = num_cus / tasks, by_k = nk / 4;
+  if (rem > 0 && rem * (tasks < num_cus ? 2 : 4) <= num_cus && nk >= 8) {
+    const int64_t by_cus = num_cus / rem, by_k = nk / 4;
     const int64_t sp = by_cus < by_k ? by_cus : by_k;
     if (sp >= 2) {
       steps = (nk + sp - 1) / sp;
@@ -648,7 +659,7 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
   }
   out[8] = splits;
   out[9] = steps;
-  if (splits > 1) out[5] = tasks * splits;
+  if (splits > 1 && tasks < num_cus) out[5] = tasks * splits;
   return DENSE_GEMM_OK;
 }
 
@@ -668,15 +679,19 @@ static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int
   int64_t plan[10];
   st = dense_gemm_plan(LAYOUT, M, N, K, info.cus, plan);
   if (st != DENSE_GEMM_OK) return st;
-  // DENSE_GEMM_SPLITK=off disables split-K; =<n> forces n splits (testing)
+  // Tiles computed whole; the plan splits the rest (the last, partial wave).
+  const int64_t tasks = plan[3] * plan[4];
+  int64_t full = plan[8] > 1 ? tasks - tasks % info.cus : tasks;
+  // DENSE_GEMM_SPLITK=off disables split-K; =<n> splits every tile in n
+  // parts (testing)
   if (const char* e = getenv("DENSE_GEMM_SPLITK")) {
-    const int64_t nk = (K + BK - 1) / BK, tasks = plan[3] * plan[4];
+    const int64_t nk = (K + BK - 1) / BK;
     int64_t want = strcmp(e, "off") == 0 ? 1 : atoll(e);
     if (want >= 1 && nk >= 1) {
       if (want > nk) want = nk;
       plan[9] = (nk + want - 1) / want;
       plan[8] = (nk + plan[9] - 1) / plan[9];
-      plan[5] = plan[8] > 1 ? tasks * plan[8] : (tasks < info.cus ? tasks : info.cus);
+      full = plan[8] > 1 ? 0 : tasks;
     }
   }
   Params p;
@@ -695,7 +710,8 @@ static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int
   p.num_tasks = (int)(plan[3] * plan[4]);
   p.num_xcds = 8;
   p.d_vec = (((uintptr_t)D & 15) == 0 && (ldd & 7) == 0) ? 1 : 0;
-  p.tiles = p.num_tasks;
+  p.full_tasks = (int)full;
+  p.tiles = (int)(tasks - full);  // tiles split in parts
   p.splits = 1;
   p.split_steps = 0;
   p.ws = nullptr;
@@ -713,7 +729,8 @@ static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int
   auto round256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t a_bytes = a_direct ? 0 : round256((size_t)M * K8 * 2);
   const size_t b_bytes = b_direct ? 0 : round256((size_t)b_rows * b_dcols * 2);
-  const size_t split_bytes = plan[8] > 1 ? (size_t)plan[8] * p.tiles * BM * BN * sizeof(float) : 0;
+  const size_t split_bytes =
+      plan[8] > 1 && p.tiles > 0 ? (size_t)plan[8] * p.tiles * BM * BN * sizeof(float) : 0;
 
   // one stream-ordered workspace: [A copy | B copy | FP32 split-K partials]
   char* ws = nullptr;
@@ -747,17 +764,19 @@ static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int
     p.ldb = (int)b_dcols;
   }
   if (split) {
-    // FP32 partials, summed by a second kernel
+    // whole tiles, then the parts of the split tiles writing FP32 partials,
+    // summed by a second kernel
     p.splits = (int)plan[8];
     p.split_steps = (int)plan[9];
     p.ws = (float*)(ws + a_bytes + b_bytes);
-    p.num_tasks = p.tiles * p.splits;
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>), dim3((unsigned)p.num_tasks), dim3(THREADS),
-                       0, stream, p);
-    const int64_t threads = (int64_t)p.M * ((p.N + 7) / 8);
-    hipLaunchKernelGGL((split_reduce<T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       stream, p);
+    p.num_tasks = p.full_tasks + p.tiles * p.splits;
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>),
+                       dim3((unsigned)(p.num_tasks < info.cus ? p.num_tasks : info.cus)),
+                       dim3(THREADS), 0, stream, p);
+    hipLaunchKernelGGL((split_reduce<T>), dim3((unsigned)(p.tiles * 32)), dim3(256), 0, stream, p);
   } else {
+    p.full_tasks = p.num_tasks;
+    p.tiles = 0;
     hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false>),
                        dim3((unsigned)(p.num_tasks < info.cus ? p.num_tasks : info.cus)),
                        dim3(THREADS), 0, stream, p);

@@ -41,10 +41,13 @@
  * that operand; the result is the same).  D is written with 16-byte stores
  * where its rows are 16-byte aligned and element by element otherwise.
  *
- * Split-K.  When the output has too few tiles to occupy the GPU and K is
- * long (see dense_gemm_plan), the K dimension is split: each part writes FP32
- * partial tiles to the workspace and a second kernel sums them in a fixed
- * order (results stay reproducible) and rounds once.  The environment
+ * Split-K.  When the tiles of the last, partial wave over the CUs (all
+ * tiles, when there are fewer tiles than CUs) would leave at least half the
+ * CUs idle (three quarters after full waves) and K is long (see
+ * dense_gemm_plan), the K dimension of those
+ * tiles is split: each part writes an FP32 partial tile to the workspace and
+ * a second kernel sums them in a fixed order (results stay reproducible) and
+ * rounds once.  The other tiles are computed whole in the same launch.  The environment
  * variable DENSE_GEMM_SPLITK=off disables split-K, DENSE_GEMM_SPLITK=<n>
  * forces n parts (for testing and measurement).
  *
@@ -158,9 +161,13 @@ dense_gemm_status dense_gemm_tile_of_task(int64_t task, int64_t tiles_m, int64_t
 /* The launch plan for a problem on a device with num_cus compute units.
  * Writes 10 values to out: BM, BN, BK, tiles_m, tiles_n, grid (workgroups of
  * the GEMM kernel), group_m, threads per workgroup, the number of K splits
- * (1: none) and the K steps (of BK) per split.  Split-K is chosen when
- * 2 * tiles <= num_cus and K spans at least 8 steps: as many parts as keep
- * one part per CU and at least 4 steps per part. */
+ * (1: none) and the K steps (of BK) per split.  Split-K applies to the
+ * r = tiles mod num_cus tiles of the last, partial wave (all tiles when
+ * tiles < num_cus) and is chosen when r > 0, 2 r <= num_cus (4 r <= num_cus
+ * when tiles > num_cus) and K spans at least 8 steps: as many parts as keep
+ * at most one part per CU (r * parts
+ * <= num_cus) and at least 4 steps per part.  The grid is then r * parts
+ * when tiles < num_cus, else num_cus. */
 dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K,
                                   int64_t num_cus, int64_t* out);
 

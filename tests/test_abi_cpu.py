@@ -202,6 +202,26 @@ def test_plan_split_k():
     # 3000 x 5000 x 4000: 240 tiles, no split
     assert lib.dense_gemm_plan(NT, 3000, 5000, 4000, 256, out) == S.OK
     assert out[8] == 1
+    # 8192 x 17408 x 5120: 2176 tiles = 8 waves + 128; a half-full last wave
+    # after full waves is not split
+    assert lib.dense_gemm_plan(NN, 8192, 17408, 5120, 256, out) == S.OK
+    assert out[8] == 1
+    # 8192 x 8320 x 4096: 1056 tiles = 4 waves + 32 -> 8 parts of 8 steps,
+    # the grid stays one per CU
+    assert lib.dense_gemm_plan(NN, 8192, 8320, 4096, 256, out) == S.OK
+    assert (out[8], out[9], out[5]) == (8, 8, 256)
+    # 17 x 16 = 272 tiles, 16 left over, K = 1000 (16 steps): 4 parts of 4
+    assert lib.dense_gemm_plan(NT, 4252, 4088, 1000, 256, out) == S.OK
+    assert (out[8], out[9], out[5]) == (4, 4, 256)
+    # 4096^3: 256 tiles fill the GPU exactly, nothing left over
+    assert lib.dense_gemm_plan(NT, 4096, 4096, 4096, 256, out) == S.OK
+    assert out[8] == 1
+    # a last wave more than half full is not split: 32 x 13 = 416 tiles
+    assert lib.dense_gemm_plan(NT, 8192, 3328, 4096, 256, out) == S.OK
+    assert out[8] == 1
+    # 32 x 17 = 544 tiles = 2 waves + 32: 8 parts of 8 steps
+    assert lib.dense_gemm_plan(NT, 8192, 4224, 4096, 256, out) == S.OK
+    assert (out[8], out[9], out[5]) == (8, 8, 256)
     # every part covers whole steps and the parts cover K exactly once
     for M, N, K in [(600, 520, 712), (128, 128, 4000), (1000, 1000, 8192), (256, 256, 5120)]:
         assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK

@@ -432,3 +432,56 @@ def test_ladder_rejects_shapes():
 def binding_raw(name):
     from dense_gemm_08_amd import binding
     return binding.raw(name)
+
+
+# ------------------------------------------------- split last partial wave --
+
+@pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
+def test_split_last_wave(layout, fmt, monkeypatch):
+    # 17 x 16 = 272 tiles on 256 CUs: 256 tiles whole, the 16 of the last wave
+    # in 4 parts of 4 K steps, all in one launch; ragged M and N.  Entries are
+    # sampled from the whole output and, half of them, from the split tiles;
+    # the run with split-K disabled is checked the same way
+    import ctypes
+    from dense_gemm_08_amd import binding
+    t = _gpu.torch()
+    cus = t.cuda.get_device_properties(0).multi_processor_count
+    M, N, K = 4252, 4088, 1000
+    lib = binding.load_library()
+    plan = (ctypes.c_int64 * 10)()
+    assert lib.dense_gemm_plan(0 if layout == "nt" else 1, M, N, K, cus, plan) == 0
+    tiles_m, tiles_n, group_m, splits = plan[3], plan[4], plan[6], plan[8]
+    tasks = tiles_m * tiles_n
+    if cus == 256:
+        assert splits == 4
+    split_tiles = []
+    if splits > 1:
+        for task in range(tasks - tasks % cus, tasks):
+            a, b = ctypes.c_int64(), ctypes.c_int64()
+            assert lib.dense_gemm_tile_of_task(task, tiles_m, tiles_n, group_m, ctypes.byref(a),
+                                               ctypes.byref(b)) == 0
+            split_tiles.append((a.value, b.value))
+    w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 101)
+    A, B = inputs.make_operands(w, M=M, N=N, K=K)
+    rng = np.random.default_rng(7)
+    rows, cols = inputs.sample_indices(M, N, 2000, 8)
+    if split_tiles:
+        pick = rng.integers(0, len(split_tiles), 2000)
+        tr = np.array([split_tiles[i][0] for i in pick]) * 256 + rng.integers(0, 256, 2000)
+        tc = np.array([split_tiles[i][1] for i in pick]) * 256 + rng.integers(0, 256, 2000)
+        keep = (tr < M) & (tc < N)
+        rows = np.concatenate([rows, tr[keep]]).astype(np.int64)
+        cols = np.concatenate([cols, tc[keep]]).astype(np.int64)
+    ldb = K if layout == "nt" else N
+    d, s_ = oracle.gemm_entries(layout, fmt, A, B, K=K, lda=K, ldb=ldb, rows=rows, cols=cols)
+    for mode in ("auto", "off"):
+        if mode == "off":
+            monkeypatch.setenv("DENSE_GEMM_SPLITK", "off")
+        else:
+            monkeypatch.delenv("DENSE_GEMM_SPLITK", raising=False)
+        D, st = _gpu.gemm(layout, fmt, A, B, M, N, K)
+        assert st == status().OK
+        res = oracle.check(fmt, d, s_, D[rows, cols])
+        assert res.ok, (mode, res)
+        D2, _ = _gpu.gemm(layout, fmt, A, B, M, N, K)
+        assert (D == D2).all()
