@@ -17,6 +17,11 @@ What it computes, with citations (page titles and sections):
   bf16 cast at the end -> :func:`gemm` with ``layout="nn"``.
 * The acceptance bound |d_gpu - d| <= ulp_out(|d|) + 2^-11 * sum_k |a*b| ->
   :func:`check`.
+* CMU "TIRx" blog, section "Evaluation", "Kernel performance": FP8
+  block-scaled matrix multiplication (groups of inputs share a scale) ->
+  :func:`gemm_mx`, in the reading stated in ``oracle.c``: E4M3 elements,
+  one E8M0 power-of-two scale per 32 consecutive K values of a row, A @ B.T,
+  BF16 output.
 
 Parity status: every function here is pinned by CPU tests (exact rational
 brute force, invariants, library special cases and the worked values printed
@@ -73,6 +78,15 @@ def _load():
     lib.oracle_round_array.restype = None
     lib.oracle_check.argtypes = [i32, i64, vp, vp, vp, vp, vp, vp]
     lib.oracle_check.restype = None
+    lib.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
+    lib.oracle_decode_e4m3.restype = dbl
+    lib.oracle_decode_e8m0.argtypes = [ctypes.c_uint8]
+    lib.oracle_decode_e8m0.restype = dbl
+    lib.oracle_gemm_mx.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, i64]
+    lib.oracle_gemm_mx.restype = i32
+    lib.oracle_gemm_mx_entries.argtypes = [i64, vp, i64, vp, i64, vp, i64, vp, i64, i64, vp, vp,
+                                           vp, vp]
+    lib.oracle_gemm_mx_entries.restype = None
     _lib = lib
     return lib
 
@@ -187,3 +201,63 @@ def check(fmt: str, d, s, g_bits) -> CheckResult:
     lib.oracle_check(FMT[fmt], d.size, _ptr(d), _ptr(s), _ptr(g), ctypes.byref(nf),
                      ctypes.byref(wi), ctypes.byref(wr))
     return CheckResult(d.size, nf.value, wi.value, wr.value)
+
+
+# ---- FP8 block-scaled (MX) product ------------------------------------------
+
+def _bytes(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8:
+        raise TypeError("FP8 operands and E8M0 scales are byte codes (uint8), got %s" % a.dtype)
+    return a
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    """Exact double value of each E4M3 byte code (NaN for S.1111.111)."""
+    lib = _load()
+    c = _bytes(codes)
+    return np.array([lib.oracle_decode_e4m3(int(v)) for v in c.reshape(-1)],
+                    dtype=np.float64).reshape(c.shape)
+
+
+def decode_e8m0(codes) -> np.ndarray:
+    """2^(e - 127) for each E8M0 byte code (NaN for 255)."""
+    lib = _load()
+    c = _bytes(codes)
+    return np.array([lib.oracle_decode_e8m0(int(v)) for v in c.reshape(-1)],
+                    dtype=np.float64).reshape(c.shape)
+
+
+def gemm_mx(A, SA, B, SB):
+    """D = A @ B.T with E4M3 A (M x K), B (N x K) and E8M0 scales SA
+    (M x ceil(K/32)), SB (N x ceil(K/32)), all dense 2-D byte arrays.
+    Returns (d, s), both (M, N) float64."""
+    lib = _load()
+    A, SA, B, SB = _bytes(A), _bytes(SA), _bytes(B), _bytes(SB)
+    M, K = A.shape
+    N = B.shape[0]
+    nb = (K + 31) // 32
+    if B.shape[1] != K or SA.shape != (M, nb) or SB.shape != (N, nb):
+        raise ValueError("gemm_mx: inconsistent shapes")
+    d = np.empty((M, N), dtype=np.float64)
+    s = np.empty((M, N), dtype=np.float64)
+    rc = lib.oracle_gemm_mx(M, N, K, _ptr(A), K, _ptr(SA), nb, _ptr(B), K, _ptr(SB), nb,
+                            _ptr(d), _ptr(s), max(N, 1))
+    if rc != 0:
+        raise MemoryError("oracle_gemm_mx could not allocate its scratch arrays")
+    return d, s
+
+
+def gemm_mx_entries(A, SA, B, SB, rows, cols):
+    """Selected elements d[rows[t], cols[t]], s[rows[t], cols[t]] of gemm_mx."""
+    lib = _load()
+    A, SA, B, SB = _bytes(A), _bytes(SA), _bytes(B), _bytes(SB)
+    K = A.shape[1]
+    nb = (K + 31) // 32
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    d = np.empty(rows.size, dtype=np.float64)
+    s = np.empty(rows.size, dtype=np.float64)
+    lib.oracle_gemm_mx_entries(K, _ptr(A), K, _ptr(SA), nb, _ptr(B), K, _ptr(SB), nb,
+                               rows.size, _ptr(rows), _ptr(cols), _ptr(d), _ptr(s))
+    return d, s

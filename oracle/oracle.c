@@ -227,3 +227,90 @@ void oracle_check(int fmt, int64_t n, const double* d, const double* s, const ui
   *worst_idx = widx;
   *worst_ratio = wr;
 }
+
+/* ---- FP8 block-scaled product --------------------------------------------
+ *
+ * CMU "TIRx" blog, section "Evaluation", "Kernel performance": FP8
+ * block-scaled matrix multiplication, in which groups of input values share
+ * scale factors.  The page fixes neither the FP8 encoding, nor the group
+ * size, nor the scale format; TileFoundry's schedule tutorial, section 4,
+ * lists fp8e4m3 operands as K-major on both sides.  The reading taken here
+ * (the OCP microscaling layout): elements are E4M3 (1 sign, 4 exponent bits
+ * with bias 7, 3 fraction bits; exponent field 0 is subnormal; S.1111.111 is
+ * NaN; no infinities), and each group of 32 consecutive K values of a row
+ * shares one E8M0 scale, the power of two 2^(e - 127) (e = 255 is NaN).
+ * A is M x K (row i at A + i*lda), B is N x K (D = A @ B.T), the scales SA
+ * are M x ceil(K/32) (row i at SA + i*ldsa), SB are N x ceil(K/32):
+ *
+ *   d[i][j] = sum_k dec8(A[i][k]) 2^(SA[i][k/32]-127) dec8(B[j][k]) 2^(SB[j][k/32]-127)
+ *   s[i][j] = the same sum of absolute values
+ *
+ * Each scaled element is exact in double (4 significant bits, exponents
+ * within +-136), so is every product; the sum runs in ascending k in
+ * double.  The output format is BF16 (the same single rounding as above). */
+
+double oracle_decode_e4m3(uint8_t v) {
+  const int e = (v >> 3) & 15, m = v & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return (v & 0x80) ? -mag : mag;
+}
+
+double oracle_decode_e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+static double mx_value(const uint8_t* X, int64_t ldx, const uint8_t* SX, int64_t ldsx, int64_t r,
+                       int64_t k) {
+  return oracle_decode_e4m3(X[r * ldx + k]) * oracle_decode_e8m0(SX[r * ldsx + k / 32]);
+}
+
+/* Full product (D, S: M x N with leading dimension ldo, either may be NULL).
+ * Returns 0, or -1 if the scratch arrays cannot be allocated. */
+int oracle_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                   const uint8_t* SA, int64_t ldsa, const uint8_t* B, int64_t ldb,
+                   const uint8_t* SB, int64_t ldsb, double* D, double* S, int64_t ldo) {
+  double* a64 = (double*)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+  double* b64 = (double*)malloc(sizeof(double) * (size_t)(N * K > 0 ? N * K : 1));
+  if (!a64 || !b64) {
+    free(a64);
+    free(b64);
+    return -1;
+  }
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t k = 0; k < K; ++k) a64[i * K + k] = mx_value(A, lda, SA, ldsa, i, k);
+  for (int64_t j = 0; j < N; ++j)
+    for (int64_t k = 0; k < K; ++k) b64[j * K + k] = mx_value(B, ldb, SB, ldsb, j, k);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < N; ++j) {
+      double d = 0.0, s = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double prod = a64[i * K + k] * b64[j * K + k]; /* exact */
+        d += prod;
+        s += fabs(prod);
+      }
+      if (D) D[i * ldo + j] = d;
+      if (S) S[i * ldo + j] = s;
+    }
+  }
+  free(a64);
+  free(b64);
+  return 0;
+}
+
+/* Selected elements (rows[t], cols[t]) for t < n. */
+void oracle_gemm_mx_entries(int64_t K, const uint8_t* A, int64_t lda, const uint8_t* SA,
+                            int64_t ldsa, const uint8_t* B, int64_t ldb, const uint8_t* SB,
+                            int64_t ldsb, int64_t n, const int64_t* rows, const int64_t* cols,
+                            double* D, double* S) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < n; ++t) {
+    double d = 0.0, s = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      double prod = mx_value(A, lda, SA, ldsa, rows[t], k) * mx_value(B, ldb, SB, ldsb, cols[t], k);
+      d += prod;
+      s += fabs(prod);
+    }
+    D[t] = d;
+    S[t] = s;
+  }
+}

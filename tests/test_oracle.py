@@ -344,3 +344,116 @@ def test_check_detects_a_dropped_k_block():
     res = oracle.check("f16", d, s, oracle.round_to("f16", d2))
     assert res.n_fail > 64 * 64 // 2
     assert oracle.check("f16", d, s, oracle.round_to("f16", d)).ok
+
+
+# ------------------------------------------------ FP8 block-scaled (MX) --
+#
+# oracle.gemm_mx: E4M3 elements, one E8M0 scale per 32 consecutive K values
+# of a row (the reading of the CMU blog's "FP8 block-scaled matrix
+# multiplication" stated in oracle.c).
+
+def _torch_e4m3(codes):
+    import torch
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    return torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+
+
+def _mx_operands(rng, M, N, K, lo=118, hi=136):
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    A = rng.choice(finite, size=(M, K)).astype(np.uint8)
+    B = rng.choice(finite, size=(N, K)).astype(np.uint8)
+    nb = (K + 31) // 32
+    SA = rng.integers(lo, hi + 1, size=(M, nb)).astype(np.uint8)
+    SB = rng.integers(lo, hi + 1, size=(N, nb)).astype(np.uint8)
+    return A, SA, B, SB
+
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine, ref = oracle.decode_e4m3(codes), _torch_e4m3(codes)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.isnan(mine).sum() == 2  # S.1111.111 only
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    # the format's landmarks: largest finite, smallest normal and subnormal
+    assert oracle.decode_e4m3(np.array([0x7E, 0x08, 0x01, 0x80], np.uint8)).tolist() == \
+        [448.0, 2.0 ** -6, 2.0 ** -9, -0.0]
+
+
+def test_e8m0_decode_matches_float32_exponent_field():
+    import struct
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.decode_e8m0(codes)
+    assert np.isnan(mine[255]) and not np.isnan(mine[:255]).any()
+    for e in range(1, 255):  # a float32 with exponent field e and no fraction is 2^(e-127)
+        assert mine[e] == struct.unpack("<f", struct.pack("<I", e << 23))[0]
+    assert mine[0] == 2.0 ** -127
+
+
+@pytest.mark.parametrize("K", [32, 40, 96])
+def test_gemm_mx_matches_exact_rationals(K):
+    rng = np.random.default_rng(K)
+    M, N = 3, 4
+    A, SA, B, SB = _mx_operands(rng, M, N, K)
+    d, s = oracle.gemm_mx(A, SA, B, SB)
+    va, vb = _torch_e4m3(A), _torch_e4m3(B)
+    for i in range(M):
+        for j in range(N):
+            exact = sum(Fraction(va[i, k]) * Fraction(2) ** (int(SA[i, k // 32]) - 127) *
+                        Fraction(vb[j, k]) * Fraction(2) ** (int(SB[j, k // 32]) - 127)
+                        for k in range(K))
+            absum = sum(abs(Fraction(va[i, k]) * Fraction(vb[j, k])) *
+                        Fraction(2) ** (int(SA[i, k // 32]) + int(SB[j, k // 32]) - 254)
+                        for k in range(K))
+            assert abs(Fraction(d[i, j]) - exact) <= K * Fraction(U53) * absum
+            assert Fraction(s[i, j]) == absum or abs(Fraction(s[i, j]) - absum) <= K * Fraction(U53) * absum
+
+
+def test_gemm_mx_unit_scales_is_the_plain_product():
+    rng = np.random.default_rng(11)
+    M, N, K = 37, 29, 160
+    A, SA, B, SB = _mx_operands(rng, M, N, K, 127, 127)
+    d, s = oracle.gemm_mx(A, SA, B, SB)
+    ref = _torch_e4m3(A) @ _torch_e4m3(B).T
+    assert np.all(np.abs(d - ref) <= 2 * K * U53 * s)
+
+
+def test_gemm_mx_scale_acts_on_its_block_only():
+    # raising one block's scale by one (x2) adds exactly that block's share:
+    # a wrong block size, a wrong block index or a scale applied to the wrong
+    # operand changes a different share
+    rng = np.random.default_rng(12)
+    M, N, K = 9, 7, 160
+    A, SA, B, SB = _mx_operands(rng, M, N, K)
+    d0, s0 = oracle.gemm_mx(A, SA, B, SB)
+    for b in range(K // 32):
+        SA2 = SA.copy()
+        SA2[:, b] += 1
+        d1, _ = oracle.gemm_mx(A, SA2, B, SB)
+        part, _ = oracle.gemm_mx(np.ascontiguousarray(A[:, 32 * b:32 * b + 32]),
+                                 np.ascontiguousarray(SA[:, b:b + 1]),
+                                 np.ascontiguousarray(B[:, 32 * b:32 * b + 32]),
+                                 np.ascontiguousarray(SB[:, b:b + 1]))
+        assert np.all(np.abs((d1 - d0) - part) <= 4 * K * U53 * 2 * s0)
+        SB2 = SB.copy()
+        SB2[:, b] -= 1
+        d2, _ = oracle.gemm_mx(A, SA, B, SB2)
+        assert np.all(np.abs((d0 - d2) - part / 2) <= 4 * K * U53 * s0)
+
+
+def test_gemm_mx_entries_agree_with_full_product():
+    rng = np.random.default_rng(13)
+    A, SA, B, SB = _mx_operands(rng, 33, 21, 224)
+    d, s = oracle.gemm_mx(A, SA, B, SB)
+    rows = rng.integers(0, 33, 50)
+    cols = rng.integers(0, 21, 50)
+    de, se = oracle.gemm_mx_entries(A, SA, B, SB, rows, cols)
+    assert np.array_equal(de, d[rows, cols]) and np.array_equal(se, s[rows, cols])
+
+
+def test_gemm_mx_nan_scale_propagates():
+    rng = np.random.default_rng(14)
+    A, SA, B, SB = _mx_operands(rng, 4, 4, 64)
+    SA[2, 1] = 255
+    d, _ = oracle.gemm_mx(A, SA, B, SB)
+    assert np.isnan(d[2]).all() and not np.isnan(np.delete(d, 2, axis=0)).any()
