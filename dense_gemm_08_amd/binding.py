@@ -48,6 +48,8 @@ SIGNATURES = {
     "gemm_nt_bf16": (_GEMM_ARGS, _i32),
     "gemm_nn_f16": (_GEMM_ARGS, _i32),
     "gemm_nt_f16_ladder": ([_i32] + _GEMM_ARGS, _i32),
+    "gemm_nt_e4m3_mx": ([_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                         _vp], _i32),
     "dense_gemm_status_string": ([_i32], ctypes.c_char_p),
     "dense_gemm_validate": ([_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64], _i32),
     "dense_gemm_tile_of_task": ([_i64, _i64, _i64, _i64, ctypes.POINTER(_i64),
@@ -159,3 +161,32 @@ def gemm_nn_f16(A, B, D=None, stream=None):
 def raw(name: str):
     """The raw ctypes function ``name`` (for calls with explicit pointers)."""
     return getattr(load_library(), name)
+
+
+def gemm_nt_e4m3_mx(A, SA, B, SB, D=None, stream=None):
+    """D = A @ B.T with E4M3 A (M x K), B (N x K) and E8M0 block scales SA
+    (M x K/32), SB (N x K/32), FP32 accumulation, BF16 out.  A and B are
+    uint8 or float8_e4m3fn device tensors, SA and SB uint8 device tensors,
+    all 2-D with unit column stride."""
+    import torch
+    lib = load_library()
+    for t, what in ((A, "A"), (SA, "SA"), (B, "B"), (SB, "SB")):
+        if t.element_size() != 1 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("%s must be a 2-D byte device tensor with unit column stride" % what)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(SA.shape) != (M, K // 32) or tuple(SB.shape) != (N, K // 32):
+        raise ValueError("inconsistent shapes: A %s, SA %s, B %s, SB %s"
+                         % (tuple(A.shape), tuple(SA.shape), tuple(B.shape), tuple(SB.shape)))
+    if D is None:
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    else:
+        _check_tensor(D, "bf16", "D")
+        if D.shape[0] != M or D.shape[1] != N:
+            raise ValueError("D has shape %s, expected (%d, %d)" % (tuple(D.shape), M, N))
+    st = lib.gemm_nt_e4m3_mx(M, N, K, A.data_ptr(), A.stride(0), SA.data_ptr(), SA.stride(0),
+                             B.data_ptr(), B.stride(0), SB.data_ptr(), SB.stride(0),
+                             D.data_ptr(), D.stride(0), _stream_handle(stream))
+    if st != Status.OK:
+        raise DenseGemmError(st, "gemm_nt_e4m3_mx")
+    return D

@@ -1,8 +1,9 @@
 """Build step for libdense_gemm.so (hipcc, gfx950 only).
 
 ``python -m dense_gemm_08_amd.build`` compiles ``csrc/dense_gemm.hip`` (the
-library's kernels and C ABI) and ``csrc/ladder.hip`` (the optimisation-step
-kernels) into ``dense_gemm_08_amd/libdense_gemm.so`` in place.
+library's kernels and C ABI), ``csrc/ladder.hip`` (the optimisation-step
+kernels) and ``csrc/gemm_mx.hip`` (the FP8 block-scaled product) into
+``dense_gemm_08_amd/libdense_gemm.so`` in place.
 """
 from __future__ import annotations
 
@@ -12,7 +13,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", "dense_gemm.hip"), os.path.join(HERE, "csrc", "ladder.hip")]
+SRCS = [os.path.join(HERE, "csrc", n) for n in ("dense_gemm.hip", "ladder.hip", "gemm_mx.hip")]
 OUT = os.path.join(HERE, "libdense_gemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

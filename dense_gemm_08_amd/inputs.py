@@ -134,6 +134,72 @@ def random_finite_bits(fmt: str, shape, seed: int) -> np.ndarray:
     return out
 
 
+# ---- FP8 block-scaled (MX) operands ----------------------------------------
+#
+# E4M3 element codes and E8M0 scale codes (one per 32 consecutive K values of
+# a row), as byte arrays.  Two recipes:
+#
+# * "quantised": A then B drawn N(0, sigma^2) in float64; each block of 32
+#   takes the power-of-two scale 2^e with e = floor(log2(max |x|)) - 8 (8 is
+#   the exponent of E4M3's largest binade), and each value x / 2^e, clipped
+#   to +-448, is rounded to E4M3 by torch's float8_e4m3fn cast (via float32).
+#   This is the OCP microscaling recipe; it puts each block's largest values
+#   in E4M3's top binade, as real quantised tensors do.
+# * "codes": every finite E4M3 code equally likely (subnormals and both
+#   zeros included) and scale codes uniform in [lo, hi].
+
+E4M3_FINITE = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def _e4m3_codes(x: np.ndarray) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def _quantise_blocks(x: np.ndarray):
+    rows, K = x.shape
+    nb = K // 32
+    blocks = x.reshape(rows, nb, 32)
+    amax = np.abs(blocks).max(axis=2)
+    e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, 0).astype(np.int64)
+    e = np.clip(e, -127, 127)
+    scaled = np.clip(blocks / np.exp2(e)[:, :, None], -448.0, 448.0).reshape(rows, K)
+    return _e4m3_codes(scaled), (e + 127).astype(np.uint8)
+
+
+def mx_operands(M: int, N: int, K: int, seed: int, kind: str = "quantised", sigma: float = 1.0,
+                lo: int = 118, hi: int = 136):
+    """(A, SA, B, SB) byte arrays: A M x K and B N x K E4M3 codes, SA M x K/32
+    and SB N x K/32 E8M0 codes (K a multiple of 32)."""
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if kind == "quantised":
+        A, SA = _quantise_blocks(rng.standard_normal(size=(M, K)) * sigma)
+        B, SB = _quantise_blocks(rng.standard_normal(size=(N, K)) * sigma)
+        return A, SA, B, SB
+    if kind == "codes":
+        A = rng.choice(E4M3_FINITE, size=(M, K))
+        B = rng.choice(E4M3_FINITE, size=(N, K))
+        SA = rng.integers(lo, hi + 1, size=(M, K // 32)).astype(np.uint8)
+        SB = rng.integers(lo, hi + 1, size=(N, K // 32)).astype(np.uint8)
+        return A, SA, B, SB
+    raise ValueError("unknown kind %r" % kind)
+
+
+def mx_small_integers(M: int, N: int, K: int, seed: int, lo: int = -3, hi: int = 3):
+    """Integer-valued E4M3 codes in [lo, hi] with scales 2^0 or 2^1: every
+    product and partial sum is an integer far below 2^24, so the FP32
+    accumulation is exact in any order."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    A = _e4m3_codes(rng.integers(lo, hi + 1, size=(M, K)).astype(np.float64))
+    B = _e4m3_codes(rng.integers(lo, hi + 1, size=(N, K)).astype(np.float64))
+    SA = rng.integers(127, 129, size=(M, K // 32)).astype(np.uint8)
+    SB = rng.integers(127, 129, size=(N, K // 32)).astype(np.uint8)
+    return A, SA, B, SB
+
+
 def sample_indices(M: int, N: int, n: int, seed: int):
     """``n`` (row, col) pairs for spot checks of large outputs: uniform draws,
     with an eighth of them moved onto the last row, an eighth onto the last

@@ -138,6 +138,33 @@ dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N, int64_t K,
                                      int64_t lda, const void* B, int64_t ldb, void* D,
                                      int64_t ldd, hipStream_t stream);
 
+/* FP8 block-scaled product: D = A @ B.T with E4M3 elements and one E8M0
+ * scale per 32 consecutive K values of each row, FP32 accumulation, BF16 out.
+ * The CMU TIRx blog ("Evaluation", "Kernel performance") benchmarks an FP8
+ * block-scaled GEMM without fixing its encodings; this entry point takes the
+ * OCP microscaling (MX) reading, the format gfx950's scaled MFMA applies:
+ *     D[i][j] = round_bf16( sum_{k < K} SA[i][k/32] A[i][k] * SB[j][k/32] B[j][k] )
+ * where A[i][k], B[j][k] are the E4M3 ("fn": no infinities, S.1111.111 is
+ * NaN, largest 448) values of the byte codes and SA, SB the E8M0 scales
+ * 2^(code - 127) (code 255 is NaN).  Both operands are K-major:
+ *   A   M x K bytes, element (i, k) at A[i * lda + k]
+ *   B   N x K bytes, element (j, k) at B[j * ldb + k]
+ *   SA  M x K/32 bytes, scale of block b of row i at SA[i * ldsa + b]
+ *   SB  N x K/32 bytes, scale of block b of row j at SB[j * ldsb + b]
+ *   D   M x N bfloat16, element (i, j) at D[i * ldd + j]
+ * K must be a multiple of 32 (DENSE_GEMM_BAD_ARG otherwise); A and B must be
+ * 16-byte aligned with lda and ldb multiples of 16 (DENSE_GEMM_MISALIGNED);
+ * D needs 2-byte alignment.  M, N and K/128 may be ragged.  The products are
+ * exact in FP32; their sum is accumulated in FP32 in a fixed order.  The call
+ * takes a workspace of 1 KiB per 256-row tile of A and of B per 128 K
+ * values for the repacked scales (hipMallocAsync / hipFreeAsync on `stream`;
+ * DENSE_GEMM_NO_MEMORY if unavailable).  The other rules (zeros for K == 0,
+ * ownership, stream order, errors) are those stated at the top of this file. */
+dense_gemm_status gemm_nt_e4m3_mx(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                  const void* SA, int64_t ldsa, const void* B, int64_t ldb,
+                                  const void* SB, int64_t ldsb, void* D, int64_t ldd,
+                                  hipStream_t stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char* dense_gemm_status_string(int status);
 

@@ -229,3 +229,33 @@ def test_plan_split_k():
         if sp > 1:
             assert (sp - 1) * st < nk <= sp * st and st >= 4 and tiles * sp <= 256
             assert out[5] == tiles * sp
+
+
+def _mx(M, N, K, A=64, lda=None, SA=64, ldsa=None, B=64, ldb=None, SB=64, ldsb=None, D=64,
+        ldd=None):
+    """gemm_nt_e4m3_mx on fake addresses: every case here is rejected (or
+    empty) before the library touches the device."""
+    lib = binding.load_library()
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldsa = K // 32 if ldsa is None else ldsa
+    ldsb = K // 32 if ldsb is None else ldsb
+    ldd = N if ldd is None else ldd
+    return S(lib.gemm_nt_e4m3_mx(M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, D, ldd, None))
+
+
+def test_mx_argument_checks_on_the_host():
+    assert _mx(-1, 8, 64) == S.INVALID_DIM
+    assert _mx(8, 8, -32) == S.INVALID_DIM
+    assert _mx(0, 8, 64) == S.OK and _mx(8, 0, 64) == S.OK  # nothing to do
+    assert _mx(1 << 31, 8, 64) == S.TOO_LARGE
+    assert _mx(8, 8, 40) == S.BAD_ARG       # K not a multiple of 32
+    assert _mx(8, 8, 64, D=0) == S.NULL_PTR
+    assert _mx(8, 8, 64, SB=0) == S.NULL_PTR
+    assert _mx(8, 8, 64, lda=48) == S.BAD_LD
+    assert _mx(8, 8, 64, ldsa=1) == S.BAD_LD
+    assert _mx(8, 8, 64, ldd=7) == S.BAD_LD
+    assert _mx(8, 8, 64, D=65) == S.MISALIGNED   # odd BF16 address
+    assert _mx(8, 8, 64, A=72) == S.MISALIGNED   # A not 16-byte aligned
+    assert _mx(8, 8, 64, ldb=72) == S.MISALIGNED  # B rows not 16-byte aligned
+    assert _mx(8, 8, 1 << 24, lda=1 << 24, ldb=1 << 24) == S.TOO_LARGE  # tile span >= 2 GiB

@@ -1,0 +1,228 @@
+"""GPU parity tests of the FP8 block-scaled product (gemm_nt_e4m3_mx) against
+the CPU oracle's gemm_mx, through the C ABI.
+
+Acceptance (per element): |d_gpu - d| <= ulp_bf16(|d|) + 2^-11 * s with d the
+oracle's exact FP64 value and s = sum_k |SA a SB b| (the products are exact
+in FP32, so only the FP32 sum and the final rounding err).  Small-integer
+inputs, whose FP32 sums are exact in any order, must give the correctly
+rounded BF16 value bit for bit.  Shapes span several 256 x 256 tiles with
+ragged M and N, and K values whose remainder modulo the 128-deep stage is 0,
+32, 64 and 96; the full-size workloads are checked on sampled entries in the
+launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_08_amd import inputs
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+BYTE_CANARY = 0x7F  # an E4M3 NaN: a read of padding would show in the result
+
+
+def status():
+    from dense_gemm_08_amd.binding import Status
+    return Status
+
+
+def bytes_dev(codes, rows, cols, ld, off=0, fill=BYTE_CANARY):
+    t = _gpu.torch()
+    host = np.full(rows * ld + off + 64, fill, dtype=np.uint8)
+    if rows and cols:
+        host[off:off + rows * ld].reshape(rows, ld)[:, :cols] = codes.reshape(rows, cols)
+    return t.from_numpy(host).to("cuda")
+
+
+def mx_call(M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, D, ldd, offs=(0, 0, 0, 0, 0)):
+    from dense_gemm_08_amd import binding
+    t = _gpu.torch()
+    ptr = lambda x, o: 0 if x is None else x.data_ptr() + o  # noqa: E731
+    fn = binding.raw("gemm_nt_e4m3_mx")
+    return binding.Status(fn(M, N, K, ptr(A, offs[0]), lda, ptr(SA, offs[1]), ldsa,
+                             ptr(B, offs[2]), ldb, ptr(SB, offs[3]), ldsb, ptr(D, offs[4]), ldd,
+                             t.cuda.current_stream().cuda_stream))
+
+
+def run_mx(A, SA, B, SB, lda=None, ldb=None, ldsa=None, ldsb=None, ldd=None):
+    """Upload, run, download.  Returns (D bits M x ldd, status)."""
+    t = _gpu.torch()
+    M, K = A.shape
+    N = B.shape[0]
+    nb = K // 32
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldsa = nb if ldsa is None else ldsa
+    ldsb = nb if ldsb is None else ldsb
+    ldd = N if ldd is None else ldd
+    dA = bytes_dev(A, M, K, lda)
+    dB = bytes_dev(B, N, K, ldb)
+    dSA = bytes_dev(SA, M, nb, ldsa, fill=0xFF)
+    dSB = bytes_dev(SB, N, nb, ldsb, fill=0xFF)
+    dD = _gpu.to_dev_at(np.zeros(0, np.uint16), M, 0, ldd, 0)
+    st = mx_call(M, N, K, dA, lda, dSA, ldsa, dB, ldb, dSB, ldsb, dD, ldd)
+    t.cuda.synchronize()
+    host = _gpu.from_dev(dD)
+    assert (host[M * ldd:] == _gpu.CANARY).all()
+    return host[:M * ldd].reshape(M, ldd), st
+
+
+def check_full(A, SA, B, SB, D):
+    M, N = A.shape[0], B.shape[0]
+    d, s = oracle.gemm_mx(A, SA, B, SB)
+    res = oracle.check("bf16", d, s, D[:, :N])
+    assert res.ok, (res, np.unravel_index(max(res.worst_idx, 0), (M, N)))
+    return d
+
+
+SHAPES = [
+    # (M, N, K): K mod 128 = 0, 32, 64, 96; ragged M and N; one tile to many
+    (256, 256, 128),
+    (300, 200, 96),
+    (513, 1000, 416),
+    (1024, 768, 1024),
+    (64, 1100, 2080),
+    (777, 530, 320),
+]
+
+
+@pytest.mark.parametrize("kind", ["quantised", "codes"])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_mx_full_parity(kind, M, N, K):
+    A, SA, B, SB = inputs.mx_operands(M, N, K, seed=M + 7 * N + K, kind=kind)
+    D, st = run_mx(A, SA, B, SB)
+    assert st == status().OK
+    check_full(A, SA, B, SB, D)
+
+
+@pytest.mark.parametrize("M,N,K", [(520, 300, 2048), (256, 512, 160)])
+def test_mx_small_integers_bit_exact(M, N, K):
+    A, SA, B, SB = inputs.mx_small_integers(M, N, K, seed=K)
+    D, st = run_mx(A, SA, B, SB)
+    assert st == status().OK
+    d, _ = oracle.gemm_mx(A, SA, B, SB)
+    want = oracle.round_to("bf16", d)
+    assert np.array_equal(D, want), np.argwhere(D != want)[:5]
+
+
+def test_mx_leading_dimensions_and_untouched_padding():
+    M, N, K = 300, 270, 352
+    A, SA, B, SB = inputs.mx_operands(M, N, K, seed=11)
+    D, st = run_mx(A, SA, B, SB, lda=K + 48, ldb=K + 16, ldsa=K // 32 + 3, ldsb=K // 32 + 1,
+                   ldd=N + 5)
+    assert st == status().OK
+    assert (D[:, N:] == _gpu.CANARY).all()
+    check_full(A, SA, B, SB, D)
+
+
+def test_mx_repeatable():
+    A, SA, B, SB = inputs.mx_operands(700, 600, 1152, seed=12, kind="codes")
+    D1, st1 = run_mx(A, SA, B, SB)
+    D2, st2 = run_mx(A, SA, B, SB)
+    assert st1 == st2 == status().OK
+    assert np.array_equal(D1, D2)
+
+
+def test_mx_k_zero_writes_zeros_and_empty_writes_nothing():
+    t = _gpu.torch()
+    D = _gpu.empty_out(40, 50)
+    st = mx_call(40, 50, 0, None, 0, None, 0, None, 0, None, 0, D, 50)
+    t.cuda.synchronize()
+    assert st == status().OK
+    assert (_gpu.from_dev(D) == 0).all()
+    D = _gpu.empty_out(8, 8)
+    for M, N in ((0, 8), (8, 0)):
+        st = mx_call(M, N, 64, None, 64, None, 2, None, 64, None, 2, D, 8)
+        assert st == status().OK
+    t.cuda.synchronize()
+    assert (_gpu.from_dev(D) == _gpu.CANARY).all()
+
+
+def test_mx_argument_errors_leave_d_untouched():
+    S = status()
+    t = _gpu.torch()
+    M, N, K = 64, 64, 128
+    A, SA, B, SB = inputs.mx_operands(M, N, K, seed=13)
+    dA, dB = bytes_dev(A, M, K, K + 32), bytes_dev(B, N, K, K)
+    dSA, dSB = bytes_dev(SA, M, 4, 4), bytes_dev(SB, N, 4, 4)
+    D = _gpu.empty_out(M + 1, N + 1)
+    base = dict(M=M, N=N, K=K, A=dA, lda=K, SA=dSA, ldsa=4, B=dB, ldb=K, SB=dSB, ldsb=4, D=D,
+                ldd=N)
+    cases = [
+        (dict(K=40), S.BAD_ARG),          # K not a multiple of the 32-value block
+        (dict(M=-1), S.INVALID_DIM),
+        (dict(lda=K - 16), S.BAD_LD),
+        (dict(ldsb=3), S.BAD_LD),
+        (dict(ldd=N - 1), S.BAD_LD),
+        (dict(lda=K + 8), S.MISALIGNED),  # rows not 16-byte aligned
+        (dict(A=None), S.NULL_PTR),
+        (dict(D=None), S.NULL_PTR),
+    ]
+    for change, want in cases:
+        a = dict(base)
+        a.update(change)
+        st = mx_call(a["M"], a["N"], a["K"], a["A"], a["lda"], a["SA"], a["ldsa"], a["B"],
+                     a["ldb"], a["SB"], a["ldsb"], a["D"], a["ldd"])
+        assert st == want, (change, st)
+    # misaligned pointers: A 8 bytes in, D at an odd byte address
+    st = mx_call(M, N, K, dA, K, dSA, 4, dB, K, dSB, 4, D, N, offs=(8, 0, 0, 0, 0))
+    assert st == S.MISALIGNED
+    st = mx_call(M, N, K, dA, K, dSA, 4, dB, K, dSB, 4, D, N, offs=(0, 0, 0, 0, 1))
+    assert st == S.MISALIGNED
+    t.cuda.synchronize()
+    assert (_gpu.from_dev(D) == _gpu.CANARY).all()
+
+
+def test_mx_python_binding_takes_float8_tensors():
+    import dense_gemm_08_amd as dg
+    t = _gpu.torch()
+    M, N, K = 260, 300, 256
+    A, SA, B, SB = inputs.mx_operands(M, N, K, seed=14)
+    dev = lambda x: t.from_numpy(x).to("cuda")  # noqa: E731
+    D = dg.gemm_nt_e4m3_mx(dev(A).view(t.float8_e4m3fn), dev(SA), dev(B), dev(SB))
+    t.cuda.synchronize()
+    assert D.dtype == t.bfloat16 and tuple(D.shape) == (M, N)
+    check_full(A, SA, B, SB, D.cpu().view(t.int16).numpy().view(np.uint16))
+
+
+MX_FULL = [
+    # the sizes the benchmark runs, in its launch configuration
+    (8192, 8192, 8192),
+    (8192, 17408, 5120),
+]
+
+
+@pytest.mark.parametrize("M,N,K", MX_FULL)
+def test_mx_full_size_sampled(M, N, K):
+    t = _gpu.torch()
+    A, SA, B, SB = inputs.mx_operands(M, N, K, seed=21)
+    nb = K // 32
+    dA, dB = t.from_numpy(A).to("cuda"), t.from_numpy(B).to("cuda")
+    dSA, dSB = t.from_numpy(SA).to("cuda"), t.from_numpy(SB).to("cuda")
+    D = t.empty((M, N), dtype=t.int16, device="cuda")
+    st = mx_call(M, N, K, dA, K, dSA, nb, dB, K, dSB, nb, D, N)
+    t.cuda.synchronize()
+    assert st == status().OK
+    rows, cols = inputs.sample_indices(M, N, 3000, seed=3)
+    d, s = oracle.gemm_mx_entries(A, SA, B, SB, rows, cols)
+    g = D.cpu().numpy().view(np.uint16)[rows, cols]
+    res = oracle.check("bf16", d, s, g)
+    assert res.ok, (res, rows[max(res.worst_idx, 0)], cols[max(res.worst_idx, 0)])
+
+
+def test_mx_nan_scale_and_nan_element_propagate_like_the_oracle():
+    M, N, K = 256, 300, 256
+    A, SA, B, SB = inputs.mx_operands(M, N, K, seed=15)
+    SA[3, 1] = 255   # E8M0 NaN: row 3 of D is NaN
+    SB[7, 6] = 255   # column 7 of D is NaN
+    A[5, 100] = 0x7F  # E4M3 NaN: row 5 of D is NaN
+    D, st = run_mx(A, SA, B, SB)
+    assert st == status().OK
+    d, s = oracle.gemm_mx(A, SA, B, SB)
+    g = oracle.decode("bf16", D)
+    assert np.array_equal(np.isnan(g), np.isnan(d))
+    assert np.isnan(d[3]).all() and np.isnan(d[:, 7]).all() and np.isnan(d[5]).all()
+    ok = ~np.isnan(d)
+    res = oracle.check("bf16", d[ok], s[ok], D[ok])
+    assert res.ok, res
