@@ -26,7 +26,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, published
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0}  # MI355X dense MFMA, published
 
 
 def parse():
@@ -34,7 +34,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="square_nt")
+    ap.add_argument("--workload", default="square_nt",
+                    help="a workload of dense_gemm_08_amd/inputs.py: WORKLOADS (FP16/BF16) or "
+                         "MX_WORKLOADS (FP8 block-scaled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ld-pad", type=int, default=0,
                     help="extra elements on every leading dimension (lda, ldb, ldd)")
@@ -54,19 +56,24 @@ def parse():
                     help="instead of one workload, time each optimisation-step kernel "
                          "(gemm_nt_f16_ladder levels 1-6) on the 4096^3 FP16 workload "
                          "(one JSON line per level)")
+    ap.add_argument("--mx-sweep", action="store_true",
+                    help="instead of one workload, time the FP8 block-scaled product at M = 8192 "
+                         "over the sweep grid (one JSON line per shape, torch._scaled_mm with "
+                         "the same block scales and with per-tensor scales timed beside it)")
     return ap.parse_args()
 
 
 SWEEP_GRID = [1024, 2048, 4096, 8192, 16384]
 
 
-def sweep_shapes():
+def sweep_shapes(k_extra: int = 40):
     """M = 8192 with N and K over powers of two from 1024 to 16384, plus
     ragged neighbours: N + 128 (a half-filled last tile column) at K = 4096
-    and K + 40 (a partial last K step) at N = 4096."""
+    and K + k_extra (a partial last K step; 32 for the block-scaled product,
+    whose K is a multiple of its 32-value scale blocks) at N = 4096."""
     shapes = [(8192, n, k) for n in SWEEP_GRID for k in SWEEP_GRID]
     shapes += [(8192, n + 128, 4096) for n in SWEEP_GRID]
-    shapes += [(8192, 4096, k + 40) for k in SWEEP_GRID]
+    shapes += [(8192, 4096, k + k_extra) for k in SWEEP_GRID]
     return shapes
 
 
@@ -168,6 +175,100 @@ def run_sweep(args):
         del A, B, D, Dt
 
 
+def _event_timer(stream):
+    import torch
+
+    def timed(fn, steps, warm):
+        for _ in range(warm):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    return timed
+
+
+def run_mx_sweep(args):
+    """The FP8 block-scaled product over the M = 8192 sweep shapes: random
+    finite E4M3 codes and E8M0 scales from torch's seeded device generator
+    (timing only; tests check the product against the oracle), HIP events
+    around about 50 ms of back-to-back calls.  Beside it, torch._scaled_mm
+    with the same 1 x 32 block scales and, where it runs, with one scale per
+    tensor (the library products of this PyTorch build)."""
+    import torch
+    from dense_gemm_08_amd import binding
+    lib = binding.load_library()
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    stream = torch.cuda.current_stream()
+    timed = _event_timer(stream)
+    for M, N, K in sweep_shapes(k_extra=32):
+        A = torch.randint(0, 255, (M, K), device=dev, generator=gen, dtype=torch.uint8)
+        B = torch.randint(0, 255, (N, K), device=dev, generator=gen, dtype=torch.uint8)
+        A[(A & 0x7F) == 0x7F] = 0
+        B[(B & 0x7F) == 0x7F] = 0
+        SA = torch.randint(120, 134, (M, K // 32), device=dev, generator=gen, dtype=torch.uint8)
+        SB = torch.randint(120, 134, (N, K // 32), device=dev, generator=gen, dtype=torch.uint8)
+        D = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        flops = 2.0 * M * N * K
+        steps = max(5, min(200, int(0.05 / (flops / 2.4e15))))
+
+        def ours():
+            st = lib.gemm_nt_e4m3_mx(M, N, K, A.data_ptr(), K, SA.data_ptr(), K // 32,
+                                     B.data_ptr(), K, SB.data_ptr(), K // 32, D.data_ptr(), N,
+                                     stream.cuda_stream)
+            if st != 0:
+                raise binding.DenseGemmError(st, "gemm_nt_e4m3_mx")
+
+        rec = {"mode": "mx_sweep", "M": M, "N": N, "K": K, "steps": steps}
+        ms = timed(ours, steps, max(3, steps // 4))
+        rec.update(kernel_ms=round(ms, 5), tflops=round(flops / ms / 1e9, 1))
+        a8, b8 = A.view(torch.float8_e4m3fn), B.view(torch.float8_e4m3fn)
+        refs = {
+            "scaled_mm_mx": lambda: torch._scaled_mm(
+                a8, b8.t(), scale_a=SA.view(torch.float8_e8m0fnu),
+                scale_b=SB.view(torch.float8_e8m0fnu), out_dtype=torch.bfloat16),
+            "scaled_mm_tensor": lambda: torch._scaled_mm(
+                a8, b8.t(), scale_a=torch.ones((), device=dev),
+                scale_b=torch.ones((), device=dev), out_dtype=torch.bfloat16),
+        }
+        for name, fn in refs.items():
+            try:
+                ms_ref = timed(fn, steps, max(3, steps // 4))
+                rec[name + "_tflops"] = round(flops / ms_ref / 1e9, 1)
+            except (RuntimeError, TypeError, AttributeError) as ex:
+                rec[name + "_tflops"] = None
+                rec[name + "_error"] = str(ex).splitlines()[0][:120]
+        print(json.dumps(rec), flush=True)
+        del A, B, SA, SB, D
+
+
+def cpu_baseline_mx(w, A, SA, B, SB, target_s: float):
+    """Time the oracle's block-scaled product on a bounded sample of rows."""
+    import oracle
+    N, K = w.N, w.K
+    oracle.gemm_mx_entries(A, SA, B, SB, np.zeros(64, np.int64), np.arange(64, dtype=np.int64))
+    t0 = time.perf_counter()
+    oracle.gemm_mx_entries(A, SA, B, SB, np.zeros(N, np.int64), np.arange(N, dtype=np.int64))
+    per_row = max(time.perf_counter() - t0, 1e-6)
+    nrows = int(max(1, min(w.M, target_s / per_row)))
+    rows = np.repeat(np.arange(nrows, dtype=np.int64), N)
+    cols = np.tile(np.arange(N, dtype=np.int64), nrows)
+    t0 = time.perf_counter()
+    oracle.gemm_mx_entries(A, SA, B, SB, rows, cols)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    return {"value": 2.0 * nrows * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d full rows of D (%d x %d outputs, K=%d), FP64 sums of decoded E4M3 "
+                      "times E8M0 scales, %.1f s" % (nrows, nrows, N, K, dt)}
+
+
 def cpu_baseline(w, A, B, target_s: float):
     """Time the oracle on a bounded sample: whole rows of D (all N columns)."""
     import oracle
@@ -211,6 +312,9 @@ def main():
     if args.ladder:
         run_ladder(args)
         return
+    if args.mx_sweep:
+        run_mx_sweep(args)
+        return
 
     if args.copy_mib:
         n = args.copy_mib << 20
@@ -228,29 +332,61 @@ def main():
                           "GB_per_s": 2 * n / dt / 1e9}), flush=True)
         return
 
-    w = inputs.WORKLOADS[args.workload]
-    lib = binding.load_library()
-    entry = getattr(lib, {("nt", "f16"): "gemm_nt_f16", ("nn", "bf16"): "gemm_nn_bf16",
-                          ("nt", "bf16"): "gemm_nt_bf16", ("nn", "f16"): "gemm_nn_f16"}
-                    [(w.layout, w.fmt)])
-    A, B = inputs.make_operands(w)
     dev = torch.device("cuda:0")
-    pad = args.ld_pad
-    lda = w.K + pad
-    ldb = (w.K if w.layout == "nt" else w.N) + pad
-    ldd = w.N + pad
-    Ad = torch.zeros((A.shape[0], lda), dtype=torch.int16, device=dev)
-    Ad[:, :A.shape[1]] = torch.from_numpy(A.view(np.int16)).to(dev)
-    Bd = torch.zeros((B.shape[0], ldb), dtype=torch.int16, device=dev)
-    Bd[:, :B.shape[1]] = torch.from_numpy(B.view(np.int16)).to(dev)
-    Dd = torch.empty((w.M, ldd), dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    lib = binding.load_library()
+    pad = args.ld_pad
+    if args.workload in inputs.MX_WORKLOADS:
+        w = inputs.MX_WORKLOADS[args.workload]
+        if pad % 16:
+            raise SystemExit("--ld-pad must be a multiple of 16 for the FP8 workloads")
+        A, SA, B, SB = inputs.mx_operands(w.M, w.N, w.K, w.seed, kind=w.kind)
+        nb = w.K // 32
+        lda = ldb = w.K + pad
+        ldd = w.N + pad
+        Ad = torch.zeros((w.M, lda), dtype=torch.uint8, device=dev)
+        Ad[:, :w.K] = torch.from_numpy(A).to(dev)
+        Bd = torch.zeros((w.N, ldb), dtype=torch.uint8, device=dev)
+        Bd[:, :w.K] = torch.from_numpy(B).to(dev)
+        SAd = torch.from_numpy(SA).to(dev)
+        SBd = torch.from_numpy(SB).to(dev)
+        Dd = torch.empty((w.M, ldd), dtype=torch.int16, device=dev)
+        fmt, src = "e4m3", "gemm_mx.hip"
 
-    def step():
-        st = entry(w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, Dd.data_ptr(), ldd, sh)
-        if st != 0:
-            raise binding.DenseGemmError(st, "gemm")
+        def step():
+            st = lib.gemm_nt_e4m3_mx(w.M, w.N, w.K, Ad.data_ptr(), lda, SAd.data_ptr(), nb,
+                                     Bd.data_ptr(), ldb, SBd.data_ptr(), nb, Dd.data_ptr(), ldd,
+                                     sh)
+            if st != 0:
+                raise binding.DenseGemmError(st, "gemm_nt_e4m3_mx")
+        config = {"workload": w.name, "layout": "nt", "M": w.M, "N": w.N, "K": w.K,
+                  "lda": lda, "ldb": ldb, "ldd": ldd, "elements": "e4m3",
+                  "scales": "e8m0 per 32 K values of a row", "out": "bf16",
+                  "recipe": w.kind, "seed": w.seed}
+    else:
+        w = inputs.WORKLOADS[args.workload]
+        entry = getattr(lib, {("nt", "f16"): "gemm_nt_f16", ("nn", "bf16"): "gemm_nn_bf16",
+                              ("nt", "bf16"): "gemm_nt_bf16", ("nn", "f16"): "gemm_nn_f16"}
+                        [(w.layout, w.fmt)])
+        A, B = inputs.make_operands(w)
+        lda = w.K + pad
+        ldb = (w.K if w.layout == "nt" else w.N) + pad
+        ldd = w.N + pad
+        Ad = torch.zeros((A.shape[0], lda), dtype=torch.int16, device=dev)
+        Ad[:, :A.shape[1]] = torch.from_numpy(A.view(np.int16)).to(dev)
+        Bd = torch.zeros((B.shape[0], ldb), dtype=torch.int16, device=dev)
+        Bd[:, :B.shape[1]] = torch.from_numpy(B.view(np.int16)).to(dev)
+        Dd = torch.empty((w.M, ldd), dtype=torch.int16, device=dev)
+        fmt, src = w.fmt, "dense_gemm.hip"
+
+        def step():
+            st = entry(w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, Dd.data_ptr(), ldd,
+                       sh)
+            if st != 0:
+                raise binding.DenseGemmError(st, "gemm")
+        config = {"workload": w.name, "layout": w.layout, "M": w.M, "N": w.N, "K": w.K,
+                  "lda": lda, "ldb": ldb, "ldd": ldd, "dist": w.dist, "seed": w.seed}
 
     for _ in range(args.warmup):
         step()
@@ -271,14 +407,14 @@ def main():
     flops = float(w.flops)
     value = flops * args.steps / wall / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.fmt]
+    peak = PEAK_TFLOPS[fmt]
 
     traffic = None
     try:
         with open(args.traffic_json) as f:
             tj = json.load(f)
         rec = tj.get(w.name)
-        if rec and rec.get("kernel_source_sha") == source_sha():
+        if rec and rec.get("kernel_source_sha") == source_sha(src):
             traffic = rec["bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         traffic = None
@@ -295,22 +431,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.fmt,
+        "dtype": fmt,
         "data": "synthetic",
-        "config": {"workload": w.name, "layout": w.layout, "M": w.M, "N": w.N, "K": w.K,
-                   "lda": lda, "ldb": ldb, "ldd": ldd, "dist": w.dist, "seed": w.seed},
+        "config": config,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel_ms": kern_ms},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
+        if fmt == "e4m3":
+            out["cpu_baseline"] = cpu_baseline_mx(w, A, SA, B, SB, args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def source_sha() -> str:
+def source_sha(name: str = "dense_gemm.hip") -> str:
     import hashlib
-    p = os.path.join(ROOT, "dense_gemm_08_amd", "csrc", "dense_gemm.hip")
+    p = os.path.join(ROOT, "dense_gemm_08_amd", "csrc", name)
     with open(p, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 

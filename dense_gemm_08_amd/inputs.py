@@ -168,6 +168,29 @@ def _quantise_blocks(x: np.ndarray):
     return _e4m3_codes(scaled), (e + 127).astype(np.uint8)
 
 
+@dataclass(frozen=True)
+class MxWorkload:
+    name: str
+    M: int
+    N: int
+    K: int
+    kind: str    # recipe of mx_operands
+    seed: int
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+# The pages time their FP8 block-scaled GEMM on eight shapes they do not list;
+# these two stand in: the FP16 page's size doubled in every dimension, and
+# the BF16 tutorial's (8192, 5120) x (5120, 17408) product.
+MX_WORKLOADS = {
+    "mx_square": MxWorkload("mx_square", 8192, 8192, 8192, "quantised", 31),
+    "mx_large": MxWorkload("mx_large", 8192, 17408, 5120, "quantised", 32),
+}
+
+
 def mx_operands(M: int, N: int, K: int, seed: int, kind: str = "quantised", sigma: float = 1.0,
                 lo: int = 118, hi: int = 136):
     """(A, SA, B, SB) byte arrays: A M x K and B N x K E4M3 codes, SA M x K/32
