@@ -9,10 +9,11 @@
 //     tile_sched.h ("TIRx GEMM on Blackwell", V6: persistent CTAs pulling
 //     tiles; TileFoundry schedule tutorial, sections 2-3: persistent CTAs and
 //     the grouped traversal);
-//   * per K step, 16-byte buffer loads of the A and B tiles into registers,
-//     written into a two-stage LDS ring while the previous stage feeds the
-//     matrix cores ("TIRx GEMM on Blackwell", V5: two shared-memory stages so
-//     loading the next K tile overlaps the MMA of the current one);
+//   * per K step, 16-byte LDS-DMA loads of the A and B tiles into LDS rings
+//     (three slots for one operand, two for the other: all 160 KiB) while
+//     the previous stage feeds the matrix cores ("TIRx GEMM on Blackwell",
+//     V5: shared-memory stages so loading the next K tile overlaps the MMA
+//     of the current one);
 //   * an XOR swizzle of 16-byte chunks inside each LDS row, so both the
 //     row-wise tile writes and the column-wise MFMA fragment reads spread over
 //     all banks (the role of the 128-byte swizzle in the TIRx and TileFoundry
@@ -46,7 +47,8 @@ enum Layout { NT = 0, NN = 1 };
 constexpr int BM = 256;              // tile rows (M)
 constexpr int BN = 256;              // tile columns (N)
 constexpr int BK = 64;               // K depth of one LDS stage (128-byte rows)
-constexpr int STAGES = 2;            // LDS ring depth
+constexpr int SLOTS3 = 3;            // LDS ring depth of the early operand (below)
+constexpr int SLOTS2 = 2;            // LDS ring depth of the other operand
 constexpr int MK = 32;               // K depth of one MFMA (16 x 16 x 32)
 constexpr int SUB = BK / MK;         // MFMA k-substeps per stage
 constexpr int WAVES = 4;             // 2 x 2 waves
@@ -58,8 +60,10 @@ constexpr int NI = WTN / 16;         //                               N directio
 constexpr int PAIRS = MI * NI / 2;   // MFMA pairs per substep
 constexpr int A_BYTES = BM * BK * 2;           // 32 KiB: 256 rows x 128 B
 constexpr int B_BYTES = BN * BK * 2;           // 32 KiB
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;  // 128 KiB of the 160 KiB per CU
+constexpr int OP_BYTES = A_BYTES;                   // one operand tile (A and B alike)
+constexpr int RING2 = SLOTS3 * OP_BYTES;            // the two-slot ring follows the other
+constexpr int LDS_BYTES = RING2 + SLOTS2 * OP_BYTES;  // all 160 KiB of a CU
+static_assert(A_BYTES == B_BYTES, "both rings hold tiles of one size");
 constexpr int DMA_PER_OPERAND = A_BYTES / (THREADS * 16);  // 16-byte loads per thread
 constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPERAND;
 // MFMA pairs of the last substep issued before its barrier: the reads of
@@ -96,6 +100,11 @@ struct Frags {
 
 template <typename T, int LAYOUT, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
+  // The operand with the three-slot ring, whose loads are issued a substep
+  // earlier (0 = A, 1 = B): B for A @ B, whose row-major tile (64 rows of
+  // 512 B, far apart in memory) is the costlier one to load (measured: 1.4%
+  // faster than A there); A for A @ B.T (the two are alike).
+  constexpr int EARLY = LAYOUT == NN ? 1 : 0;
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const uint32_t lds0 = lds_addr(smem);
 
@@ -150,7 +159,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
       fa[s] = (wm * WTM + l16) * 128 + (((4 * s + lq) ^ swz_k(l16)) << 4);
-      fb[s] = A_BYTES + (wn * WTN + l16) * 128 + (((4 * s + lq) ^ swz_k(l16)) << 4);
+      fb[s] = (wn * WTN + l16) * 128 + (((4 * s + lq) ^ swz_k(l16)) << 4);
     }
     {
       // transposing reads (NN B): in 16-lane block lq, lane i supplies row
@@ -161,7 +170,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       const int fl = (lane >> 2) & 3;  // == k & 3 of every row this lane reads
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        fbn[j] = A_BYTES + klane * 512 +
+        fbn[j] = klane * 512 +
                  ((wn * 16 + ((2 * j + ((lane & 3) >> 1)) ^ (fl << 2))) << 4) + (lane & 1) * 8;
     }
 
@@ -202,7 +211,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       }
     }
 
-    // LDS-DMA loads of K step ks into ring slot `slot`: the A tile (half 0)
+    // LDS-DMA loads of K step ks into slot `slot` of its ring: the A tile (half 0)
     // or the B tile (half 1), issued one load at a time.  The descriptor
     // starts at the step's first column (K-contiguous tiles) or row (NN B)
     // and ends with the tile's last valid row, rounded up to a whole 8-element
@@ -221,7 +230,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       const int k0 = ks * BK - koff;
       const bool live = ks < kend;
       h.k0 = k0;
-      h.base = lds0 + slot * STAGE_BYTES + half * A_BYTES + (8 * wave) * 1024;
+      h.base = lds0 + (half == EARLY ? 0 : RING2) + slot * OP_BYTES + (8 * wave) * 1024;
       if (half == 0 || LAYOUT == NT) {
         // columns k0 .. K8 of the tile's rows
         const uint64_t src = half == 0 ? (uint64_t)(uintptr_t)(p.A + (int64_t)m0 * p.lda)
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       fence();
     };
     auto refill_stage = [&](int ks, int slot) {
-      const Half ha = half_setup(ks, slot, 0);
+      const Half ha = half_setup(ks, slot, 0);  // A and B slots agree for stages 0 and 1
       const Half hb = half_setup(ks, slot, 1);
 #pragma unroll
       for (int i = 0; i < DMA_PER_OPERAND; ++i) refill_one(ha, 0, i, true);
@@ -262,16 +271,17 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     // instruction at a time: item f < MI reads A fragment f; the rest read the
     // B fragments (NT: one ds_read_b128 each; NN: two transposing reads each).
     constexpr int READS = MI + (LAYOUT == NT ? NI : 2 * NI);
-    auto read_item = [&](int slot, int s, Frags& F, int f) {
-      const char* base = smem + slot * STAGE_BYTES;
+    auto read_item = [&](int es, int ls, int s, Frags& F, int f) {
+      const char* abase = smem + (EARLY == 0 ? es * OP_BYTES : RING2 + ls * OP_BYTES);
+      const char* bbase = smem + (EARLY == 1 ? es * OP_BYTES : RING2 + ls * OP_BYTES);
       if (f < MI) {
-        F.a[f] = *(const u32x4*)(base + fa[s] + f * 2048);
+        F.a[f] = *(const u32x4*)(abase + fa[s] + f * 2048);
       } else if (LAYOUT == NT) {
         const int j = f - MI;
-        F.b[j] = *(const u32x4*)(base + fb[s] + j * 2048);
+        F.b[j] = *(const u32x4*)(bbase + fb[s] + j * 2048);
       } else {
         const int j = (f - MI) >> 1, h = (f - MI) & 1;
-        const u32x2 v = read_tr(base + fbn[j] + (s * 32 + 4 * h) * 512);
+        const u32x2 v = read_tr(bbase + fbn[j] + (s * 32 + 4 * h) * 512);
         F.b[j][2 * h] = v[0];
         F.b[j][2 * h + 1] = v[1];
       }
@@ -280,10 +290,10 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     // loop head then sees the same sequence of outstanding reads from the
     // prologue as from the loop's back edge, and waits only for the ones the
     // first MFMAs need.
-    auto read_frags = [&](int slot, int s, Frags& F) {
+    auto read_frags = [&](int es, int ls, int s, Frags& F) {
 #pragma unroll
       for (int f = 0; f < READS; ++f) {
-        read_item(slot, s, F, f);
+        read_item(es, ls, s, F, f);
         fence();
       }
     };
@@ -302,48 +312,61 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       for (int t = 2 * q; t < 2 * q + 2; ++t) mfma16<T>(acc[t % MI][t / MI], F.b[t / MI], F.a[t % MI]);
     };
 
-    // The ring: stage ks lives in slot ks % 2.  Entering step ks, stage ks
-    // has landed, stage ks+1 is in flight, and F0 holds substep 0 of stage
-    // ks.  Substep 0 runs its 64 MFMAs in pairs with the reads of substep 1
-    // spread between them (spread, not bunched: a burst of reads fills the
-    // LDS command queue and stalls the MFMA issue behind it).  Substep 1 runs
-    // BAR_PAIR pairs, then the barrier: stage ks+1 has landed for every wave
-    // and every wave is done reading stage ks, so the rest of substep 1
-    // interleaves the reads of stage ks+1's first substep with the refill of
-    // stage ks's slot by stage ks+2.
+    // The rings: stage ks (counted from the task's first step) keeps its
+    // EARLY operand's tile in slot ks % 3 of the three-slot ring and the
+    // other's in slot ks % 2 of the two-slot ring.  Entering step ks, stage
+    // ks has landed, stage ks+1 is in flight, and F0 holds substep 0 of
+    // stage ks.  Substep 0 runs its 64 MFMAs in pairs with the reads of
+    // substep 1 spread between them (spread, not bunched: a burst of reads
+    // fills the LDS command queue and stalls the MFMA issue behind it), and
+    // with the loads of stage ks+2's EARLY tile: its slot held stage ks-1,
+    // which every wave finished reading before the last barrier.  Substep 1
+    // runs BAR_PAIR pairs, then the barrier: stage ks+1 has landed for every
+    // wave (only the 8 EARLY loads just issued may be in flight: loads
+    // complete in order) and every wave is done reading stage ks, so the rest
+    // of substep 1 interleaves the reads of stage ks+1's first substep with
+    // the loads of stage ks+2's other tile into stage ks's two-ring slot.
+    // The third slot spreads a stage's loads over the whole step instead of
+    // its second half, halving the requests in flight at a time (measured:
+    // 3-4% faster on the large and ragged shapes).
     Frags F0, F1;
     refill_stage(kbeg, 0);
     refill_stage(kbeg + 1, 1);
     wait_vm_barrier<DMA_PER_STAGE>();
-    read_frags(0, 0, F0);
+    read_frags(0, 0, 0, F0);
 
+    int es = 0;  // early-ring slot of stage ks
     for (int ks = kbeg; ks < kend; ++ks) {
-      const int slot = (ks - kbeg) & 1;
+      const int ls = (ks - kbeg) & 1;           // two-slot-ring slot of stage ks
+      const int es1 = es == 2 ? 0 : es + 1;     // early-ring slot of stage ks+1
+      const int es2 = es1 == 2 ? 0 : es1 + 1;   // early-ring slot of stage ks+2
+      Half he;
 #pragma unroll
       for (int q = 0; q < PAIRS; ++q) {
-        share(q, PAIRS, READS, [&](int f) { read_item(slot, 1, F1, f); });
+        share(q, PAIRS, READS, [&](int f) { read_item(es, ls, 1, F1, f); });
         mfma_pair(F0, q);
         fence();
+        // (the descriptor's scalar work goes behind the first MFMAs)
+        if (q == 0) he = half_setup(ks + 2, es2, EARLY);
+        // stages from the third on start at k >= 0: no masks
+        share(q, PAIRS, DMA_PER_OPERAND, [&](int i) { refill_one(he, EARLY, i, false); });
       }
-      const Half ha = half_setup(ks + 2, slot, 0);
-      const Half hb = half_setup(ks + 2, slot, 1);
+      const Half hl = half_setup(ks + 2, ls, 1 - EARLY);
 #pragma unroll
       for (int q = 0; q < PAIRS; ++q) {
         if (q == BAR_PAIR) {
-          wait_vm_barrier<0>();
+          wait_vm_barrier<DMA_PER_OPERAND>();
           fence();
         }
         if (q >= BAR_PAIR)
-          share(q - BAR_PAIR, PAIRS - BAR_PAIR, READS, [&](int f) { read_item(slot ^ 1, 0, F0, f); });
+          share(q - BAR_PAIR, PAIRS - BAR_PAIR, READS, [&](int f) { read_item(es1, ls ^ 1, 0, F0, f); });
         mfma_pair(F1, q);
         fence();
         if (q >= BAR_PAIR)
-          share(q - BAR_PAIR, PAIRS - BAR_PAIR, DMA_PER_STAGE, [&](int i) {
-            // stages from the third on start at k >= 0: no masks
-            if (i < DMA_PER_OPERAND) refill_one(ha, 0, i, false);
-            else refill_one(hb, 1, i - DMA_PER_OPERAND, false);
-          });
+          share(q - BAR_PAIR, PAIRS - BAR_PAIR, DMA_PER_OPERAND,
+                [&](int i) { refill_one(hl, 1 - EARLY, i, false); });
       }
+      es = es1;
     }
 
     wait_vm_barrier<0>();  // every wave is done with the ring; reuse it for staging

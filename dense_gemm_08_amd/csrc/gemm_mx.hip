@@ -21,8 +21,9 @@
 //     32 consecutive k of block q: measured on the GPU), selected by op_sel
 //     from a register holding four scales;
 //   * the scales of each stage arrive in LDS with the data: a pre-pass packs
-//     them per tile and stage into a 1 KiB panel ordered so that each lane
-//     reads its eight scale bytes with one 8-byte LDS read;
+//     them per tile and stage into a 1 KiB panel ordered so that each lane's
+//     four-scale words are consecutive across the wave (conflict-free 4-byte
+//     LDS reads);
 //   * each stage runs as two halves of 32 MFMAs (A fragments 0-3, then
 //     4-7), so that all fragments fit in 128 VGPRs: the first half reads A
 //     fragments 4-7, the second half (after the stage barrier) reads the next
@@ -73,9 +74,11 @@ struct MxParams {
   int koff;  // leading pad of the first stage (K elements)
 };
 
-// Panel layout: byte ((w*16 + l16)*4 + s)*8 + i holds the scale of row
-// w*128 + 16 i + l16 of the tile for block s of the stage, i.e. lane
-// (l16, s) of wave row (or column) w reads bytes i = 0..7 at once.
+// Panel layout: byte ((w*2 + h)*64 + s*16 + l16)*4 + b holds the scale of
+// row w*128 + 16 (4 h + b) + l16 of the tile for block s of the stage: lane
+// l = 16 s + l16 of wave row (or column) w finds the scales of its fragments
+// 4h .. 4h+3 in the word at ((w*2 + h)*64 + l)*4, and the 64 lanes of a
+// wave read 256 consecutive bytes.
 __global__ __launch_bounds__(256) void scale_pack(const uint8_t* __restrict__ S, int rows, int nb,
                                                   int lds_, int tiles, int nks, int koff,
                                                   uint8_t* __restrict__ P) {
@@ -84,8 +87,9 @@ __global__ __launch_bounds__(256) void scale_pack(const uint8_t* __restrict__ S,
   const int within = (int)(idx % SC_BYTES);
   const int64_t panel = idx / SC_BYTES;
   const int ks = (int)(panel % nks), rb = (int)(panel / nks);
-  const int i = within & 7, s = (within >> 3) & 3, l16 = (within >> 5) & 15, w = within >> 9;
-  const int row = rb * BM + w * WT + 16 * i + l16;
+  const int b = within & 3, l16 = (within >> 2) & 15, s = (within >> 6) & 3;
+  const int h = (within >> 8) & 1, w = within >> 9;
+  const int row = rb * BM + w * WT + 16 * (4 * h + b) + l16;
   const int blk = ks * (BKE / GROUP) - koff / GROUP + s;
   // rows past the matrix and blocks before K = 0 hold scale 1 (their data is
   // zero, and a zero times a finite scale stays zero)
@@ -188,8 +192,8 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
     const int fa1 = (wm * WT + l16) * 128 + (((lq + 4) ^ sw) << 4);
     const int fb0 = OP_BYTES + (wn * WT + l16) * 128 + ((lq ^ sw) << 4);
     const int fb1 = OP_BYTES + (wn * WT + l16) * 128 + (((lq + 4) ^ sw) << 4);
-    const int fsa = 2 * OP_BYTES + (wm * 16 + l16) * 32 + lq * 8;
-    const int fsb = 2 * OP_BYTES + SC_BYTES + (wn * 16 + l16) * 32 + lq * 8;
+    const int fsa = 2 * OP_BYTES + wm * 512 + lane * 4;  // fragments 0-3; 4-7 at +256
+    const int fsb = 2 * OP_BYTES + SC_BYTES + wn * 512 + lane * 4;
 
     // Loader (the FP16 kernel's, in bytes): load i of this thread covers tile
     // row (8 wave + i) * 8 + lane / 8 and the logical chunk the swizzle puts
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
         case 11: sb[0] = read_s(slot, fsb); break;
         case 12: F.b[6] = read_b(slot, 6); break;
         case 13: F.b[7] = read_b(slot, 7); break;
-        default: sb[1] = read_s(slot, fsb + 4); break;
+        default: sb[1] = read_s(slot, fsb + 256); break;
       }
       fence();
     };
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
       static_for<0, HALF_PAIRS>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
         if constexpr (q % 4 == 1) F.hi[q / 4] = read_a(slot, 4 + q / 4);
-        if constexpr (q == 3) sa[1] = read_s(slot, fsa + 4);  // A fragments 4-7
+        if constexpr (q == 3) sa[1] = read_s(slot, fsa + 256);  // A fragments 4-7
         mfma_mx<(2 * q) % 4, (2 * q) / 4>(acc, F.b[(2 * q) / 4], F.lo[(2 * q) % 4], sa, sb);
         mfma_mx<(2 * q + 1) % 4, (2 * q + 1) / 4>(acc, F.b[(2 * q + 1) / 4], F.lo[(2 * q + 1) % 4], sa, sb);
         fence();
