@@ -663,20 +663,36 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
   out[5] = grid;
   out[6] = choose_group_m(tiles_m, tiles_n, grid);
   out[7] = THREADS;
-  // split-K for the tiles of the last, partial wave (all tiles when there
-  // are fewer than CUs) when K is long and they would leave at least half the
-  // CUs idle -- three quarters after full waves (measured: splitting a
-  // half-full last wave gains nothing, its partial sums and the reduce cost
-  // what the idle CUs would have saved): at most one part per idle CU, at
-  // least 4 K steps per part
+  // Split-K for the tiles of the last, partial wave (all tiles when there
+  // are fewer than CUs), at most one part per idle CU and at least 4 K steps
+  // per part.
+  //   * Fewer tiles than CUs: the split (if any) with the least estimated
+  //     time, from a model fitted to measured times on the MI355X (in units
+  //     of 0.01 us): a K step of a tile 105, a split call's fixed cost (the
+  //     reduce launch, the workspace) 1200 plus 12 per partial tile (its
+  //     FP32 write and read back).
+  //   * After full waves: split when the last wave would leave at least
+  //     three quarters of the CUs idle (measured: splitting a half-full last
+  //     wave gains nothing), into as many parts as fit.
   const int64_t nk = (K + BK - 1) / BK;
   const int64_t rem = tasks % num_cus;
   int64_t splits = 1, steps = nk;
-  if (rem > 0 && rem * (tasks < num_cus ? 2 : 4) <= num_cus && nk >= 8) {
+  if (rem > 0 && nk >= 8) {
     const int64_t by_cus = num_cus / rem, by_k = nk / 4;
-    const int64_t sp = by_cus < by_k ? by_cus : by_k;
-    if (sp >= 2) {
-      steps = (nk + sp - 1) / sp;
+    const int64_t most = by_cus < by_k ? by_cus : by_k;
+    if (tasks < num_cus) {
+      int64_t best = nk * 105;
+      for (int64_t sp = 2; sp <= most; ++sp) {
+        const int64_t st = (nk + sp - 1) / sp, parts = (nk + st - 1) / st;
+        const int64_t t = st * 105 + 1200 + 12 * parts * rem;
+        if (t < best) {
+          best = t;
+          steps = st;
+          splits = parts;
+        }
+      }
+    } else if (rem * 4 <= num_cus && most >= 2) {
+      steps = (nk + most - 1) / most;
       splits = (nk + steps - 1) / steps;
     }
   }

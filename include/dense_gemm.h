@@ -42,14 +42,14 @@
  * where its rows are 16-byte aligned and element by element otherwise.
  *
  * Split-K.  When the tiles of the last, partial wave over the CUs (all
- * tiles, when there are fewer tiles than CUs) would leave at least half the
- * CUs idle (three quarters after full waves) and K is long (see
- * dense_gemm_plan), the K dimension of those
- * tiles is split: each part writes an FP32 partial tile to the workspace and
- * a second kernel sums them in a fixed order (results stay reproducible) and
- * rounds once.  The other tiles are computed whole in the same launch.  The environment
- * variable DENSE_GEMM_SPLITK=off disables split-K, DENSE_GEMM_SPLITK=<n>
- * forces n parts (for testing and measurement).
+ * tiles, when there are fewer tiles than CUs) would leave CUs idle and K is
+ * long enough for the parts to pay for their partial sums (see
+ * dense_gemm_plan), the K dimension of those tiles is split: each part
+ * writes an FP32 partial tile to the workspace and a second kernel sums them
+ * in a fixed order (results stay reproducible) and rounds once.  The other
+ * tiles are computed whole in the same launch.  The environment variable
+ * DENSE_GEMM_SPLITK=off disables split-K, DENSE_GEMM_SPLITK=<n> forces n
+ * parts (for testing and measurement).
  *
  * Workspace.  A call that repacks an operand or splits K takes one workspace
  * with hipMallocAsync on `stream` and returns it with hipFreeAsync on the same
@@ -190,11 +190,13 @@ dense_gemm_status dense_gemm_tile_of_task(int64_t task, int64_t tiles_m, int64_t
  * the GEMM kernel), group_m, threads per workgroup, the number of K splits
  * (1: none) and the K steps (of BK) per split.  Split-K applies to the
  * r = tiles mod num_cus tiles of the last, partial wave (all tiles when
- * tiles < num_cus) and is chosen when r > 0, 2 r <= num_cus (4 r <= num_cus
- * when tiles > num_cus) and K spans at least 8 steps: as many parts as keep
- * at most one part per CU (r * parts
- * <= num_cus) and at least 4 steps per part.  The grid is then r * parts
- * when tiles < num_cus, else num_cus. */
+ * tiles < num_cus), with K spanning at least 8 steps, at most one part per
+ * CU (r * parts <= num_cus) and at least 4 steps per part.  When tiles <
+ * num_cus the number of parts p minimises the estimate (in 0.01 us)
+ * ceil(steps / p) * 105 + 1200 + 12 * p * r against steps * 105 unsplit (a
+ * model fitted to times measured on the MI355X); when tiles > num_cus the
+ * last wave is split, into as many parts as fit, only if 4 r <= num_cus.
+ * The grid is then r * parts when tiles < num_cus, else num_cus. */
 dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K,
                                   int64_t num_cus, int64_t* out);
 

@@ -193,9 +193,19 @@ def test_plan_split_k():
     # K too short to split
     assert lib.dense_gemm_plan(NT, 128, 128, 448, 256, out) == S.OK
     assert out[8] == 1
-    # 128 tiles leave half of 256 CUs idle: two parts
+    # 128 tiles leave half of 256 CUs idle; with K = 8192 two parts pay
     assert lib.dense_gemm_plan(NN, 2048, 4096, 8192, 256, out) == S.OK
     assert (out[8], out[9], out[5]) == (2, 64, 256)
+    # ... with K = 2048 (32 steps) the partial tiles cost more than they save
+    assert lib.dense_gemm_plan(NT, 8192, 1024, 2048, 256, out) == S.OK
+    assert out[8] == 1
+    # 16 tiles, K = 4096: the model's best is 6 parts of 11 steps (the
+    # estimate st * 105 + 1200 + 12 * parts * 16 is least there)
+    assert lib.dense_gemm_plan(NT, 1024, 1024, 4096, 256, out) == S.OK
+    assert (out[8], out[9], out[5]) == (6, 11, 96)
+    # K = 1024 (16 steps) on 64 tiles: no split
+    assert lib.dense_gemm_plan(NT, 2048, 2048, 1024, 256, out) == S.OK
+    assert out[8] == 1
     # more tiles than half the CUs: no split
     assert lib.dense_gemm_plan(NN, 2304, 4096, 8192, 256, out) == S.OK
     assert out[8] == 1
