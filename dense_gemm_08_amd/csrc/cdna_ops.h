@@ -57,6 +57,16 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t off, uint32_t m0) {
                : "v"(off), "s"(rsrc), "s"(m0)
                : "memory", "m0");
 }
+// The same with the LDS address given as base + imm, where imm must be a
+// constant once the caller's loops are unrolled: the sum goes straight into
+// m0, so no address register is computed ahead of the load.  (The add sets
+// SCC, hence that clobber.)
+__device__ __forceinline__ void dma16_at(i32x4 rsrc, uint32_t off, uint32_t base, int imm) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(base), "i"(imm)
+               : "memory", "m0", "scc");
+}
 #pragma clang diagnostic pop
 
 // Scheduling fence: the compiler may move no instruction across it.

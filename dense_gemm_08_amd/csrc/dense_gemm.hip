@@ -251,10 +251,10 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     auto refill_one = [&](const Half& h, int half, int i, bool masked) {
       if (half == 0 || LAYOUT == NT) {
         const uint32_t off = half == 0 ? a_off[i] : b_off[i];
-        dma16(h.r, !masked || h.k0 + (kc[i & 1] << 3) >= 0 ? off : OOB, h.base + i * 1024);
+        dma16_at(h.r, !masked || h.k0 + (kc[i & 1] << 3) >= 0 ? off : OOB, h.base, i * 1024);
       } else {
         const int k = 2 * (8 * wave + i) + nn_row_lo;
-        dma16(h.r, !masked || h.k0 + k >= 0 ? b_off[i] : OOB, h.base + i * 1024);
+        dma16_at(h.r, !masked || h.k0 + k >= 0 ? b_off[i] : OOB, h.base, i * 1024);
       }
       fence();
     };

@@ -211,6 +211,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
     struct Stage {
       i32x4 ra, rb, rs;  // A, B and scale-panel descriptors
       uint32_t base;     // LDS slot
+      uint32_t wbase;    // this wave's first 1 KiB of the slot's A tile
       int k0;            // first k of the stage (negative only for the first)
     };
     auto stage_setup = [&](int ks, int slot) {
@@ -219,6 +220,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
       const bool live = ks < nk;
       st.k0 = k0;
       st.base = lds0 + slot * SLOT;
+      st.wbase = st.base + (8 * wave) * 1024;
       st.ra = make_rsrc((uint64_t)(uintptr_t)(p.A + (int64_t)m0 * p.lda) + k0,
                         live ? (uint32_t)((vm - 1) * p.lda + p.K - k0) : 0u);
       st.rb = make_rsrc((uint64_t)(uintptr_t)(p.B + (int64_t)n0 * p.ldb) + k0,
@@ -237,9 +239,9 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
         const int op = i / DMA, j = i % DMA;
         const uint32_t off = op == 0 ? a_off[j] : b_off[j];
         const bool in = !masked || st.k0 + kc[j & 1] * 16 >= 0;
-        dma16(op == 0 ? st.ra : st.rb, in ? off : OOB, st.base + op * OP_BYTES + (8 * wave + j) * 1024);
+        dma16_at(op == 0 ? st.ra : st.rb, in ? off : OOB, st.wbase, op * OP_BYTES + j * 1024);
       } else {
-        dma16(st.rs, (uint32_t)(lane * 16), st.base + 2 * OP_BYTES + (wave & 1) * SC_BYTES);
+        dma16_at(st.rs, (uint32_t)(lane * 16), st.base + (wave & 1) * SC_BYTES, 2 * OP_BYTES);
       }
       fence();
     };
