@@ -378,11 +378,11 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
         const int row = row0 + rr;
         const int col = col0 + cc * 8;
         if (interior) {
-          *(u32x4*)(p.D + (int64_t)row * p.ldd + col) = v;
+          __builtin_nontemporal_store(v, (u32x4*)(p.D + (int64_t)row * p.ldd + col));
         } else if (row < p.M && col < p.N) {
           uint16_t* dst = p.D + (int64_t)row * p.ldd + col;
           if (p.d_vec && col + 8 <= p.N) {
-            *(u32x4*)dst = v;
+            __builtin_nontemporal_store(v, (u32x4*)dst);
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
