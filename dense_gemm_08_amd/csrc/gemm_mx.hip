@@ -79,21 +79,36 @@ struct MxParams {
 // l = 16 s + l16 of wave row (or column) w finds the scales of its fragments
 // 4h .. 4h+3 in the word at ((w*2 + h)*64 + l)*4, and the 64 lanes of a
 // wave read 256 consecutive bytes.
-__global__ __launch_bounds__(256) void scale_pack(const uint8_t* __restrict__ S, int rows, int nb,
-                                                  int lds_, int tiles, int nks, int koff,
+struct PackArgs {
+  const uint8_t* S[2];  // SA, SB
+  int rows[2];          // M, N
+  int ld[2];            // ldsa, ldsb
+  int tiles[2];         // tile rows of A, tile columns of B
+};
+
+// One launch packs both operands: workgroup g builds panel g (A's panels
+// first, then B's), each thread one 4-byte word of it.  Rows past the
+// matrix and blocks before K = 0 get scale 1 (their data is zero, and zero
+// times a finite scale stays zero).
+__global__ __launch_bounds__(256) void scale_pack(PackArgs a, int nb, int nks, int koff,
                                                   uint8_t* __restrict__ P) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)tiles * nks * SC_BYTES) return;
-  const int within = (int)(idx % SC_BYTES);
-  const int64_t panel = idx / SC_BYTES;
-  const int ks = (int)(panel % nks), rb = (int)(panel / nks);
-  const int b = within & 3, l16 = (within >> 2) & 15, s = (within >> 6) & 3;
-  const int h = (within >> 8) & 1, w = within >> 9;
-  const int row = rb * BM + w * WT + 16 * (4 * h + b) + l16;
+  int panel = blockIdx.x;
+  const int op = panel >= a.tiles[0] * nks ? 1 : 0;
+  const size_t out = (size_t)panel * SC_BYTES;
+  if (op) panel -= a.tiles[0] * nks;
+  const int ks = panel % nks, rb = panel / nks;
+  const int t = threadIdx.x;
+  const int l16 = t & 15, s = (t >> 4) & 3, h = (t >> 6) & 1, w = t >> 7;
   const int blk = ks * (BKE / GROUP) - koff / GROUP + s;
-  // rows past the matrix and blocks before K = 0 hold scale 1 (their data is
-  // zero, and a zero times a finite scale stays zero)
-  P[idx] = (row < rows && blk >= 0 && blk < nb) ? S[(int64_t)row * lds_ + blk] : (uint8_t)127;
+  const bool in_k = blk >= 0 && blk < nb;
+  uint32_t word = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int row = rb * BM + w * WT + 16 * (4 * h + b) + l16;
+    const uint32_t v = in_k && row < a.rows[op] ? a.S[op][(int64_t)row * a.ld[op] + blk] : 127u;
+    word |= v << (8 * b);
+  }
+  *(uint32_t*)(P + out + 4 * t) = word;
 }
 
 struct Frags {
@@ -456,10 +471,10 @@ extern "C" dense_gemm_status gemm_nt_e4m3_mx(int64_t M, int64_t N, int64_t K, co
   p.PSA = ws;
   p.PSB = ws + pa;
   if (p.nks > 0) {
-    hipLaunchKernelGGL(mx::scale_pack, dim3((unsigned)((pa + 255) / 256)), dim3(256), 0, stream,
-                       (const uint8_t*)SA, p.M, (int)nb, (int)ldsa, p.tiles_m, p.nks, p.koff, ws);
-    hipLaunchKernelGGL(mx::scale_pack, dim3((unsigned)((pb + 255) / 256)), dim3(256), 0, stream,
-                       (const uint8_t*)SB, p.N, (int)nb, (int)ldsb, p.tiles_n, p.nks, p.koff, ws + pa);
+    mx::PackArgs pk{{(const uint8_t*)SA, (const uint8_t*)SB}, {p.M, p.N}, {(int)ldsa, (int)ldsb},
+                    {p.tiles_m, p.tiles_n}};
+    hipLaunchKernelGGL(mx::scale_pack, dim3((unsigned)((p.tiles_m + p.tiles_n) * p.nks)), dim3(256),
+                       0, stream, pk, (int)nb, p.nks, p.koff, ws);
   }
   hipLaunchKernelGGL(mx::gemm_mx_kernel, dim3((unsigned)(p.num_tasks < cus ? p.num_tasks : cus)),
                      dim3(mx::THREADS), 0, stream, p);
