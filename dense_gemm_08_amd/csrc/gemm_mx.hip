@@ -86,29 +86,62 @@ struct PackArgs {
   int tiles[2];         // tile rows of A, tile columns of B
 };
 
-// One launch packs both operands: workgroup g builds panel g (A's panels
-// first, then B's), each thread one 4-byte word of it.  Rows past the
-// matrix and blocks before K = 0 get scale 1 (their data is zero, and zero
-// times a finite scale stays zero).
+// One launch packs both operands.  Workgroup (g, c) takes tile g (A's tile
+// rows first, then B's tile columns) and the 4 stages of chunk c: it copies
+// the tile's 256 rows x 16 scale bytes of those stages into LDS, four
+// threads per row (4-byte reads where the rows allow it), then writes each
+// stage's panel, one 4-byte word per thread (each panel a contiguous 1 KiB).
+// Rows past the matrix and blocks outside [0, K/32) get scale 1 (their data
+// is zero, and zero times a finite scale stays zero).
+constexpr int PACK_STAGES = 4;
 __global__ __launch_bounds__(256) void scale_pack(PackArgs a, int nb, int nks, int koff,
                                                   uint8_t* __restrict__ P) {
-  int panel = blockIdx.x;
-  const int op = panel >= a.tiles[0] * nks ? 1 : 0;
-  const size_t out = (size_t)panel * SC_BYTES;
-  if (op) panel -= a.tiles[0] * nks;
-  const int ks = panel % nks, rb = panel / nks;
+  __shared__ uint32_t rowbuf[BM][PACK_STAGES];  // 4 scale bytes (one stage) per word
+  int tile = blockIdx.x;
+  const int op = tile >= a.tiles[0] ? 1 : 0;
+  const size_t out0 = (size_t)tile * nks * SC_BYTES;  // panels of earlier tiles
+  if (op) tile -= a.tiles[0];
+  const int ks0 = blockIdx.y * PACK_STAGES;
+  const int c0 = ks0 * (BKE / GROUP) - koff / GROUP;  // first block of the chunk
   const int t = threadIdx.x;
-  const int l16 = t & 15, s = (t >> 4) & 3, h = (t >> 6) & 1, w = t >> 7;
-  const int blk = ks * (BKE / GROUP) - koff / GROUP + s;
-  const bool in_k = blk >= 0 && blk < nb;
-  uint32_t word = 0;
+  const uint8_t* S = a.S[op];
+  const int ld = a.ld[op], rows = a.rows[op];
+  // whole words of the row are read in place when the row starts, the
+  // stride and the chunk's first block are 4-byte aligned and the chunk
+  // lies inside [0, nb)
+  const bool words = (((uintptr_t)S | (uintptr_t)ld | (uintptr_t)c0) & 3) == 0 && c0 >= 0 &&
+                     c0 + 4 * PACK_STAGES <= nb;
+  const int j = t & 3;  // stage j of the chunk: blocks c0 + 4 j .. +3
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int row = rb * BM + w * WT + 16 * (4 * h + b) + l16;
-    const uint32_t v = in_k && row < a.rows[op] ? a.S[op][(int64_t)row * a.ld[op] + blk] : 127u;
-    word |= v << (8 * b);
+  for (int pass = 0; pass < BM / 64; ++pass) {
+    const int r = pass * 64 + (t >> 2);
+    const int row = tile * BM + r;
+    uint32_t v = 0x7F7F7F7Fu;
+    if (row < rows) {
+      const uint8_t* src = S + (int64_t)row * ld + c0 + 4 * j;
+      if (words) {
+        v = *(const uint32_t*)src;
+      } else {
+        v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int blk = c0 + 4 * j + b;
+          v |= (uint32_t)(blk >= 0 && blk < nb ? src[b] : (uint8_t)127) << (8 * b);
+        }
+      }
+    }
+    rowbuf[r][j] = v;
   }
-  *(uint32_t*)(P + out + 4 * t) = word;
+  __syncthreads();
+  const int l16 = t & 15, s = (t >> 4) & 3, h = (t >> 6) & 1, w = t >> 7;
+  const int kn = min(PACK_STAGES, nks - ks0);
+  for (int k = 0; k < kn; ++k) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      word |= ((rowbuf[w * WT + 16 * (4 * h + b) + l16][k] >> (8 * s)) & 0xFFu) << (8 * b);
+    *(uint32_t*)(P + out0 + (size_t)(ks0 + k) * SC_BYTES + 4 * t) = word;
+  }
 }
 
 struct Frags {
@@ -473,8 +506,10 @@ extern "C" dense_gemm_status gemm_nt_e4m3_mx(int64_t M, int64_t N, int64_t K, co
   if (p.nks > 0) {
     mx::PackArgs pk{{(const uint8_t*)SA, (const uint8_t*)SB}, {p.M, p.N}, {(int)ldsa, (int)ldsb},
                     {p.tiles_m, p.tiles_n}};
-    hipLaunchKernelGGL(mx::scale_pack, dim3((unsigned)((p.tiles_m + p.tiles_n) * p.nks)), dim3(256),
-                       0, stream, pk, (int)nb, p.nks, p.koff, ws);
+    hipLaunchKernelGGL(mx::scale_pack,
+                       dim3((unsigned)(p.tiles_m + p.tiles_n),
+                            (unsigned)((p.nks + mx::PACK_STAGES - 1) / mx::PACK_STAGES)),
+                       dim3(256), 0, stream, pk, (int)nb, p.nks, p.koff, ws);
   }
   hipLaunchKernelGGL(mx::gemm_mx_kernel, dim3((unsigned)(p.num_tasks < cus ? p.num_tasks : cus)),
                      dim3(mx::THREADS), 0, stream, p);
