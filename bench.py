@@ -8,8 +8,10 @@ seeded synthetic workloads in ``dense_gemm_08_amd/inputs.py``.
 
 Reported:
 * value: TFLOP/s = 2*M*N*K*steps / (wall time of the timed region);
-* roofline: the GEMM kernel against the dense FP16/BF16 MFMA peak, with its
-  average duration from HIP events recorded on the launch stream;
+* roofline: the GEMM kernel against the dense FP16/BF16 (or FP8) MFMA peak,
+  with its average duration from HIP events recorded on the launch stream
+  around the timed calls, and the 10th/50th/90th percentiles of up to 200
+  further calls timed one by one;
 * cpu_baseline: the CPU oracle (FP64, test infrastructure) timed on a bounded
   row sample of the same workload on this host's cores.
 """
@@ -404,6 +406,19 @@ def main():
     wall = time.perf_counter() - t0
     kern_ms = ev0.elapsed_time(ev1) / args.steps
 
+    # per-launch spread (after the timed region, so it does not perturb it):
+    # an event pair around each of up to 200 more back-to-back calls
+    n_pl = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_pl)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_launch = sorted(a.elapsed_time(b) for a, b in evs)
+    pct = lambda q: per_launch[min(n_pl - 1, int(q * n_pl))]  # noqa: E731
+
     flops = float(w.flops)
     value = flops * args.steps / wall / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -436,7 +451,9 @@ def main():
         "config": config,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "kernel_ms": kern_ms},
+                     "traffic": traffic, "kernel_ms": kern_ms,
+                     "kernel_ms_p10": pct(0.1), "kernel_ms_p50": pct(0.5),
+                     "kernel_ms_p90": pct(0.9), "per_launch_samples": n_pl},
     }
     if not args.no_cpu_baseline:
         if fmt == "e4m3":
