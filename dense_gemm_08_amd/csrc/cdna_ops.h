@@ -27,9 +27,11 @@ constexpr uint32_t OOB = 0x80000000u;  // a buffer offset past every range
 // land in distinct bank groups.
 __device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
 // N-contiguous B tile (NN): row k holds 256 elements = 32 chunks; chunk c is
-// stored at slot c ^ swz_n(k), so the four k rows read together by one
-// transposing load sit in different banks.
-__device__ __forceinline__ int swz_n(int k) { return (k & 3) << 2; }
+// stored at slot c ^ swz_n(k).  One transposing load reads 32 bytes (two
+// chunks) from each of 16 rows k = 8 q + 4 h + r (q, r = 0..3, h fixed);
+// the XOR of chunk bits 1-4 with r and q puts each of those rows' 32 bytes
+// in a different 32-byte group of the 512-byte row, i.e. in distinct banks.
+__device__ __forceinline__ int swz_n(int k) { return ((k & 3) | (((k >> 3) & 3) << 2)) << 1; }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void*)p;

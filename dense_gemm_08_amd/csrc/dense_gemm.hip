@@ -167,11 +167,12 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       // four columns n = wn*128 + 16 j + 4 (i % 4) .. +3, so that it receives
       // column 16 j + i at four consecutive k
       const int klane = 8 * lq + (l16 >> 2);
-      const int fl = (lane >> 2) & 3;  // == k & 3 of every row this lane reads
+      // swz_n of every row this lane reads (the +4 and +32 row offsets of the
+      // reads leave bits 0-1 and 3-4 of k unchanged)
+      const int fl = swz_n(klane);
 #pragma unroll
       for (int j = 0; j < NI; ++j)
-        fbn[j] = klane * 512 +
-                 ((wn * 16 + ((2 * j + ((lane & 3) >> 1)) ^ (fl << 2))) << 4) + (lane & 1) * 8;
+        fbn[j] = klane * 512 + (((wn * 16 + 2 * j + ((lane & 3) >> 1)) ^ fl) << 4) + (lane & 1) * 8;
     }
 
     // Per-lane load offsets, fixed for the tile; the buffer descriptor of
