@@ -45,7 +45,8 @@ enum Layout { NT = 0, NN = 1 };
 
 // ---- tile configuration -------------------------------------------------
 constexpr int BM = 256;              // tile rows (M)
-constexpr int BN = 256;              // tile columns (N)
+constexpr int BN = 256;              // tile columns (N); A @ B.T also has a 128-wide
+                                     // tile for outputs too narrow to fill the CUs
 constexpr int BK = 64;               // K depth of one LDS stage (128-byte rows)
 constexpr int SLOTS3 = 3;            // LDS ring depth of the early operand (below)
 constexpr int SLOTS2 = 2;            // LDS ring depth of the other operand
@@ -53,25 +54,16 @@ constexpr int MK = 32;               // K depth of one MFMA (16 x 16 x 32)
 constexpr int SUB = BK / MK;         // MFMA k-substeps per stage
 constexpr int WAVES = 4;             // 2 x 2 waves
 constexpr int THREADS = WAVES * 64;
-constexpr int WTM = 128;             // wave tile rows
-constexpr int WTN = 128;             // wave tile columns
+constexpr int WTM = 128;             // wave tile rows (columns: half the tile width)
 constexpr int MI = WTM / 16;         // 16 x 16 MFMA blocks per wave, M direction
-constexpr int NI = WTN / 16;         //                               N direction
-constexpr int PAIRS = MI * NI / 2;   // MFMA pairs per substep
 constexpr int A_BYTES = BM * BK * 2;           // 32 KiB: 256 rows x 128 B
-constexpr int B_BYTES = BN * BK * 2;           // 32 KiB
-constexpr int OP_BYTES = A_BYTES;                   // one operand tile (A and B alike)
-constexpr int RING2 = SLOTS3 * OP_BYTES;            // the two-slot ring follows the other
-constexpr int LDS_BYTES = RING2 + SLOTS2 * OP_BYTES;  // all 160 KiB of a CU
-static_assert(A_BYTES == B_BYTES, "both rings hold tiles of one size");
-constexpr int DMA_PER_OPERAND = A_BYTES / (THREADS * 16);  // 16-byte loads per thread
-constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPERAND;
+constexpr int DMA_PER_OPERAND = A_BYTES / (THREADS * 16);  // 16-byte loads per thread (A)
 // MFMA pairs of the last substep issued before its barrier: the reads of
 // that substep's fragments (issued during the previous substep) complete
 // meanwhile, so the barrier's LDS wait costs nothing
 constexpr int BAR_PAIR = 2;
 
-static_assert(DMA_PER_OPERAND == 8, "each wave fills 8 KiB of each operand per stage");
+static_assert(DMA_PER_OPERAND == 8, "each wave fills 8 KiB of the A tile per stage");
 static_assert(BK == 64 && BM == 256 && BN == 256, "swizzles below assume these sizes");
 static_assert(SUB == 2, "the ring schedule below has two substeps per stage");
 
@@ -87,24 +79,41 @@ struct Params {
   // the rest are (tile, part) pairs over the last `tiles` tiles of the
   // order.  Task full_tasks + u is part u / tiles of tile full_tasks +
   // u % tiles; the part covers K steps [part * split_steps, min(nk, (part +
-  // 1) * split_steps)) and writes its FP32 partial tile (row-major BM x BN)
-  // to ws at index part * tiles + u % tiles
+  // 1) * split_steps)) and writes its FP32 partial tile (row-major BM x TN,
+  // TN the tile width) to ws at index part * tiles + u % tiles
   int full_tasks, splits, split_steps, tiles;
   float* ws;
 };
 
+template <int NB>
 struct Frags {
   u32x4 a[MI];
-  u32x4 b[NI];
+  u32x4 b[NB];
 };
 
-template <typename T, int LAYOUT, bool SPLIT>
+// Tile width TN: 256 (four 128 x 128 wave tiles), or for A @ B.T 128 (four
+// 128 x 64 wave tiles: twice the tiles where 256-wide ones would leave half
+// the CUs idle, at more operand traffic per FLOP).
+template <typename T, int LAYOUT, bool SPLIT, int TN>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
+  static_assert(TN == BN || (TN == BN / 2 && LAYOUT == NT), "tile widths 256, and 128 for A @ B.T");
+  constexpr int WTN = TN / 2;                      // wave tile columns
+  constexpr int NI = WTN / 16;                     // 16 x 16 blocks per wave, N direction
+  constexpr int PAIRS = MI * NI / 2;               // MFMA pairs per substep
+  constexpr int B_TILE = TN * BK * 2;              // bytes of a B tile
+  constexpr int DMA_B = B_TILE / (THREADS * 16);   // 16-byte loads per thread (B)
   // The operand with the three-slot ring, whose loads are issued a substep
   // earlier (0 = A, 1 = B): B for A @ B, whose row-major tile (64 rows of
   // 512 B, far apart in memory) is the costlier one to load (measured: 1.4%
   // faster than A there); A for A @ B.T (the two are alike).
   constexpr int EARLY = LAYOUT == NN ? 1 : 0;
+  constexpr int DMA_E = EARLY == 0 ? DMA_PER_OPERAND : DMA_B;   // loads of the early tile
+  constexpr int DMA_L = EARLY == 0 ? DMA_B : DMA_PER_OPERAND;   // and of the other
+  constexpr int E_BYTES = EARLY == 0 ? A_BYTES : B_TILE;
+  constexpr int L_BYTES = EARLY == 0 ? B_TILE : A_BYTES;
+  constexpr int RING2 = SLOTS3 * E_BYTES;            // the two-slot ring follows the other
+  constexpr int LDS_BYTES = RING2 + SLOTS2 * L_BYTES;  // all 160 KiB for 256-wide tiles
+  using Frags = dg::Frags<NI>;
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const uint32_t lds0 = lds_addr(smem);
 
@@ -126,9 +135,9 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     const int kbeg = split * p.split_steps;
     const int kend = part ? min(nk, kbeg + p.split_steps) : nk;
     const int m0 = tm * BM;
-    const int n0 = tn * BN;
+    const int n0 = tn * TN;
     const int vm = min(BM, p.M - m0);  // valid rows of the A tile
-    const int vn = min(BN, p.N - n0);  // valid columns of D in this tile
+    const int vn = min(TN, p.N - n0);  // valid columns of D in this tile
 
     // MFMA operand layout (16 x 16 x 32): lane l holds row l % 16 of a
     // 16-row fragment and k = 8 (l / 16) .. +7 of the substep's 32
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     // per-lane masks.
     const int K8 = (p.K + 7) & ~7;
     const int koff = (BK - (K8 & (BK - 1))) & (BK - 1);
-    uint32_t a_off[DMA_PER_OPERAND], b_off[DMA_PER_OPERAND];
+    uint32_t a_off[DMA_PER_OPERAND], b_off[DMA_B];
     int kc[2];  // logical chunk of this lane for even / odd instruction index
 #pragma unroll
     for (int h = 0; h < 2; ++h) kc[h] = (lane & 7) ^ swz_k(h * 8 + (lane >> 3));
@@ -199,13 +208,13 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     }
     if (LAYOUT == NT) {
 #pragma unroll
-      for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-        const int r = (8 * wave + i) * 8 + (lane >> 3);
+      for (int i = 0; i < DMA_B; ++i) {
+        const int r = (DMA_B * wave + i) * 8 + (lane >> 3);
         b_off[i] = r < vn ? (uint32_t)(r * p.ldb * 2 + kc[i & 1] * 16) : OOB;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+      for (int i = 0; i < DMA_B; ++i) {
         const int k = 2 * (8 * wave + i) + nn_row_lo;
         const int c = (lane & 31) ^ swz_n(k);
         b_off[i] = (uint32_t)(k * p.ldb * 2 + c * 16);
@@ -231,7 +240,8 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       const int k0 = ks * BK - koff;
       const bool live = ks < kend;
       h.k0 = k0;
-      h.base = lds0 + (half == EARLY ? 0 : RING2) + slot * OP_BYTES + (8 * wave) * 1024;
+      h.base = lds0 + (half == EARLY ? 0 : RING2) + slot * (half == 0 ? A_BYTES : B_TILE) +
+               ((half == 0 ? DMA_PER_OPERAND : DMA_B) * wave) * 1024;
       if (half == 0 || LAYOUT == NT) {
         // columns k0 .. K8 of the tile's rows
         const uint64_t src = half == 0 ? (uint64_t)(uintptr_t)(p.A + (int64_t)m0 * p.lda)
@@ -265,7 +275,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < DMA_PER_OPERAND; ++i) refill_one(ha, 0, i, true);
 #pragma unroll
-      for (int i = 0; i < DMA_PER_OPERAND; ++i) refill_one(hb, 1, i, true);
+      for (int i = 0; i < DMA_B; ++i) refill_one(hb, 1, i, true);
     };
 
     // Fragment reads of k-substep s of the stage in slot `slot`, one LDS
@@ -273,8 +283,8 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     // B fragments (NT: one ds_read_b128 each; NN: two transposing reads each).
     constexpr int READS = MI + (LAYOUT == NT ? NI : 2 * NI);
     auto read_item = [&](int es, int ls, int s, Frags& F, int f) {
-      const char* abase = smem + (EARLY == 0 ? es * OP_BYTES : RING2 + ls * OP_BYTES);
-      const char* bbase = smem + (EARLY == 1 ? es * OP_BYTES : RING2 + ls * OP_BYTES);
+      const char* abase = smem + (EARLY == 0 ? es * A_BYTES : RING2 + ls * A_BYTES);
+      const char* bbase = smem + (EARLY == 1 ? es * B_TILE : RING2 + ls * B_TILE);
       if (f < MI) {
         F.a[f] = *(const u32x4*)(abase + fa[s] + f * 2048);
       } else if (LAYOUT == NT) {
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     Frags F0, F1;
     refill_stage(kbeg, 0);
     refill_stage(kbeg + 1, 1);
-    wait_vm_barrier<DMA_PER_STAGE>();
+    wait_vm_barrier<DMA_PER_OPERAND + DMA_B>();
     read_frags(0, 0, 0, F0);
 
     int es = 0;  // early-ring slot of stage ks
@@ -350,13 +360,13 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
         // (the descriptor's scalar work goes behind the first MFMAs)
         if (q == 0) he = half_setup(ks + 2, es2, EARLY);
         // stages from the third on start at k >= 0: no masks
-        share(q, PAIRS, DMA_PER_OPERAND, [&](int i) { refill_one(he, EARLY, i, false); });
+        share(q, PAIRS, DMA_E, [&](int i) { refill_one(he, EARLY, i, false); });
       }
       const Half hl = half_setup(ks + 2, ls, 1 - EARLY);
 #pragma unroll
       for (int q = 0; q < PAIRS; ++q) {
         if (q == BAR_PAIR) {
-          wait_vm_barrier<DMA_PER_OPERAND>();
+          wait_vm_barrier<DMA_E>();
           fence();
         }
         if (q >= BAR_PAIR)
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
         mfma_pair(F1, q);
         fence();
         if (q >= BAR_PAIR)
-          share(q - BAR_PAIR, PAIRS - BAR_PAIR, DMA_PER_OPERAND,
+          share(q - BAR_PAIR, PAIRS - BAR_PAIR, DMA_L,
                 [&](int i) { refill_one(hl, 1 - EARLY, i, false); });
       }
       es = es1;
@@ -379,15 +389,15 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       // FP32 partial tile, row-major 256 x 256: lane holds row l16 of each
       // 16-row block and columns j*16 + 4*lq .. +3 (16 contiguous bytes);
       // 16 x 16 blocks wholly outside D are skipped (nothing reads them)
-      float* w = p.ws + (size_t)(split * p.tiles + u % p.tiles) * (BM * BN) +
-                 (size_t)(wm * WTM + l16) * BN + wn * WTN + 4 * lq;
+      float* w = p.ws + (size_t)(split * p.tiles + u % p.tiles) * (BM * TN) +
+                 (size_t)(wm * WTM + l16) * TN + wn * WTN + 4 * lq;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         if (wm * WTM + i * 16 >= vm) break;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
           if (wn * WTN + j * 16 >= vn) break;
-          *(float4*)(w + i * 16 * BN + j * 16) =
+          *(float4*)(w + i * 16 * TN + j * 16) =
               make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -396,10 +406,12 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     }
 
     // Epilogue: per 32-row band (two 16-row blocks), round, stage the band's
-    // 32 x 128 outputs of this wave in LDS (chunk-swizzled rows of 256 B),
-    // then store 16-byte row chunks.
-    char* stg = smem + wave * (32 * 256);
-    const bool interior = p.d_vec && vm == BM && vn == BN;
+    // 32 x WTN outputs of this wave in LDS (rows of CH 16-byte chunks,
+    // swizzled by row), then store 16-byte row chunks.
+    constexpr int CH = WTN / 8;       // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CH;      // rows per wave instruction of the read-back
+    char* stg = smem + wave * (32 * CH * 16);
+    const bool interior = p.d_vec && vm == BM && vn == TN;
 #pragma unroll
     for (int band = 0; band < MI / 2; ++band) {
 #pragma unroll
@@ -414,30 +426,29 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
           v[0] = pack2<T>(acc[i][j][0], acc[i][j][1]);
           v[1] = pack2<T>(acc[i][j][2], acc[i][j][3]);
           const int chunk = 2 * j + (lq >> 1);
-          *(u32x2*)(stg + row * 256 + ((chunk ^ (row & 15)) << 4) + (lq & 1) * 8) = v;
+          *(u32x2*)(stg + row * (CH * 16) + ((chunk ^ (row & (CH - 1))) << 4) + (lq & 1) * 8) = v;
         }
         // keep the conversions of one block together (bounded live registers)
         __builtin_amdgcn_sched_barrier(0);
       }
       const int row0 = m0 + wm * WTM + band * 32;
       const int col0 = n0 + wn * WTN;
+      const int cc = lane % CH;
       // D is written once and not read again here: non-temporal stores
       // (measured 0.3-1% faster, 4.7% on the large FP8 product)
       if (interior) {
         // the whole tile is inside D and its rows are 16-byte aligned
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int rr = t * 4 + (lane >> 4);
-          const int cc = lane & 15;
-          const u32x4 v = *(const u32x4*)(stg + rr * 256 + ((cc ^ (rr & 15)) << 4));
+        for (int t = 0; t < 32 / RPI; ++t) {
+          const int rr = t * RPI + lane / CH;
+          const u32x4 v = *(const u32x4*)(stg + rr * (CH * 16) + ((cc ^ (rr & (CH - 1))) << 4));
           __builtin_nontemporal_store(v, (u32x4*)(p.D + (int64_t)(row0 + rr) * p.ldd + col0 + cc * 8));
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int rr = t * 4 + (lane >> 4);
-          const int cc = lane & 15;
-          const u32x4 v = *(const u32x4*)(stg + rr * 256 + ((cc ^ (rr & 15)) << 4));
+        for (int t = 0; t < 32 / RPI; ++t) {
+          const int rr = t * RPI + lane / CH;
+          const u32x4 v = *(const u32x4*)(stg + rr * (CH * 16) + ((cc ^ (rr & (CH - 1))) << 4));
           const int row = row0 + rr;
           const int col = col0 + cc * 8;
           if (row < p.M && col < p.N) {
@@ -462,20 +473,24 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
 
 // Sum of the split-K partials of every output element of the split tiles in
 // part order 0, 1, ... (a fixed order: results are reproducible), rounded
-// once to the output type.  Workgroup b covers rows 8 (b % 32) .. +7 of
-// split tile b / 32; one thread per 8 consecutive columns of a row.
-template <typename T>
+// once to the output type.  One thread per 8 consecutive columns of a row:
+// a workgroup covers 256 / (TN / 8) rows, BM * TN / 2048 workgroups a split
+// tile.
+template <typename T, int TN>
 __global__ __launch_bounds__(256) void split_reduce(Params p) {
-  const int st = blockIdx.x >> 5;  // split tile (0 .. tiles-1)
+  constexpr int TPR = TN / 8;           // threads per row
+  constexpr int RPW = 256 / TPR;        // rows per workgroup
+  constexpr int WPT = BM / RPW;         // workgroups per split tile
+  const int st = blockIdx.x / WPT;      // split tile (0 .. tiles-1)
   int tm, tn;
   tile_of_task(p.full_tasks + st, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
-  const int r = (blockIdx.x & 31) * 8 + (threadIdx.x >> 5);
-  const int c = (threadIdx.x & 31) * 8;
+  const int r = (blockIdx.x % WPT) * RPW + (int)threadIdx.x / TPR;
+  const int c = ((int)threadIdx.x % TPR) * 8;
   const int row = tm * BM + r;
-  const int col = tn * BN + c;
+  const int col = tn * TN + c;
   if (row >= p.M || col >= p.N) return;
-  const float* w = p.ws + (size_t)st * (BM * BN) + (size_t)r * BN + c;
-  const size_t stride = (size_t)p.tiles * (BM * BN);  // between the partials of two splits
+  const float* w = p.ws + (size_t)st * (BM * TN) + (size_t)r * TN + c;
+  const size_t stride = (size_t)p.tiles * (BM * TN);  // between the partials of two splits
   float s[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.0f;
@@ -655,11 +670,20 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
   if ((layout != NT && layout != NN) || M <= 0 || N <= 0 || K < 0 || num_cus <= 0 || !out)
     return DENSE_GEMM_BAD_ARG;
   const int64_t tiles_m = (M + BM - 1) / BM;
-  const int64_t tiles_n = (N + BN - 1) / BN;
+  // Tile width: 256, or for A @ B.T 128 when 256-wide tiles would occupy at
+  // most half the CUs (one wave) and the output is wider than 128: twice the
+  // tiles, still one wave.  Narrow tiles read A twice as often, so they are
+  // kept for operands that stay in the 256 MB Infinity Cache (at most
+  // 192 MiB); beyond it (measured: 8192 x 1024 x 16384) 256-wide tiles with
+  // split-K are faster.
+  const int64_t t256 = tiles_m * ((N + BN - 1) / BN);
+  const bool cached = (M + N) * K * 2 <= ((int64_t)192 << 20);
+  const int64_t tw = layout == NT && N > BN / 2 && 2 * t256 <= num_cus && cached ? BN / 2 : BN;
+  const int64_t tiles_n = (N + tw - 1) / tw;
   const int64_t tasks = tiles_m * tiles_n;
   const int64_t grid = tasks < num_cus ? tasks : num_cus;
   out[0] = BM;
-  out[1] = BN;
+  out[1] = tw;
   out[2] = BK;
   out[3] = tiles_m;
   out[4] = tiles_n;
@@ -671,9 +695,10 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
   // per part.
   //   * Fewer tiles than CUs: the split (if any) with the least estimated
   //     time, from a model fitted to measured times on the MI355X (in units
-  //     of 0.01 us): a K step of a tile 105, a split call's fixed cost (the
-  //     reduce launch, the workspace) 1200 plus 12 per partial tile (its
-  //     FP32 write and read back).
+  //     of 0.01 us): a K step of a 256-wide tile 105 (128-wide: 70), a split
+  //     call's fixed cost (the reduce launch, the workspace) 1200 plus 12 per
+  //     256-wide partial tile (6 per 128-wide one) for its FP32 write and
+  //     read back.
   //   * After full waves: split when the last wave would leave at least
   //     three quarters of the CUs idle (measured: splitting a half-full last
   //     wave gains nothing), into as many parts as fit.
@@ -684,10 +709,11 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
     const int64_t by_cus = num_cus / rem, by_k = nk / 4;
     const int64_t most = by_cus < by_k ? by_cus : by_k;
     if (tasks < num_cus) {
-      int64_t best = nk * 105;
+      const int64_t step_cost = tw == BN ? 105 : 70, part_cost = tw == BN ? 12 : 6;
+      int64_t best = nk * step_cost;
       for (int64_t sp = 2; sp <= most; ++sp) {
         const int64_t st = (nk + sp - 1) / sp, parts = (nk + st - 1) / st;
-        const int64_t t = st * 105 + 1200 + 12 * parts * rem;
+        const int64_t t = st * step_cost + 1200 + part_cost * parts * rem;
         if (t < best) {
           best = t;
           steps = st;
@@ -709,18 +735,11 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
 
 namespace dg {
 
-template <typename T, int LAYOUT>
-static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                             const void* B, int64_t ldb, void* D, int64_t ldd,
-                             hipStream_t stream) {
-  dense_gemm_status st = dense_gemm_validate(LAYOUT, M, N, K, A, lda, B, ldb, D, ldd);
-  if (st != DENSE_GEMM_OK || M == 0 || N == 0) return st;
-  DeviceInfo info;
-  st = device_info(&info);
-  if (st != DENSE_GEMM_OK) return st;
-  int64_t plan[10];
-  st = dense_gemm_plan(LAYOUT, M, N, K, info.cus, plan);
-  if (st != DENSE_GEMM_OK) return st;
+// The launches of one call with tile width TN, for the plan of run().
+template <typename T, int LAYOUT, int TN>
+static dense_gemm_status launch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, void* D, int64_t ldd, int64_t* plan,
+                                const DeviceInfo& info, hipStream_t stream) {
   // Tiles computed whole; the plan splits the rest (the last, partial wave).
   const int64_t tasks = plan[3] * plan[4];
   int64_t full = plan[8] > 1 ? tasks - tasks % info.cus : tasks;
@@ -772,7 +791,7 @@ static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int
   const size_t a_bytes = a_direct ? 0 : round256((size_t)M * K8 * 2);
   const size_t b_bytes = b_direct ? 0 : round256((size_t)b_rows * b_dcols * 2);
   const size_t split_bytes =
-      plan[8] > 1 && p.tiles > 0 ? (size_t)plan[8] * p.tiles * BM * BN * sizeof(float) : 0;
+      plan[8] > 1 && p.tiles > 0 ? (size_t)plan[8] * p.tiles * BM * TN * sizeof(float) : 0;
 
   // one stream-ordered workspace: [A copy | B copy | FP32 split-K partials]
   char* ws = nullptr;
@@ -812,20 +831,52 @@ static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int
     p.split_steps = (int)plan[9];
     p.ws = (float*)(ws + a_bytes + b_bytes);
     p.num_tasks = p.full_tasks + p.tiles * p.splits;
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>),
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true, TN>),
                        dim3((unsigned)(p.num_tasks < info.cus ? p.num_tasks : info.cus)),
                        dim3(THREADS), 0, stream, p);
-    hipLaunchKernelGGL((split_reduce<T>), dim3((unsigned)(p.tiles * 32)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((split_reduce<T, TN>), dim3((unsigned)(p.tiles * (TN / 8))), dim3(256), 0,
+                       stream, p);
   } else {
     p.full_tasks = p.num_tasks;
     p.tiles = 0;
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false>),
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false, TN>),
                        dim3((unsigned)(p.num_tasks < info.cus ? p.num_tasks : info.cus)),
                        dim3(THREADS), 0, stream, p);
   }
-  const hipError_t launch = hipGetLastError();
+  const hipError_t err = hipGetLastError();
   if (ws != nullptr) (void)hipFreeAsync(ws, stream);
-  return launch == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
+  return err == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
+}
+
+template <typename T, int LAYOUT>
+static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                             const void* B, int64_t ldb, void* D, int64_t ldd,
+                             hipStream_t stream) {
+  dense_gemm_status st = dense_gemm_validate(LAYOUT, M, N, K, A, lda, B, ldb, D, ldd);
+  if (st != DENSE_GEMM_OK || M == 0 || N == 0) return st;
+  DeviceInfo info;
+  st = device_info(&info);
+  if (st != DENSE_GEMM_OK) return st;
+  int64_t plan[10];
+  st = dense_gemm_plan(LAYOUT, M, N, K, info.cus, plan);
+  if (st != DENSE_GEMM_OK) return st;
+  // DENSE_GEMM_TILE_N=128 or 256 forces the tile width of A @ B.T (testing)
+  if (const char* e = getenv("DENSE_GEMM_TILE_N")) {
+    const int64_t want = atoll(e);
+    if (LAYOUT == NT && (want == BN || want == BN / 2) && want != plan[1]) {
+      plan[1] = want;
+      plan[4] = (N + want - 1) / want;
+      plan[5] = plan[3] * plan[4] < info.cus ? plan[3] * plan[4] : info.cus;
+      plan[6] = choose_group_m(plan[3], plan[4], plan[5]);
+      plan[8] = 1;  // (the split below is then forced or none)
+      plan[9] = (K + BK - 1) / BK;
+    }
+  }
+  if constexpr (LAYOUT == NT) {
+    if (plan[1] == BN / 2)
+      return launch<T, LAYOUT, BN / 2>(M, N, K, A, lda, B, ldb, D, ldd, plan, info, stream);
+  }
+  return launch<T, LAYOUT, BN>(M, N, K, A, lda, B, ldb, D, ldd, plan, info, stream);
 }
 
 }  // namespace dg

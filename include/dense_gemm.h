@@ -51,6 +51,12 @@
  * DENSE_GEMM_SPLITK=off disables split-K, DENSE_GEMM_SPLITK=<n> forces n
  * parts (for testing and measurement).
  *
+ * Tile width.  Output tiles are 256 x 256.  For D = A @ B.T whose 256-wide
+ * tiles would occupy at most half the CUs, with N > 128 and operands of at
+ * most 192 MiB, they are 256 x 128 instead (twice the tiles, one wave).
+ * Either width sums each output in the same order, so results are identical.
+ * DENSE_GEMM_TILE_N=128 or 256 forces the width of A @ B.T (for testing).
+ *
  * Workspace.  A call that repacks an operand or splits K takes one workspace
  * with hipMallocAsync on `stream` and returns it with hipFreeAsync on the same
  * stream (stream-ordered, served by the device's default memory pool).  If it
@@ -186,8 +192,9 @@ dense_gemm_status dense_gemm_tile_of_task(int64_t task, int64_t tiles_m, int64_t
                                           int64_t group_m, int64_t* tile_m, int64_t* tile_n);
 
 /* The launch plan for a problem on a device with num_cus compute units.
- * Writes 10 values to out: BM, BN, BK, tiles_m, tiles_n, grid (workgroups of
- * the GEMM kernel), group_m, threads per workgroup, the number of K splits
+ * Writes 10 values to out: BM, the tile width BN (256, or 128 as described
+ * under "Tile width" above), BK, tiles_m, tiles_n, grid (workgroups of the
+ * GEMM kernel), group_m, threads per workgroup, the number of K splits
  * (1: none) and the K steps (of BK) per split.  Split-K applies to the
  * r = tiles mod num_cus tiles of the last, partial wave (all tiles when
  * tiles < num_cus), with K spanning at least 8 steps, at most one part per

@@ -199,10 +199,10 @@ def test_plan_split_k():
     # ... with K = 2048 (32 steps) the partial tiles cost more than they save
     assert lib.dense_gemm_plan(NT, 8192, 1024, 2048, 256, out) == S.OK
     assert out[8] == 1
-    # 16 tiles, K = 4096: the model's best is 6 parts of 11 steps (the
-    # estimate st * 105 + 1200 + 12 * parts * 16 is least there)
+    # 1024 x 1024 x 4096: 128-wide tiles (32); the model's best is 5 parts of
+    # 13 steps (st * 70 + 1200 + 6 * parts * 32 is least there)
     assert lib.dense_gemm_plan(NT, 1024, 1024, 4096, 256, out) == S.OK
-    assert (out[8], out[9], out[5]) == (6, 11, 96)
+    assert (out[1], out[8], out[9], out[5]) == (128, 5, 13, 160)
     # K = 1024 (16 steps) on 64 tiles: no split
     assert lib.dense_gemm_plan(NT, 2048, 2048, 1024, 256, out) == S.OK
     assert out[8] == 1
@@ -269,3 +269,25 @@ def test_mx_argument_checks_on_the_host():
     assert _mx(8, 8, 64, A=72) == S.MISALIGNED   # A not 16-byte aligned
     assert _mx(8, 8, 64, ldb=72) == S.MISALIGNED  # B rows not 16-byte aligned
     assert _mx(8, 8, 1 << 24, lda=1 << 24, ldb=1 << 24) == S.TOO_LARGE  # tile span >= 2 GiB
+
+
+def test_plan_tile_width():
+    lib = binding.load_library()
+    out = (ctypes.c_int64 * 10)()
+    # A.B^T whose 256-wide tiles fill at most half the CUs: 128-wide tiles
+    for M, N, K, tiles_n in [(8192, 1024, 2048, 8), (2048, 2048, 1024, 16), (256, 1024, 1024, 8),
+                             (1000, 130, 712, 2)]:
+        assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK
+        assert (out[1], out[4]) == (128, tiles_n), (M, N, K)
+    # wider outputs, N <= 128, A.B, and operands beyond 192 MiB keep 256-wide
+    # tiles
+    for layout, M, N, K in [(NT, 8192, 2048, 1024), (NT, 4096, 4096, 4096), (NT, 3000, 5000, 4000),
+                            (NT, 128, 128, 4096), (NN, 8192, 1024, 2048), (NT, 8192, 1024, 16384)]:
+        assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
+        assert out[1] == 256, (layout, M, N, K)
+    # one wave either way: 128-wide tiles never exceed the CUs
+    for M in range(256, 8193, 256):
+        for N in (129, 500, 1024, 2048):
+            assert lib.dense_gemm_plan(NT, M, N, 1024, 256, out) == S.OK
+            if out[1] == 128:
+                assert out[3] * out[4] <= 256

@@ -98,11 +98,12 @@ def test_workload_full_size_sampled(name):
 # ------------------------------------------------- bitwise special cases --
 
 @pytest.mark.parametrize("M,N,K", [(8192, 16384 + 128, 4096), (8192, 4096, 16384 + 40),
-                                   (8192, 1024, 1024)])
+                                   (8192, 1024, 1024), (8192, 1024, 16384)])
 def test_m8192_sweep_shapes_sampled(M, N, K):
     # extreme shapes of the benchmark's M = 8192 sweep (FP16 A.B^T, N(0,1)/8):
     # the widest N with a ragged last tile column, the deepest K with a partial
-    # last step, and the smallest (split-K) shape; sampled against the oracle
+    # last step, and the narrowest N (128-wide tiles; split-K at K = 16384);
+    # sampled against the oracle
     w = inputs.WORKLOADS["square_nt"]
     A, B = inputs.make_operands(w, seed=M + N + K, M=M, N=N, K=K)
     D, st = _gpu.gemm("nt", "f16", A, B, M, N, K)
@@ -485,3 +486,51 @@ def test_split_last_wave(layout, fmt, monkeypatch):
         assert res.ok, (mode, res)
         D2, _ = _gpu.gemm(layout, fmt, A, B, M, N, K)
         assert (D == D2).all()
+
+
+# ------------------------------------------------------ 128-wide tiles --
+
+TILE128 = [
+    # (M, N, K): ragged M, N (N = 130: a second tile column of 2), K tails
+    (300, 500, 400),
+    (256, 1024, 1024),
+    (1000, 130, 712),
+    (512, 384, 4000),
+    (96, 700, 64),
+]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", TILE128)
+def test_tile128_full_check(fmt, M, N, K, splitk, monkeypatch):
+    monkeypatch.setenv("DENSE_GEMM_TILE_N", "128")
+    w = inputs.Workload("x", "nt", fmt, 0, 0, 0, "uniform", 0.0, 301)
+    A, B = inputs.make_operands(w, M=M, N=N, K=K)
+    D, st = _gpu.gemm("nt", fmt, A, B, M, N, K)
+    assert st == status().OK
+    check_full("nt", fmt, A, B, M, N, K, D)
+
+
+@pytest.mark.parametrize("parts", ["3", "16"])
+def test_tile128_forced_split(parts, monkeypatch):
+    monkeypatch.setenv("DENSE_GEMM_TILE_N", "128")
+    monkeypatch.setenv("DENSE_GEMM_SPLITK", parts)
+    M, N, K = 520, 300, 2000
+    A, B = inputs.make_operands(inputs.WORKLOADS["ragged_nt"], M=M, N=N, K=K)
+    D, st = _gpu.gemm("nt", "f16", A, B, M, N, K)
+    assert st == status().OK
+    check_full("nt", "f16", A, B, M, N, K, D)
+
+
+def test_tile128_bitwise_equals_tile256(monkeypatch):
+    # each output is the same sequence of MFMA accumulations in either tile
+    # width, so the results agree bit for bit (split-K off)
+    monkeypatch.setenv("DENSE_GEMM_SPLITK", "off")
+    M, N, K = 1000, 900, 1500
+    A, B = inputs.make_operands(inputs.WORKLOADS["square_nt"], M=M, N=N, K=K)
+    out = {}
+    for tn in ("128", "256"):
+        monkeypatch.setenv("DENSE_GEMM_TILE_N", tn)
+        out[tn], st = _gpu.gemm("nt", "f16", A, B, M, N, K)
+        assert st == status().OK
+    assert np.array_equal(out["128"], out["256"])
