@@ -677,7 +677,7 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
   // 192 MiB); beyond it (measured: 8192 x 1024 x 16384) 256-wide tiles with
   // split-K are faster.
   const int64_t t256 = tiles_m * ((N + BN - 1) / BN);
-  const bool cached = (M + N) * K * 2 <= ((int64_t)192 << 20);
+  const bool cached = K == 0 || (M + N) <= ((int64_t)96 << 20) / K;  // (M + N) K 2 B <= 192 MiB
   const int64_t tw = layout == NT && N > BN / 2 && 2 * t256 <= num_cus && cached ? BN / 2 : BN;
   const int64_t tiles_n = (N + tw - 1) / tw;
   const int64_t tasks = tiles_m * tiles_n;
