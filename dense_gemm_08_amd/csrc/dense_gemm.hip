@@ -18,16 +18,19 @@
 //     row-wise tile writes and the column-wise MFMA fragment reads spread over
 //     all banks (the role of the 128-byte swizzle in the TIRx and TileFoundry
 //     shared-memory layouts);
-//   * v_mfma_f32_32x32x16_{f16,bf16} with FP32 accumulators; four waves each
-//     own a 128 x 128 quarter of a 256 x 256 tile and read the shared A and B
-//     stages ("TIRx GEMM on Blackwell", V8/V9: larger tiles and several
-//     consumers reusing one staged operand tile);
+//   * v_mfma_f32_16x16x32_{f16,bf16} with FP32 accumulators; four waves each
+//     own a 128 x 128 quarter of a 256 x 256 tile (128 x 64 of a 256 x 128
+//     tile for narrow A @ B.T outputs) and read the shared A and B stages
+//     ("TIRx GEMM on Blackwell", V8/V9: larger tiles and several consumers
+//     reusing one staged operand tile);
 //   * an epilogue that rounds to the output type, stages each wave's rows in
 //     LDS and writes whole 16-byte row chunks (TileFoundry tutorial, section 5:
 //     the output tile is staged in shared memory before the store);
 //   * ragged M, N and K handled by masking: out-of-range loads read zeros
 //     through the buffer descriptor's range check, out-of-range stores are
-//     skipped (the pages' shapes all divide the tiles; this is our reading).
+//     skipped (the pages' shapes all divide the tiles; this is our reading);
+//   * split-K for the last, partial wave of tiles, and a repack of operands
+//     the 16-byte loads cannot read in place (host side, below).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
