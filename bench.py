@@ -464,10 +464,19 @@ def main():
 
 
 def source_sha(name: str = "dense_gemm.hip") -> str:
+    """sha256 prefix of a kernel source and the headers it shares, with
+    comments and blank space removed: the traffic figures recorded for it
+    stay valid across comment edits, not across code changes."""
     import hashlib
-    p = os.path.join(ROOT, "dense_gemm_08_amd", "csrc", name)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    h = hashlib.sha256()
+    for f in (name, "cdna_ops.h", "tile_sched.h"):
+        with open(os.path.join(ROOT, "dense_gemm_08_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", " ", text).encode())
+    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":
