@@ -534,25 +534,31 @@ __global__ __launch_bounds__(256) void split_reduce(Params p) {
 // Copy of a rows x cols matrix of 16-bit elements (any leading dimension,
 // 2-byte alignment) into a dense, 16-byte aligned rows x dcols matrix
 // (dcols = cols rounded up to 8), zero-filling columns cols .. dcols-1: the
-// layout the tiled kernel's 16-byte chunk loads need.  One thread per
-// 8-element chunk of the destination.
+// layout the tiled kernel's 16-byte chunk loads need.  Each thread handles
+// 8-element chunks of the destination, striding over the grid.
+constexpr int64_t REPACK_MAX_BLOCKS = 1 << 16;
 __global__ __launch_bounds__(256) void repack(const uint16_t* __restrict__ src, int64_t rows,
                                               int64_t cols, int64_t ld, uint16_t* __restrict__ dst,
                                               int64_t dcols) {
-  const int64_t chunks = dcols / 8;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= rows * chunks) return;
-  const int64_t r = gid / chunks;
-  const int64_t c0 = (gid % chunks) * 8;
-  const uint16_t* s = src + r * ld + c0;
-  uint32_t w[4];
+  const int64_t chunks = dcols / 8, total = rows * chunks;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < total; gid += stride) {
+    const int64_t r = gid / chunks;
+    const int64_t c0 = (gid % chunks) * 8;
+    const uint16_t* s = src + r * ld + c0;
+    uint32_t w[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t lo = c0 + 2 * e < cols ? s[2 * e] : 0u;
-    const uint32_t hi = c0 + 2 * e + 1 < cols ? s[2 * e + 1] : 0u;
-    w[e] = lo | (hi << 16);
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = c0 + 2 * e < cols ? s[2 * e] : 0u;
+      const uint32_t hi = c0 + 2 * e + 1 < cols ? s[2 * e + 1] : 0u;
+      w[e] = lo | (hi << 16);
+    }
+    *(u32x4*)(dst + r * dcols + c0) = (u32x4){w[0], w[1], w[2], w[3]};
   }
-  *(u32x4*)(dst + r * dcols + c0) = (u32x4){w[0], w[1], w[2], w[3]};
+}
+static unsigned repack_blocks(int64_t chunks) {
+  const int64_t b = (chunks + 255) / 256;
+  return (unsigned)(b < REPACK_MAX_BLOCKS ? b : REPACK_MAX_BLOCKS);
 }
 
 // ---- host side ----------------------------------------------------------
@@ -627,6 +633,8 @@ dense_gemm_status dense_gemm_validate(int layout, int64_t M, int64_t N, int64_t 
   if (M < 0 || N < 0 || K < 0) return DENSE_GEMM_INVALID_DIM;
   if (M == 0 || N == 0) return DENSE_GEMM_OK;
   if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return DENSE_GEMM_TOO_LARGE;
+  // task numbers are 32-bit: the tile count at the narrower tile width
+  if (((M + BM - 1) / BM) * ((N + BN / 2 - 1) / (BN / 2)) >= kMaxDim) return DENSE_GEMM_TOO_LARGE;
   if (D == nullptr) return DENSE_GEMM_NULL_PTR;
   if (K > 0 && (A == nullptr || B == nullptr)) return DENSE_GEMM_NULL_PTR;
   if (ldd < N) return DENSE_GEMM_BAD_LD;
@@ -813,16 +821,14 @@ static dense_gemm_status launch(int64_t M, int64_t N, int64_t K, const void* A, 
   }
   if (!a_direct) {
     uint16_t* a2 = (uint16_t*)ws;
-    const int64_t threads = M * (K8 / 8);
-    hipLaunchKernelGGL(repack, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(repack, dim3(repack_blocks(M * (K8 / 8))), dim3(256), 0, stream,
                        (const uint16_t*)A, M, K, lda, a2, K8);
     p.A = a2;
     p.lda = (int)K8;
   }
   if (!b_direct) {
     uint16_t* b2 = (uint16_t*)(ws + a_bytes);
-    const int64_t threads = b_rows * (b_dcols / 8);
-    hipLaunchKernelGGL(repack, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(repack, dim3(repack_blocks(b_rows * (b_dcols / 8))), dim3(256), 0, stream,
                        (const uint16_t*)B, b_rows, b_cols, ldb, b2, b_dcols);
     p.B = b2;
     p.ldb = (int)b_dcols;

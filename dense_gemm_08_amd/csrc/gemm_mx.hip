@@ -458,6 +458,8 @@ extern "C" dense_gemm_status gemm_nt_e4m3_mx(int64_t M, int64_t N, int64_t K, co
   if (M == 0 || N == 0) return DENSE_GEMM_OK;
   const int64_t lim = (int64_t)1 << 31;
   if (M >= lim || N >= lim || K >= lim) return DENSE_GEMM_TOO_LARGE;
+  // task numbers are 32-bit
+  if (((M + mx::BM - 1) / mx::BM) * ((N + mx::BN - 1) / mx::BN) >= lim) return DENSE_GEMM_TOO_LARGE;
   if (K % mx::GROUP != 0) return DENSE_GEMM_BAD_ARG;
   const int64_t nb = K / mx::GROUP;
   if (D == nullptr) return DENSE_GEMM_NULL_PTR;

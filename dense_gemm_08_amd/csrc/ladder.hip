@@ -213,6 +213,9 @@ extern "C" dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N,
     return DENSE_GEMM_MISALIGNED;
   if (((tile - 1) * lda + K) * 2 >= ((int64_t)1 << 31) || ((tile - 1) * ldb + K) * 2 >= ((int64_t)1 << 31))
     return DENSE_GEMM_TOO_LARGE;
+  // 32-bit row pitch of D and tile numbers
+  if (ldd >= ((int64_t)1 << 31) || (M / tile) * (N / tile) >= ((int64_t)1 << 31))
+    return DENSE_GEMM_TOO_LARGE;
   int cus = 0;
   const dense_gemm_status st = device_cus(&cus);
   if (st != DENSE_GEMM_OK) return st;

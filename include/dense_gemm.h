@@ -95,7 +95,8 @@ typedef enum dense_gemm_status {
   DENSE_GEMM_NULL_PTR = 2,      /* D null with M*N > 0; A or B null with M*N*K > 0 */
   DENSE_GEMM_BAD_LD = 3,        /* a leading dimension below its minimum */
   DENSE_GEMM_MISALIGNED = 4,    /* A, B or D at an odd address */
-  DENSE_GEMM_TOO_LARGE = 5,     /* a dimension >= 2^31, or a per-tile operand span >= 2^31 bytes */
+  DENSE_GEMM_TOO_LARGE = 5,     /* a dimension >= 2^31, 2^31 or more output tiles,
+                                   or a per-tile operand span >= 2^31 bytes */
   DENSE_GEMM_LAUNCH_FAILED = 6, /* the HIP runtime rejected the launch */
   DENSE_GEMM_NO_DEVICE = 7,     /* no current HIP device, or it is not a gfx950 */
   DENSE_GEMM_BAD_ARG = 8,       /* an argument of a helper below is out of its range */

@@ -98,6 +98,10 @@ def test_validate_error_codes():
     assert _v(NT, 1 << 31, 8, 8) == S.TOO_LARGE
     assert _v(NT, 8, 8, 8, lda=1 << 23) == S.TOO_LARGE
     assert _v(NN, 8, 8, 8, ldb=1 << 26) == S.TOO_LARGE
+    # task numbers are 32-bit: at most 2^31 - 1 tiles of 256 x 128
+    assert _v(NT, 1 << 23, 1 << 22, 8) == S.OK          # 2^15 x 2^15 tiles
+    assert _v(NT, 1 << 24, 1 << 23, 8) == S.TOO_LARGE   # 2^16 x 2^16 tiles
+    assert _v(NN, (1 << 31) - 1, (1 << 31) - 1, 0) == S.TOO_LARGE
 
 
 def tile_of(task, tm, tn, g):
@@ -259,6 +263,7 @@ def test_mx_argument_checks_on_the_host():
     assert _mx(8, 8, -32) == S.INVALID_DIM
     assert _mx(0, 8, 64) == S.OK and _mx(8, 0, 64) == S.OK  # nothing to do
     assert _mx(1 << 31, 8, 64) == S.TOO_LARGE
+    assert _mx(1 << 24, 1 << 23, 64) == S.TOO_LARGE  # 2^16 x 2^15 tiles of 256 x 256
     assert _mx(8, 8, 40) == S.BAD_ARG       # K not a multiple of 32
     assert _mx(8, 8, 64, D=0) == S.NULL_PTR
     assert _mx(8, 8, 64, SB=0) == S.NULL_PTR
@@ -291,3 +296,27 @@ def test_plan_tile_width():
             assert lib.dense_gemm_plan(NT, M, N, 1024, 256, out) == S.OK
             if out[1] == 128:
                 assert out[3] * out[4] <= 256
+
+
+def test_ladder_argument_checks_on_the_host():
+    # every case is rejected before the library touches the device (fake,
+    # 16-byte aligned addresses)
+    fn = binding.raw("gemm_nt_f16_ladder")
+    ok = dict(M=256, N=256, K=64, A=64, lda=64, B=64, ldb=64, D=64, ldd=256)
+
+    def lad(level, **kw):
+        a = dict(ok, **kw)
+        return S(fn(level, a["M"], a["N"], a["K"], a["A"], a["lda"], a["B"], a["ldb"], a["D"],
+                    a["ldd"], None))
+
+    assert lad(0) == S.BAD_ARG and lad(7) == S.BAD_ARG
+    assert lad(5, M=384) == S.BAD_ARG          # level 5 tiles are 256 x 256
+    assert lad(1, K=100) == S.BAD_ARG          # K a multiple of 64
+    assert lad(1, M=1 << 31) == S.BAD_ARG
+    assert lad(1, D=0) == S.NULL_PTR
+    assert lad(1, ldd=255) == S.BAD_LD
+    assert lad(2, A=66) == S.MISALIGNED
+    assert lad(2, ldd=260) == S.MISALIGNED     # not a multiple of 8
+    assert lad(1, lda=1 << 24) == S.TOO_LARGE  # tile span >= 2 GiB
+    assert lad(1, ldd=1 << 31) == S.TOO_LARGE  # 32-bit row pitch of D
+    assert lad(1, M=(1 << 31) - 128, N=(1 << 31) - 128, ldd=(1 << 31) - 128) == S.TOO_LARGE

@@ -303,6 +303,25 @@ def test_repacked_equals_direct(layout, fmt):
     assert (D1 == D2).all() and (D1 == D3).all()
 
 
+def test_repack_beyond_one_grid_pass():
+    # the repack kernel strides over a capped grid (65536 workgroups of 256
+    # threads, one 8-element chunk per thread and pass): an A of 8200 rows
+    # with K = 16390 (rows padded to 16392) holds 16,801,800 chunks, so rows
+    # 8188 and up are copied by a second pass.  Sampled entries, and every
+    # entry of the last 12 rows, against the oracle.
+    w = inputs.WORKLOADS["square_nt"]
+    M, N, K = 8200, 256, 16390
+    A, B = inputs.make_operands(w, seed=77, M=M, N=N, K=K)
+    D, st = _gpu.gemm("nt", "f16", A, B, M, N, K)
+    assert st == status().OK
+    check_sampled("nt", "f16", A, B, M, N, K, D, n=1000, seed=77)
+    rows = np.repeat(np.arange(M - 12, M), N)
+    cols = np.tile(np.arange(N), 12)
+    d, s = oracle.gemm_entries("nt", "f16", A, B, K=K, lda=K, ldb=K, rows=rows, cols=cols)
+    res = oracle.check("f16", d, s, D[rows, cols])
+    assert res.ok, (res, rows[max(res.worst_idx, 0)], cols[max(res.worst_idx, 0)])
+
+
 def test_zero_k_writes_zeros_and_empty_is_noop():
     t = _gpu.torch()
     D = _gpu.empty_out(40, 48)
