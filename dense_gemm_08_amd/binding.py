@@ -92,13 +92,30 @@ def _status_string(status: int) -> str:
             return "unknown status"
 
 
-def _stream_handle(stream) -> int:
+def _stream_handle(stream, device) -> int:
+    """The HIP stream handle: ``stream`` itself, or the current stream of
+    ``device`` when it is None."""
     if stream is None:
         import torch
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _ld(t) -> int:
+    """Leading dimension (elements between rows) of a 2-D tensor with unit
+    column stride.  A single row may carry any row stride (a transposed
+    column, an expanded view): its leading dimension is then its width."""
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def _same_device(*ts):
+    dev = ts[0].device
+    for t in ts[1:]:
+        if t.device != dev:
+            raise ValueError("operands on different devices: %s and %s" % (dev, t.device))
+    return dev
 
 
 def _check_tensor(t, dtype_name: str, what: str):
@@ -108,7 +125,7 @@ def _check_tensor(t, dtype_name: str, what: str):
         raise TypeError("%s must be %s, got %s" % (what, want, t.dtype))
     if not t.is_cuda:
         raise ValueError("%s must be a device tensor" % what)
-    if t.dim() != 2 or t.stride(1) != 1:
+    if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
         raise ValueError("%s must be 2-D with unit column stride" % what)
 
 
@@ -131,8 +148,11 @@ def _call(name: str, layout: str, fmt: str, A, B, D=None, stream=None):
         _check_tensor(D, fmt, "D")
         if D.shape[0] != M or D.shape[1] != N:
             raise ValueError("D has shape %s, expected (%d, %d)" % (tuple(D.shape), M, N))
-    st = getattr(lib, name)(M, N, K, A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0),
-                            D.data_ptr(), D.stride(0), _stream_handle(stream))
+    dev = _same_device(A, B, D)
+    # the library launches on the current device
+    with torch.cuda.device(dev):
+        st = getattr(lib, name)(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
+                                D.data_ptr(), _ld(D), _stream_handle(stream, dev))
     if st != Status.OK:
         raise DenseGemmError(st, name)
     return D
@@ -171,7 +191,7 @@ def gemm_nt_e4m3_mx(A, SA, B, SB, D=None, stream=None):
     import torch
     lib = load_library()
     for t, what in ((A, "A"), (SA, "SA"), (B, "B"), (SB, "SB")):
-        if t.element_size() != 1 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+        if t.element_size() != 1 or not t.is_cuda or t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
             raise ValueError("%s must be a 2-D byte device tensor with unit column stride" % what)
     M, K = A.shape
     N = B.shape[0]
@@ -184,9 +204,11 @@ def gemm_nt_e4m3_mx(A, SA, B, SB, D=None, stream=None):
         _check_tensor(D, "bf16", "D")
         if D.shape[0] != M or D.shape[1] != N:
             raise ValueError("D has shape %s, expected (%d, %d)" % (tuple(D.shape), M, N))
-    st = lib.gemm_nt_e4m3_mx(M, N, K, A.data_ptr(), A.stride(0), SA.data_ptr(), SA.stride(0),
-                             B.data_ptr(), B.stride(0), SB.data_ptr(), SB.stride(0),
-                             D.data_ptr(), D.stride(0), _stream_handle(stream))
+    dev = _same_device(A, SA, B, SB, D)
+    with torch.cuda.device(dev):
+        st = lib.gemm_nt_e4m3_mx(M, N, K, A.data_ptr(), _ld(A), SA.data_ptr(), _ld(SA),
+                                 B.data_ptr(), _ld(B), SB.data_ptr(), _ld(SB),
+                                 D.data_ptr(), _ld(D), _stream_handle(stream, dev))
     if st != Status.OK:
         raise DenseGemmError(st, "gemm_nt_e4m3_mx")
     return D

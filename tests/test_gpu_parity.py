@@ -393,6 +393,27 @@ def test_python_binding_roundtrip():
                d2.cpu().view(t.int16).numpy().view(np.uint16))
 
 
+def test_python_binding_row_and_column_views():
+    # one-row operands whose row stride is not their width (a transposed
+    # column), a one-column output, and a row-sliced B: the binding passes
+    # valid leading dimensions for each
+    t = _gpu.torch()
+    import dense_gemm_08_amd as dg
+    a = t.randn(72, 1, device="cuda").half().t()          # 1 x 72, strides (1, 1)
+    b = t.randn(40, 72, device="cuda").half()
+    d = dg.gemm_nt_f16(a, b)
+    t.cuda.synchronize()
+    to_bits = lambda x: x.contiguous().cpu().view(t.int16).numpy().view(np.uint16)  # noqa: E731
+    check_full("nt", "f16", to_bits(a), to_bits(b), 1, 40, 72, to_bits(d))
+    a2 = t.randn(33, 64, device="cuda").bfloat16()
+    b2 = t.randn(128, 9, device="cuda").bfloat16()[:64, :1]  # 64 x 1, row stride 9
+    d2 = dg.gemm_nn_bf16(a2, b2)
+    t.cuda.synchronize()
+    check_full("nn", "bf16", to_bits(a2), to_bits(b2), 33, 1, 64, to_bits(d2))
+    with pytest.raises(ValueError):
+        dg.gemm_nt_f16(a, b.cpu())
+
+
 # ----------------------------------------------- optimisation-step kernels --
 
 LEVELS = [1, 2, 3, 4, 5, 6]
