@@ -114,6 +114,21 @@ def small_integers(fmt: str, shape, seed: int, lo: int = -3, hi: int = 3) -> np.
     return to_bits(fmt, rng.integers(lo, hi + 1, size=shape).astype(np.float64))
 
 
+def small_integers_large(fmt: str, shape, seed: int, lo: int = -1, hi: int = 1,
+                         chunk: int = 1 << 26) -> np.ndarray:
+    """Integers uniform in [lo, hi] as FP16/BF16 bits, for operands of
+    gigabytes: drawn as int8 in chunks of ``chunk`` values and encoded through
+    a table of the few distinct values (a stream of its own, not the one
+    ``small_integers`` draws)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    table = to_bits(fmt, np.arange(lo, hi + 1, dtype=np.float64))
+    out = np.empty(int(np.prod(shape)), dtype=np.uint16)
+    for i in range(0, out.size, chunk):
+        n = min(chunk, out.size - i)
+        out[i:i + n] = table[rng.integers(0, hi - lo + 1, size=n, dtype=np.int8)]
+    return out.reshape(shape)
+
+
 def identity(fmt: str, n: int) -> np.ndarray:
     return to_bits(fmt, np.eye(n))
 
@@ -220,6 +235,29 @@ def mx_small_integers(M: int, N: int, K: int, seed: int, lo: int = -3, hi: int =
     B = _e4m3_codes(rng.integers(lo, hi + 1, size=(N, K)).astype(np.float64))
     SA = rng.integers(127, 129, size=(M, K // 32)).astype(np.uint8)
     SB = rng.integers(127, 129, size=(N, K // 32)).astype(np.uint8)
+    return A, SA, B, SB
+
+
+def mx_small_integers_large(M: int, N: int, K: int, seed: int, lo: int = -1, hi: int = 1,
+                            chunk: int = 1 << 26):
+    """Integer-valued E4M3 codes in [lo, hi] with unit scales (2^0) for
+    operands of gigabytes, drawn as int8 in chunks and encoded through a
+    table: every partial sum is an integer of magnitude at most
+    K * max(|lo|, |hi|)^2."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    table = _e4m3_codes(np.arange(lo, hi + 1, dtype=np.float64))
+
+    def draw(rows):
+        out = np.empty(rows * K, dtype=np.uint8)
+        for i in range(0, out.size, chunk):
+            n = min(chunk, out.size - i)
+            out[i:i + n] = table[rng.integers(0, hi - lo + 1, size=n, dtype=np.int8)]
+        return out.reshape(rows, K)
+
+    A = draw(M)
+    B = draw(N)
+    SA = np.full((M, K // 32), 127, dtype=np.uint8)
+    SB = np.full((N, K // 32), 127, dtype=np.uint8)
     return A, SA, B, SB
 
 

@@ -98,6 +98,11 @@ def test_validate_error_codes():
     assert _v(NT, 1 << 31, 8, 8) == S.TOO_LARGE
     assert _v(NT, 8, 8, 8, lda=1 << 23) == S.TOO_LARGE
     assert _v(NN, 8, 8, 8, ldb=1 << 26) == S.TOO_LARGE
+    # the largest accepted operand spans (one row of tiles short of 2^31 bytes)
+    assert _v(NT, 256, 256, 4194296) == S.OK
+    assert _v(NT, 256, 256, 4194304) == S.TOO_LARGE
+    assert _v(NN, 16, 16777208, 64) == S.OK
+    assert _v(NN, 16, 16777216, 64) == S.TOO_LARGE
     # task numbers are 32-bit: at most 2^31 - 1 tiles of 256 x 128
     assert _v(NT, 1 << 23, 1 << 22, 8) == S.OK          # 2^15 x 2^15 tiles
     assert _v(NT, 1 << 24, 1 << 23, 8) == S.TOO_LARGE   # 2^16 x 2^16 tiles
@@ -264,6 +269,7 @@ def test_mx_argument_checks_on_the_host():
     assert _mx(0, 8, 64) == S.OK and _mx(8, 0, 64) == S.OK  # nothing to do
     assert _mx(1 << 31, 8, 64) == S.TOO_LARGE
     assert _mx(1 << 24, 1 << 23, 64) == S.TOO_LARGE  # 2^16 x 2^15 tiles of 256 x 256
+    assert _mx(256, 256, 1 << 23) == S.TOO_LARGE  # tile span 2^31 bytes (K - 32 is accepted)
     assert _mx(8, 8, 40) == S.BAD_ARG       # K not a multiple of 32
     assert _mx(8, 8, 64, D=0) == S.NULL_PTR
     assert _mx(8, 8, 64, SB=0) == S.NULL_PTR

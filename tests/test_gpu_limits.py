@@ -1,0 +1,109 @@
+"""GPU parity at the largest sizes the library accepts.
+
+Every tile's operand loads are addressed by 32-bit buffer offsets from a
+per-tile base, so the argument check rejects any tile whose operand span
+reaches 2^31 bytes (status TOO_LARGE).  These tests run the library just
+below that bound, where the offsets use their full range:
+
+* D = A @ B.T, FP16, M = N = 256 (one tile, split over the CUs), K = 4,194,296:
+  a tile's A and B rows span 2^31 - 4096 bytes;
+* D = A @ B, BF16, M = 16, N = 16,777,208, K = 64: a K step's B rows span
+  2^31 - 1024 bytes (65,536 tiles);
+* FP8 block-scaled D = A @ B.T, M = N = 256, K = 8,388,576: a tile's rows
+  span 2^31 - 8192 bytes (65,536 K steps in one tile).
+
+Entries are integers in {-1, 0, 1} (unit scales for FP8), so every FP32
+partial sum is an exact integer below 2^24 and each output must equal the
+oracle's correctly rounded value bit for bit.  The next size up in each case
+is rejected before any launch.  Operands take gigabytes; entries are checked
+on a sample (the corners, the last row and column included).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_08_amd import binding, inputs
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+S = binding.Status
+
+
+def _dev(a):
+    t = _gpu.torch()
+    return t.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to("cuda")
+
+
+def _exact(fmt, D, d, rows, cols):
+    want = oracle.round_to(fmt, d)
+    got = D[rows, cols]
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (bad.size, rows[bad[0]], cols[bad[0]], got[bad[0]], want[bad[0]])
+
+
+def test_nt_f16_tile_span_at_the_limit():
+    M, N, K = 256, 256, 4194296
+    print("A.B^T FP16 %d x %d x %d" % (M, N, K), flush=True)
+    A = inputs.small_integers_large("f16", (M, K), seed=101)
+    B = inputs.small_integers_large("f16", (N, K), seed=102)
+    Ad, Bd = _dev(A), _dev(B)
+    Dd = _gpu.empty_out(M, N)
+    assert _gpu.call("nt", "f16", M, N, K, Ad, K, Bd, K, Dd, N) == S.OK
+    _gpu.torch().cuda.synchronize()
+    D = _gpu.from_dev(Dd)
+    rows, cols = inputs.sample_indices(M, N, 512, seed=101)
+    d, _ = oracle.gemm_entries("nt", "f16", A, B, K=K, lda=K, ldb=K, rows=rows, cols=cols)
+    _exact("f16", D, d, rows, cols)
+    # one K step more: the span reaches 2^31 bytes
+    D0 = _gpu.empty_out(M, N)
+    assert _gpu.call("nt", "f16", M, N, K + 8, Ad, K + 8, Bd, K + 8, D0, N) == S.TOO_LARGE
+    _gpu.torch().cuda.synchronize()
+    assert (_gpu.from_dev(D0) == _gpu.CANARY).all()
+
+
+def test_nn_bf16_step_span_at_the_limit():
+    M, N, K = 16, 16777208, 64
+    print("A.B BF16 %d x %d x %d" % (M, N, K), flush=True)
+    A = inputs.small_integers_large("bf16", (M, K), seed=103)
+    B = inputs.small_integers_large("bf16", (K, N), seed=104)
+    Ad, Bd = _dev(A), _dev(B)
+    Dd = _gpu.empty_out(M, N)
+    assert _gpu.call("nn", "bf16", M, N, K, Ad, K, Bd, N, Dd, N) == S.OK
+    _gpu.torch().cuda.synchronize()
+    D = _gpu.from_dev(Dd)
+    rows, cols = inputs.sample_indices(M, N, 2048, seed=103)
+    d, _ = oracle.gemm_entries("nn", "bf16", A, B, K=K, lda=K, ldb=N, rows=rows, cols=cols)
+    _exact("bf16", D, d, rows, cols)
+    # every entry is finite (|d| <= 64): no tile was skipped or misplaced
+    assert np.isfinite(oracle.decode("bf16", D[:, ::4093])).all()
+    D0 = _gpu.empty_out(M, 8)
+    assert _gpu.call("nn", "bf16", M, N + 8, K, Ad, K, Bd, N + 8, D0, N + 8) == S.TOO_LARGE
+    _gpu.torch().cuda.synchronize()
+    assert (_gpu.from_dev(D0) == _gpu.CANARY).all()
+
+
+def test_mx_tile_span_at_the_limit():
+    M, N, K = 256, 256, 8388576
+    print("FP8 block-scaled A.B^T %d x %d x %d" % (M, N, K), flush=True)
+    A, SA, B, SB = inputs.mx_small_integers_large(M, N, K, seed=105)
+    Ad, SAd, Bd, SBd = _dev(A), _dev(SA), _dev(B), _dev(SB)
+    Dd = _gpu.empty_out(M, N)
+    fn = binding.raw("gemm_nt_e4m3_mx")
+    stream = _gpu.torch().cuda.current_stream().cuda_stream
+    nb = K // 32
+    st = fn(M, N, K, Ad.data_ptr(), K, SAd.data_ptr(), nb, Bd.data_ptr(), K, SBd.data_ptr(), nb,
+            Dd.data_ptr(), N, stream)
+    assert S(st) == S.OK
+    _gpu.torch().cuda.synchronize()
+    D = _gpu.from_dev(Dd)
+    rows, cols = inputs.sample_indices(M, N, 256, seed=105)
+    d, _ = oracle.gemm_mx_entries(A, SA, B, SB, rows, cols)
+    _exact("bf16", D, d, rows, cols)
+    D0 = _gpu.empty_out(M, N)
+    K2 = K + 32  # 2^23: the span reaches 2^31 bytes
+    st = fn(M, N, K2, Ad.data_ptr(), K2, SAd.data_ptr(), K2 // 32, Bd.data_ptr(), K2,
+            SBd.data_ptr(), K2 // 32, D0.data_ptr(), N, stream)
+    assert S(st) == S.TOO_LARGE
+    _gpu.torch().cuda.synchronize()
+    assert (_gpu.from_dev(D0) == _gpu.CANARY).all()
