@@ -320,10 +320,15 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     // Operand order (B fragment first) leaves each lane holding one row of D
     // and four consecutive columns.  Consecutive MFMAs share a B fragment, so
     // the next substep's reads (A fragments first, then B) arrive in the
-    // order its MFMAs need them.
+    // order its MFMAs need them; the A fragments run forwards under even B
+    // fragments and backwards under odd ones, so each MFMA changes one
+    // operand only.
     auto mfma_pair = [&](const Frags& F, int q) {
 #pragma unroll
-      for (int t = 2 * q; t < 2 * q + 2; ++t) mfma16<T>(acc[t % MI][t / MI], F.b[t / MI], F.a[t % MI]);
+      for (int t = 2 * q; t < 2 * q + 2; ++t) {
+        const int j = t / MI, i = (j & 1) ? MI - 1 - t % MI : t % MI;
+        mfma16<T>(acc[i][j], F.b[j], F.a[i]);
+      }
     };
 
     // The rings: stage ks (counted from the task's first step) keeps its

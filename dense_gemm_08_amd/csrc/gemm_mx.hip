@@ -207,6 +207,11 @@ __device__ __forceinline__ void mfma_mx(f32x4 (&acc)[MI][NI], const i32x8& bf, c
                                         const u32x2& sa, const u32x2& sb) {
   mx_mfma<J % 4, I % 4>(acc[I][J], bf, af, sb[J / 4], sa[I / 4]);
 }
+// MFMA t (0..31) of a half stage: B fragment t / 4 against A fragment
+// base + i, with i running forwards under even B fragments and backwards
+// under odd ones, so that each MFMA changes one operand only.
+template <int T>
+constexpr int snake_i() { return ((T / 4) & 1) ? 3 - T % 4 : T % 4; }
 
 __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
@@ -352,15 +357,16 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
 
     for (int ks = 0; ks < nk; ++ks) {
       const int slot = ks & 1;
-      // first half: A fragments 0-3 against B fragments 0-7 (pair q: blocks
-      // (2q % 4, 2q / 4) and the next); A fragments 4-7 of this stage are read
-      // in between
+      // first half: A fragments 0-3 against B fragments 0-7 (pair q: B
+      // fragment 2q / 4, two A fragments in snake order); A fragments 4-7 of
+      // this stage are read in between
       static_for<0, HALF_PAIRS>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
         if constexpr (q % 4 == 1) F.hi[q / 4] = read_a(slot, 4 + q / 4);
         if constexpr (q == 3) sa[1] = read_s(slot, fsa + 256);  // A fragments 4-7
-        mfma_mx<(2 * q) % 4, (2 * q) / 4>(acc, F.b[(2 * q) / 4], F.lo[(2 * q) % 4], sa, sb);
-        mfma_mx<(2 * q + 1) % 4, (2 * q + 1) / 4>(acc, F.b[(2 * q + 1) / 4], F.lo[(2 * q + 1) % 4], sa, sb);
+        mfma_mx<snake_i<2 * q>(), (2 * q) / 4>(acc, F.b[(2 * q) / 4], F.lo[snake_i<2 * q>()], sa, sb);
+        mfma_mx<snake_i<2 * q + 1>(), (2 * q + 1) / 4>(acc, F.b[(2 * q + 1) / 4],
+                                                       F.lo[snake_i<2 * q + 1>()], sa, sb);
         fence();
       });
       // second half: A fragments 4-7.  After BARQ pairs, the barrier: stage
@@ -378,8 +384,9 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
         // stage ks+1's reads: B fragment j (and sb[0]) only after its last
         // MFMA of this stage (pairs 2j, 2j+1; sb[0] serves pairs 0-7)
         if constexpr (q >= BARQ && q <= 14) read_next(slot ^ 1, q - BARQ);
-        mfma_mx<4 + (2 * q) % 4, (2 * q) / 4>(acc, F.b[(2 * q) / 4], F.hi[(2 * q) % 4], sa, sb);
-        mfma_mx<4 + (2 * q + 1) % 4, (2 * q + 1) / 4>(acc, F.b[(2 * q + 1) / 4], F.hi[(2 * q + 1) % 4], sa, sb);
+        mfma_mx<4 + snake_i<2 * q>(), (2 * q) / 4>(acc, F.b[(2 * q) / 4], F.hi[snake_i<2 * q>()], sa, sb);
+        mfma_mx<4 + snake_i<2 * q + 1>(), (2 * q + 1) / 4>(acc, F.b[(2 * q + 1) / 4],
+                                                           F.hi[snake_i<2 * q + 1>()], sa, sb);
         fence();
         if constexpr (q >= BARQ) {
           constexpr int n = HALF_PAIRS - BARQ, tot = 2 * DMA + 1;
