@@ -415,58 +415,72 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
 
     // Epilogue: per 32-row band (two 16-row blocks), round, stage the band's
     // 32 x WTN outputs of this wave in LDS (rows of CH 16-byte chunks,
-    // swizzled by row), then store 16-byte row chunks.
+    // swizzled by row), then store 16-byte row chunks.  Each phase is issued
+    // whole before the next (all conversions into registers of their own,
+    // all LDS writes, all read-backs, then the stores), so that their
+    // latencies overlap instead of adding up per chunk.
     constexpr int CH = WTN / 8;       // 16-byte chunks per staged row
     constexpr int RPI = 64 / CH;      // rows per wave instruction of the read-back
+    constexpr int NR = 32 / RPI;      // read-back instructions per band
     char* stg = smem + wave * (32 * CH * 16);
     const bool interior = p.d_vec && vm == BM && vn == TN;
 #pragma unroll
     for (int band = 0; band < MI / 2; ++band) {
+      // lane holds row half*16 + l16 of the band, columns j*16 + 4*lq + 0..3
+      // of each block j: 16-byte chunk 2j + lq/2, its lower or upper 8 bytes
+      u32x2 v[2][NI];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          v[half][j][0] = pack2<T>(acc[2 * band + half][j][0], acc[2 * band + half][j][1]);
+          v[half][j][1] = pack2<T>(acc[2 * band + half][j][2], acc[2 * band + half][j][3]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int i = 2 * band + half;
         const int row = half * 16 + l16;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-          // lane holds row `row` of the band, columns j*16 + 4*lq + 0..3:
-          // 16-byte chunk 2j + lq/2, its lower or upper 8 bytes
-          u32x2 v;
-          v[0] = pack2<T>(acc[i][j][0], acc[i][j][1]);
-          v[1] = pack2<T>(acc[i][j][2], acc[i][j][3]);
           const int chunk = 2 * j + (lq >> 1);
-          *(u32x2*)(stg + row * (CH * 16) + ((chunk ^ (row & (CH - 1))) << 4) + (lq & 1) * 8) = v;
+          *(u32x2*)(stg + row * (CH * 16) + ((chunk ^ (row & (CH - 1))) << 4) + (lq & 1) * 8) =
+              v[half][j];
         }
-        // keep the conversions of one block together (bounded live registers)
-        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_sched_barrier(0);
       const int row0 = m0 + wm * WTM + band * 32;
       const int col0 = n0 + wn * WTN;
       const int cc = lane % CH;
+      u32x4 r[NR];
+#pragma unroll
+      for (int t = 0; t < NR; ++t) {
+        const int rr = t * RPI + lane / CH;
+        r[t] = *(const u32x4*)(stg + rr * (CH * 16) + ((cc ^ (rr & (CH - 1))) << 4));
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // D is written once and not read again here: non-temporal stores
       // (measured 0.3-1% faster, 4.7% on the large FP8 product)
       if (interior) {
         // the whole tile is inside D and its rows are 16-byte aligned
 #pragma unroll
-        for (int t = 0; t < 32 / RPI; ++t) {
+        for (int t = 0; t < NR; ++t) {
           const int rr = t * RPI + lane / CH;
-          const u32x4 v = *(const u32x4*)(stg + rr * (CH * 16) + ((cc ^ (rr & (CH - 1))) << 4));
-          __builtin_nontemporal_store(v, (u32x4*)(p.D + (int64_t)(row0 + rr) * p.ldd + col0 + cc * 8));
+          __builtin_nontemporal_store(r[t], (u32x4*)(p.D + (int64_t)(row0 + rr) * p.ldd + col0 + cc * 8));
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < 32 / RPI; ++t) {
+        for (int t = 0; t < NR; ++t) {
           const int rr = t * RPI + lane / CH;
-          const u32x4 v = *(const u32x4*)(stg + rr * (CH * 16) + ((cc ^ (rr & (CH - 1))) << 4));
           const int row = row0 + rr;
           const int col = col0 + cc * 8;
           if (row < p.M && col < p.N) {
             uint16_t* dst = p.D + (int64_t)row * p.ldd + col;
             if (p.d_vec && col + 8 <= p.N) {
-              __builtin_nontemporal_store(v, (u32x4*)dst);
+              __builtin_nontemporal_store(r[t], (u32x4*)dst);
             } else {
 #pragma unroll
               for (int e = 0; e < 8; ++e)
-                if (col + e < p.N) dst[e] = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
+                if (col + e < p.N) dst[e] = (uint16_t)(r[t][e >> 1] >> ((e & 1) * 16));
             }
           }
         }
