@@ -148,8 +148,12 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     const int l16 = lane & 15;
     const int lq = lane >> 4;
 
-    // Accumulators, reset before the prologue so that many instructions
-    // separate the reset from the first MFMA that reads it.
+    // Accumulators start at zero.  The compiler places the zeroing just
+    // before the K loop, after the prologue's barrier and fragment reads: at
+    // least 30 instructions separate each register's reset from the first
+    // (asm, so unguarded) MFMA that reads it, far more than the wait states
+    // the hardware needs.  (Pinning it earlier, under the first loads, made
+    // the register allocator spill.)
     f32x4 acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
