@@ -349,14 +349,18 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
       for (int i = 0; i < 2 * DMA + 1; ++i) load(s0, i, true);
       const Stage s1 = stage_setup(1, 1);
 #pragma unroll
-      for (int i = 0; i < 2 * DMA + 1; ++i) load(s1, i, true);
-      wait_vm_barrier<2 * DMA + 1>();  // stage 0 has landed
+      for (int i = 0; i < DMA; ++i) load(s1, i, true);
+      load(s1, 2 * DMA, true);
+      wait_vm_barrier<DMA + 1>();  // stage 0 has landed
 #pragma unroll
       for (int step = 0; step < 15; ++step) read_next(0, step);
     }
 
     for (int ks = 0; ks < nk; ++ks) {
       const int slot = ks & 1;
+      // stage ks+1's B tile, into the other slot (free since the last
+      // barrier): issued over the first half's first DMA pairs
+      const Stage sn1 = stage_setup(ks + 1, slot ^ 1);
       // first half: A fragments 0-3 against B fragments 0-7 (pair q: B
       // fragment 2q / 4, two A fragments in snake order); A fragments 4-7 of
       // this stage are read in between
@@ -368,12 +372,15 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
         mfma_mx<snake_i<2 * q + 1>(), (2 * q + 1) / 4>(acc, F.b[(2 * q + 1) / 4],
                                                        F.lo[snake_i<2 * q + 1>()], sa, sb);
         fence();
+        if constexpr (q < DMA) load(sn1, DMA + q, false);
       });
       // second half: A fragments 4-7.  After BARQ pairs, the barrier: stage
       // ks+1 has landed for every wave and every wave is done reading stage
       // ks; then stage ks+1's A fragments 0-3 and scales are read, each B
       // fragment once its last MFMA of this stage has issued, and stage ks's
-      // slot is refilled with stage ks+2.
+      // slot is refilled with stage ks+2's A tile and scales (its B tile
+      // during the next stage's first half: the refill loads are split over
+      // two halves rather than bunched into one).
       const Stage sn = stage_setup(ks + 2, slot);
       static_for<0, HALF_PAIRS>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
@@ -389,9 +396,13 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
                                                            F.hi[snake_i<2 * q + 1>()], sa, sb);
         fence();
         if constexpr (q >= BARQ) {
-          constexpr int n = HALF_PAIRS - BARQ, tot = 2 * DMA + 1;
-          static_for<((q - BARQ) * tot) / n, ((q - BARQ + 1) * tot) / n>(
-              [&](auto ic) { load(sn, decltype(ic)::value, false); });
+          // stage ks+2's A tile and scale panel (its B tile follows in the
+          // next stage's first half)
+          constexpr int n = HALF_PAIRS - BARQ, tot = DMA + 1;
+          static_for<((q - BARQ) * tot) / n, ((q - BARQ + 1) * tot) / n>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            load(sn, i < DMA ? i : 2 * DMA, false);
+          });
         }
       });
       read_next(slot ^ 1, 13);  // B fragment 7, free after the last pair
