@@ -59,6 +59,9 @@ constexpr int LDS = 2 * SLOT;              // 132 KiB
 constexpr int DMA = OP_BYTES / (THREADS * 16);  // 8 loads per thread per operand
 constexpr int HALF_PAIRS = 16;             // MFMA pairs per half stage
 constexpr int BARQ = 2;                    // pairs of the second half before its barrier
+// (the next stage's read step 2j, B fragment j, runs at pair BARQ + 2j and
+// must follow the fragment's last MFMA pair 2j + 1; 3 and 4 measured no faster)
+static_assert(BARQ >= 2, "B fragment reads would overtake their last MFMAs");
 
 struct MxParams {
   const uint8_t* A;
@@ -405,8 +408,9 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
           });
         }
       });
-      read_next(slot ^ 1, 13);  // B fragment 7, free after the last pair
-      read_next(slot ^ 1, 14);  // sb[1]
+      // the remaining reads (B fragment 7 and sb[1] last: free after the
+      // last pair)
+      static_for<15 - BARQ, 15>([&](auto sc) { read_next(slot ^ 1, decltype(sc)::value); });
     }
 
     wait_vm_barrier<0>();  // every wave is done with the ring; reuse it for staging
