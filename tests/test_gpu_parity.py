@@ -374,6 +374,54 @@ def test_deterministic_and_stream_ordered():
     assert (outs[0] == outs[1]).all() and (outs[1] == outs[2]).all()
 
 
+def test_concurrent_streams_with_workspaces():
+    # calls that each take a stream-ordered workspace (split-K partials, a
+    # repacked operand, FP8 scale panels), issued back to back on two
+    # streams at once, give the same bits as the same calls run alone
+    t = _gpu.torch()
+    w = inputs.WORKLOADS["square_nt"]
+    A1, B1 = inputs.make_operands(w, seed=61, M=128, N=128, K=4096)           # split-K
+    wn = inputs.WORKLOADS["large_nn"]
+    A2, B2 = inputs.make_operands(wn, seed=62, M=264, N=304, K=1032)          # repacked A
+    A1d, B1d = _gpu.to_dev(A1, 128, 4096), _gpu.to_dev(B1, 128, 4096)
+    A2d, B2d = _gpu.to_dev(A2, 264, 1032, ld=1033), _gpu.to_dev(B2, 1032, 304)
+    XA, XSA, XB, XSB = [t.from_numpy(x).cuda() for x in inputs.mx_operands(280, 300, 160, seed=63)]
+    mx = binding_raw("gemm_nt_e4m3_mx")
+
+    def run(kind, D, stream):
+        h = stream.cuda_stream
+        if kind == 0:
+            return _gpu.call("nt", "f16", 128, 128, 4096, A1d, 4096, B1d, 4096, D, 128, stream)
+        if kind == 1:
+            return _gpu.call("nn", "bf16", 264, 304, 1032, A2d, 1033, B2d, 304, D, 304, stream)
+        return status()(mx(280, 300, 160, XA.data_ptr(), 160, XSA.data_ptr(), 5, XB.data_ptr(), 160,
+                           XSB.data_ptr(), 5, D.data_ptr(), 300, h))
+
+    shapes = [(128, 128), (264, 304), (280, 300)]
+    ref = []
+    main = t.cuda.current_stream()
+    for kind in range(3):
+        D = _gpu.empty_out(*shapes[kind])
+        assert run(kind, D, main) == status().OK
+        t.cuda.synchronize()
+        ref.append(_gpu.from_dev(D))
+    streams = [t.cuda.Stream(), t.cuda.Stream()]
+    # outputs (canary-filled on the main stream) first; then both streams
+    # wait for that work and run without synchronising with each other
+    outs = [((it + si) % 3, si, _gpu.empty_out(*shapes[(it + si) % 3]))
+            for it in range(12) for si in range(2)]
+    for st in streams:
+        st.wait_stream(main)
+    for kind, si, D in outs:
+        with t.cuda.stream(streams[si]):
+            assert run(kind, D, streams[si]) == status().OK
+    for st in streams:
+        main.wait_stream(st)
+    t.cuda.synchronize()
+    for kind, _, D in outs:
+        assert (_gpu.from_dev(D) == ref[kind]).all(), kind
+
+
 def test_python_binding_roundtrip():
     t = _gpu.torch()
     import dense_gemm_08_amd as dg
