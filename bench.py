@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=8192)
     ap.add_argument("--ladder", action="store_true",
                     help="instead of one workload, time each optimisation-step kernel "
-                         "(gemm_nt_f16_ladder levels 1-6) on the 4096^3 FP16 workload "
+                         "(gemm_nt_f16_ladder levels 1-7) on the 4096^3 FP16 workload "
                          "(one JSON line per level)")
     ap.add_argument("--mx-sweep", action="store_true",
                     help="instead of one workload, time the FP8 block-scaled product at M = 8192 "
@@ -92,6 +92,7 @@ LADDER = {
     4: "V6: + persistent grouped XCD-aware grid",
     5: "V8/V9: + 256x256 tiles (staged tiles shared by two waves each)",
     6: "library kernel: + fine-grained schedule",
+    7: "V7: level 4 + a producer wave issuing every load (warp specialization)",
 }
 
 

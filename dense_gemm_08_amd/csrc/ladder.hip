@@ -20,11 +20,16 @@
 //   level 6       the library kernel: the same tile with the fine-grained
 //                 schedule (reads and loads spread between MFMA pairs, one
 //                 barrier per stage, descriptors rebased per step)
+//   level 7 (V7)  level 4 with warp specialization: a fifth wave issues every
+//                 LDS-DMA load while the four computing waves only read LDS
+//                 and run MFMAs, the stages handed over by two workgroup
+//                 barriers per step (the page's producer warp and its
+//                 full/empty barriers; numbered last to keep levels 1-6)
 //
-// The page's V7 (a producer warp feeding consumer warps) has no level: with
-// one wave per SIMD holding 256 accumulator registers there is no fifth wave
-// to dedicate to loads, and LDS-DMA loads are issued asynchronously by the
-// computing waves themselves.
+// The library kernel does not specialize: with 256 x 256 tiles one wave per
+// SIMD holds 256 accumulator registers, leaving no room for a fifth wave,
+// and LDS-DMA loads are issued asynchronously by the computing waves
+// themselves.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -180,6 +185,126 @@ __global__ __launch_bounds__(256) void ladder_kernel(LParams p) {
   }
 }
 
+// Level 7: 128 x 128 tiles, two LDS stages, persistent grouped order (as
+// level 4), and five waves: waves 0-3 compute (2 x 2, 64 x 64 each), wave 4
+// loads.  Per K step every wave passes two barriers: "full" (the producer
+// has waited for step ks's loads; the consumers may read its slot) and
+// "empty" (the consumers are done reading step ks; the producer may refill
+// that slot with step ks+2).  Both roles pass the same barriers in the same
+// order, tile after tile, so no wave waits on a barrier the others skip.
+constexpr int PTILE = 128;
+constexpr int PTHREADS = 5 * 64;
+__global__ __launch_bounds__(PTHREADS) void ladder_producer_kernel(LParams p) {
+  constexpr int W = PTILE / 2;
+  constexpr int MI = W / 16, NI = W / 16;
+  constexpr int OPB = PTILE * BK * 2;         // 16 KiB per operand tile per stage
+  constexpr int STB = 2 * OPB;
+  constexpr int PLOADS = OPB / (64 * 16);     // 16 loads per operand by the producer
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STB];
+  const uint32_t lds0 = lds_addr(smem);
+
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const bool producer = wave == 4;
+  const int wm = (wave >> 1) & 1, wn = wave & 1;
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int nk = p.K / BK;
+
+  for (int t = xcd_slot(blockIdx.x, gridDim.x, 8); t < p.num_tiles; t += gridDim.x) {
+    int tm, tn;
+    tile_of_task(t, p.tiles_m, p.tiles_n, p.tiles_m < 8 ? p.tiles_m : 8, &tm, &tn);
+    const uint16_t* a0 = p.A + (int64_t)tm * PTILE * p.lda;
+    const uint16_t* b0 = p.B + (int64_t)tn * PTILE * p.ldb;
+    const i32x4 ra = make_rsrc((uint64_t)(uintptr_t)a0, (uint32_t)(((int64_t)(PTILE - 1) * p.lda + p.K) * 2));
+    const i32x4 rb = make_rsrc((uint64_t)(uintptr_t)b0, (uint32_t)(((int64_t)(PTILE - 1) * p.ldb + p.K) * 2));
+    // producer: load i of an operand covers rows 8 i .. 8 i + 7 (lane / 8)
+    // and the logical chunk the swizzle puts at physical chunk lane % 8
+    // operand op (0: A, 1: B) of step ks into slot
+    auto load = [&](int ks, int slot, int op) {
+      const int k0 = ks * BK;
+#pragma unroll
+      for (int i = 0; i < PLOADS; ++i) {
+        const int r = i * 8 + (lane >> 3), c = (lane & 7) ^ swz_k(r);
+        const uint32_t m0 = lds0 + slot * STB + op * OPB + i * 1024;
+        dma16(op == 0 ? ra : rb, (uint32_t)((r * (op == 0 ? p.lda : p.ldb) + k0 + c * 8) * 2), m0);
+      }
+    };
+
+    f32x4 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) acc[i][j] = (f32x4){};
+    fence();
+
+    if (producer) {
+      load(0, 0, 0);
+      load(0, 0, 1);
+    }
+    for (int ks = 0; ks < nk; ++ks) {
+      if (producer) {
+        // step ks+1 goes into the slot step ks-1 left at the last "empty"
+        // barrier: its A tile before the wait for step ks, its B tile after
+        // (at most 48 loads in flight, within the wave's vmcnt range)
+        if (ks + 1 < nk) {
+          load(ks + 1, (ks + 1) & 1, 0);
+          asm volatile("s_waitcnt vmcnt(%0)" : : "n"(PLOADS) : "memory");  // step ks landed
+          load(ks + 1, (ks + 1) & 1, 1);
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+      }
+      wait_lds_barrier();  // "full": step ks is in its slot
+      if (!producer) {
+        const char* base = smem + (ks & 1) * STB;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int off = (((4 * s + lq) ^ swz_k(l16)) << 4);
+          u32x4 a[MI], b[NI];
+#pragma unroll
+          for (int i = 0; i < MI; ++i) a[i] = *(const u32x4*)(base + (wm * W + i * 16 + l16) * 128 + off);
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            b[j] = *(const u32x4*)(base + OPB + (wn * W + j * 16 + l16) * 128 + off);
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int i = 0; i < MI; ++i) mfma16<_Float16>(acc[i][j], b[j], a[i]);
+        }
+      }
+      wait_lds_barrier();  // "empty": every consumer is done reading step ks
+    }
+
+    if (!producer) {
+      // wait states between the last MFMAs and the reads of their results
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+      fence();
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int row = tm * PTILE + wm * W + i * 16 + l16;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int col = tn * PTILE + wn * W + j * 16 + 4 * lq;
+          u32x2 v;
+          v[0] = pack2<_Float16>(acc[i][j][0], acc[i][j][1]);
+          v[1] = pack2<_Float16>(acc[i][j][2], acc[i][j][3]);
+          *(u32x2*)(p.D + (int64_t)row * p.ldd + col) = v;
+        }
+      }
+    }
+  }
+}
+
+static dense_gemm_status launch_producer(const LParams& p0, int cus, hipStream_t stream) {
+  LParams p = p0;
+  p.tiles_m = p.M / PTILE;
+  p.tiles_n = p.N / PTILE;
+  p.num_tiles = p.tiles_m * p.tiles_n;
+  const int grid = p.num_tiles < cus ? p.num_tiles : cus;
+  hipLaunchKernelGGL(ladder_producer_kernel, dim3((unsigned)grid), dim3(PTHREADS), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
+}
+
 template <int TILE, bool DMA, int STAGES, bool PERSIST>
 static dense_gemm_status launch(const LParams& p0, int cus, hipStream_t stream) {
   LParams p = p0;
@@ -201,7 +326,7 @@ extern "C" dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N,
                                                 const void* A, int64_t lda, const void* B,
                                                 int64_t ldb, void* D, int64_t ldd,
                                                 hipStream_t stream) {
-  if (level < 1 || level > 6) return DENSE_GEMM_BAD_ARG;
+  if (level < 1 || level > 7) return DENSE_GEMM_BAD_ARG;
   if (level == 6) return gemm_nt_f16(M, N, K, A, lda, B, ldb, D, ldd, stream);
   const int64_t tile = level == 5 ? 256 : 128;
   if (M <= 0 || N <= 0 || K <= 0 || M % tile || N % tile || K % ladder::BK) return DENSE_GEMM_BAD_ARG;
@@ -226,6 +351,7 @@ extern "C" dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N,
     case 2: return ladder::launch<128, true, 1, false>(p, cus, stream);
     case 3: return ladder::launch<128, true, 2, false>(p, cus, stream);
     case 4: return ladder::launch<128, true, 2, true>(p, cus, stream);
+    case 7: return ladder::launch_producer(p, cus, stream);
     default: return ladder::launch<256, true, 2, true>(p, cus, stream);
   }
 }

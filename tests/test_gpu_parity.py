@@ -464,7 +464,7 @@ def test_python_binding_row_and_column_views():
 
 # ----------------------------------------------- optimisation-step kernels --
 
-LEVELS = [1, 2, 3, 4, 5, 6]
+LEVELS = [1, 2, 3, 4, 5, 6, 7]
 
 
 @pytest.mark.parametrize("level", LEVELS)
@@ -502,6 +502,17 @@ def test_ladder_small_integers_exact():
         assert (D == want).all(), level
 
 
+@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (128, 256, 128), (384, 128, 192)])
+def test_ladder_producer_short_k(M, N, K):
+    # the producer-wave level with one, two and three K steps (the prologue
+    # load, the last step without a refill) and fewer tiles than CUs
+    w = inputs.WORKLOADS["single_tile"]
+    A, B = inputs.make_operands(w, seed=M + N + K, M=M, N=N, K=K)
+    D, st = _gpu.ladder(7, A, B, M, N, K)
+    assert st == status().OK
+    check_full("nt", "f16", A, B, M, N, K, D)
+
+
 def test_ladder_rejects_shapes():
     Sx = status()
     A = _gpu.to_dev(np.zeros((512, 512), np.uint16), 512, 512)
@@ -510,7 +521,8 @@ def test_ladder_rejects_shapes():
     s = _gpu.torch().cuda.current_stream().cuda_stream
     p = A.data_ptr()
     assert Sx(fn(0, 256, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
-    assert Sx(fn(7, 256, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
+    assert Sx(fn(8, 256, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
+    assert Sx(fn(7, 384, 200, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
     assert Sx(fn(5, 384, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
     assert Sx(fn(1, 256, 256, 100, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
     assert Sx(fn(2, 256, 256, 64, p + 2, 512, p, 512, D.data_ptr(), 512, s)) == Sx.MISALIGNED
