@@ -40,6 +40,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# tests only: load another build of oracle.c (the planted-mistake tests)
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIB")
 
 FMT = {"f16": 0, "bf16": 1}
 LAYOUT = {"nt": 0, "nn": 1}
@@ -61,9 +63,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
     i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
     vp = ctypes.c_void_p
     lib.oracle_decode.argtypes = [i32, ctypes.c_uint16]
