@@ -278,13 +278,55 @@ def test_against_numpy_float64_matmul():
         assert (np.abs(s - refs) <= bound).all()
 
 
-def test_entries_agree_with_full_product():
-    w = inputs.WORKLOADS["large_nn"]
-    A, B = inputs.make_operands(w, M=50, N=70, K=90)
-    d, s = oracle.gemm("nn", "bf16", A, B)
-    rows, cols = inputs.sample_indices(50, 70, 64, seed=2)
-    de, se = oracle.gemm_entries("nn", "bf16", A, B, K=90, lda=90, ldb=70, rows=rows, cols=cols)
+def _padded(X, ld, fill=0x7C00):
+    """X in a wider row-major array (leading dimension ld) whose padding
+    holds +Inf (FP16) / a huge value (BF16): a read of it shows in the sums."""
+    P = np.full((X.shape[0], ld), fill, np.uint16)
+    P[:, :X.shape[1]] = X
+    return P
+
+
+@pytest.mark.parametrize("layout", ["nt", "nn"])
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_entries_agree_with_full_product(layout, fmt):
+    # non-square (M, N, K all different, so a transposed read of B or a
+    # stride taken from the wrong dimension lands elsewhere), with padded
+    # leading dimensions on both operands; every entry of a 31 x 47 product
+    # plus repeated and out-of-order samples
+    M, N, K = 31, 47, 90
+    w = inputs.Workload("t", layout, fmt, 0, 0, 0, "uniform", 0.0, 40 + len(layout + fmt))
+    A, B = inputs.make_operands(w, M=M, N=N, K=K)
+    d, s = oracle.gemm(layout, fmt, A, B)
+    lda = K + 13
+    ldb = (K + 5) if layout == "nt" else (N + 7)
+    Ap, Bp = _padded(A, lda), _padded(B, ldb)
+    rows = np.concatenate([np.repeat(np.arange(M), N),
+                           inputs.sample_indices(M, N, 64, seed=2)[0]])
+    cols = np.concatenate([np.tile(np.arange(N), M),
+                           inputs.sample_indices(M, N, 64, seed=2)[1]])
+    de, se = oracle.gemm_entries(layout, fmt, Ap, Bp, K=K, lda=lda, ldb=ldb, rows=rows, cols=cols)
     assert (de == d[rows, cols]).all() and (se == s[rows, cols]).all()
+
+
+@pytest.mark.parametrize("layout", ["nt", "nn"])
+def test_entries_match_exact_rationals_with_padding(layout):
+    # the sampled-entry path against exact arithmetic on its own (not only
+    # against the full product): 3 x 4 x 5 with padded leading dimensions
+    M, N, K = 3, 4, 5
+    rng = np.random.default_rng(77)
+    sa, sb = inputs.operand_shapes(layout, M, N, K)
+    A = inputs.to_bits("f16", rng.uniform(-4, 4, sa))
+    B = inputs.to_bits("f16", rng.uniform(-4, 4, sb))
+    de, se = _exact.gemm(layout, "f16", A.tolist(), B.tolist())
+    lda, ldb = K + 3, (K + 2 if layout == "nt" else N + 3)
+    rows = np.repeat(np.arange(M), N)
+    cols = np.tile(np.arange(N), M)
+    d, s = oracle.gemm_entries(layout, "f16", _padded(A, lda), _padded(B, ldb), K=K, lda=lda,
+                               ldb=ldb, rows=rows, cols=cols)
+    for t in range(M * N):
+        bound = Fraction(K * U53) * se[rows[t]][cols[t]]
+        assert abs(Fraction(d[t]) - de[rows[t]][cols[t]]) <= bound
+        assert abs(Fraction(s[t]) - se[rows[t]][cols[t]]) <= bound
 
 
 # ------------------------------------------------- worked values on pages --

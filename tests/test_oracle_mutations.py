@@ -32,6 +32,17 @@ MUTATIONS = [
     ("single entries of A.B read B transposed",
      "                                     : oracle_decode(fmt, B[k * ldb + j]);\n    double prod",
      "                                     : oracle_decode(fmt, B[j * ldb + k]);\n    double prod", 1),
+    ("single entries of A.B^T read B transposed",
+     "double b = (layout == ORACLE_NT) ? oracle_decode(fmt, B[j * ldb + k])",
+     "double b = (layout == ORACLE_NT) ? oracle_decode(fmt, B[k * ldb + j])", 1),
+    ("single entries of A.B^T stride B by K instead of ldb",
+     "double b = (layout == ORACLE_NT) ? oracle_decode(fmt, B[j * ldb + k])",
+     "double b = (layout == ORACLE_NT) ? oracle_decode(fmt, B[j * K + k])", 1),
+    ("single entries ignore lda", "double a = oracle_decode(fmt, A[i * lda + k]);",
+     "double a = oracle_decode(fmt, A[i * K + k]);", 1),
+    ("single entries of A.B stride B by K instead of ldb",
+     "                                     : oracle_decode(fmt, B[k * ldb + j]);\n    double prod",
+     "                                     : oracle_decode(fmt, B[k * K + j]);\n    double prod", 1),
     ("sum of |a b| signed", "s += fabs(prod);\n      }", "s += prod;\n      }", 1),
     ("rounding truncates", "double r = nearbyint(a / q) * q;", "double r = trunc(a / q) * q;", 1),
     ("rounding half away from zero", "double r = nearbyint(a / q) * q;",
