@@ -27,6 +27,17 @@ class Status(enum.IntEnum):
     NO_DEVICE = 7
     BAD_ARG = 8
     NO_MEMORY = 9
+    WORKSPACE_TOO_SMALL = 10
+
+
+# dense_gemm_op: the type and layout pairings of dense_gemm_ex
+OPS = {("nt", "f16"): 0, ("nn", "bf16"): 1, ("nt", "bf16"): 2, ("nn", "f16"): 3}
+
+
+class Options(ctypes.Structure):
+    """dense_gemm_options: split_k (0 = the library's choice, 1 = none,
+    n = n parts) and tile_n (0 = the library's choice, 128 or 256)."""
+    _fields_ = [("split_k", ctypes.c_int32), ("tile_n", ctypes.c_int32)]
 
 
 class DenseGemmError(RuntimeError):
@@ -56,6 +67,13 @@ SIGNATURES = {
                                  ctypes.POINTER(_i64)], _i32),
     "dense_gemm_xcd_slot": ([_i64, _i64, _i64], _i64),
     "dense_gemm_plan": ([_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_i64)], _i32),
+    "dense_gemm_workspace_size": ([_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
+                                   ctypes.POINTER(Options), ctypes.POINTER(ctypes.c_size_t)], _i32),
+    "dense_gemm_ex": ([_i32] + _GEMM_ARGS[:-1] + [ctypes.POINTER(Options), _vp, ctypes.c_size_t,
+                                                 _vp], _i32),
+    "gemm_nt_e4m3_mx_workspace_size": ([_i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)], _i32),
+    "gemm_nt_e4m3_mx_ex": ([_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                            _i64, _vp, ctypes.c_size_t, _vp], _i32),
 }
 
 
@@ -129,8 +147,23 @@ def _check_tensor(t, dtype_name: str, what: str):
         raise ValueError("%s must be 2-D with unit column stride" % what)
 
 
-def _call(name: str, layout: str, fmt: str, A, B, D=None, stream=None):
-    """D = A @ B.T (layout "nt", B is N x K) or D = A @ B ("nn", B is K x N)."""
+def workspace_size(layout: str, fmt: str, M: int, N: int, K: int, A_ptr: int, lda: int,
+                   B_ptr: int, ldb: int, options: Options | None = None, num_cus: int = 0) -> int:
+    """Bytes of workspace dense_gemm_ex needs (dense_gemm_workspace_size)."""
+    lib = load_library()
+    out = ctypes.c_size_t()
+    st = lib.dense_gemm_workspace_size(OPS[(layout, fmt)], M, N, K, A_ptr, lda, B_ptr, ldb,
+                                       num_cus, ctypes.byref(options) if options else None,
+                                       ctypes.byref(out))
+    if st != Status.OK:
+        raise DenseGemmError(st, "dense_gemm_workspace_size")
+    return out.value
+
+
+def _call(name: str, layout: str, fmt: str, A, B, D=None, stream=None, workspace=None):
+    """D = A @ B.T (layout "nt", B is N x K) or D = A @ B ("nn", B is K x N).
+    With ``workspace`` (a device tensor, or True to take one from torch's
+    allocator), the call goes through dense_gemm_ex with that workspace."""
     import torch
     lib = load_library()
     _check_tensor(A, fmt, "A")
@@ -151,31 +184,48 @@ def _call(name: str, layout: str, fmt: str, A, B, D=None, stream=None):
     dev = _same_device(A, B, D)
     # the library launches on the current device
     with torch.cuda.device(dev):
-        st = getattr(lib, name)(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
-                                D.data_ptr(), _ld(D), _stream_handle(stream, dev))
+        if workspace is None:
+            st = getattr(lib, name)(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
+                                    D.data_ptr(), _ld(D), _stream_handle(stream, dev))
+        else:
+            if workspace is True:
+                need = workspace_size(layout, fmt, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(),
+                                      _ld(B))
+                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            if not workspace.is_cuda or workspace.device != dev:
+                raise ValueError("workspace must be a device tensor on %s" % dev)
+            st = lib.dense_gemm_ex(OPS[(layout, fmt)], M, N, K, A.data_ptr(), _ld(A),
+                                   B.data_ptr(), _ld(B), D.data_ptr(), _ld(D), None,
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream_handle(stream, dev))
+            name = "dense_gemm_ex"
     if st != Status.OK:
         raise DenseGemmError(st, name)
     return D
 
 
-def gemm_nt_f16(A, B, D=None, stream=None):
-    """D = A @ B.T in FP16 (FP32 accumulation); A is M x K, B is N x K."""
-    return _call("gemm_nt_f16", "nt", "f16", A, B, D, stream)
+def gemm_nt_f16(A, B, D=None, stream=None, workspace=None):
+    """D = A @ B.T in FP16 (FP32 accumulation); A is M x K, B is N x K.
+    ``workspace``: see :func:`_call`."""
+    return _call("gemm_nt_f16", "nt", "f16", A, B, D, stream, workspace)
 
 
-def gemm_nn_bf16(A, B, D=None, stream=None):
-    """D = A @ B in BF16 (FP32 accumulation); A is M x K, B is K x N."""
-    return _call("gemm_nn_bf16", "nn", "bf16", A, B, D, stream)
+def gemm_nn_bf16(A, B, D=None, stream=None, workspace=None):
+    """D = A @ B in BF16 (FP32 accumulation); A is M x K, B is K x N.
+    ``workspace``: see :func:`_call`."""
+    return _call("gemm_nn_bf16", "nn", "bf16", A, B, D, stream, workspace)
 
 
-def gemm_nt_bf16(A, B, D=None, stream=None):
-    """D = A @ B.T in BF16 (FP32 accumulation); A is M x K, B is N x K."""
-    return _call("gemm_nt_bf16", "nt", "bf16", A, B, D, stream)
+def gemm_nt_bf16(A, B, D=None, stream=None, workspace=None):
+    """D = A @ B.T in BF16 (FP32 accumulation); A is M x K, B is N x K.
+    ``workspace``: see :func:`_call`."""
+    return _call("gemm_nt_bf16", "nt", "bf16", A, B, D, stream, workspace)
 
 
-def gemm_nn_f16(A, B, D=None, stream=None):
-    """D = A @ B in FP16 (FP32 accumulation); A is M x K, B is K x N."""
-    return _call("gemm_nn_f16", "nn", "f16", A, B, D, stream)
+def gemm_nn_f16(A, B, D=None, stream=None, workspace=None):
+    """D = A @ B in FP16 (FP32 accumulation); A is M x K, B is K x N.
+    ``workspace``: see :func:`_call`."""
+    return _call("gemm_nn_f16", "nn", "f16", A, B, D, stream, workspace)
 
 
 def raw(name: str):

@@ -588,6 +588,7 @@ static unsigned repack_blocks(int64_t chunks) {
 
 struct DeviceInfo {
   int cus = 0;
+  int xcds = 1;
   bool gfx950 = false;
 };
 
@@ -595,6 +596,9 @@ static std::mutex g_mu;
 static DeviceInfo g_dev[64];
 static bool g_dev_ok[64];
 
+// Properties of the current device, queried once per device.  The XCD count
+// (8 on an unpartitioned MI355X, fewer when the chip is partitioned into
+// several devices) sets the workgroup-to-L2 remap of the tile scheduler.
 static dense_gemm_status device_info(DeviceInfo* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DENSE_GEMM_NO_DEVICE;
@@ -602,7 +606,13 @@ static dense_gemm_status device_info(DeviceInfo* out) {
   if (!g_dev_ok[dev]) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DENSE_GEMM_NO_DEVICE;
+    int xcds = 1;
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1) {
+      (void)hipGetLastError();
+      xcds = 1;
+    }
     g_dev[dev].cus = prop.multiProcessorCount;
+    g_dev[dev].xcds = xcds;
     g_dev[dev].gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     g_dev_ok[dev] = true;
   }
@@ -610,22 +620,35 @@ static dense_gemm_status device_info(DeviceInfo* out) {
   return out->gfx950 && out->cus > 0 ? DENSE_GEMM_OK : DENSE_GEMM_NO_DEVICE;
 }
 
-dense_gemm_status device_cus(int* cus) {
+dense_gemm_status device_topology(int* cus, int* xcds) {
   DeviceInfo info;
   const dense_gemm_status st = device_info(&info);
-  if (st == DENSE_GEMM_OK) *cus = info.cus;
+  if (st == DENSE_GEMM_OK) {
+    *cus = info.cus;
+    *xcds = info.xcds;
+  }
   return st;
 }
 
 static constexpr int64_t kMaxDim = (int64_t)1 << 31;
 
-static int choose_group_m(int64_t tiles_m, int64_t tiles_n, int64_t grid) {
-  // Workgroups resident together on one XCD form a block of tiles; an 8-row
-  // group makes that block close to square for the grids this library sees.
-  (void)tiles_n;
-  (void)grid;
-  return (int)(tiles_m < 8 ? tiles_m : 8);
-}
+// Tile rows per group of the grouped order.  The workgroups resident on one
+// XCD take consecutive tasks, i.e. a block of group_m tile rows by a few
+// tile columns that shares its A and B panels in that XCD's L2; 8 rows made
+// that block closest to square for the grids measured (32 workgroups per
+// XCD at 4096^3: an 8 x 4 block of 12 panels).
+static int choose_group_m(int64_t tiles_m) { return (int)(tiles_m < 8 ? tiles_m : 8); }
+
+// Everything one call launches, decided on the host before any launch.
+struct CallPlan {
+  int64_t plan[10];          // as dense_gemm_plan, after the caller's options
+  int64_t full_tasks;        // tiles computed whole
+  int64_t split_tiles;       // tiles computed in K parts
+  bool a_direct, b_direct;   // operands read in place (else repacked)
+  size_t a_bytes, b_bytes;   // workspace of the repacked copies
+  size_t split_bytes;        // workspace of the FP32 partial tiles
+  size_t total() const { return a_bytes + b_bytes + split_bytes; }
+};
 
 }  // namespace dg
 
@@ -644,7 +667,9 @@ const char* dense_gemm_status_string(int status) {
     case DENSE_GEMM_LAUNCH_FAILED: return "kernel launch failed";
     case DENSE_GEMM_NO_DEVICE: return "no gfx950 device current";
     case DENSE_GEMM_BAD_ARG: return "bad argument";
-    case DENSE_GEMM_NO_MEMORY: return "no device memory for the operand repack workspace";
+    case DENSE_GEMM_NO_MEMORY: return "no device memory for the workspace";
+    case DENSE_GEMM_WORKSPACE_TOO_SMALL:
+      return "workspace smaller than the call needs (see the workspace size query)";
     default: return "unknown status";
   }
 }
@@ -722,7 +747,7 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
   out[3] = tiles_m;
   out[4] = tiles_n;
   out[5] = grid;
-  out[6] = choose_group_m(tiles_m, tiles_n, grid);
+  out[6] = choose_group_m(tiles_m);
   out[7] = THREADS;
   // Split-K for the tiles of the last, partial wave (all tiles when there
   // are fewer than CUs), at most one part per idle CU and at least 4 K steps
@@ -769,26 +794,81 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
 
 namespace dg {
 
-// The launches of one call with tile width TN, for the plan of run().
-template <typename T, int LAYOUT, int TN>
-static dense_gemm_status launch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                                const void* B, int64_t ldb, void* D, int64_t ldd, int64_t* plan,
-                                const DeviceInfo& info, hipStream_t stream) {
-  // Tiles computed whole; the plan splits the rest (the last, partial wave).
-  const int64_t tasks = plan[3] * plan[4];
-  int64_t full = plan[8] > 1 ? tasks - tasks % info.cus : tasks;
-  // DENSE_GEMM_SPLITK=off disables split-K; =<n> splits every tile in n
-  // parts (testing)
-  if (const char* e = getenv("DENSE_GEMM_SPLITK")) {
-    const int64_t nk = (K + BK - 1) / BK;
-    int64_t want = strcmp(e, "off") == 0 ? 1 : atoll(e);
-    if (want >= 1 && nk >= 1) {
-      if (want > nk) want = nk;
+static bool valid_op(int op) { return op >= DENSE_GEMM_NT_F16 && op <= DENSE_GEMM_NN_F16; }
+static int op_layout(int op) { return op == DENSE_GEMM_NN_BF16 || op == DENSE_GEMM_NN_F16 ? NN : NT; }
+
+// The plan of one call on a device with `cus` CUs: dense_gemm_plan, the
+// caller's options, and the workspace the call needs.  Arguments must have
+// passed dense_gemm_validate, with M, N > 0.
+static dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const void* A,
+                                   int64_t lda, const void* B, int64_t ldb, int64_t cus,
+                                   const dense_gemm_options* opt, CallPlan* cp) {
+  int64_t* plan = cp->plan;
+  dense_gemm_status st = dense_gemm_plan(layout, M, N, K, cus, plan);
+  if (st != DENSE_GEMM_OK) return st;
+  const int64_t nk = (K + BK - 1) / BK;
+  bool forced_split = false;
+  if (opt != nullptr) {
+    if (opt->tile_n != 0) {
+      const int64_t want = opt->tile_n;
+      if (want != BN && !(want == BN / 2 && layout == NT)) return DENSE_GEMM_BAD_ARG;
+      if (want != plan[1]) {
+        plan[1] = want;
+        plan[4] = (N + want - 1) / want;
+        plan[5] = plan[3] * plan[4] < cus ? plan[3] * plan[4] : cus;
+        plan[6] = choose_group_m(plan[3]);
+        plan[8] = 1;  // the split is then forced below, or none
+        plan[9] = nk;
+      }
+    }
+    if (opt->split_k < 0) return DENSE_GEMM_BAD_ARG;
+    if (opt->split_k > 0 && nk >= 1) {
+      // n parts on every tile (at most one per K step): the K steps per part
+      // and the number of non-empty parts that gives
+      const int64_t want = opt->split_k < nk ? opt->split_k : nk;
       plan[9] = (nk + want - 1) / want;
       plan[8] = (nk + plan[9] - 1) / plan[9];
-      full = plan[8] > 1 ? 0 : tasks;
+      forced_split = true;
     }
   }
+  const int64_t tasks = plan[3] * plan[4];
+  if (plan[8] > 1) {
+    cp->full_tasks = forced_split ? 0 : tasks - tasks % cus;
+    cp->split_tiles = tasks - cp->full_tasks;
+    plan[5] = cp->full_tasks + cp->split_tiles * plan[8];
+    if (plan[5] > cus) plan[5] = cus;
+  } else {
+    plan[8] = 1;
+    plan[9] = nk;
+    cp->full_tasks = tasks;
+    cp->split_tiles = 0;
+    plan[5] = tasks < cus ? tasks : cus;
+  }
+  // Operands the 16-byte chunk loader cannot read in place (a pointer not
+  // 16-byte aligned, a leading dimension or K -- or N for the A.B layout's
+  // B -- not a multiple of 8) are first copied into a dense, zero-padded
+  // layout (`repack`) in the workspace.
+  const int64_t K8 = (K + 7) & ~(int64_t)7, N8 = (N + 7) & ~(int64_t)7;
+  cp->a_direct = K == 0 || (((uintptr_t)A & 15) == 0 && (lda & 7) == 0 && (K & 7) == 0);
+  cp->b_direct = K == 0 || (((uintptr_t)B & 15) == 0 && (ldb & 7) == 0 &&
+                            (layout == NT ? (K & 7) == 0 : (N & 7) == 0));
+  const int64_t b_rows = layout == NT ? N : K, b_dcols = layout == NT ? K8 : N8;
+  auto round256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  cp->a_bytes = cp->a_direct ? 0 : round256((size_t)M * K8 * 2);
+  cp->b_bytes = cp->b_direct ? 0 : round256((size_t)b_rows * b_dcols * 2);
+  cp->split_bytes = plan[8] > 1 ? (size_t)plan[8] * cp->split_tiles * BM * plan[1] * sizeof(float) : 0;
+  return DENSE_GEMM_OK;
+}
+
+// The launches of one call with tile width TN, given its plan and a
+// workspace of at least cp.total() bytes (256-byte aligned; null when the
+// plan needs none).
+template <typename T, int LAYOUT, int TN>
+static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                 const void* B, int64_t ldb, void* D, int64_t ldd,
+                                 const CallPlan& cp, const DeviceInfo& info, char* ws,
+                                 hipStream_t stream) {
+  const int64_t* plan = cp.plan;
   Params p;
   p.A = (const uint16_t*)A;
   p.B = (const uint16_t*)B;
@@ -802,84 +882,83 @@ static dense_gemm_status launch(int64_t M, int64_t N, int64_t K, const void* A, 
   p.tiles_m = (int)plan[3];
   p.tiles_n = (int)plan[4];
   p.group_m = (int)plan[6];
-  p.num_tasks = (int)(plan[3] * plan[4]);
-  p.num_xcds = 8;
+  p.num_xcds = info.xcds;
   p.d_vec = (((uintptr_t)D & 15) == 0 && (ldd & 7) == 0) ? 1 : 0;
-  p.full_tasks = (int)full;
-  p.tiles = (int)(tasks - full);  // tiles split in parts
-  p.splits = 1;
-  p.split_steps = 0;
-  p.ws = nullptr;
+  p.full_tasks = (int)cp.full_tasks;
+  p.tiles = (int)cp.split_tiles;
+  p.splits = (int)plan[8];
+  p.split_steps = (int)plan[9];
+  p.num_tasks = (int)(cp.full_tasks + cp.split_tiles * plan[8]);
+  p.ws = plan[8] > 1 ? (float*)(ws + cp.a_bytes + cp.b_bytes) : nullptr;
 
-  // Operands the 16-byte chunk loader cannot read directly (a pointer not
-  // 16-byte aligned, a leading dimension or K -- or N for the A.B layout's
-  // B -- not a multiple of 8) are first copied into a dense, zero-padded
-  // layout (`repack`) in the workspace.
   const int64_t K8 = (K + 7) & ~(int64_t)7, N8 = (N + 7) & ~(int64_t)7;
-  const bool a_direct = K == 0 || (((uintptr_t)A & 15) == 0 && (lda & 7) == 0 && (K & 7) == 0);
-  const bool b_direct = K == 0 || (((uintptr_t)B & 15) == 0 && (ldb & 7) == 0 &&
-                                   (LAYOUT == NT ? (K & 7) == 0 : (N & 7) == 0));
-  const int64_t b_rows = LAYOUT == NT ? N : K, b_cols = LAYOUT == NT ? K : N;
-  const int64_t b_dcols = LAYOUT == NT ? K8 : N8;
-  auto round256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t a_bytes = a_direct ? 0 : round256((size_t)M * K8 * 2);
-  const size_t b_bytes = b_direct ? 0 : round256((size_t)b_rows * b_dcols * 2);
-  const size_t split_bytes =
-      plan[8] > 1 && p.tiles > 0 ? (size_t)plan[8] * p.tiles * BM * TN * sizeof(float) : 0;
-
-  // one stream-ordered workspace: [A copy | B copy | FP32 split-K partials]
-  char* ws = nullptr;
-  bool split = split_bytes > 0;
-  if (a_bytes + b_bytes + split_bytes > 0) {
-    if (hipMallocAsync((void**)&ws, a_bytes + b_bytes + split_bytes, stream) != hipSuccess) {
-      (void)hipGetLastError();
-      ws = nullptr;
-      split = false;  // retry without the partials: run unsplit
-      if (a_bytes + b_bytes > 0 &&
-          hipMallocAsync((void**)&ws, a_bytes + b_bytes, stream) != hipSuccess) {
-        (void)hipGetLastError();
-        return DENSE_GEMM_NO_MEMORY;
-      }
-    }
-  }
-  if (!a_direct) {
+  if (!cp.a_direct) {
     uint16_t* a2 = (uint16_t*)ws;
     hipLaunchKernelGGL(repack, dim3(repack_blocks(M * (K8 / 8))), dim3(256), 0, stream,
                        (const uint16_t*)A, M, K, lda, a2, K8);
     p.A = a2;
     p.lda = (int)K8;
   }
-  if (!b_direct) {
-    uint16_t* b2 = (uint16_t*)(ws + a_bytes);
+  if (!cp.b_direct) {
+    const int64_t b_rows = LAYOUT == NT ? N : K, b_cols = LAYOUT == NT ? K : N;
+    const int64_t b_dcols = LAYOUT == NT ? K8 : N8;
+    uint16_t* b2 = (uint16_t*)(ws + cp.a_bytes);
     hipLaunchKernelGGL(repack, dim3(repack_blocks(b_rows * (b_dcols / 8))), dim3(256), 0, stream,
                        (const uint16_t*)B, b_rows, b_cols, ldb, b2, b_dcols);
     p.B = b2;
     p.ldb = (int)b_dcols;
   }
-  if (split) {
+  const unsigned grid = (unsigned)(p.num_tasks < info.cus ? p.num_tasks : info.cus);
+  if (p.splits > 1) {
     // whole tiles, then the parts of the split tiles writing FP32 partials,
     // summed by a second kernel
-    p.splits = (int)plan[8];
-    p.split_steps = (int)plan[9];
-    p.ws = (float*)(ws + a_bytes + b_bytes);
-    p.num_tasks = p.full_tasks + p.tiles * p.splits;
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true, TN>),
-                       dim3((unsigned)(p.num_tasks < info.cus ? p.num_tasks : info.cus)),
-                       dim3(THREADS), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true, TN>), dim3(grid), dim3(THREADS), 0, stream, p);
     hipLaunchKernelGGL((split_reduce<T, TN>), dim3((unsigned)(p.tiles * (TN / 8))), dim3(256), 0,
                        stream, p);
   } else {
-    p.full_tasks = p.num_tasks;
-    p.tiles = 0;
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false, TN>),
-                       dim3((unsigned)(p.num_tasks < info.cus ? p.num_tasks : info.cus)),
-                       dim3(THREADS), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false, TN>), dim3(grid), dim3(THREADS), 0, stream,
+                       p);
   }
-  const hipError_t err = hipGetLastError();
-  if (ws != nullptr) (void)hipFreeAsync(ws, stream);
-  return err == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
+  return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
 
+template <typename T, int LAYOUT>
+static dense_gemm_status enqueue_width(int64_t M, int64_t N, int64_t K, const void* A,
+                                       int64_t lda, const void* B, int64_t ldb, void* D,
+                                       int64_t ldd, const CallPlan& cp, const DeviceInfo& info,
+                                       char* ws, hipStream_t stream) {
+  if constexpr (LAYOUT == NT) {
+    if (cp.plan[1] == BN / 2)
+      return enqueue<T, LAYOUT, BN / 2>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws, stream);
+  }
+  return enqueue<T, LAYOUT, BN>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws, stream);
+}
+
+// A call with the caller's workspace (ws, ws_bytes): nothing is allocated.
+template <typename T, int LAYOUT>
+static dense_gemm_status run_with(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                  const void* B, int64_t ldb, void* D, int64_t ldd,
+                                  const dense_gemm_options* opt, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  dense_gemm_status st = dense_gemm_validate(LAYOUT, M, N, K, A, lda, B, ldb, D, ldd);
+  if (st != DENSE_GEMM_OK || M == 0 || N == 0) return st;
+  DeviceInfo info;
+  st = device_info(&info);
+  if (st != DENSE_GEMM_OK) return st;
+  CallPlan cp;
+  st = plan_call(LAYOUT, M, N, K, A, lda, B, ldb, info.cus, opt, &cp);
+  if (st != DENSE_GEMM_OK) return st;
+  if (cp.total() > 0) {
+    if (ws == nullptr || ws_bytes < cp.total()) return DENSE_GEMM_WORKSPACE_TOO_SMALL;
+    if (((uintptr_t)ws & 255) != 0) return DENSE_GEMM_MISALIGNED;
+  }
+  return enqueue_width<T, LAYOUT>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, (char*)ws, stream);
+}
+
+// A call of the plain entry points: the workspace (if the plan needs one)
+// is taken with hipMallocAsync on `stream` and returned with hipFreeAsync
+// after the launches.  A split call that cannot get its workspace runs
+// unsplit; a repack that cannot get it returns DENSE_GEMM_NO_MEMORY.
 template <typename T, int LAYOUT>
 static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                              const void* B, int64_t ldb, void* D, int64_t ldd,
@@ -889,26 +968,35 @@ static dense_gemm_status run(int64_t M, int64_t N, int64_t K, const void* A, int
   DeviceInfo info;
   st = device_info(&info);
   if (st != DENSE_GEMM_OK) return st;
-  int64_t plan[10];
-  st = dense_gemm_plan(LAYOUT, M, N, K, info.cus, plan);
+  CallPlan cp;
+  st = plan_call(LAYOUT, M, N, K, A, lda, B, ldb, info.cus, nullptr, &cp);
   if (st != DENSE_GEMM_OK) return st;
-  // DENSE_GEMM_TILE_N=128 or 256 forces the tile width of A @ B.T (testing)
-  if (const char* e = getenv("DENSE_GEMM_TILE_N")) {
-    const int64_t want = atoll(e);
-    if (LAYOUT == NT && (want == BN || want == BN / 2) && want != plan[1]) {
-      plan[1] = want;
-      plan[4] = (N + want - 1) / want;
-      plan[5] = plan[3] * plan[4] < info.cus ? plan[3] * plan[4] : info.cus;
-      plan[6] = choose_group_m(plan[3], plan[4], plan[5]);
-      plan[8] = 1;  // (the split below is then forced or none)
-      plan[9] = (K + BK - 1) / BK;
+  char* ws = nullptr;
+  if (cp.total() > 0 && hipMallocAsync((void**)&ws, cp.total(), stream) != hipSuccess) {
+    (void)hipGetLastError();
+    ws = nullptr;
+    if (cp.split_bytes > 0) {
+      // retry without the partials: run unsplit, same tile width
+      const dense_gemm_options unsplit = {1, (int32_t)cp.plan[1]};
+      st = plan_call(LAYOUT, M, N, K, A, lda, B, ldb, info.cus, &unsplit, &cp);
+      if (st != DENSE_GEMM_OK) return st;
+    }
+    if (cp.total() > 0 && hipMallocAsync((void**)&ws, cp.total(), stream) != hipSuccess) {
+      (void)hipGetLastError();
+      return DENSE_GEMM_NO_MEMORY;
     }
   }
-  if constexpr (LAYOUT == NT) {
-    if (plan[1] == BN / 2)
-      return launch<T, LAYOUT, BN / 2>(M, N, K, A, lda, B, ldb, D, ldd, plan, info, stream);
-  }
-  return launch<T, LAYOUT, BN>(M, N, K, A, lda, B, ldb, D, ldd, plan, info, stream);
+  st = enqueue_width<T, LAYOUT>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws, stream);
+  if (ws != nullptr) (void)hipFreeAsync(ws, stream);
+  return st;
+}
+
+template <typename T, int LAYOUT>
+static dense_gemm_status run_op_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                   const void* B, int64_t ldb, void* D, int64_t ldd,
+                                   const dense_gemm_options* opt, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return run_with<T, LAYOUT>(M, N, K, A, lda, B, ldb, D, ldd, opt, ws, ws_bytes, stream);
 }
 
 }  // namespace dg
@@ -937,6 +1025,52 @@ dense_gemm_status gemm_nn_f16(int64_t M, int64_t N, int64_t K, const void* A, in
                               const void* B, int64_t ldb, void* D, int64_t ldd,
                               hipStream_t stream) {
   return run<_Float16, NN>(M, N, K, A, lda, B, ldb, D, ldd, stream);
+}
+
+dense_gemm_status dense_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K,
+                                            const void* A, int64_t lda, const void* B,
+                                            int64_t ldb, int64_t num_cus,
+                                            const dense_gemm_options* opt, size_t* bytes) {
+  if (!valid_op(op) || bytes == nullptr || num_cus < 0) return DENSE_GEMM_BAD_ARG;
+  const int layout = op_layout(op);
+  // D is not looked at beyond its null check: any non-null stand-in will do
+  dense_gemm_status st =
+      dense_gemm_validate(layout, M, N, K, A, lda, B, ldb, (const void*)(uintptr_t)16, N);
+  if (st != DENSE_GEMM_OK) return st;
+  *bytes = 0;
+  if (M == 0 || N == 0) return DENSE_GEMM_OK;
+  if (num_cus == 0) {
+    DeviceInfo info;
+    st = device_info(&info);
+    if (st != DENSE_GEMM_OK) return st;
+    num_cus = info.cus;
+  }
+  CallPlan cp;
+  st = plan_call(layout, M, N, K, A, lda, B, ldb, num_cus, opt, &cp);
+  if (st == DENSE_GEMM_OK) *bytes = cp.total();
+  return st;
+}
+
+dense_gemm_status dense_gemm_ex(int op, int64_t M, int64_t N, int64_t K, const void* A,
+                                int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd,
+                                const dense_gemm_options* opt, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  switch (op) {
+    case DENSE_GEMM_NT_F16:
+      return run_op_ex<_Float16, NT>(M, N, K, A, lda, B, ldb, D, ldd, opt, workspace,
+                                     workspace_bytes, stream);
+    case DENSE_GEMM_NN_BF16:
+      return run_op_ex<__bf16, NN>(M, N, K, A, lda, B, ldb, D, ldd, opt, workspace,
+                                   workspace_bytes, stream);
+    case DENSE_GEMM_NT_BF16:
+      return run_op_ex<__bf16, NT>(M, N, K, A, lda, B, ldb, D, ldd, opt, workspace,
+                                   workspace_bytes, stream);
+    case DENSE_GEMM_NN_F16:
+      return run_op_ex<_Float16, NN>(M, N, K, A, lda, B, ldb, D, ldd, opt, workspace,
+                                     workspace_bytes, stream);
+    default:
+      return DENSE_GEMM_BAD_ARG;
+  }
 }
 
 }  // extern "C"

@@ -39,8 +39,8 @@
 
 namespace dg {
 
-// current device's CU count, checked to be a gfx950 (dense_gemm.hip)
-dense_gemm_status device_cus(int* cus);
+// current device's CU and XCD counts, checked to be a gfx950 (dense_gemm.hip)
+dense_gemm_status device_topology(int* cus, int* xcds);
 
 namespace ladder {
 
@@ -53,6 +53,7 @@ struct LParams {
   int M, N, K;
   int lda, ldb, ldd;
   int tiles_m, tiles_n, num_tiles;
+  int num_xcds;  // XCDs of the device (the scheduler's L2 remap)
 };
 
 template <int TILE, bool DMA, int STAGES, bool PERSIST>
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(256) void ladder_kernel(LParams p) {
   const int l16 = lane & 15, lq = lane >> 4;
   const int nk = p.K / BK;
 
-  const int first = PERSIST ? xcd_slot(blockIdx.x, gridDim.x, 8) : blockIdx.x;
+  const int first = PERSIST ? xcd_slot(blockIdx.x, gridDim.x, p.num_xcds) : blockIdx.x;
   const int stride = PERSIST ? gridDim.x : p.num_tiles;
   for (int t = first; t < p.num_tiles; t += stride) {
     int tm, tn;
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(PTHREADS) void ladder_producer_kernel(LParams p) {
   const int l16 = lane & 15, lq = lane >> 4;
   const int nk = p.K / BK;
 
-  for (int t = xcd_slot(blockIdx.x, gridDim.x, 8); t < p.num_tiles; t += gridDim.x) {
+  for (int t = xcd_slot(blockIdx.x, gridDim.x, p.num_xcds); t < p.num_tiles; t += gridDim.x) {
     int tm, tn;
     tile_of_task(t, p.tiles_m, p.tiles_n, p.tiles_m < 8 ? p.tiles_m : 8, &tm, &tn);
     const uint16_t* a0 = p.A + (int64_t)tm * PTILE * p.lda;
@@ -341,11 +342,11 @@ extern "C" dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N,
   // 32-bit row pitch of D and tile numbers
   if (ldd >= ((int64_t)1 << 31) || (M / tile) * (N / tile) >= ((int64_t)1 << 31))
     return DENSE_GEMM_TOO_LARGE;
-  int cus = 0;
-  const dense_gemm_status st = device_cus(&cus);
+  int cus = 0, xcds = 1;
+  const dense_gemm_status st = device_topology(&cus, &xcds);
   if (st != DENSE_GEMM_OK) return st;
   ladder::LParams p{(const uint16_t*)A, (const uint16_t*)B, (uint16_t*)D, (int)M, (int)N, (int)K,
-                    (int)lda, (int)ldb, (int)ldd, 0, 0, 0};
+                    (int)lda, (int)ldb, (int)ldd, 0, 0, 0, xcds};
   switch (level) {
     case 1: return ladder::launch<128, false, 1, false>(p, cus, stream);
     case 2: return ladder::launch<128, true, 1, false>(p, cus, stream);

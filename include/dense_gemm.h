@@ -47,29 +47,34 @@
  * dense_gemm_plan), the K dimension of those tiles is split: each part
  * writes an FP32 partial tile to the workspace and a second kernel sums them
  * in a fixed order (results stay reproducible) and rounds once.  The other
- * tiles are computed whole in the same launch.  The environment variable
- * DENSE_GEMM_SPLITK=off disables split-K, DENSE_GEMM_SPLITK=<n> forces n
- * parts (for testing and measurement).
+ * tiles are computed whole in the same launch.  dense_gemm_ex can force a
+ * number of parts, or none (dense_gemm_options).
  *
  * Tile width.  Output tiles are 256 x 256.  For D = A @ B.T whose 256-wide
  * tiles would occupy at most half the CUs, with N > 128 and operands of at
  * most 192 MiB, they are 256 x 128 instead (twice the tiles, one wave).
  * Either width sums each output in the same order, so results are identical.
- * DENSE_GEMM_TILE_N=128 or 256 forces the width of A @ B.T (for testing).
+ * dense_gemm_ex can force the width of A @ B.T.
  *
- * Workspace.  A call that repacks an operand or splits K takes one workspace
- * with hipMallocAsync on `stream` and returns it with hipFreeAsync on the same
- * stream (stream-ordered, served by the device's default memory pool).  If it
- * cannot be had, a split call runs unsplit, and a call that needs a repack
- * returns DENSE_GEMM_NO_MEMORY (nothing launched).  Aligned operands with
- * enough output tiles need none.
+ * Workspace.  A call that repacks an operand or splits K needs device
+ * memory beyond A, B and D: dense_gemm_workspace_size gives the amount.
+ * dense_gemm_ex takes it from the caller (the destination-passing form of
+ * TileFoundry's schedule tutorial, section 6, whose lowered kernel takes its
+ * scratch buffers as arguments) and allocates nothing.  The plain entry
+ * points (gemm_nt_f16 and the rest, whose argument list has no workspace)
+ * take it with hipMallocAsync on `stream` and return it with hipFreeAsync on
+ * the same stream (stream-ordered, from the device's default memory pool);
+ * if it cannot be had, a split call runs unsplit and a call that needs a
+ * repack returns DENSE_GEMM_NO_MEMORY (nothing launched).  Aligned operands
+ * with enough output tiles need none.
  *
  * Ownership and concurrency.  The caller owns every buffer and the stream.
  * The library keeps no pointers after a call returns and caches only
  * per-device properties (thread-safe); apart from the workspace above it
- * allocates no device memory.  A, B and D must not overlap.  Calls
- * are asynchronous and ordered on `stream` (0 is the null stream); the caller
- * synchronizes.  Calls on different streams may run concurrently.
+ * allocates no device memory.  A, B, D and a workspace must not overlap.
+ * Calls are asynchronous and ordered on `stream` (0 is the null stream); the
+ * caller synchronizes.  Calls on different streams may run concurrently (each
+ * with its own workspace).
  *
  * Errors.  Every entry point validates its arguments before launching and
  * returns a dense_gemm_status; on any error nothing is launched and D is
@@ -80,6 +85,7 @@
 #ifndef DENSE_GEMM_H
 #define DENSE_GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -100,8 +106,31 @@ typedef enum dense_gemm_status {
   DENSE_GEMM_LAUNCH_FAILED = 6, /* the HIP runtime rejected the launch */
   DENSE_GEMM_NO_DEVICE = 7,     /* no current HIP device, or it is not a gfx950 */
   DENSE_GEMM_BAD_ARG = 8,       /* an argument of a helper below is out of its range */
-  DENSE_GEMM_NO_MEMORY = 9      /* no device memory for the repack workspace */
+  DENSE_GEMM_NO_MEMORY = 9,     /* no device memory for the workspace */
+  DENSE_GEMM_WORKSPACE_TOO_SMALL = 10  /* the caller's workspace is null or smaller
+                                          than the size query reports */
 } dense_gemm_status;
+
+/* The four type and layout pairings, for dense_gemm_ex and
+ * dense_gemm_workspace_size. */
+typedef enum dense_gemm_op {
+  DENSE_GEMM_NT_F16 = 0,   /* D = A @ B.T, FP16 (gemm_nt_f16)  */
+  DENSE_GEMM_NN_BF16 = 1,  /* D = A @ B,   BF16 (gemm_nn_bf16) */
+  DENSE_GEMM_NT_BF16 = 2,  /* D = A @ B.T, BF16 (gemm_nt_bf16) */
+  DENSE_GEMM_NN_F16 = 3    /* D = A @ B,   FP16 (gemm_nn_f16)  */
+} dense_gemm_op;
+
+/* Overrides of the library's launch plan (a null pointer, or zeros, keep
+ * its own choice).  They change the FP32 summation order of the outputs they
+ * touch (split_k), or the tiling (tile_n, which keeps the order), never the
+ * operation; both stay within the rounding bound.
+ *   split_k  0: the library's choice; 1: no split; n > 1: every tile's K
+ *            steps in min(n, steps) parts of equal length (the last shorter)
+ *   tile_n   0: the library's choice; 256; or 128 (D = A @ B.T only) */
+typedef struct dense_gemm_options {
+  int32_t split_k;
+  int32_t tile_n;
+} dense_gemm_options;
 
 /* D = A @ B.T; FP16 in, FP32 accumulate, FP16 out.  A is M x K, B is N x K.
  * The FP16 product of "TIRx GEMM on Blackwell", "The short version". */
@@ -173,6 +202,52 @@ dense_gemm_status gemm_nt_e4m3_mx(int64_t M, int64_t N, int64_t K, const void* A
                                   const void* SA, int64_t ldsa, const void* B, int64_t ldb,
                                   const void* SB, int64_t ldsb, void* D, int64_t ldd,
                                   hipStream_t stream);
+
+/* ---- caller-owned workspace (nothing allocated) ------------------------
+ * The workspace-passing forms of the entry points above, for callers that
+ * manage device memory themselves (a memory pool, graph capture, a serving
+ * loop): the same operation, kernels and results (bit for bit, for the same
+ * options), with the scratch memory given as `workspace` (256-byte aligned,
+ * at least the size the query reports; it may be null when that size is
+ * 0).  A workspace below the size returns DENSE_GEMM_WORKSPACE_TOO_SMALL,
+ * one off 256-byte alignment DENSE_GEMM_MISALIGNED, before any launch.  The
+ * workspace is used by the launches of this call only (stream-ordered:
+ * after the call's work on `stream` completes it may be reused; two calls in
+ * flight at once need two workspaces).  Its contents need no initialisation
+ * and are left undefined. */
+
+/* Bytes of workspace dense_gemm_ex needs for these arguments (0 if none).
+ * `op` is a dense_gemm_op; the pointers A and B are only tested for null
+ * and alignment (an operand off 16-byte alignment, or with K, its leading
+ * dimension or, for the A @ B layout's B, N not a multiple of 8, takes a
+ * repacked copy).  num_cus: the device's compute units (0: query the
+ * current device).  `opt` as for dense_gemm_ex (may be null).  Errors as
+ * dense_gemm_validate, DENSE_GEMM_BAD_ARG for a bad op, option or null
+ * `bytes`, DENSE_GEMM_NO_DEVICE if num_cus is 0 and no gfx950 is current. */
+dense_gemm_status dense_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K,
+                                            const void* A, int64_t lda, const void* B,
+                                            int64_t ldb, int64_t num_cus,
+                                            const dense_gemm_options* opt, size_t* bytes);
+
+/* The product `op` (a dense_gemm_op) with the caller's workspace and
+ * optional plan overrides; arguments, layouts and errors as the entry point
+ * of that op. */
+dense_gemm_status dense_gemm_ex(int op, int64_t M, int64_t N, int64_t K, const void* A,
+                                int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd,
+                                const dense_gemm_options* opt, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace gemm_nt_e4m3_mx_ex needs: the repacked scale panels,
+ * 1 KiB per 256-row tile of A and of B per 128 K values (0 when M or N is
+ * 0).  DENSE_GEMM_BAD_ARG for K not a multiple of 32 or a null `bytes`. */
+dense_gemm_status gemm_nt_e4m3_mx_workspace_size(int64_t M, int64_t N, int64_t K, size_t* bytes);
+
+/* gemm_nt_e4m3_mx with the caller's workspace. */
+dense_gemm_status gemm_nt_e4m3_mx_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                     const void* SA, int64_t ldsa, const void* B, int64_t ldb,
+                                     const void* SB, int64_t ldsb, void* D, int64_t ldd,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* dense_gemm_status_string(int status);

@@ -40,16 +40,49 @@ def from_dev(t_dev) -> np.ndarray:
     return t_dev.cpu().numpy().view(np.uint16)
 
 
-def call(layout, fmt, M, N, K, A, lda, B, ldb, D, ldd, stream=None, offsets=(0, 0, 0)):
-    """Run the entry point for (layout, fmt) on device tensors; returns the
-    status.  ``offsets`` are byte offsets added to the A, B and D pointers."""
+def workspace(nbytes: int):
+    """A device workspace of ``nbytes`` (256-byte aligned) from torch."""
     t = torch()
-    fn = binding.raw(ENTRY[(layout, fmt)])
+    ws = t.empty(max(nbytes, 1) + 256, dtype=t.uint8, device="cuda")
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + max(nbytes, 1)]
+
+
+def call(layout, fmt, M, N, K, A, lda, B, ldb, D, ldd, stream=None, offsets=(0, 0, 0),
+         opts=None):
+    """Run the entry point for (layout, fmt) on device tensors; returns the
+    status.  ``offsets`` are byte offsets added to the A, B and D pointers.
+    With ``opts`` = (split_k, tile_n) the call goes through dense_gemm_ex
+    with those plan overrides and a workspace of the size the library's query
+    reports, allocated here and held in _KEEP until the next gemm() has
+    synchronised."""
+    t = torch()
     st = t.cuda.current_stream() if stream is None else stream
     ptr = lambda x, o: 0 if x is None else x.data_ptr() + o  # noqa: E731
     oa, ob, od = offsets
-    return binding.Status(fn(M, N, K, ptr(A, oa), lda, ptr(B, ob), ldb, ptr(D, od), ldd,
-                             st.cuda_stream))
+    if opts is None:
+        fn = binding.raw(ENTRY[(layout, fmt)])
+        return binding.Status(fn(M, N, K, ptr(A, oa), lda, ptr(B, ob), ldb, ptr(D, od), ldd,
+                                 st.cuda_stream))
+    lib = binding.load_library()
+    o = binding.Options(*opts)
+    import ctypes
+    need = ctypes.c_size_t()
+    rc = binding.Status(lib.dense_gemm_workspace_size(binding.OPS[(layout, fmt)], M, N, K,
+                                                      ptr(A, oa), lda, ptr(B, ob), ldb, 0,
+                                                      ctypes.byref(o), ctypes.byref(need)))
+    if rc != binding.Status.OK:
+        return rc
+    ws = workspace(need.value)
+    _KEEP.append(ws)
+    return binding.Status(lib.dense_gemm_ex(binding.OPS[(layout, fmt)], M, N, K, ptr(A, oa), lda,
+                                            ptr(B, ob), ldb, ptr(D, od), ldd, ctypes.byref(o),
+                                            ws.data_ptr(), need.value, st.cuda_stream))
+
+
+# workspaces of calls made through call(..., opts=...): released at the next
+# gemm() (after its synchronisation), so none is freed while in use
+_KEEP = []
 
 
 def to_dev_at(bits: np.ndarray, rows: int, cols: int, ld: int, off: int, fill: int = CANARY):
@@ -62,9 +95,10 @@ def to_dev_at(bits: np.ndarray, rows: int, cols: int, ld: int, off: int, fill: i
 
 
 def gemm(layout, fmt, Abits, Bbits, M, N, K, lda=None, ldb=None, ldd=None, stream=None,
-         a_off=0, b_off=0, d_off=0):
+         a_off=0, b_off=0, d_off=0, opts=None):
     """Upload, run, download.  Returns (D bits M x ldd, status).  ``*_off``
-    place a matrix that many elements into its buffer (misaligned pointers)."""
+    place a matrix that many elements into its buffer (misaligned pointers).
+    ``opts`` = (split_k, tile_n): through dense_gemm_ex (see call)."""
     t = torch()
     lda = K if lda is None else lda
     ldb = (K if layout == "nt" else N) if ldb is None else ldb
@@ -76,8 +110,9 @@ def gemm(layout, fmt, Abits, Bbits, M, N, K, lda=None, ldb=None, ldd=None, strea
         B = to_dev_at(Bbits, K, N, ldb, b_off)
     D = to_dev_at(np.zeros(0, np.uint16), M, 0, ldd, d_off)
     st = call(layout, fmt, M, N, K, A, lda, B, ldb, D, ldd, stream,
-              offsets=(2 * a_off, 2 * b_off, 2 * d_off))
+              offsets=(2 * a_off, 2 * b_off, 2 * d_off), opts=opts)
     t.cuda.synchronize()
+    _KEEP.clear()
     out = from_dev(D)[d_off:d_off + M * ldd].reshape(M, ldd) if M else np.zeros((0, ldd), np.uint16)
     assert (from_dev(D)[:d_off] == CANARY).all() and (from_dev(D)[d_off + M * ldd:] == CANARY).all()
     return out, st

@@ -98,7 +98,8 @@ def test_validate_error_codes():
     assert _v(NT, 1 << 31, 8, 8) == S.TOO_LARGE
     assert _v(NT, 8, 8, 8, lda=1 << 23) == S.TOO_LARGE
     assert _v(NN, 8, 8, 8, ldb=1 << 26) == S.TOO_LARGE
-    # the largest accepted operand spans (one row of tiles short of 2^31 bytes)
+    # the largest accepted operand spans (one row of tiles short of 2^31 bytes;
+    # tests/test_gpu_limits.py runs them) and one step beyond
     assert _v(NT, 256, 256, 4194296) == S.OK
     assert _v(NT, 256, 256, 4194304) == S.TOO_LARGE
     assert _v(NN, 16, 16777208, 64) == S.OK
@@ -125,14 +126,18 @@ def test_scheduler_covers_every_tile_once(tiles_m, tiles_n, g):
 
 
 def test_scheduler_matches_page_grouped_order():
-    # TileFoundry tutorial, section 5: task -> g = task // (GN*G), bn = (task//G) % GN,
-    # mi = task % G, tile = (g*G + mi, bn); the 64 x 68 tile grid with G = 16.
+    # TileFoundry tutorial, sections 3 and 5 (the 64 x 68 tile grid, groups of
+    # G = 16 tile rows): the tasks of a group come before those of the next
+    # group; inside a group they walk the tile columns in order, and inside a
+    # column the group's rows.  So tile row r = 16 g + i, tile column c is
+    # task number (g * 68 + c) * 16 + i; check that inverse on every tile.
     GM, GN, G = 64, 68, 16
     gold = golden()
     assert GM * GN == gold["tiles_8192x17408_128x256"]
-    for task in range(0, GM * GN, 7):
-        g, bn, mi = task // (GN * G), (task // G) % GN, task % G
-        assert tile_of(task, GM, GN, G) == (g * G + mi, bn)
+    for r in range(GM):
+        for c in range(GN):
+            task = ((r // G) * GN + c) * G + r % G
+            assert tile_of(task, GM, GN, G) == (r, c)
 
 
 def test_page_persistent_assignment_covers_each_tile_once():
@@ -149,12 +154,13 @@ def test_page_persistent_assignment_covers_each_tile_once():
             owners[t] = p
     assert len(owners) == GM * GN
     assert -(-GM * GN // CTAS) == gold["waves_4352_tiles_132_ctas"]
-    # the section-3 loop nest, written out, visits the same (m, n) per CTA
-    for p in (0, 1, 77, 131):
-        page = [((g * 16 + mi), bn) for g in range(64 // 16) for bn in range(68)
-                for mi in range((p - (g * 68 + bn) * 16) % 132, 16, 132)]
-        ours = [tile_of(task, GM, GN, G) for task in range(p, GM * GN, CTAS)]
-        assert page == ours
+    # the page's rule for which CTA computes a tile (section 3: the CTAs deal
+    # the grouped task order out round-robin): the tile in row r and column
+    # c is task ((r // 16) * 68 + c) * 16 + r % 16, owned by that task
+    # number mod 132
+    for r in range(GM):
+        for c in range(GN):
+            assert owners[(r, c)] == (((r // G) * GN + c) * G + r % G) % CTAS
 
 
 def test_ragged_last_group():
@@ -326,3 +332,114 @@ def test_ladder_argument_checks_on_the_host():
     assert lad(1, lda=1 << 24) == S.TOO_LARGE  # tile span >= 2 GiB
     assert lad(1, ldd=1 << 31) == S.TOO_LARGE  # 32-bit row pitch of D
     assert lad(1, M=(1 << 31) - 128, N=(1 << 31) - 128, ldd=(1 << 31) - 128) == S.TOO_LARGE
+
+
+# ------------------------------------------------ caller-owned workspace --
+
+def _ws(layout, fmt, M, N, K, A=256, lda=None, B=256, ldb=None, cus=256, opts=None):
+    lib = binding.load_library()
+    lda = K if lda is None else lda
+    ldb = (K if layout == "nt" else N) if ldb is None else ldb
+    out = ctypes.c_size_t(12345)
+    o = binding.Options(*opts) if opts is not None else None
+    st = S(lib.dense_gemm_workspace_size(binding.OPS[(layout, fmt)], M, N, K, A, lda, B, ldb, cus,
+                                         ctypes.byref(o) if o is not None else None,
+                                         ctypes.byref(out)))
+    return st, out.value
+
+
+def test_workspace_size_of_the_workloads():
+    # aligned operands with at least a wave of tiles need none
+    assert _ws("nt", "f16", 4096, 4096, 4096) == (S.OK, 0)
+    assert _ws("nn", "bf16", 8192, 17408, 5120) == (S.OK, 0)
+    assert _ws("nt", "f16", 3000, 5000, 4000) == (S.OK, 0)
+    assert _ws("nt", "f16", 128, 128, 64) == (S.OK, 0)
+    # one 256 x 256 tile, 64 K steps in 16 parts: 16 FP32 partial tiles
+    assert _ws("nt", "f16", 128, 128, 4096) == (S.OK, 16 * 256 * 256 * 4)
+    # K not a multiple of 8: both operands repacked with rows of K8 = 4096
+    assert _ws("nt", "f16", 4096, 4096, 4095) == (S.OK, 2 * 4096 * 4096 * 2)
+    # a misaligned pointer repacks that operand only
+    assert _ws("nt", "f16", 4096, 4096, 4096, A=258) == (S.OK, 4096 * 4096 * 2)
+    assert _ws("nn", "bf16", 4096, 4096, 4096, B=250) == (S.OK, 4096 * 4096 * 2)
+    # ... with its size rounded up to 256 bytes, before the next part
+    assert _ws("nt", "f16", 4096, 4096, 4100, A=258) == \
+        (S.OK, 2 * ((4096 * 4104 * 2 + 255) // 256 * 256))
+    # empty products need none
+    assert _ws("nt", "f16", 0, 64, 64) == (S.OK, 0)
+
+
+def test_workspace_size_follows_the_options():
+    # forced parts on every tile: parts x tiles FP32 partial tiles of the width
+    assert _ws("nn", "bf16", 300, 264, 1000, opts=(4, 0)) == (S.OK, 4 * 4 * 256 * 256 * 4)
+    assert _ws("nt", "f16", 300, 264, 1000, opts=(4, 128)) == (S.OK, 4 * 6 * 256 * 128 * 4)
+    # more parts than K steps: one per step
+    assert _ws("nt", "f16", 256, 256, 128, opts=(7, 256)) == (S.OK, 2 * 256 * 256 * 4)
+    # split_k = 1: no partials
+    assert _ws("nt", "f16", 128, 128, 4096, opts=(1, 0)) == (S.OK, 0)
+    # bad options and ops
+    assert _ws("nt", "f16", 128, 128, 64, opts=(-1, 0))[0] == S.BAD_ARG
+    assert _ws("nt", "f16", 128, 128, 64, opts=(0, 64))[0] == S.BAD_ARG
+    assert _ws("nn", "bf16", 128, 128, 64, opts=(0, 128))[0] == S.BAD_ARG  # A.B: 256 only
+    lib = binding.load_library()
+    out = ctypes.c_size_t()
+    assert S(lib.dense_gemm_workspace_size(4, 8, 8, 8, 256, 8, 256, 8, 256, None,
+                                           ctypes.byref(out))) == S.BAD_ARG
+    assert S(lib.dense_gemm_workspace_size(0, 8, 8, 8, 256, 8, 256, 8, 256, None,
+                                           None)) == S.BAD_ARG
+    # the argument check comes first
+    assert _ws("nt", "f16", -1, 8, 8)[0] == S.INVALID_DIM
+    assert _ws("nt", "f16", 8, 8, 16, lda=8)[0] == S.BAD_LD
+    assert _ws("nt", "f16", 256, 256, 4194304)[0] == S.TOO_LARGE
+
+
+def test_workspace_size_matches_the_plan():
+    # the partial tiles the size counts are those of dense_gemm_plan
+    lib = binding.load_library()
+    plan = (ctypes.c_int64 * 10)()
+    for layout, M, N, K in [("nt", 128, 128, 4096), ("nt", 4252, 4088, 1000),
+                            ("nn", 4252, 4088, 1000), ("nt", 256, 2048, 16384),
+                            ("nt", 8192, 1024, 16384)]:
+        fmt = "f16" if layout == "nt" else "bf16"
+        assert lib.dense_gemm_plan(NT if layout == "nt" else NN, M, N, K, 256, plan) == S.OK
+        tasks = plan[3] * plan[4]
+        split_tiles = (tasks % 256) if plan[8] > 1 else 0
+        want = plan[8] * split_tiles * 256 * plan[1] * 4 if plan[8] > 1 else 0
+        assert _ws(layout, fmt, M, N, K) == (S.OK, want), (layout, M, N, K)
+
+
+def test_ex_argument_checks_on_the_host():
+    lib = binding.load_library()
+
+    def ex(op, M, N, K, A=256, lda=64, B=256, ldb=64, D=256, ldd=64, ws=0, nbytes=0):
+        return S(lib.dense_gemm_ex(op, M, N, K, A, lda, B, ldb, D, ldd, None, ws, nbytes, None))
+
+    assert ex(4, 8, 8, 8) == S.BAD_ARG
+    assert ex(-1, 8, 8, 8) == S.BAD_ARG
+    assert ex(0, -1, 8, 8) == S.INVALID_DIM
+    assert ex(1, 8, 8, 8, D=0) == S.NULL_PTR
+    assert ex(2, 8, 8, 16, lda=8) == S.BAD_LD
+    assert ex(3, 8, 8, 8, A=255) == S.MISALIGNED
+    assert ex(0, 0, 8, 8) == S.OK  # empty: nothing to do
+    assert ex(0, 256, 256, 4194304, lda=4194304, ldb=4194304, ldd=256) == S.TOO_LARGE
+
+
+def test_mx_workspace_size():
+    lib = binding.load_library()
+    out = ctypes.c_size_t()
+
+    def ws(M, N, K):
+        st = S(lib.gemm_nt_e4m3_mx_workspace_size(M, N, K, ctypes.byref(out)))
+        return st, out.value
+
+    # 1 KiB per 256-row tile of A and of B per 128-deep K stage
+    assert ws(8192, 8192, 8192) == (S.OK, (32 + 32) * 64 * 1024)
+    assert ws(8192, 17408, 5120) == (S.OK, (32 + 68) * 40 * 1024)
+    assert ws(280, 300, 160) == (S.OK, (2 + 2) * 2 * 1024)
+    assert ws(256, 256, 0) == (S.OK, 2 * 1024)
+    assert ws(0, 256, 64) == (S.OK, 0)
+    assert ws(8, 8, 40)[0] == S.BAD_ARG
+    assert ws(-1, 8, 32)[0] == S.INVALID_DIM
+    assert S(lib.gemm_nt_e4m3_mx_workspace_size(8, 8, 32, None)) == S.BAD_ARG
+    fn = lib.gemm_nt_e4m3_mx_ex
+    assert S(fn(8, 8, 40, 256, 48, 256, 2, 256, 48, 256, 2, 256, 8, 0, 0, None)) == S.BAD_ARG
+    assert S(fn(8, 8, 64, 256, 64, 256, 2, 256, 64, 256, 2, 0, 8, 0, 0, None)) == S.NULL_PTR

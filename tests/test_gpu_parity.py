@@ -4,9 +4,13 @@ Acceptance (per element): |d_gpu - d| <= ulp_out(|d|) + 2^-11 * sum_k |a*b|,
 with d the oracle's FP64 value.  Where the FP32 sum is exact (small-integer,
 identity and all-ones inputs) the result must equal the oracle's correctly
 rounded value bit for bit.  Shapes: every workload at a reduced size checked
-element by element (several tiles and a ragged tail in M, N and K), and at its
-full size in the launch configuration the benchmark times, on sampled entries.
+element by element (several tiles and a ragged tail in M, N and K), and every
+workload at its full size, in the launch configuration the benchmark times,
+element by element as well (the oracle's full product of the largest,
+8192 x 17408 x 5120, takes about a minute on 16 host cores).
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -31,14 +35,6 @@ def check_full(layout, fmt, A, B, M, N, K, D):
     return d
 
 
-def check_sampled(layout, fmt, A, B, M, N, K, D, n=3000, seed=0):
-    rows, cols = inputs.sample_indices(M, N, n, seed)
-    ldb = K if layout == "nt" else N
-    d, s = oracle.gemm_entries(layout, fmt, A, B, K=K, lda=K, ldb=ldb, rows=rows, cols=cols)
-    res = oracle.check(fmt, d, s, D[rows, cols])
-    assert res.ok, (res, rows[max(res.worst_idx, 0)], cols[max(res.worst_idx, 0)])
-
-
 # --------------------------------------------------- workloads, reduced --
 
 REDUCED = [
@@ -52,20 +48,18 @@ REDUCED = [
 
 
 @pytest.fixture(params=["auto", "off"])
-def splitk(request, monkeypatch):
-    """Run with the library's own split-K choice, and with split-K disabled."""
-    if request.param == "off":
-        monkeypatch.setenv("DENSE_GEMM_SPLITK", "off")
-    else:
-        monkeypatch.delenv("DENSE_GEMM_SPLITK", raising=False)
-    return request.param
+def splitk(request):
+    """Run with the library's own split-K choice (the plain entry point), and
+    with split-K disabled (dense_gemm_ex with split_k = 1): the plan
+    overrides as _gpu.gemm takes them."""
+    return None if request.param == "auto" else (1, 0)
 
 
 @pytest.mark.parametrize("name,M,N,K", REDUCED)
 def test_workload_reduced_full_check(name, M, N, K, splitk):
     w = inputs.WORKLOADS[name]
     A, B = inputs.make_operands(w, M=M, N=N, K=K)
-    D, st = _gpu.gemm(w.layout, w.fmt, A, B, M, N, K)
+    D, st = _gpu.gemm(w.layout, w.fmt, A, B, M, N, K, opts=splitk)
     assert st == status().OK
     check_full(w.layout, w.fmt, A, B, M, N, K, D)
 
@@ -82,33 +76,69 @@ def test_other_type_layout_pairs(layout, fmt):
 
 # ------------------------------------------------ workloads, full size --
 
-@pytest.mark.parametrize("name", ["single_tile", "k_loop", "square_nt", "large_nn", "ragged_nt"])
-def test_workload_full_size_sampled(name):
-    w = inputs.WORKLOADS[name]
+@functools.lru_cache(maxsize=1)
+def square_nt_reference():
+    """Operands and oracle (d, s) of the 4096^3 FP16 A.B^T workload (shared
+    by the tests of the library kernel and of the step ladder at that size)."""
+    w = inputs.WORKLOADS["square_nt"]
     A, B = inputs.make_operands(w)
+    d, s = oracle.gemm("nt", "f16", A, B)
+    return A, B, d, s
+
+
+def check_against(fmt, d, s, D, what):
+    res = oracle.check(fmt, d, s, D[:, :d.shape[1]])
+    assert res.ok, (what, res, np.unravel_index(max(res.worst_idx, 0), d.shape))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["single_tile", "k_loop", "square_nt", "large_nn", "ragged_nt"])
+def test_workload_full_size_every_output(name):
+    # the benchmark's call (the plain entry point, the library's own plan:
+    # 256 x 256 tiles for the three large workloads, split-K for k_loop),
+    # every output against the oracle
+    w = inputs.WORKLOADS[name]
+    print("full size %s %dx%dx%d" % (name, w.M, w.N, w.K), flush=True)
+    if name == "square_nt":
+        A, B, d, s = square_nt_reference()
+    else:
+        A, B = inputs.make_operands(w)
+        d, s = oracle.gemm(w.layout, w.fmt, A, B)
     D, st = _gpu.gemm(w.layout, w.fmt, A, B, w.M, w.N, w.K)
     assert st == status().OK
-    if w.M * w.N * w.K <= 128 * 128 * 4096:
-        check_full(w.layout, w.fmt, A, B, w.M, w.N, w.K, D)
-    else:
-        check_sampled(w.layout, w.fmt, A, B, w.M, w.N, w.K, D, n=3000, seed=w.seed)
-        assert np.isfinite(oracle.decode(w.fmt, D[:: max(w.M // 64, 1), :: max(w.N // 64, 1)])).all()
+    check_against(w.fmt, d, s, D, name)
+
+
+@pytest.mark.parametrize("layout,fmt,M,N,K", [("nt", "f16", 4096, 8192, 1024),
+                                              ("nn", "bf16", 1536, 17408, 1024)])
+def test_two_tiles_per_workgroup_every_output(layout, fmt, M, N, K):
+    # persistent workgroups that compute a second tile after their first
+    # (the ring slot carried across tiles, the first tile's stores draining
+    # under the second tile's loads), no split: 512 tiles of 256 x 256 on 256
+    # workgroups (A.B^T), and 408 tiles with 152 workgroups doing two (A.B,
+    # the large A.B workload's N, layout and distribution); every output
+    w = inputs.WORKLOADS["square_nt" if layout == "nt" else "large_nn"]
+    A, B = inputs.make_operands(w, seed=M + N + K, M=M, N=N, K=K)
+    D, st = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    assert st == status().OK
+    check_full(layout, fmt, A, B, M, N, K, D)
 
 
 # ------------------------------------------------- bitwise special cases --
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("M,N,K", [(8192, 16384 + 128, 4096), (8192, 4096, 16384 + 40),
                                    (8192, 1024, 1024), (8192, 1024, 16384)])
-def test_m8192_sweep_shapes_sampled(M, N, K):
+def test_m8192_sweep_shapes_every_output(M, N, K):
     # extreme shapes of the benchmark's M = 8192 sweep (FP16 A.B^T, N(0,1)/8):
     # the widest N with a ragged last tile column, the deepest K with a partial
-    # last step, and the narrowest N (128-wide tiles; split-K at K = 16384);
-    # sampled against the oracle
+    # last step (both operands repacked), and the narrowest N (128-wide
+    # tiles; split-K at K = 16384); every output against the oracle
     w = inputs.WORKLOADS["square_nt"]
     A, B = inputs.make_operands(w, seed=M + N + K, M=M, N=N, K=K)
     D, st = _gpu.gemm("nt", "f16", A, B, M, N, K)
     assert st == status().OK
-    check_sampled("nt", "f16", A, B, M, N, K, D, n=2000, seed=N + K)
+    check_full("nt", "f16", A, B, M, N, K, D)
 
 
 @pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16"), ("nt", "bf16"), ("nn", "f16")])
@@ -120,7 +150,7 @@ def test_small_integers_exact(layout, fmt, splitk):
     sa, sb = inputs.operand_shapes(layout, M, N, K)
     A = inputs.small_integers(fmt, sa, seed=31)
     B = inputs.small_integers(fmt, sb, seed=32)
-    D, st = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    D, st = _gpu.gemm(layout, fmt, A, B, M, N, K, opts=splitk)
     assert st == status().OK
     d, _ = oracle.gemm(layout, fmt, A, B)
     want = oracle.round_to(fmt, d)
@@ -166,29 +196,29 @@ def test_power_of_two_scaling():
 
 @pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
 @pytest.mark.parametrize("parts", ["2", "3", "7", "64"])
-def test_forced_split_k(layout, fmt, parts, monkeypatch):
+def test_forced_split_k(layout, fmt, parts):
     # split-K forced on shapes of several tiles, a ragged K tail and parts of
     # unequal length; the summation order is fixed, so a rerun is bitwise equal
-    monkeypatch.setenv("DENSE_GEMM_SPLITK", parts)
+    opts = (int(parts), 0)
     w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 71)
     M, N, K = 300, 264, 1000
     A, B = inputs.make_operands(w, M=M, N=N, K=K)
-    D, st = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    D, st = _gpu.gemm(layout, fmt, A, B, M, N, K, opts=opts)
     assert st == status().OK
     check_full(layout, fmt, A, B, M, N, K, D)
-    D2, _ = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    D2, _ = _gpu.gemm(layout, fmt, A, B, M, N, K, opts=opts)
     assert (D == D2).all()
 
 
 @pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
 @pytest.mark.parametrize("parts", ["off", "4"])
-def test_k_remainder_equals_leading_zero_padding(layout, fmt, parts, monkeypatch):
+def test_k_remainder_equals_leading_zero_padding(layout, fmt, parts):
     # K = 4000 is not a multiple of the 64-deep K step: the kernel pads its
     # first step in front (k from -32), so the result must equal, bit for bit,
     # the same data with 32 zero columns of A (and zero k-rows or columns of
     # B) put in front, K = 4032, which has the same steps, unsplit or in 4
     # parts of 16 steps
-    monkeypatch.setenv("DENSE_GEMM_SPLITK", parts)
+    opts = (1, 0) if parts == "off" else (int(parts), 0)
     w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 5)
     M, N, K = 272, 264, 4000
     pad = (64 - K % 64) % 64
@@ -202,8 +232,8 @@ def test_k_remainder_equals_leading_zero_padding(layout, fmt, parts, monkeypatch
     else:
         Bp = np.zeros((Kp, N), np.uint16)
         Bp[pad:] = B
-    D1, _ = _gpu.gemm(layout, fmt, A, B, M, N, K)
-    D2, _ = _gpu.gemm(layout, fmt, Ap, Bp, M, N, Kp)
+    D1, _ = _gpu.gemm(layout, fmt, A, B, M, N, K, opts=opts)
+    D2, _ = _gpu.gemm(layout, fmt, Ap, Bp, M, N, Kp, opts=opts)
     assert (D1 == D2).all()
     check_full(layout, fmt, A, B, M, N, K, D1)
 
@@ -307,19 +337,14 @@ def test_repack_beyond_one_grid_pass():
     # the repack kernel strides over a capped grid (65536 workgroups of 256
     # threads, one 8-element chunk per thread and pass): an A of 8200 rows
     # with K = 16390 (rows padded to 16392) holds 16,801,800 chunks, so rows
-    # 8188 and up are copied by a second pass.  Sampled entries, and every
-    # entry of the last 12 rows, against the oracle.
+    # 8188 and up are copied by a second pass.  Every output against the
+    # oracle.
     w = inputs.WORKLOADS["square_nt"]
     M, N, K = 8200, 256, 16390
     A, B = inputs.make_operands(w, seed=77, M=M, N=N, K=K)
     D, st = _gpu.gemm("nt", "f16", A, B, M, N, K)
     assert st == status().OK
-    check_sampled("nt", "f16", A, B, M, N, K, D, n=1000, seed=77)
-    rows = np.repeat(np.arange(M - 12, M), N)
-    cols = np.tile(np.arange(N), 12)
-    d, s = oracle.gemm_entries("nt", "f16", A, B, K=K, lda=K, ldb=K, rows=rows, cols=cols)
-    res = oracle.check("f16", d, s, D[rows, cols])
-    assert res.ok, (res, rows[max(res.worst_idx, 0)], cols[max(res.worst_idx, 0)])
+    check_full("nt", "f16", A, B, M, N, K, D)
 
 
 def test_zero_k_writes_zeros_and_empty_is_noop():
@@ -480,13 +505,13 @@ def test_ladder_level_full_check(level):
 
 
 @pytest.mark.parametrize("level", LEVELS)
-def test_ladder_level_4096_sampled(level):
+def test_ladder_level_4096_every_output(level):
     # the benchmark's shape, in the configuration the ladder benchmark times
     w = inputs.WORKLOADS["square_nt"]
-    A, B = inputs.make_operands(w)
+    A, B, d, s = square_nt_reference()
     D, st = _gpu.ladder(level, A, B, w.M, w.N, w.K)
     assert st == status().OK
-    check_sampled("nt", "f16", A, B, w.M, w.N, w.K, D, n=2000, seed=level)
+    check_against("f16", d, s, D, "ladder level %d" % level)
 
 
 def test_ladder_small_integers_exact():
@@ -538,11 +563,11 @@ def binding_raw(name):
 # ------------------------------------------------- split last partial wave --
 
 @pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
-def test_split_last_wave(layout, fmt, monkeypatch):
+def test_split_last_wave(layout, fmt):
     # 17 x 16 = 272 tiles on 256 CUs: 256 tiles whole, the 16 of the last wave
-    # in 4 parts of 4 K steps, all in one launch; ragged M and N.  Entries are
-    # sampled from the whole output and, half of them, from the split tiles;
-    # the run with split-K disabled is checked the same way
+    # in 4 parts of 4 K steps, all in one launch; ragged M and N.  Every
+    # output against the oracle, plus entries drawn from the split tiles
+    # alone; the run with split-K disabled is checked the same way
     import ctypes
     from dense_gemm_08_amd import binding
     t = _gpu.torch()
@@ -575,16 +600,14 @@ def test_split_last_wave(layout, fmt, monkeypatch):
         cols = np.concatenate([cols, tc[keep]]).astype(np.int64)
     ldb = K if layout == "nt" else N
     d, s_ = oracle.gemm_entries(layout, fmt, A, B, K=K, lda=K, ldb=ldb, rows=rows, cols=cols)
-    for mode in ("auto", "off"):
-        if mode == "off":
-            monkeypatch.setenv("DENSE_GEMM_SPLITK", "off")
-        else:
-            monkeypatch.delenv("DENSE_GEMM_SPLITK", raising=False)
-        D, st = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    dfull, sfull = oracle.gemm(layout, fmt, A, B)
+    for mode, opts in (("auto", None), ("off", (1, 0))):
+        D, st = _gpu.gemm(layout, fmt, A, B, M, N, K, opts=opts)
         assert st == status().OK
         res = oracle.check(fmt, d, s_, D[rows, cols])
         assert res.ok, (mode, res)
-        D2, _ = _gpu.gemm(layout, fmt, A, B, M, N, K)
+        check_against(fmt, dfull, sfull, D, mode)
+        D2, _ = _gpu.gemm(layout, fmt, A, B, M, N, K, opts=opts)
         assert (D == D2).all()
 
 
@@ -600,37 +623,178 @@ TILE128 = [
 ]
 
 
+@pytest.mark.parametrize("tile_n", [128, 256])
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("M,N,K", TILE128)
-def test_tile128_full_check(fmt, M, N, K, splitk, monkeypatch):
-    monkeypatch.setenv("DENSE_GEMM_TILE_N", "128")
+def test_tile_width_full_check(fmt, M, N, K, splitk, tile_n):
+    # both tile widths of A.B^T forced on the same shapes (the plan picks 128
+    # for most of them), with the library's split-K choice and without
+    opts = (0 if splitk is None else 1, tile_n)
     w = inputs.Workload("x", "nt", fmt, 0, 0, 0, "uniform", 0.0, 301)
     A, B = inputs.make_operands(w, M=M, N=N, K=K)
-    D, st = _gpu.gemm("nt", fmt, A, B, M, N, K)
+    D, st = _gpu.gemm("nt", fmt, A, B, M, N, K, opts=opts)
     assert st == status().OK
     check_full("nt", fmt, A, B, M, N, K, D)
 
 
 @pytest.mark.parametrize("parts", ["3", "16"])
-def test_tile128_forced_split(parts, monkeypatch):
-    monkeypatch.setenv("DENSE_GEMM_TILE_N", "128")
-    monkeypatch.setenv("DENSE_GEMM_SPLITK", parts)
+def test_tile128_forced_split(parts):
     M, N, K = 520, 300, 2000
     A, B = inputs.make_operands(inputs.WORKLOADS["ragged_nt"], M=M, N=N, K=K)
-    D, st = _gpu.gemm("nt", "f16", A, B, M, N, K)
+    D, st = _gpu.gemm("nt", "f16", A, B, M, N, K, opts=(int(parts), 128))
     assert st == status().OK
     check_full("nt", "f16", A, B, M, N, K, D)
 
 
-def test_tile128_bitwise_equals_tile256(monkeypatch):
+def test_tile128_bitwise_equals_tile256():
     # each output is the same sequence of MFMA accumulations in either tile
     # width, so the results agree bit for bit (split-K off)
-    monkeypatch.setenv("DENSE_GEMM_SPLITK", "off")
     M, N, K = 1000, 900, 1500
     A, B = inputs.make_operands(inputs.WORKLOADS["square_nt"], M=M, N=N, K=K)
     out = {}
-    for tn in ("128", "256"):
-        monkeypatch.setenv("DENSE_GEMM_TILE_N", tn)
-        out[tn], st = _gpu.gemm("nt", "f16", A, B, M, N, K)
+    for tn in (128, 256):
+        out[tn], st = _gpu.gemm("nt", "f16", A, B, M, N, K, opts=(1, tn))
         assert st == status().OK
-    assert np.array_equal(out["128"], out["256"])
+    assert np.array_equal(out[128], out[256])
+
+
+# ------------------------------------------------ caller-owned workspace --
+
+def _need(layout, fmt, M, N, K, A, lda, B, ldb, offsets=(0, 0), opts=None):
+    import ctypes
+    from dense_gemm_08_amd import binding
+    lib = binding.load_library()
+    out = ctypes.c_size_t()
+    o = binding.Options(*opts) if opts else None
+    st = lib.dense_gemm_workspace_size(binding.OPS[(layout, fmt)], M, N, K,
+                                       A.data_ptr() + offsets[0], lda,
+                                       B.data_ptr() + offsets[1], ldb, 0,
+                                       ctypes.byref(o) if o else None, ctypes.byref(out))
+    assert st == 0
+    return out.value
+
+
+def _ex(layout, fmt, M, N, K, A, lda, B, ldb, D, ldd, ws_ptr, nbytes, stream=None,
+        offsets=(0, 0), opts=None):
+    import ctypes
+    from dense_gemm_08_amd import binding
+    t = _gpu.torch()
+    lib = binding.load_library()
+    st = t.cuda.current_stream() if stream is None else stream
+    o = binding.Options(*opts) if opts else None
+    return status()(lib.dense_gemm_ex(binding.OPS[(layout, fmt)], M, N, K,
+                                      A.data_ptr() + offsets[0], lda, B.data_ptr() + offsets[1],
+                                      ldb, D.data_ptr(), ldd, ctypes.byref(o) if o else None,
+                                      ws_ptr, nbytes, st.cuda_stream))
+
+
+WS_CASES = [
+    # (layout, fmt, M, N, K, lda_extra, a_off): what takes the workspace
+    ("nt", "f16", 128, 128, 4096, 0, 0),    # one tile in 16 K parts
+    ("nn", "bf16", 264, 304, 1032, 1, 0),   # A repacked (odd leading dimension)
+    ("nt", "f16", 4252, 4088, 1000, 0, 0),  # the last wave's 16 tiles in 4 parts
+    ("nt", "bf16", 280, 272, 200, 0, 3),    # A repacked (pointer off 16-byte alignment)
+    ("nn", "f16", 300, 264, 1001, 0, 0),    # both repacked (K odd), then split
+]
+
+
+@pytest.mark.parametrize("case", WS_CASES, ids=lambda c: "%s_%s_%dx%dx%d" % c[:5])
+def test_workspace_call_equals_plain_call(case):
+    # dense_gemm_ex with exactly the workspace the query reports gives the
+    # plain entry point's result bit for bit (same plan and kernels), which
+    # passes the oracle; a workspace one byte short, or a null one, is
+    # rejected and a misaligned one too, with D untouched
+    layout, fmt, M, N, K, xa, oa = case
+    t = _gpu.torch()
+    w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 401)
+    A, B = inputs.make_operands(w, seed=M + N + K, M=M, N=N, K=K)
+    lda, ldb = K + xa, (K if layout == "nt" else N)
+    Ad = _gpu.to_dev_at(A, M, K, lda, oa)
+    Bd = _gpu.to_dev(B, *((N, K) if layout == "nt" else (K, N)))
+    need = _need(layout, fmt, M, N, K, Ad, lda, Bd, ldb, offsets=(2 * oa, 0))
+    assert need > 0
+    D1 = _gpu.empty_out(M, N)
+    assert _gpu.call(layout, fmt, M, N, K, Ad, lda, Bd, ldb, D1, N, offsets=(2 * oa, 0, 0)) == \
+        status().OK
+    ws = _gpu.workspace(need + 512)
+    D2 = _gpu.empty_out(M, N)
+    assert _ex(layout, fmt, M, N, K, Ad, lda, Bd, ldb, D2, N, ws.data_ptr(), need,
+               offsets=(2 * oa, 0)) == status().OK
+    D3 = _gpu.empty_out(M, N)
+    assert _ex(layout, fmt, M, N, K, Ad, lda, Bd, ldb, D3, N, ws.data_ptr(), need - 1,
+               offsets=(2 * oa, 0)) == status().WORKSPACE_TOO_SMALL
+    assert _ex(layout, fmt, M, N, K, Ad, lda, Bd, ldb, D3, N, 0, 0,
+               offsets=(2 * oa, 0)) == status().WORKSPACE_TOO_SMALL
+    assert _ex(layout, fmt, M, N, K, Ad, lda, Bd, ldb, D3, N, ws.data_ptr() + 16, need,
+               offsets=(2 * oa, 0)) == status().MISALIGNED
+    t.cuda.synchronize()
+    g1, g2 = _gpu.from_dev(D1), _gpu.from_dev(D2)
+    assert (g1 == g2).all()
+    assert (_gpu.from_dev(D3) == _gpu.CANARY).all()
+    check_full(layout, fmt, A, B, M, N, K, g2)
+
+
+def test_workspace_calls_on_two_streams():
+    # calls that each need a workspace (split-K partials, a repacked operand),
+    # each given its own, issued back to back on two streams that do not
+    # wait for each other, give the bits of the same calls run alone
+    t = _gpu.torch()
+    w = inputs.WORKLOADS["square_nt"]
+    A1, B1 = inputs.make_operands(w, seed=71, M=128, N=128, K=4096)
+    wn = inputs.WORKLOADS["large_nn"]
+    A2, B2 = inputs.make_operands(wn, seed=72, M=264, N=304, K=1032)
+    A1d, B1d = _gpu.to_dev(A1, 128, 4096), _gpu.to_dev(B1, 128, 4096)
+    A2d, B2d = _gpu.to_dev(A2, 264, 1032, ld=1033), _gpu.to_dev(B2, 1032, 304)
+    cases = [("nt", "f16", 128, 128, 4096, A1d, 4096, B1d, 4096),
+             ("nn", "bf16", 264, 304, 1032, A2d, 1033, B2d, 304)]
+    needs = [_need(c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], c[8]) for c in cases]
+    ref = []
+    for c in cases:
+        D = _gpu.empty_out(c[2], c[3])
+        assert _gpu.call(c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], c[8], D, c[3]) == \
+            status().OK
+        t.cuda.synchronize()
+        ref.append(_gpu.from_dev(D))
+    main = t.cuda.current_stream()
+    streams = [t.cuda.Stream(), t.cuda.Stream()]
+    jobs = []
+    for it in range(12):
+        for si in range(2):
+            k = (it + si) % 2
+            c = cases[k]
+            jobs.append((k, si, _gpu.empty_out(c[2], c[3]), _gpu.workspace(needs[k])))
+    for st in streams:
+        st.wait_stream(main)
+    for k, si, D, ws in jobs:
+        c = cases[k]
+        with t.cuda.stream(streams[si]):
+            assert _ex(c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], c[8], D, c[3],
+                       ws.data_ptr(), needs[k], stream=streams[si]) == status().OK
+    for st in streams:
+        main.wait_stream(st)
+    t.cuda.synchronize()
+    for k, _, D, _ in jobs:
+        assert (_gpu.from_dev(D) == ref[k]).all(), k
+
+
+def test_mx_workspace_call_equals_plain_call():
+    import ctypes
+    from dense_gemm_08_amd import binding
+    t = _gpu.torch()
+    lib = binding.load_library()
+    M, N, K = 520, 300, 416
+    XA, XSA, XB, XSB = [t.from_numpy(x).cuda() for x in inputs.mx_operands(M, N, K, seed=73)]
+    nb = K // 32
+    need = ctypes.c_size_t()
+    assert lib.gemm_nt_e4m3_mx_workspace_size(M, N, K, ctypes.byref(need)) == 0
+    ws = _gpu.workspace(need.value)
+    h = t.cuda.current_stream().cuda_stream
+    args = (M, N, K, XA.data_ptr(), K, XSA.data_ptr(), nb, XB.data_ptr(), K, XSB.data_ptr(), nb)
+    D1, D2, D3 = (_gpu.empty_out(M, N) for _ in range(3))
+    assert lib.gemm_nt_e4m3_mx(*args, D1.data_ptr(), N, h) == 0
+    assert lib.gemm_nt_e4m3_mx_ex(*args, D2.data_ptr(), N, ws.data_ptr(), need.value, h) == 0
+    assert status()(lib.gemm_nt_e4m3_mx_ex(*args, D3.data_ptr(), N, ws.data_ptr(),
+                                           need.value - 1, h)) == status().WORKSPACE_TOO_SMALL
+    t.cuda.synchronize()
+    assert (_gpu.from_dev(D1) == _gpu.from_dev(D2)).all()
+    assert (_gpu.from_dev(D3) == _gpu.CANARY).all()
