@@ -28,6 +28,7 @@ class Status(enum.IntEnum):
     BAD_ARG = 8
     NO_MEMORY = 9
     WORKSPACE_TOO_SMALL = 10
+    SCRATCH_TOO_SMALL = 11
 
 
 # dense_gemm_op: the type and layout pairings of dense_gemm_ex
@@ -71,6 +72,7 @@ SIGNATURES = {
                                    ctypes.POINTER(Options), ctypes.POINTER(ctypes.c_size_t)], _i32),
     "dense_gemm_ex": ([_i32] + _GEMM_ARGS[:-1] + [ctypes.POINTER(Options), _vp, ctypes.c_size_t,
                                                  _vp], _i32),
+    "gemm_nt_f16_noalloc": (_GEMM_ARGS, _i32),
     "gemm_nt_e4m3_mx_workspace_size": ([_i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)], _i32),
     "gemm_nt_e4m3_mx_ex": ([_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                             _i64, _vp, ctypes.c_size_t, _vp], _i32),

@@ -670,6 +670,9 @@ const char* dense_gemm_status_string(int status) {
     case DENSE_GEMM_NO_MEMORY: return "no device memory for the workspace";
     case DENSE_GEMM_WORKSPACE_TOO_SMALL:
       return "workspace smaller than the call needs (see the workspace size query)";
+    case DENSE_GEMM_SCRATCH_TOO_SMALL:
+      return "the call needs more scratch memory than the 64 MiB the no-allocation entry "
+             "point holds per device (use dense_gemm_ex with a larger workspace)";
     default: return "unknown status";
   }
 }
@@ -955,6 +958,59 @@ static dense_gemm_status run_with(int64_t M, int64_t N, int64_t K, const void* A
   return enqueue_width<T, LAYOUT>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, (char*)ws, stream);
 }
 
+// ---- the entry point that allocates nothing --------------------------------
+// gemm_nt_f16_noalloc takes its scratch memory (split-K partial tiles and
+// repacked operands) from this fixed array instead of the caller or the
+// allocator.  Each device the library runs on holds its own copy, from the
+// code object's load until the process ends.  64 MiB holds every split-K
+// plan on a 256-CU device (at most one partial tile of 256 KiB per CU) and
+// repacked operands up to that size.  In host code `scratch` only stands in
+// for the symbol: its device address, looked up once per device with that
+// device current, is what the launches take.
+constexpr size_t SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[SCRATCH_BYTES];
+
+static void* g_scratch[64];
+static bool g_scratch_ok[64];
+
+static dense_gemm_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DENSE_GEMM_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_scratch_ok[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return DENSE_GEMM_NO_MEMORY;
+    }
+    g_scratch[dev] = ptr;
+    g_scratch_ok[dev] = true;
+  }
+  *out = g_scratch[dev];
+  return DENSE_GEMM_OK;
+}
+
+// A call with the device's fixed scratch array: the library's own plan,
+// rejected (before any launch) if it needs more than the array holds.
+template <typename T, int LAYOUT>
+static dense_gemm_status run_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                     const void* B, int64_t ldb, void* D, int64_t ldd,
+                                     hipStream_t stream) {
+  dense_gemm_status st = dense_gemm_validate(LAYOUT, M, N, K, A, lda, B, ldb, D, ldd);
+  if (st != DENSE_GEMM_OK || M == 0 || N == 0) return st;
+  DeviceInfo info;
+  st = device_info(&info);
+  if (st != DENSE_GEMM_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != DENSE_GEMM_OK) return st;
+  CallPlan cp;
+  st = plan_call(LAYOUT, M, N, K, A, lda, B, ldb, info.cus, nullptr, &cp);
+  if (st != DENSE_GEMM_OK) return st;
+  if (cp.total() > SCRATCH_BYTES) return DENSE_GEMM_SCRATCH_TOO_SMALL;
+  return enqueue_width<T, LAYOUT>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, (char*)ws, stream);
+}
+
 // A call of the plain entry points: the workspace (if the plan needs one)
 // is taken with hipMallocAsync on `stream` and returned with hipFreeAsync
 // after the launches.  A split call that cannot get its workspace runs
@@ -1025,6 +1081,12 @@ dense_gemm_status gemm_nn_f16(int64_t M, int64_t N, int64_t K, const void* A, in
                               const void* B, int64_t ldb, void* D, int64_t ldd,
                               hipStream_t stream) {
   return run<_Float16, NN>(M, N, K, A, lda, B, ldb, D, ldd, stream);
+}
+
+dense_gemm_status gemm_nt_f16_noalloc(int64_t M, int64_t N, int64_t K, const void* A,
+                                      int64_t lda, const void* B, int64_t ldb, void* D,
+                                      int64_t ldd, hipStream_t stream) {
+  return run_noalloc<_Float16, NT>(M, N, K, A, lda, B, ldb, D, ldd, stream);
 }
 
 dense_gemm_status dense_gemm_workspace_size(int op, int64_t M, int64_t N, int64_t K,

@@ -107,8 +107,10 @@ typedef enum dense_gemm_status {
   DENSE_GEMM_NO_DEVICE = 7,     /* no current HIP device, or it is not a gfx950 */
   DENSE_GEMM_BAD_ARG = 8,       /* an argument of a helper below is out of its range */
   DENSE_GEMM_NO_MEMORY = 9,     /* no device memory for the workspace */
-  DENSE_GEMM_WORKSPACE_TOO_SMALL = 10  /* the caller's workspace is null or smaller
+  DENSE_GEMM_WORKSPACE_TOO_SMALL = 10, /* the caller's workspace is null or smaller
                                           than the size query reports */
+  DENSE_GEMM_SCRATCH_TOO_SMALL = 11    /* gemm_nt_f16_noalloc: the call needs more than
+                                          its fixed 64 MiB of scratch */
 } dense_gemm_status;
 
 /* The four type and layout pairings, for dense_gemm_ex and
@@ -236,6 +238,23 @@ dense_gemm_status dense_gemm_ex(int op, int64_t M, int64_t N, int64_t K, const v
                                 int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd,
                                 const dense_gemm_options* opt, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/* gemm_nt_f16 for callers that cannot allocate device memory at all (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc) and keep no workspace of their own: the same arguments, plan,
+ * kernels and results (bit for bit), with the scratch memory taken from a
+ * fixed 64 MiB array that the library holds on each device it runs on from
+ * its first use until the process ends.  A call that needs more (repacked
+ * operands beyond it; every split-K plan on a 256-CU device fits) returns
+ * DENSE_GEMM_SCRATCH_TOO_SMALL before any launch.  It calls no allocator.
+ * All calls on one device share that array and leave their contents in it:
+ * two calls whose work overlaps on one device (on different streams, or
+ * from different threads) race and give undefined results; calls ordered
+ * on one stream, or synchronized, are safe.  Nothing in it needs to start
+ * at zero. */
+dense_gemm_status gemm_nt_f16_noalloc(int64_t M, int64_t N, int64_t K, const void* A,
+                                      int64_t lda, const void* B, int64_t ldb, void* D,
+                                      int64_t ldd, hipStream_t stream);
 
 /* Bytes of workspace gemm_nt_e4m3_mx_ex needs: the repacked scale panels,
  * 1 KiB per 256-row tile of A and of B per 128 K values (0 when M or N is
