@@ -10,10 +10,13 @@ Reported:
 * value: TFLOP/s = 2*M*N*K*steps / (wall time of the timed region);
 * roofline: the GEMM kernel against the dense FP16/BF16 (or FP8) MFMA peak,
   with its average duration from HIP events recorded on the launch stream
-  around the timed calls, and the 10th/50th/90th percentiles of up to 200
-  further calls timed one by one;
-* cpu_baseline: the CPU oracle (FP64, test infrastructure) timed on a bounded
-  row sample of the same workload on this host's cores.
+  around the timed calls; HBM-side bytes per call from profiles/traffic.json
+  (rocprofv3 counters recorded for this kernel source, else null); and the
+  10th/50th/90th percentiles of up to 200 further calls each bracketed by
+  its own pair of events (isolated calls: see launch_note);
+* cpu_baseline: the CPU oracle's full product (FP64, test infrastructure)
+  timed on a bounded block of rows of the same workload on this host's
+  cores, with the CPU model.
 """
 from __future__ import annotations
 
@@ -46,6 +49,17 @@ def parse():
                     help="a workload of dense_gemm_08_amd/inputs.py: WORKLOADS (FP16/BF16) or "
                          "MX_WORKLOADS (FP8 block-scaled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="before the warm-up steps, run untimed calls back to back for this many "
+                         "milliseconds: under this load the chip's power management takes tens "
+                         "of milliseconds to settle its clocks, and the calls in that window run "
+                         "up to 30%% slower than in the steady state (0: no settling)")
+    ap.add_argument("--workspace", action="store_true",
+                    help="call the workspace-passing entry point (dense_gemm_ex / "
+                         "gemm_nt_e4m3_mx_ex) with a workspace allocated once, before the "
+                         "timed region, instead of the plain entry point (which takes its "
+                         "workspace, where the call needs one, from the stream-ordered allocator "
+                         "on every call)")
     ap.add_argument("--ld-pad", type=int, default=0,
                     help="extra elements on every leading dimension (lda, ldb, ldd)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -62,8 +76,13 @@ def parse():
     ap.add_argument("--seed", type=int, default=8192)
     ap.add_argument("--ladder", action="store_true",
                     help="instead of one workload, time each optimisation-step kernel "
-                         "(gemm_nt_f16_ladder levels 1-7) on the 4096^3 FP16 workload "
+                         "(gemm_nt_f16_ladder levels 1-8) on the 4096^3 FP16 workload "
                          "(one JSON line per level)")
+    ap.add_argument("--ladder-levels", default="1,2,3,4,5,6,7,8",
+                    help="with --ladder: the levels to time, comma-separated")
+    ap.add_argument("--ladder-seconds", type=float, default=0.0,
+                    help="with --ladder: time each level over this many seconds of back-to-back "
+                         "calls (after the clock settling) instead of --steps / 5 calls")
     ap.add_argument("--mx-sweep", action="store_true",
                     help="instead of one workload, time the FP8 block-scaled product at M = 8192 "
                          "over the sweep grid (one JSON line per shape, torch._scaled_mm with "
@@ -93,13 +112,14 @@ LADDER = {
     5: "V8/V9: + 256x256 tiles (staged tiles shared by two waves each)",
     6: "library kernel: + fine-grained schedule",
     7: "V7: level 4 + a producer wave issuing every load (warp specialization)",
+    8: "level 5 with 32x32x16 MFMAs instead of 16x16x32 (MFMA shape comparison)",
 }
 
 
 def run_ladder(args):
     """Each optimisation-step kernel on the 4096^3 FP16 A @ B.T workload
-    (operands resident in HBM): warm-up, then HIP events around back-to-back
-    calls on the launch stream."""
+    (operands resident in HBM): clock settling and warm-up, then HIP events
+    around back-to-back calls on the launch stream."""
     import torch
     from dense_gemm_08_amd import binding, inputs
     lib = binding.load_library()
@@ -110,12 +130,20 @@ def run_ladder(args):
     Bd = torch.from_numpy(B.view(np.int16)).to(dev)
     Dd = torch.empty((w.M, w.N), dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
-    for level, what in LADDER.items():
+    levels = [int(x) for x in args.ladder_levels.split(",") if x]
+    for level in levels:
+        what = LADDER[level]
+
         def step():
             st = lib.gemm_nt_f16_ladder(level, w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(),
                                         w.K, Dd.data_ptr(), w.N, stream.cuda_stream)
             if st != 0:
                 raise binding.DenseGemmError(st, "gemm_nt_f16_ladder")
+        t_end = time.perf_counter() + args.settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
         for _ in range(max(3, args.warmup // 10)):
             step()
         torch.cuda.synchronize()
@@ -123,8 +151,17 @@ def run_ladder(args):
         e1 = torch.cuda.Event(enable_timing=True)
         steps = max(5, args.steps // 5)
         e0.record(stream)
-        for _ in range(steps):
-            step()
+        if args.ladder_seconds > 0:
+            steps = 0
+            t_end = time.perf_counter() + args.ladder_seconds
+            while time.perf_counter() < t_end:
+                for _ in range(20):
+                    step()
+                steps += 20
+                torch.cuda.synchronize()
+        else:
+            for _ in range(steps):
+                step()
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
@@ -257,52 +294,57 @@ def run_mx_sweep(args):
         del A, B, SA, SB, D
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_threads() -> int:
+    return int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+
+
+def _time_rows(run, M: int, target_s: float):
+    """Time ``run(n)`` (the oracle on the first n rows) on a block of rows
+    grown from 16 until one run takes at least half of target_s (or covers
+    all M rows); returns the rows and seconds of that last run."""
+    n = min(M, 16)
+    while True:
+        t0 = time.perf_counter()
+        run(n)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * target_s or n >= M:
+            return n, dt
+        n = int(min(M, max(2 * n, n * target_s / max(dt, 1e-6))))
+
+
 def cpu_baseline_mx(w, A, SA, B, SB, target_s: float):
-    """Time the oracle's block-scaled product on a bounded sample of rows."""
+    """Time the oracle's block-scaled full product on a block of rows."""
     import oracle
     N, K = w.N, w.K
-    oracle.gemm_mx_entries(A, SA, B, SB, np.zeros(64, np.int64), np.arange(64, dtype=np.int64))
-    t0 = time.perf_counter()
-    oracle.gemm_mx_entries(A, SA, B, SB, np.zeros(N, np.int64), np.arange(N, dtype=np.int64))
-    per_row = max(time.perf_counter() - t0, 1e-6)
-    nrows = int(max(1, min(w.M, target_s / per_row)))
-    rows = np.repeat(np.arange(nrows, dtype=np.int64), N)
-    cols = np.tile(np.arange(N, dtype=np.int64), nrows)
-    t0 = time.perf_counter()
-    oracle.gemm_mx_entries(A, SA, B, SB, rows, cols)
-    dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
-    return {"value": 2.0 * nrows * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
-            "sample": "%d full rows of D (%d x %d outputs, K=%d), FP64 sums of decoded E4M3 "
-                      "times E8M0 scales, %.1f s" % (nrows, nrows, N, K, dt)}
+    nrows, dt = _time_rows(lambda n: oracle.gemm_mx(A[:n], SA[:n], B, SB), w.M, target_s)
+    return {"value": 2.0 * nrows * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": _cpu_threads(),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": "the first %d rows of D (%d x %d outputs, K=%d) by oracle.gemm_mx: FP64 sums "
+                      "of decoded E4M3 times E8M0 scales, %.1f s" % (nrows, nrows, N, K, dt)}
 
 
 def cpu_baseline(w, A, B, target_s: float):
-    """Time the oracle on a bounded sample: whole rows of D (all N columns)."""
+    """Time the oracle's full product on a block of rows (all N columns)."""
     import oracle
     K, N = w.K, w.N
-    lda = K
-    ldb = K if w.layout == "nt" else N
-    oracle.gemm_entries(w.layout, w.fmt, A, B, K=K, lda=lda, ldb=ldb,
-                        rows=np.zeros(64, np.int64), cols=np.arange(64, dtype=np.int64) % N)
-    # calibrate on one row, then size the sample to the target time
-    t0 = time.perf_counter()
-    rows = np.zeros(N, np.int64)
-    cols = np.arange(N, dtype=np.int64)
-    oracle.gemm_entries(w.layout, w.fmt, A, B, K=K, lda=lda, ldb=ldb, rows=rows, cols=cols)
-    per_row = max(time.perf_counter() - t0, 1e-6)
-    nrows = int(max(1, min(w.M, target_s / per_row)))
-    rows = np.repeat(np.arange(nrows, dtype=np.int64), N)
-    cols = np.tile(np.arange(N, dtype=np.int64), nrows)
-    t0 = time.perf_counter()
-    oracle.gemm_entries(w.layout, w.fmt, A, B, K=K, lda=lda, ldb=ldb, rows=rows, cols=cols)
-    dt = time.perf_counter() - t0
+    nrows, dt = _time_rows(lambda n: oracle.gemm(w.layout, w.fmt, A[:n], B, M=n, N=N, K=K),
+                           w.M, target_s)
     flops = 2.0 * nrows * N * K
-    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": "%d full rows of D (%d x %d outputs, K=%d), FP64 accumulation, %.1f s"
-                      % (nrows, nrows, N, K, dt)}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _cpu_threads(),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": "the first %d rows of D (%d x %d outputs, K=%d) by oracle.gemm: FP64 "
+                      "accumulation, %.1f s" % (nrows, nrows, N, K, dt)}
 
 
 def main():
@@ -361,14 +403,26 @@ def main():
         SAd = torch.from_numpy(SA).to(dev)
         SBd = torch.from_numpy(SB).to(dev)
         Dd = torch.empty((w.M, ldd), dtype=torch.int16, device=dev)
-        fmt, src = "e4m3", "gemm_mx.hip"
+        fmt, src = "e4m3", "gemm_mx_kernel.h"
+        if args.workspace:
+            import ctypes
+            need = ctypes.c_size_t()
+            assert lib.gemm_nt_e4m3_mx_workspace_size(w.M, w.N, w.K, ctypes.byref(need)) == 0
+            ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
 
-        def step():
-            st = lib.gemm_nt_e4m3_mx(w.M, w.N, w.K, Ad.data_ptr(), lda, SAd.data_ptr(), nb,
-                                     Bd.data_ptr(), ldb, SBd.data_ptr(), nb, Dd.data_ptr(), ldd,
-                                     sh)
-            if st != 0:
-                raise binding.DenseGemmError(st, "gemm_nt_e4m3_mx")
+            def step():
+                st = lib.gemm_nt_e4m3_mx_ex(w.M, w.N, w.K, Ad.data_ptr(), lda, SAd.data_ptr(), nb,
+                                            Bd.data_ptr(), ldb, SBd.data_ptr(), nb, Dd.data_ptr(),
+                                            ldd, ws.data_ptr(), need.value, sh)
+                if st != 0:
+                    raise binding.DenseGemmError(st, "gemm_nt_e4m3_mx_ex")
+        else:
+            def step():
+                st = lib.gemm_nt_e4m3_mx(w.M, w.N, w.K, Ad.data_ptr(), lda, SAd.data_ptr(), nb,
+                                         Bd.data_ptr(), ldb, SBd.data_ptr(), nb, Dd.data_ptr(),
+                                         ldd, sh)
+                if st != 0:
+                    raise binding.DenseGemmError(st, "gemm_nt_e4m3_mx")
         config = {"workload": w.name, "layout": "nt", "M": w.M, "N": w.N, "K": w.K,
                   "lda": lda, "ldb": ldb, "ldd": ldd, "elements": "e4m3",
                   "scales": "e8m0 per 32 K values of a row", "out": "bf16",
@@ -387,16 +441,37 @@ def main():
         Bd = torch.zeros((B.shape[0], ldb), dtype=torch.int16, device=dev)
         Bd[:, :B.shape[1]] = torch.from_numpy(B.view(np.int16)).to(dev)
         Dd = torch.empty((w.M, ldd), dtype=torch.int16, device=dev)
-        fmt, src = w.fmt, "dense_gemm.hip"
+        fmt, src = w.fmt, "gemm_kernel.h"
+        if args.workspace:
+            need = binding.workspace_size(w.layout, w.fmt, w.M, w.N, w.K, Ad.data_ptr(), lda,
+                                          Bd.data_ptr(), ldb)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            op = binding.OPS[(w.layout, w.fmt)]
 
-        def step():
-            st = entry(w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, Dd.data_ptr(), ldd,
-                       sh)
-            if st != 0:
-                raise binding.DenseGemmError(st, "gemm")
+            def step():
+                st = lib.dense_gemm_ex(op, w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb,
+                                       Dd.data_ptr(), ldd, None, ws.data_ptr(), need, sh)
+                if st != 0:
+                    raise binding.DenseGemmError(st, "dense_gemm_ex")
+        else:
+            def step():
+                st = entry(w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, Dd.data_ptr(),
+                           ldd, sh)
+                if st != 0:
+                    raise binding.DenseGemmError(st, "gemm")
         config = {"workload": w.name, "layout": w.layout, "M": w.M, "N": w.N, "K": w.K,
                   "lda": lda, "ldb": ldb, "ldd": ldd, "dist": w.dist, "seed": w.seed}
+    config["entry"] = ("dense_gemm_ex" if src == "gemm_kernel.h" else "gemm_nt_e4m3_mx_ex") \
+        if args.workspace else ("gemm_nt_e4m3_mx" if src == "gemm_mx_kernel.h" else entry.__name__)
 
+    # untimed: let the clocks settle under this load, then the warm-up steps
+    settle_calls = 0
+    t_end = time.perf_counter() + args.settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            step()
+        settle_calls += 8
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -456,11 +531,23 @@ def main():
         "dtype": fmt,
         "data": "synthetic",
         "config": config,
+        "settle": {"ms": args.settle_ms, "calls": settle_calls,
+                   "note": "untimed calls before the warm-up steps, for the clocks to reach "
+                           "their steady state under this load"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "kernel_ms": kern_ms,
-                     "kernel_ms_p10": pct(0.1), "kernel_ms_p50": pct(0.5),
-                     "kernel_ms_p90": pct(0.9), "per_launch_samples": n_pl},
+                     "traffic": traffic,
+                     "traffic_source": "profiles/traffic.json: rocprofv3 --pmc FETCH_SIZE and "
+                                       "WRITE_SIZE of this workload, recorded for kernel source "
+                                       "%s" % source_sha(src) if traffic is not None else
+                                       "none recorded for this kernel source",
+                     "kernel_ms": kern_ms,
+                     "launch_ms_p10": pct(0.1), "launch_ms_p50": pct(0.5),
+                     "launch_ms_p90": pct(0.9), "launch_samples": n_pl,
+                     "launch_note": "calls timed one by one, each between its own pair of HIP "
+                                    "events recorded on the launch stream: the pair's own cost "
+                                    "is in every sample; kernel_ms (back-to-back calls) is what "
+                                    "achieved is computed from"},
     }
     if w.name in PAGE_TFLOPS:
         out["vs_baseline_basis"] = {"value": PAGE_TFLOPS[w.name][0], "unit": "TFLOP/s",
@@ -473,10 +560,11 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def source_sha(name: str = "dense_gemm.hip") -> str:
-    """sha256 prefix of a kernel source and the headers it shares, with
-    comments and blank space removed: the traffic figures recorded for it
-    stay valid across comment edits, not across code changes."""
+def source_sha(name: str = "gemm_kernel.h") -> str:
+    """sha256 prefix of a kernel source (gemm_kernel.h, gemm_mx_kernel.h) and
+    the headers it shares, with comments and blank space removed: the
+    traffic figures recorded for it stay valid across comment edits and
+    host-side changes, not across changes of the kernels."""
     import hashlib
     import re
     h = hashlib.sha256()

@@ -105,6 +105,15 @@ __device__ __forceinline__ void mfma16<__bf16>(f32x4& c, u32x4 a, u32x4 b) {
   asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
+// c += a-rows x b-columns over 16 k: v_mfma_f32_32x32x16_f16, the 32 x 32
+// accumulator (16 registers per lane) updated in place.  Used only by the
+// step-ladder kernel that compares this MFMA shape with 16 x 16 x 32 at the
+// same tile, loads and schedule; the same wait-state rules apply.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ void mfma32_f16(f32x16& c, u32x4 a, u32x4 b) {
+  asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
 // Round two floats to the output type (round-to-nearest-even) and pack them
 // (one v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
 typedef float f32x2 __attribute__((ext_vector_type(2)));

@@ -25,6 +25,12 @@
 //                 and run MFMAs, the stages handed over by two workgroup
 //                 barriers per step (the page's producer warp and its
 //                 full/empty barriers; numbered last to keep levels 1-6)
+//   level 8       level 5 with v_mfma_f32_32x32x16_f16 in place of the
+//                 16 x 16 x 32 MFMA (four 32 x 32 blocks per wave direction,
+//                 four 16-deep substeps per stage): the same tile, loads,
+//                 LDS layout and schedule, so the two levels differ only in
+//                 the MFMA shape (not a step of the page; the comparison
+//                 behind the library kernel's choice of 16 x 16 x 32)
 //
 // The library kernel does not specialize: with 256 x 256 tiles one wave per
 // SIMD holds 256 accumulator registers, leaving no room for a fifth wave,
@@ -56,10 +62,12 @@ struct LParams {
   int num_xcds;  // XCDs of the device (the scheduler's L2 remap)
 };
 
-template <int TILE, bool DMA, int STAGES, bool PERSIST>
+template <int TILE, bool DMA, int STAGES, bool PERSIST, int MF = 16>
 __global__ __launch_bounds__(256) void ladder_kernel(LParams p) {
+  static_assert(MF == 16 || MF == 32, "16 x 16 x 32 or 32 x 32 x 16 MFMAs");
   constexpr int W = TILE / 2;                 // wave tile (2 x 2 waves)
   constexpr int MI = W / 16, NI = W / 16;     // 16 x 16 MFMA blocks per wave
+  constexpr int MB = W / 32;                  // 32 x 32 MFMA blocks per wave and direction
   constexpr int OPB = TILE * BK * 2;          // bytes of one operand tile per stage
   constexpr int STB = 2 * OPB;                // A tile, then B tile
   constexpr int LOADS = OPB / (256 * 16);     // 16-byte loads per thread per operand
@@ -85,11 +93,21 @@ __global__ __launch_bounds__(256) void ladder_kernel(LParams p) {
     const uint16_t* a0 = p.A + (int64_t)tm * TILE * p.lda;
     const uint16_t* b0 = p.B + (int64_t)tn * TILE * p.ldb;
 
+    // (only one of the two accumulator sets is used: the compiler drops the
+    // other, MF being a template argument)
     f32x4 acc[MI][NI];
+    f32x16 acc32[MB][MB];
+    if (MF == 16) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NI; ++j) acc[i][j] = (f32x4){};
+        for (int j = 0; j < NI; ++j) acc[i][j] = (f32x4){};
+    } else {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j) acc32[i][j] = (f32x16){};
+    }
     fence();
 
     // Load i of this thread covers tile row r = (LOADS*wave + i)*8 + lane/8
@@ -125,9 +143,30 @@ __global__ __launch_bounds__(256) void ladder_kernel(LParams p) {
         }
       }
     };
-    // Two 32-deep substeps: read the wave's A and B fragments, then its MFMAs.
+    // Two 32-deep substeps (four 16-deep ones for 32 x 32 x 16 MFMAs): read
+    // the wave's A and B fragments, then its MFMAs.
     auto compute = [&](int slot) {
       const char* base = smem + slot * STB;
+      if (MF == 32) {
+        // lane l holds row l % 32 of a 32-row fragment and k = 8 (l / 32) ..
+        // +7 of the substep's 16: chunk 2 s + l / 32 of the 128-byte row
+        const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int off = (((2 * s + h) ^ swz_k(r32)) << 4);
+          u32x4 a[MB], b[MB];
+#pragma unroll
+          for (int i = 0; i < MB; ++i) a[i] = *(const u32x4*)(base + (wm * W + i * 32 + r32) * 128 + off);
+#pragma unroll
+          for (int j = 0; j < MB; ++j)
+            b[j] = *(const u32x4*)(base + OPB + (wn * W + j * 32 + r32) * 128 + off);
+#pragma unroll
+          for (int j = 0; j < MB; ++j)
+#pragma unroll
+            for (int i = 0; i < MB; ++i) mfma32_f16(acc32[i][j], b[j], a[i]);
+        }
+        return;
+      }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int off = (((4 * s + lq) ^ swz_k(l16)) << 4);
@@ -170,6 +209,26 @@ __global__ __launch_bounds__(256) void ladder_kernel(LParams p) {
     // wait states between the last MFMAs and the reads of their results
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     fence();
+    if (MF == 32) {
+      // lane l holds row l % 32 of each 32 x 32 block and, for g = 0..3, the
+      // four columns 8 g + 4 (l / 32) .. +3 in accumulators 4 g .. 4 g + 3
+      const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int row = tm * TILE + wm * W + i * 32 + r32;
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = tn * TILE + wn * W + j * 32 + 8 * g + 4 * h;
+            u32x2 v;
+            v[0] = pack2<_Float16>(acc32[i][j][4 * g], acc32[i][j][4 * g + 1]);
+            v[1] = pack2<_Float16>(acc32[i][j][4 * g + 2], acc32[i][j][4 * g + 3]);
+            *(u32x2*)(p.D + (int64_t)row * p.ldd + col) = v;
+          }
+      }
+      continue;
+    }
     // lane holds row l16 of each 16-row block and 4 consecutive columns
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -306,15 +365,15 @@ static dense_gemm_status launch_producer(const LParams& p0, int cus, hipStream_t
   return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
 
-template <int TILE, bool DMA, int STAGES, bool PERSIST>
+template <int TILE, bool DMA, int STAGES, bool PERSIST, int MF = 16>
 static dense_gemm_status launch(const LParams& p0, int cus, hipStream_t stream) {
   LParams p = p0;
   p.tiles_m = p.M / TILE;
   p.tiles_n = p.N / TILE;
   p.num_tiles = p.tiles_m * p.tiles_n;
   const int grid = PERSIST ? (p.num_tiles < cus ? p.num_tiles : cus) : p.num_tiles;
-  hipLaunchKernelGGL((ladder_kernel<TILE, DMA, STAGES, PERSIST>), dim3((unsigned)grid), dim3(256), 0,
-                     stream, p);
+  hipLaunchKernelGGL((ladder_kernel<TILE, DMA, STAGES, PERSIST, MF>), dim3((unsigned)grid), dim3(256),
+                     0, stream, p);
   return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
 
@@ -327,9 +386,9 @@ extern "C" dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N,
                                                 const void* A, int64_t lda, const void* B,
                                                 int64_t ldb, void* D, int64_t ldd,
                                                 hipStream_t stream) {
-  if (level < 1 || level > 7) return DENSE_GEMM_BAD_ARG;
+  if (level < 1 || level > 8) return DENSE_GEMM_BAD_ARG;
   if (level == 6) return gemm_nt_f16(M, N, K, A, lda, B, ldb, D, ldd, stream);
-  const int64_t tile = level == 5 ? 256 : 128;
+  const int64_t tile = level == 5 || level == 8 ? 256 : 128;
   if (M <= 0 || N <= 0 || K <= 0 || M % tile || N % tile || K % ladder::BK) return DENSE_GEMM_BAD_ARG;
   if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
     return DENSE_GEMM_BAD_ARG;
@@ -353,6 +412,7 @@ extern "C" dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N,
     case 3: return ladder::launch<128, true, 2, false>(p, cus, stream);
     case 4: return ladder::launch<128, true, 2, true>(p, cus, stream);
     case 7: return ladder::launch_producer(p, cus, stream);
+    case 8: return ladder::launch<256, true, 2, true, 32>(p, cus, stream);
     default: return ladder::launch<256, true, 2, true>(p, cus, stream);
   }
 }

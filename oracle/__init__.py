@@ -25,7 +25,8 @@ What it computes, with citations (page titles and sections):
 
 Parity status: every function here is pinned by CPU tests (exact rational
 brute force, invariants, library special cases and the worked values printed
-on the pages); none is "parity unpinned".  The FP8 encodings of gemm_mx
+on the pages), the sampled-entry path on both layouts with padded leading
+dimensions included; none is "parity unpinned".  The FP8 encodings of gemm_mx
 (element and scale formats, group size) are not on the pages: they are the
 reading stated in oracle.c, and its pins check that reading.
 """

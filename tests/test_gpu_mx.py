@@ -222,3 +222,74 @@ def test_mx_nan_scale_and_nan_element_propagate_like_the_oracle():
     ok = ~np.isnan(d)
     res = oracle.check("bf16", d[ok], s[ok], D[ok])
     assert res.ok, res
+
+
+# ------------------------------------------------ the ends of the scale range --
+
+def _check_in_fp32_range(A, SA, B, SB, D):
+    """The acceptance bound on every output whose sum of |products| S stays
+    below 2^127 (no FP32 partial sum can overflow there, in any order);
+    outputs with S >= 2^127 are exempt (an FP32 partial sum may overflow:
+    the FP32-accumulating product may return +-Inf or NaN where the FP64
+    oracle is finite) but must be non-finite or within the bound.  Returns
+    the numbers of checked, exempt and non-finite exempt outputs."""
+    d, s = oracle.gemm_mx(A, SA, B, SB)
+    inside = s < 2.0 ** 127
+    res = oracle.check("bf16", d[inside], s[inside], D[inside])
+    assert res.ok, res
+    g = D[~inside]
+    finite = np.isfinite(oracle.decode("bf16", g))
+    res = oracle.check("bf16", d[~inside][finite], s[~inside][finite], g[finite])
+    assert res.ok, res
+    return int(inside.sum()), int((~inside).sum()), int((~finite).sum())
+
+
+def _range_operands(case, M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    nb = K // 32
+    A = rng.choice(inputs.E4M3_FINITE, size=(M, K))
+    B = rng.choice(inputs.E4M3_FINITE, size=(N, K))
+    if case == "compensated":
+        # every 32-wide block of A at scale 2^t, of B at 2^-t (plus a little
+        # jitter), t from -126 to 126 over the blocks: scale codes from the
+        # ends of the E8M0 range while the products stay near 1
+        t = np.linspace(-126, 126, nb).round().astype(int)
+        SA = np.clip(127 + t[None, :] + rng.integers(-3, 4, (M, nb)), 0, 254).astype(np.uint8)
+        SB = np.clip(127 - t[None, :] + rng.integers(-3, 4, (N, nb)), 0, 254).astype(np.uint8)
+        assert SA.min() <= 3 and SA.max() >= 251 and SB.min() <= 3 and SB.max() >= 251
+        return A, SA, B, SB
+    e = {"top": 100, "bottom_normal": -140, "bottom_subnormal": -150, "bottom_zero": -254}.get(case)
+    if e is not None:
+        # every product scaled by 2^e: top, sums near 2^121; bottom, results in
+        # BF16's normal range, its subnormal range, and far below it
+        SA = np.full((M, nb), max(0, 127 + e // 2), np.uint8)
+        SB = np.full((N, nb), max(0, 127 + e - e // 2), np.uint8)
+        return A, SA, B, SB
+    SA = rng.integers(118, 137, (M, nb)).astype(np.uint8)
+    SB = rng.integers(118, 137, (N, nb)).astype(np.uint8)
+    if case == "overflow_rows":
+        SA[:16] = 254  # rows 0..15: products beyond the FP32 range
+    elif case == "cancelling_overflow":
+        # rows 0..7: two blocks of +-448 x 448 at scale 2^127 x 2^73 cancel
+        # exactly in FP64; an FP32 partial sum overflows on the way
+        A[:8, 0:32], A[:8, 32:64] = 0x7E, 0xFE
+        B[:, 0:64] = 0x7E
+        SA[:8, 0:2], SB[:, 0:2] = 254, 200
+    return A, SA, B, SB
+
+
+@pytest.mark.parametrize("case", ["compensated", "top", "bottom_normal", "bottom_subnormal",
+                                  "bottom_zero", "overflow_rows", "cancelling_overflow"])
+def test_mx_scale_range_ends(case):
+    M, N, K = 256, 272, 512
+    A, SA, B, SB = _range_operands(case, M, N, K, seed=len(case))
+    D, st = run_mx(A, SA, B, SB)
+    assert st == status().OK
+    checked, exempt, nonfinite = _check_in_fp32_range(A, SA, B, SB, D)
+    print("%s: %d outputs checked, %d exempt (%d of them non-finite)"
+          % (case, checked, exempt, nonfinite), flush=True)
+    if case in ("compensated", "top") or case.startswith("bottom"):
+        assert exempt == 0 and checked == M * N
+    else:
+        # only the rows built to overflow are exempt; the rest pass the bound
+        assert checked >= (M - 16) * N and 0 < exempt <= 16 * N
