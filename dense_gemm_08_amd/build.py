@@ -1,8 +1,10 @@
 """Build step for libdense_gemm.so (hipcc, gfx950 only).
 
-``python -m dense_gemm_08_amd.build`` compiles ``csrc/dense_gemm.hip`` (the
-library's kernels and C ABI), ``csrc/ladder.hip`` (the optimisation-step
-kernels) and ``csrc/gemm_mx.hip`` (the FP8 block-scaled product) into
+``python -m dense_gemm_08_amd.build`` compiles ``csrc/plan.cpp`` (host-side
+argument checks and launch planning, plain C++), ``csrc/dense_gemm.hip`` (the
+FP16/BF16 entry points, kernels in ``gemm_kernel.h``), ``csrc/ladder.hip``
+(the optimisation-step kernels) and ``csrc/gemm_mx.hip`` (the FP8
+block-scaled product, kernels in ``gemm_mx_kernel.h``) into
 ``dense_gemm_08_amd/libdense_gemm.so`` in place.
 """
 from __future__ import annotations
@@ -13,7 +15,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", n) for n in ("dense_gemm.hip", "ladder.hip", "gemm_mx.hip")]
+SRCS = [os.path.join(HERE, "csrc", n)
+        for n in ("plan.cpp", "dense_gemm.hip", "ladder.hip", "gemm_mx.hip")]
 OUT = os.path.join(HERE, "libdense_gemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -35,23 +35,16 @@
 #include <stdint.h>
 
 #include "cdna_ops.h"
+#include "tile_config.h"
 #include "tile_sched.h"
 
 namespace dg {
 
-enum Layout { NT = 0, NN = 1 };
-
-// ---- tile configuration -------------------------------------------------
-constexpr int BM = 256;              // tile rows (M)
-constexpr int BN = 256;              // tile columns (N); A @ B.T also has a 128-wide
-                                     // tile for outputs too narrow to fill the CUs
-constexpr int BK = 64;               // K depth of one LDS stage (128-byte rows)
+// ---- tile configuration (Layout, BM, BN, BK, WAVES, THREADS: tile_config.h)
 constexpr int SLOTS3 = 3;            // LDS ring depth of the early operand (below)
 constexpr int SLOTS2 = 2;            // LDS ring depth of the other operand
 constexpr int MK = 32;               // K depth of one MFMA (16 x 16 x 32)
 constexpr int SUB = BK / MK;         // MFMA k-substeps per stage
-constexpr int WAVES = 4;             // 2 x 2 waves
-constexpr int THREADS = WAVES * 64;
 constexpr int WTM = 128;             // wave tile rows (columns: half the tile width)
 constexpr int MI = WTM / 16;         // 16 x 16 MFMA blocks per wave, M direction
 constexpr int A_BYTES = BM * BK * 2;           // 32 KiB: 256 rows x 128 B

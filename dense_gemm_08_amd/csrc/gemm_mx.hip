@@ -33,6 +33,7 @@ static dense_gemm_status validate(int64_t M, int64_t N, int64_t K, const void* A
   if (((uintptr_t)D & 1) != 0) return DENSE_GEMM_MISALIGNED;
   if (K > 0 && ((((uintptr_t)A | (uintptr_t)B) & 15) != 0 || ((lda | ldb) & 15) != 0))
     return DENSE_GEMM_MISALIGNED;
+  if (K > 0 && (lda >= lim || ldb >= lim)) return DENSE_GEMM_TOO_LARGE;  // before the spans
   if (K > 0 && ((BM - 1) * lda + K >= lim - 16 || (BN - 1) * ldb + K >= lim - 16))
     return DENSE_GEMM_TOO_LARGE;
   if (ldd >= lim || lda >= lim || ldb >= lim || ldsa >= lim || ldsb >= lim) return DENSE_GEMM_TOO_LARGE;

@@ -396,6 +396,7 @@ extern "C" dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N,
   if (lda < K || ldb < K || ldd < N) return DENSE_GEMM_BAD_LD;
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)D) & 15 || (lda | ldb | ldd) & 7)
     return DENSE_GEMM_MISALIGNED;
+  if (lda >= ((int64_t)1 << 31) || ldb >= ((int64_t)1 << 31)) return DENSE_GEMM_TOO_LARGE;
   if (((tile - 1) * lda + K) * 2 >= ((int64_t)1 << 31) || ((tile - 1) * ldb + K) * 2 >= ((int64_t)1 << 31))
     return DENSE_GEMM_TOO_LARGE;
   // 32-bit row pitch of D and tile numbers

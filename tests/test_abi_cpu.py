@@ -98,6 +98,10 @@ def test_validate_error_codes():
     assert _v(NT, 1 << 31, 8, 8) == S.TOO_LARGE
     assert _v(NT, 8, 8, 8, lda=1 << 23) == S.TOO_LARGE
     assert _v(NN, 8, 8, 8, ldb=1 << 26) == S.TOO_LARGE
+    # leading dimensions far beyond 2^31 (the span check must not overflow)
+    assert _v(NT, 8, 8, 8, lda=(1 << 62) - 1) == S.TOO_LARGE
+    assert _v(NN, 8, 8, 8, ldb=(1 << 62) - 1) == S.TOO_LARGE
+    assert _v(NT, 8, 8, 8, ldd=(1 << 62) - 1) == S.TOO_LARGE
     # the largest accepted operand spans (one row of tiles short of 2^31 bytes;
     # tests/test_gpu_limits.py runs them) and one step beyond
     assert _v(NT, 256, 256, 4194296) == S.OK
