@@ -76,9 +76,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=8192)
     ap.add_argument("--ladder", action="store_true",
                     help="instead of one workload, time each optimisation-step kernel "
-                         "(gemm_nt_f16_ladder levels 1-8) on the 4096^3 FP16 workload "
+                         "(gemm_nt_f16_ladder levels 1-9) on the 4096^3 FP16 workload "
                          "(one JSON line per level)")
-    ap.add_argument("--ladder-levels", default="1,2,3,4,5,6,7,8",
+    ap.add_argument("--ladder-levels", default="1,2,3,4,5,6,7,8,9",
                     help="with --ladder: the levels to time, comma-separated")
     ap.add_argument("--ladder-seconds", type=float, default=0.0,
                     help="with --ladder: time each level over this many seconds of back-to-back "
@@ -113,6 +113,7 @@ LADDER = {
     6: "library kernel: + fine-grained schedule",
     7: "V7: level 4 + a producer wave issuing every load (warp specialization)",
     8: "level 5 with 32x32x16 MFMAs instead of 16x16x32 (MFMA shape comparison)",
+    9: "level 5 with eight 128x64 waves (two per SIMD) instead of four 128x128",
 }
 
 

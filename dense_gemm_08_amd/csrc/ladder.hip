@@ -31,6 +31,10 @@
 //                 LDS layout and schedule, so the two levels differ only in
 //                 the MFMA shape (not a step of the page; the comparison
 //                 behind the library kernel's choice of 16 x 16 x 32)
+//   level 9       level 5 with eight waves (two per SIMD) of 128 x 64 in
+//                 place of four of 128 x 128: while one wave of a SIMD waits
+//                 (barrier, LDS) the other can issue MFMAs, at 1.5 times the
+//                 LDS fragment reads (a comparison, not a page step)
 //
 // The library kernel does not specialize: with 256 x 256 tiles one wave per
 // SIMD holds 256 accumulator registers, leaving no room for a fifth wave,
@@ -62,20 +66,22 @@ struct LParams {
   int num_xcds;  // XCDs of the device (the scheduler's L2 remap)
 };
 
-template <int TILE, bool DMA, int STAGES, bool PERSIST, int MF = 16>
-__global__ __launch_bounds__(256) void ladder_kernel(LParams p) {
+template <int TILE, bool DMA, int STAGES, bool PERSIST, int MF = 16, int NW = 4>
+__global__ __launch_bounds__(NW * 64) void ladder_kernel(LParams p) {
   static_assert(MF == 16 || MF == 32, "16 x 16 x 32 or 32 x 32 x 16 MFMAs");
-  constexpr int W = TILE / 2;                 // wave tile (2 x 2 waves)
-  constexpr int MI = W / 16, NI = W / 16;     // 16 x 16 MFMA blocks per wave
+  static_assert(NW == 4 || (NW == 8 && MF == 16), "2 x 2 waves, or 2 x 4 with 16 x 16 x 32");
+  constexpr int W = TILE / 2;                 // wave tile rows (2 wave rows)
+  constexpr int WN = TILE / (NW / 2);         // wave tile columns (NW / 2 wave columns)
+  constexpr int MI = W / 16, NI = WN / 16;    // 16 x 16 MFMA blocks per wave
   constexpr int MB = W / 32;                  // 32 x 32 MFMA blocks per wave and direction
   constexpr int OPB = TILE * BK * 2;          // bytes of one operand tile per stage
   constexpr int STB = 2 * OPB;                // A tile, then B tile
-  constexpr int LOADS = OPB / (256 * 16);     // 16-byte loads per thread per operand
+  constexpr int LOADS = OPB / (NW * 64 * 16);  // 16-byte loads per thread per operand
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STB];
   const uint32_t lds0 = lds_addr(smem);
 
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, lq = lane >> 4;
   const int nk = p.K / BK;
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(256) void ladder_kernel(LParams p) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) a[i] = *(const u32x4*)(base + (wm * W + i * 16 + l16) * 128 + off);
 #pragma unroll
-        for (int j = 0; j < NI; ++j) b[j] = *(const u32x4*)(base + OPB + (wn * W + j * 16 + l16) * 128 + off);
+        for (int j = 0; j < NI; ++j) b[j] = *(const u32x4*)(base + OPB + (wn * WN + j * 16 + l16) * 128 + off);
 #pragma unroll
         for (int j = 0; j < NI; ++j)
 #pragma unroll
@@ -235,7 +241,7 @@ __global__ __launch_bounds__(256) void ladder_kernel(LParams p) {
       const int row = tm * TILE + wm * W + i * 16 + l16;
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const int col = tn * TILE + wn * W + j * 16 + 4 * lq;
+        const int col = tn * TILE + wn * WN + j * 16 + 4 * lq;
         u32x2 v;
         v[0] = pack2<_Float16>(acc[i][j][0], acc[i][j][1]);
         v[1] = pack2<_Float16>(acc[i][j][2], acc[i][j][3]);
@@ -365,15 +371,15 @@ static dense_gemm_status launch_producer(const LParams& p0, int cus, hipStream_t
   return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
 
-template <int TILE, bool DMA, int STAGES, bool PERSIST, int MF = 16>
+template <int TILE, bool DMA, int STAGES, bool PERSIST, int MF = 16, int NW = 4>
 static dense_gemm_status launch(const LParams& p0, int cus, hipStream_t stream) {
   LParams p = p0;
   p.tiles_m = p.M / TILE;
   p.tiles_n = p.N / TILE;
   p.num_tiles = p.tiles_m * p.tiles_n;
   const int grid = PERSIST ? (p.num_tiles < cus ? p.num_tiles : cus) : p.num_tiles;
-  hipLaunchKernelGGL((ladder_kernel<TILE, DMA, STAGES, PERSIST, MF>), dim3((unsigned)grid), dim3(256),
-                     0, stream, p);
+  hipLaunchKernelGGL((ladder_kernel<TILE, DMA, STAGES, PERSIST, MF, NW>), dim3((unsigned)grid),
+                     dim3(NW * 64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
 
@@ -386,9 +392,9 @@ extern "C" dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N,
                                                 const void* A, int64_t lda, const void* B,
                                                 int64_t ldb, void* D, int64_t ldd,
                                                 hipStream_t stream) {
-  if (level < 1 || level > 8) return DENSE_GEMM_BAD_ARG;
+  if (level < 1 || level > 9) return DENSE_GEMM_BAD_ARG;
   if (level == 6) return gemm_nt_f16(M, N, K, A, lda, B, ldb, D, ldd, stream);
-  const int64_t tile = level == 5 || level == 8 ? 256 : 128;
+  const int64_t tile = level == 5 || level >= 8 ? 256 : 128;
   if (M <= 0 || N <= 0 || K <= 0 || M % tile || N % tile || K % ladder::BK) return DENSE_GEMM_BAD_ARG;
   if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
     return DENSE_GEMM_BAD_ARG;
@@ -414,6 +420,7 @@ extern "C" dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N,
     case 4: return ladder::launch<128, true, 2, true>(p, cus, stream);
     case 7: return ladder::launch_producer(p, cus, stream);
     case 8: return ladder::launch<256, true, 2, true, 32>(p, cus, stream);
+    case 9: return ladder::launch<256, true, 2, true, 16, 8>(p, cus, stream);
     default: return ladder::launch<256, true, 2, true>(p, cus, stream);
   }
 }

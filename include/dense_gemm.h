@@ -169,11 +169,13 @@ dense_gemm_status gemm_nn_f16(int64_t M, int64_t N, int64_t K, const void* A, in
  *      waves compute (warp specialization)                        (V7)
  *   8  as 5, with v_mfma_f32_32x32x16 in place of the 16 x 16 x 32
  *      MFMA (a comparison of the two MFMA shapes, not a page step)
- * Levels 1-5, 7 and 8 take only shapes that divide their tile: M and N
- * multiples of 128 (256 for levels 5 and 8), K a positive multiple of 64,
- * A, B and D 16-byte aligned with lda, ldb and ldd multiples of 8
+ *   9  as 5, with eight waves of 128 x 64 (two per SIMD) in place of
+ *      four of 128 x 128 (a comparison, not a page step)
+ * Levels 1-5 and 7-9 take only shapes that divide their tile: M and N
+ * multiples of 128 (256 for levels 5, 8 and 9), K a positive multiple of
+ * 64, A, B and D 16-byte aligned with lda, ldb and ldd multiples of 8
  * (DENSE_GEMM_BAD_ARG, _BAD_LD, _MISALIGNED or _TOO_LARGE otherwise; a
- * level outside 1..8 is DENSE_GEMM_BAD_ARG).  Same ownership, stream and error rules as the
+ * level outside 1..9 is DENSE_GEMM_BAD_ARG).  Same ownership, stream and error rules as the
  * entry points above; the FP32 accumulation order differs between levels,
  * so results agree within the rounding bound, not bit for bit. */
 dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N, int64_t K, const void* A,

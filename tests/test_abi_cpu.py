@@ -325,9 +325,10 @@ def test_ladder_argument_checks_on_the_host():
         return S(fn(level, a["M"], a["N"], a["K"], a["A"], a["lda"], a["B"], a["ldb"], a["D"],
                     a["ldd"], None))
 
-    assert lad(0) == S.BAD_ARG and lad(9) == S.BAD_ARG
+    assert lad(0) == S.BAD_ARG and lad(10) == S.BAD_ARG
     assert lad(5, M=384) == S.BAD_ARG          # level 5 tiles are 256 x 256
     assert lad(8, N=384) == S.BAD_ARG          # so are level 8's
+    assert lad(9, M=384) == S.BAD_ARG          # and level 9's
     assert lad(1, K=100) == S.BAD_ARG          # K a multiple of 64
     assert lad(1, M=1 << 31) == S.BAD_ARG
     assert lad(1, D=0) == S.NULL_PTR

@@ -489,7 +489,7 @@ def test_python_binding_row_and_column_views():
 
 # ----------------------------------------------- optimisation-step kernels --
 
-LEVELS = [1, 2, 3, 4, 5, 6, 7, 8]
+LEVELS = [1, 2, 3, 4, 5, 6, 7, 8, 9]
 
 
 @pytest.mark.parametrize("level", LEVELS)
@@ -546,7 +546,7 @@ def test_ladder_rejects_shapes():
     s = _gpu.torch().cuda.current_stream().cuda_stream
     p = A.data_ptr()
     assert Sx(fn(0, 256, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
-    assert Sx(fn(9, 256, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
+    assert Sx(fn(10, 256, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
     assert Sx(fn(8, 384, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
     assert Sx(fn(7, 384, 200, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
     assert Sx(fn(5, 384, 256, 64, p, 512, p, 512, D.data_ptr(), 512, s)) == Sx.BAD_ARG
