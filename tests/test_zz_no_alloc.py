@@ -67,3 +67,48 @@ def test_noalloc_rejects_a_call_beyond_its_scratch():
     assert _gpu.call("nt", "f16", M, N, K, Ad, K, Bd, K, D, N) == S.OK
     t.cuda.synchronize()
     assert (_gpu.from_dev(D) == 0).all()
+
+
+def test_noalloc_call_captured_in_a_graph():
+    # the callers this entry point is for: a HIP graph captured once and
+    # replayed.  One tile in 16 K parts (two kernels, the split partials in
+    # the fixed scratch), captured, then replayed three times with new
+    # operands copied in eagerly between replays; every replay must give
+    # the plain entry point's bits for its operands
+    t = _gpu.torch()
+    M, N, K = 128, 128, 4096
+    w = inputs.WORKLOADS["k_loop"]
+    Ad = t.empty((M, K), dtype=t.int16, device="cuda")
+    Bd = t.empty((N, K), dtype=t.int16, device="cuda")
+    D = t.empty((M, N), dtype=t.int16, device="cuda")
+    A0, B0 = inputs.make_operands(w, seed=900, M=M, N=N, K=K)
+    Ad.copy_(t.from_numpy(A0.view(np.int16)))
+    Bd.copy_(t.from_numpy(B0.view(np.int16)))
+    t.cuda.synchronize()
+    fn = binding.raw("gemm_nt_f16_noalloc")
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(s):  # one eager call first (sets up the scratch address)
+        assert S(fn(M, N, K, Ad.data_ptr(), K, Bd.data_ptr(), K, D.data_ptr(), N,
+                    s.cuda_stream)) == S.OK
+    t.cuda.current_stream().wait_stream(s)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g, stream=s):
+        st = fn(M, N, K, Ad.data_ptr(), K, Bd.data_ptr(), K, D.data_ptr(), N, s.cuda_stream)
+    assert S(st) == S.OK
+    for rep in range(3):
+        A, B = inputs.make_operands(w, seed=901 + rep, M=M, N=N, K=K)
+        Ad.copy_(t.from_numpy(A.view(np.int16)))
+        Bd.copy_(t.from_numpy(B.view(np.int16)))
+        D.fill_(-1)
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        got = _gpu.from_dev(D)
+        Dp = _gpu.empty_out(M, N)
+        assert _gpu.call("nt", "f16", M, N, K, Ad, K, Bd, K, Dp, N) == S.OK
+        t.cuda.synchronize()
+        assert (got == _gpu.from_dev(Dp)).all(), rep
+        d, s_ = oracle.gemm("nt", "f16", A, B)
+        assert oracle.check("f16", d, s_, got).ok, rep
