@@ -222,10 +222,24 @@ dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const v
   cp->b_direct = K == 0 || (((uintptr_t)B & 15) == 0 && (ldb & 7) == 0 &&
                             (layout == NT ? (K & 7) == 0 : (N & 7) == 0));
   const int64_t b_rows = layout == NT ? N : K, b_dcols = layout == NT ? K8 : N8;
-  auto round256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  cp->a_bytes = cp->a_direct ? 0 : round256((size_t)M * K8 * 2);
-  cp->b_bytes = cp->b_direct ? 0 : round256((size_t)b_rows * b_dcols * 2);
-  cp->split_bytes = plan[8] > 1 ? (size_t)plan[8] * cp->split_tiles * BM * plan[1] * sizeof(float) : 0;
+  // sizes in bytes, checked for overflow (a forced split of a huge product
+  // could exceed 2^64 bytes): such a plan is TOO_LARGE
+  const size_t cap = (size_t)1 << 62;
+  auto bytes_of = [&](size_t a, size_t b, size_t c, size_t* out) {
+    size_t ab, abc;
+    if (__builtin_mul_overflow(a, b, &ab) || __builtin_mul_overflow(ab, c, &abc) || abc > cap)
+      return false;
+    *out = (abc + 255) & ~(size_t)255;
+    return true;
+  };
+  cp->a_bytes = cp->b_bytes = cp->split_bytes = 0;
+  if (!cp->a_direct && !bytes_of((size_t)M, (size_t)K8, 2, &cp->a_bytes)) return DENSE_GEMM_TOO_LARGE;
+  if (!cp->b_direct && !bytes_of((size_t)b_rows, (size_t)b_dcols, 2, &cp->b_bytes))
+    return DENSE_GEMM_TOO_LARGE;
+  if (plan[8] > 1 && !bytes_of((size_t)plan[8] * (size_t)cp->split_tiles, (size_t)BM * plan[1],
+                               sizeof(float), &cp->split_bytes))
+    return DENSE_GEMM_TOO_LARGE;
+  if (cp->a_bytes + cp->b_bytes + cp->split_bytes > cap) return DENSE_GEMM_TOO_LARGE;
   return DENSE_GEMM_OK;
 }
 

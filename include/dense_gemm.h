@@ -128,7 +128,11 @@ typedef enum dense_gemm_op {
  * operation; both stay within the rounding bound.
  *   split_k  0: the library's choice; 1: no split; n > 1: every tile's K
  *            steps in min(n, steps) parts of equal length (the last shorter)
- *   tile_n   0: the library's choice; 256; or 128 (D = A @ B.T only) */
+ *   tile_n   0: the library's choice; 256; or 128 (D = A @ B.T only).  A
+ *            width other than the library's own drops its split-K choice
+ *            (made for its width): split_k 0 then means no split.
+ * A forced split whose partial tiles would exceed 2^62 bytes of workspace
+ * returns DENSE_GEMM_TOO_LARGE. */
 typedef struct dense_gemm_options {
   int32_t split_k;
   int32_t tile_n;
