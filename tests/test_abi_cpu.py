@@ -393,9 +393,10 @@ def test_workspace_size_follows_the_options():
     assert S(lib.dense_gemm_workspace_size(0, 8, 8, 8, 256, 8, 256, 8, 256, None,
                                            None)) == S.BAD_ARG
     # a forced split whose partial tiles would pass 2^62 bytes: TOO_LARGE, not
-    # a wrapped size (2^30 tiles x 2^15 parts x 256 KiB = 2^63 bytes)
-    assert _ws("nt", "f16", 1 << 23, 1 << 23, 1 << 21, opts=(1 << 15, 0))[0] == S.TOO_LARGE
-    assert _ws("nt", "f16", 1 << 23, 1 << 23, 1 << 21) == (S.OK, 0)
+    # a wrapped size (about 2^30 tiles x 2^15 parts x 256 KiB = 2^63 bytes)
+    big = (1 << 23, (1 << 23) - 256, 1 << 21)
+    assert _ws("nt", "f16", *big, opts=(1 << 15, 0))[0] == S.TOO_LARGE
+    assert _ws("nt", "f16", *big) == (S.OK, 0)
     # the argument check comes first
     assert _ws("nt", "f16", -1, 8, 8)[0] == S.INVALID_DIM
     assert _ws("nt", "f16", 8, 8, 16, lda=8)[0] == S.BAD_LD
