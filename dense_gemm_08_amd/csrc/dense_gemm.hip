@@ -1,9 +1,11 @@
 // dense_gemm.hip -- host side of the FP16/BF16 tiled GEMM for the MI355X
-// (gfx950): argument checks, the launch plan, workspaces and the C ABI.
+// (gfx950): device properties, workspaces, the launches and the C ABI entry
+// points.  The argument checks and the launch plan are in plan.cpp, the
+// kernels in gemm_kernel.h.
 //
 // The operation (D = A @ B.T in FP16, D = A @ B in BF16, FP32 accumulation,
 // one rounding to the output type) is defined in include/dense_gemm.h with
-// its citations; the kernels are in gemm_kernel.h.
+// its citations.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -16,8 +18,6 @@
 #include "plan.h"
 
 namespace dg {
-
-// ---- host side ----------------------------------------------------------
 
 // Workgroups of a repack launch (capped; the kernel strides over the rest).
 static unsigned repack_blocks(int64_t chunks) {

@@ -170,8 +170,8 @@ bool valid_op(int op) { return op >= DENSE_GEMM_NT_F16 && op <= DENSE_GEMM_NN_F1
 int op_layout(int op) { return op == DENSE_GEMM_NN_BF16 || op == DENSE_GEMM_NN_F16 ? NN : NT; }
 
 dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const void* A,
-                                   int64_t lda, const void* B, int64_t ldb, int64_t cus,
-                                   const dense_gemm_options* opt, CallPlan* cp) {
+                            int64_t lda, const void* B, int64_t ldb, int64_t cus,
+                            const dense_gemm_options* opt, CallPlan* cp) {
   int64_t* plan = cp->plan;
   dense_gemm_status st = dense_gemm_plan(layout, M, N, K, cus, plan);
   if (st != DENSE_GEMM_OK) return st;
