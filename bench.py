@@ -562,14 +562,16 @@ def main():
 
 
 def source_sha(name: str = "gemm_kernel.h") -> str:
-    """sha256 prefix of a kernel source (gemm_kernel.h, gemm_mx_kernel.h) and
-    the headers it shares, with comments and blank space removed: the
-    traffic figures recorded for it stay valid across comment edits and
-    host-side changes, not across changes of the kernels."""
+    """sha256 prefix of a kernel source (gemm_kernel.h, gemm_mx_kernel.h), the
+    headers it shares and the launch planning (plan.cpp), with comments and
+    blank space removed: the traffic figures recorded for it stay valid
+    across comment edits and other host-side changes, not across changes of
+    the kernels or of which kernels a call runs."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in (name, "cdna_ops.h", "tile_sched.h"):
+    # (plan.cpp decides the tile widths and splits, i.e. which kernels run)
+    for f in (name, "cdna_ops.h", "tile_sched.h", "tile_config.h", "plan.cpp"):
         with open(os.path.join(ROOT, "dense_gemm_08_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)

@@ -50,11 +50,13 @@
  * tiles are computed whole in the same launch.  dense_gemm_ex can force a
  * number of parts, or none (dense_gemm_options).
  *
- * Tile width.  Output tiles are 256 x 256.  For D = A @ B.T whose 256-wide
- * tiles would occupy at most half the CUs, with N > 128 and operands of at
- * most 192 MiB, they are 256 x 128 instead (twice the tiles, one wave).
- * Either width sums each output in the same order, so results are identical.
- * dense_gemm_ex can force the width of A @ B.T.
+ * Tile width.  Output tiles are 256 x 256.  For D = A @ B.T they are
+ * 256 x 128 instead when N <= 128 (one tile column either way, half the
+ * work of a half-empty 256-wide tile), or when 256-wide tiles would occupy
+ * at most half the CUs and the operands take at most 192 MiB (twice the
+ * tiles, one wave).  Either width sums each output in the same order, so
+ * unsplit results are identical.  dense_gemm_ex can force the width of
+ * A @ B.T.
  *
  * Workspace.  A call that repacks an operand or splits K needs device
  * memory beyond A, B and D: dense_gemm_workspace_size gives the amount.

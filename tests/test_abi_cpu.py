@@ -300,10 +300,14 @@ def test_plan_tile_width():
                              (1000, 130, 712, 2)]:
         assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK
         assert (out[1], out[4]) == (128, tiles_n), (M, N, K)
-    # wider outputs, N <= 128, A.B, and operands beyond 192 MiB keep 256-wide
-    # tiles
+    # A.B^T at most 128 wide: one 128-wide tile column, whatever the size
+    for M, N, K in [(128, 128, 64), (128, 128, 4096), (8192, 128, 8192), (8192, 64, 16384),
+                    (65536, 1, 4096)]:
+        assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK
+        assert (out[1], out[4]) == (128, 1), (M, N, K)
+    # wider outputs, A.B, and operands beyond 192 MiB keep 256-wide tiles
     for layout, M, N, K in [(NT, 8192, 2048, 1024), (NT, 4096, 4096, 4096), (NT, 3000, 5000, 4000),
-                            (NT, 128, 128, 4096), (NN, 8192, 1024, 2048), (NT, 8192, 1024, 16384)]:
+                            (NN, 128, 128, 4096), (NN, 8192, 1024, 2048), (NT, 8192, 1024, 16384)]:
         assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
         assert out[1] == 256, (layout, M, N, K)
     # one wave either way: 128-wide tiles never exceed the CUs
@@ -360,8 +364,8 @@ def test_workspace_size_of_the_workloads():
     assert _ws("nn", "bf16", 8192, 17408, 5120) == (S.OK, 0)
     assert _ws("nt", "f16", 3000, 5000, 4000) == (S.OK, 0)
     assert _ws("nt", "f16", 128, 128, 64) == (S.OK, 0)
-    # one 256 x 256 tile, 64 K steps in 16 parts: 16 FP32 partial tiles
-    assert _ws("nt", "f16", 128, 128, 4096) == (S.OK, 16 * 256 * 256 * 4)
+    # one 256 x 128 tile, 64 K steps in 16 parts: 16 FP32 partial tiles
+    assert _ws("nt", "f16", 128, 128, 4096) == (S.OK, 16 * 256 * 128 * 4)
     # K not a multiple of 8: both operands repacked with rows of K8 = 4096
     assert _ws("nt", "f16", 4096, 4096, 4095) == (S.OK, 2 * 4096 * 4096 * 2)
     # a misaligned pointer repacks that operand only

@@ -28,7 +28,7 @@ def _noalloc(M, N, K, A, lda, B, ldb, D, ldd):
 CASES = [
     # (M, N, K, lda, what takes the scratch): a larger call, then a smaller one
     (4252, 4088, 1000, 1000, "the last wave's 16 tiles in 4 K parts (16 MiB of partials)"),
-    (128, 128, 4096, 4096, "one tile in 16 K parts (4 MiB of partials)"),
+    (128, 128, 4096, 4096, "one tile in 16 K parts (2 MiB of partials)"),
     (300, 264, 1000, 1001, "A repacked (odd leading dimension)"),
 ]
 
