@@ -83,8 +83,9 @@ struct Frags {
 };
 
 // Tile width TN: 256 (four 128 x 128 wave tiles), or for A @ B.T 128 (four
-// 128 x 64 wave tiles: twice the tiles where 256-wide ones would leave half
-// the CUs idle, at more operand traffic per FLOP).
+// 128 x 64 wave tiles): for outputs at most 128 wide (half the work of a
+// half-padded 256-wide tile), and for twice the tiles where 256-wide ones
+// would leave half the CUs idle, at more operand traffic per FLOP.
 template <typename T, int LAYOUT, bool SPLIT, int TN>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
   static_assert(TN == BN || (TN == BN / 2 && LAYOUT == NT), "tile widths 256, and 128 for A @ B.T");
