@@ -73,6 +73,10 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of one workload, time D = A @ B.T (FP16) at M = 8192 over a grid "
                          "of N and K (one JSON line per shape, torch.mm timed beside it)")
+    ap.add_argument("--small-m-sweep", action="store_true",
+                    help="instead of one workload, time D = A @ B.T (FP16) at small M (1 to 512) "
+                         "against N, K of 4096 to 16384, torch.mm timed beside it (shapes outside "
+                         "the pages' workloads: where the 256-row tile computes mostly padding)")
     ap.add_argument("--seed", type=int, default=8192)
     ap.add_argument("--ladder", action="store_true",
                     help="instead of one workload, time each optimisation-step kernel "
@@ -171,7 +175,11 @@ def run_ladder(args):
                           "tflops": round(w.flops / ms / 1e9, 1)}), flush=True)
 
 
-def run_sweep(args):
+SMALL_M = [(m, n, k) for m in (1, 16, 64, 128, 256, 512)
+           for n, k in ((4096, 4096), (8192, 8192), (16384, 4096))]
+
+
+def run_sweep(args, shapes=None):
     """Per shape: N(0,1)/8 FP16 operands from torch's seeded device generator
     (timing only; tests check these shapes against the oracle on sampled
     entries), warm-up, then HIP events around about 50 ms of back-to-back
@@ -196,7 +204,7 @@ def run_sweep(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    for M, N, K in sweep_shapes():
+    for M, N, K in (shapes or sweep_shapes()):
         A = (torch.randn(M, K, device=dev, generator=gen) * 0.125).half()
         B = (torch.randn(N, K, device=dev, generator=gen) * 0.125).half()
         D = torch.empty(M, N, dtype=torch.half, device=dev)
@@ -215,10 +223,13 @@ def run_sweep(args):
 
         ms = timed(ours, steps, max(3, steps // 4))
         ms_ref = timed(ref, steps, max(3, steps // 4))
+        nbytes = 2.0 * (M * K + N * K + M * N)  # A, B and D once
         print(json.dumps({"mode": "sweep", "M": M, "N": N, "K": K, "steps": steps,
                           "kernel_ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
+                          "alg_tb_s": round(nbytes / ms / 1e9, 3),
                           "torch_mm_ms": round(ms_ref, 5),
-                          "torch_mm_tflops": round(flops / ms_ref / 1e9, 1)}), flush=True)
+                          "torch_mm_tflops": round(flops / ms_ref / 1e9, 1),
+                          "torch_mm_alg_tb_s": round(nbytes / ms_ref / 1e9, 3)}), flush=True)
         del A, B, D, Dt
 
 
@@ -360,6 +371,9 @@ def main():
 
     if args.sweep:
         run_sweep(args)
+        return
+    if args.small_m_sweep:
+        run_sweep(args, SMALL_M)
         return
     if args.ladder:
         run_ladder(args)

@@ -135,7 +135,9 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
   //     of 0.01 us): a K step of a 256-wide tile 105 (128-wide: 70), a split
   //     call's fixed cost (the reduce launch, the workspace) 1200 plus 12 per
   //     256-wide partial tile (6 per 128-wide one) for its FP32 write and
-  //     read back.
+  //     read back.  A partial tile writes and the reduction reads only its
+  //     16-row blocks inside D, so with one tile row (M < 256) that last
+  //     term shrinks to its share of those blocks.
   //   * After full waves: split when the last wave would leave at least
   //     three quarters of the CUs idle (measured: splitting a half-full last
   //     wave gains nothing), into as many parts as fit.
@@ -146,11 +148,13 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
     const int64_t by_cus = num_cus / rem, by_k = nk / 4;
     const int64_t most = by_cus < by_k ? by_cus : by_k;
     if (tasks < num_cus) {
-      const int64_t step_cost = tw == BN ? 105 : 70, part_cost = tw == BN ? 12 : 6;
+      // (in 1/16 of the units above: the partial tiles' share of 16-row blocks)
+      const int64_t step_cost = 16 * (tw == BN ? 105 : 70), part_cost = tw == BN ? 12 : 6;
+      const int64_t blocks16 = tiles_m == 1 ? (M + 15) / 16 : BM / 16;
       int64_t best = nk * step_cost;
       for (int64_t sp = 2; sp <= most; ++sp) {
         const int64_t st = (nk + sp - 1) / sp, parts = (nk + st - 1) / st;
-        const int64_t t = st * step_cost + 1200 + part_cost * parts * rem;
+        const int64_t t = st * step_cost + 16 * 1200 + part_cost * blocks16 * parts * rem;
         if (t < best) {
           best = t;
           steps = st;

@@ -307,10 +307,13 @@ dense_gemm_status dense_gemm_tile_of_task(int64_t task, int64_t tiles_m, int64_t
  * tiles < num_cus), with K spanning at least 8 steps, at most one part per
  * CU (r * parts <= num_cus) and at least 4 steps per part.  When tiles <
  * num_cus the number of parts p minimises the estimate (in 0.01 us)
- * ceil(steps / p) * 105 + 1200 + 12 * p * r against steps * 105 unsplit (a
- * model fitted to times measured on the MI355X); when tiles > num_cus the
- * last wave is split, into as many parts as fit, only if 4 r <= num_cus.
- * The grid is then r * parts when tiles < num_cus, else num_cus. */
+ * ceil(steps / p) * 105 + 1200 + 12 * f * p * r against steps * 105
+ * unsplit, for 256-wide tiles (70 and 6 for 128-wide ones), with f the
+ * share of a tile's 16-row blocks inside D (ceil(M / 16) / 16 when M < 256,
+ * else 1: partial tiles skip the blocks outside D) -- a model fitted to
+ * times measured on the MI355X; when tiles > num_cus the last wave is
+ * split, into as many parts as fit, only if 4 r <= num_cus.  The grid is
+ * then r * parts when tiles < num_cus, else num_cus. */
 dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K,
                                   int64_t num_cus, int64_t* out);
 

@@ -251,6 +251,13 @@ def test_plan_split_k():
     # 32 x 17 = 544 tiles = 2 waves + 32: 8 parts of 8 steps
     assert lib.dense_gemm_plan(NT, 8192, 4224, 4096, 256, out) == S.OK
     assert (out[8], out[9], out[5]) == (8, 8, 256)
+    # one row of tiles (M < 256): partial tiles write only their rows inside D,
+    # so the split pays sooner: 128 narrow tiles of 1 x 16384 x 4096 in 2 parts
+    assert lib.dense_gemm_plan(NT, 1, 16384, 4096, 256, out) == S.OK
+    assert (out[1], out[4], out[8], out[9], out[5]) == (128, 128, 2, 32, 256)
+    # ... which a full tile row would not pay for (256 rows x 128 tiles)
+    assert lib.dense_gemm_plan(NT, 256, 16384, 4096, 256, out) == S.OK
+    assert out[8] == 1
     # every part covers whole steps and the parts cover K exactly once
     for M, N, K in [(600, 520, 712), (128, 128, 4000), (1000, 1000, 8192), (256, 256, 5120)]:
         assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK
