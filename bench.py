@@ -87,6 +87,13 @@ def parse():
     ap.add_argument("--ladder-seconds", type=float, default=0.0,
                     help="with --ladder: time each level over this many seconds of back-to-back "
                          "calls (after the clock settling) instead of --steps / 5 calls")
+    ap.add_argument("--wave-fill", action="store_true",
+                    help="instead of one workload, time D = A @ B.T (FP16) at M = 256 t, N = K = "
+                         "4096 for t = 8 ... 16 (128 to 256 tiles of 256 x 256 on the chip's "
+                         "256 CUs, one tile each, no split), each for --fill-seconds after the "
+                         "clock settling: how the call time follows the number of busy CUs")
+    ap.add_argument("--fill-seconds", type=float, default=4.0,
+                    help="with --wave-fill: seconds of back-to-back calls timed per shape")
     ap.add_argument("--mx-sweep", action="store_true",
                     help="instead of one workload, time the FP8 block-scaled product at M = 8192 "
                          "over the sweep grid (one JSON line per shape, torch._scaled_mm with "
@@ -231,6 +238,75 @@ def run_sweep(args, shapes=None):
                           "torch_mm_tflops": round(flops / ms_ref / 1e9, 1),
                           "torch_mm_alg_tb_s": round(nbytes / ms_ref / 1e9, 3)}), flush=True)
         del A, B, D, Dt
+
+
+WAVE_FILL = [8, 10, 12, 14, 15, 16]
+
+
+def run_wave_fill(args):
+    """Products with 128 ... 256 tiles of 256 x 256 (one per CU at most) and
+    the same K, through dense_gemm_ex with the tile width and the split fixed
+    (256 wide, no split), so that only the number of busy CUs changes.  Per
+    shape: the clock settling, then HIP events around --fill-seconds of
+    back-to-back calls.  Under the board's power limit, a call time that
+    falls in proportion to the tiles means the idle CUs' power goes to the
+    busy ones; a flat one, that the idle CUs are lost."""
+    import ctypes
+    import torch
+    from dense_gemm_08_amd import binding
+    lib = binding.load_library()
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    stream = torch.cuda.current_stream()
+    opts = binding.Options(1, 256)
+    N = K = 4096
+    B = (torch.randn(N, K, device=dev, generator=gen) * 0.125).half()
+    A_all = (torch.randn(256 * max(WAVE_FILL), K, device=dev, generator=gen) * 0.125).half()
+    D = torch.empty(256 * max(WAVE_FILL), N, dtype=torch.half, device=dev)
+    rows = []
+    for t in WAVE_FILL:
+        M = 256 * t
+        need = binding.workspace_size("nt", "f16", M, N, K, A_all.data_ptr(), K, B.data_ptr(), K,
+                                      opts)
+        if need:
+            raise RuntimeError("the wave-fill shapes need no workspace, got %d bytes" % need)
+
+        def step():
+            st = lib.dense_gemm_ex(binding.OPS[("nt", "f16")], M, N, K, A_all.data_ptr(), K,
+                                   B.data_ptr(), K, D.data_ptr(), N, ctypes.byref(opts),
+                                   None, 0, stream.cuda_stream)
+            if st != 0:
+                raise binding.DenseGemmError(st, "dense_gemm_ex")
+        t_end = time.perf_counter() + args.settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        steps = 0
+        e0.record(stream)
+        t_end = time.perf_counter() + args.fill_seconds
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                step()
+            steps += 20
+            torch.cuda.synchronize()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        rows.append((t, ms))
+        flops = 2.0 * M * N * K
+        print(json.dumps({"mode": "wave_fill", "M": M, "N": N, "K": K, "tiles": 16 * t,
+                          "steps": steps, "kernel_ms": round(ms, 5),
+                          "tflops": round(flops / ms / 1e9, 1)}), flush=True)
+    full = dict(rows).get(16)
+    if full:
+        for t, ms in rows:
+            print(json.dumps({"mode": "wave_fill_ratio", "tiles": 16 * t,
+                              "time_over_full": round(ms / full, 4),
+                              "tiles_over_full": round(t / 16, 4)}), flush=True)
 
 
 def _event_timer(stream):
@@ -380,6 +456,9 @@ def main():
         return
     if args.mx_sweep:
         run_mx_sweep(args)
+        return
+    if args.wave_fill:
+        run_wave_fill(args)
         return
 
     if args.copy_mib:
