@@ -60,6 +60,13 @@ def parse():
                          "timed region, instead of the plain entry point (which takes its "
                          "workspace, where the call needs one, from the stream-ordered allocator "
                          "on every call)")
+    ap.add_argument("--split-k", type=int, default=0,
+                    help="with --workspace (FP16/BF16 workloads): the plan override "
+                         "dense_gemm_options.split_k (0: the library's choice, 1: no split, "
+                         "n: n parts)")
+    ap.add_argument("--tile-n", type=int, default=0,
+                    help="with --workspace (FP16/BF16 workloads): the plan override "
+                         "dense_gemm_options.tile_n (0: the library's choice, 128 or 256)")
     ap.add_argument("--ld-pad", type=int, default=0,
                     help="extra elements on every leading dimension (lda, ldb, ldd)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -442,6 +449,9 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    if (args.split_k or args.tile_n) and not args.workspace:
+        raise SystemExit("--split-k and --tile-n are options of dense_gemm_ex: add --workspace")
+
     import torch
     from dense_gemm_08_amd import binding, inputs
 
@@ -537,14 +547,17 @@ def main():
         Dd = torch.empty((w.M, ldd), dtype=torch.int16, device=dev)
         fmt, src = w.fmt, "gemm_kernel.h"
         if args.workspace:
+            import ctypes
+            opts = binding.Options(args.split_k, args.tile_n)
             need = binding.workspace_size(w.layout, w.fmt, w.M, w.N, w.K, Ad.data_ptr(), lda,
-                                          Bd.data_ptr(), ldb)
+                                          Bd.data_ptr(), ldb, opts)
             ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
             op = binding.OPS[(w.layout, w.fmt)]
 
             def step():
                 st = lib.dense_gemm_ex(op, w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb,
-                                       Dd.data_ptr(), ldd, None, ws.data_ptr(), need, sh)
+                                       Dd.data_ptr(), ldd, ctypes.byref(opts), ws.data_ptr(),
+                                       need, sh)
                 if st != 0:
                     raise binding.DenseGemmError(st, "dense_gemm_ex")
         else:
@@ -555,6 +568,8 @@ def main():
                     raise binding.DenseGemmError(st, "gemm")
         config = {"workload": w.name, "layout": w.layout, "M": w.M, "N": w.N, "K": w.K,
                   "lda": lda, "ldb": ldb, "ldd": ldd, "dist": w.dist, "seed": w.seed}
+        if args.split_k or args.tile_n:
+            config["options"] = {"split_k": args.split_k, "tile_n": args.tile_n}
     config["entry"] = ("dense_gemm_ex" if src == "gemm_kernel.h" else "gemm_nt_e4m3_mx_ex") \
         if args.workspace else ("gemm_nt_e4m3_mx" if src == "gemm_mx_kernel.h" else entry.__name__)
 

@@ -122,8 +122,14 @@ static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A,
     // whole tiles, then the parts of the split tiles writing FP32 partials,
     // summed by a second kernel
     hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true, TN>), dim3(grid), dim3(THREADS), 0, stream, p);
-    hipLaunchKernelGGL((split_reduce<T, TN>), dim3((unsigned)(p.tiles * (TN / 8))), dim3(256), 0,
-                       stream, p);
+    // (one-wave workgroups where 256-thread ones would not cover the CUs)
+    const int64_t wide = p.tiles * (int64_t)reduce_blocks_per_tile<TN, 256>();
+    if (wide < info.cus)
+      hipLaunchKernelGGL((split_reduce<T, TN, 64>),
+                         dim3((unsigned)(p.tiles * reduce_blocks_per_tile<TN, 64>())), dim3(64), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((split_reduce<T, TN, 256>), dim3((unsigned)wide), dim3(256), 0, stream, p);
   } else {
     hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false, TN>), dim3(grid), dim3(THREADS), 0, stream,
                        p);

@@ -488,14 +488,21 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
 
 // Sum of the split-K partials of every output element of the split tiles in
 // part order 0, 1, ... (a fixed order: results are reproducible), rounded
-// once to the output type.  One thread per 8 consecutive columns of a row:
-// a workgroup covers 256 / (TN / 8) rows, BM * TN / 2048 workgroups a split
-// tile.
-template <typename T, int TN>
-__global__ __launch_bounds__(256) void split_reduce(Params p) {
-  constexpr int TPR = TN / 8;           // threads per row
-  constexpr int RPW = 256 / TPR;        // rows per workgroup
-  constexpr int WPT = BM / RPW;         // workgroups per split tile
+// once to the output type.  One thread per 8 consecutive columns of a row,
+// RT threads per workgroup: a workgroup covers RT / (TN / 8) rows, a split
+// tile BM * TN / (8 RT) workgroups.  The host takes RT = 64 (one wave) when
+// 256-thread workgroups would be fewer than the CUs, so that the partials'
+// reads spread over more CUs (measured with 16 parts of one 128 x 128
+// output: 3.1 against 3.6 us), and RT = 256 otherwise (one-wave workgroups
+// measured up to 1% slower on the split products of the M = 8192 sweep).
+template <int TN, int RT>
+constexpr int reduce_blocks_per_tile() { return BM * TN / (8 * RT); }
+template <typename T, int TN, int RT>
+__global__ __launch_bounds__(RT) void split_reduce(Params p) {
+  constexpr int TPR = TN / 8;      // threads per row
+  constexpr int RPW = RT / TPR;    // rows per workgroup
+  constexpr int WPT = BM / RPW;    // workgroups per split tile
+  static_assert(RT % TPR == 0 && WPT == reduce_blocks_per_tile<TN, RT>(), "whole rows per workgroup");
   const int st = blockIdx.x / WPT;      // split tile (0 .. tiles-1)
   int tm, tn;
   tile_of_task(p.full_tasks + st, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
@@ -509,8 +516,10 @@ __global__ __launch_bounds__(256) void split_reduce(Params p) {
   float s[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.0f;
-  // eight splits' loads in flight at once, then added in split order
-  constexpr int U = 8;
+  // U splits' loads in flight at once, then added in split order: 16 for the
+  // few one-wave workgroups, 8 (half the registers, so more waves per SIMD)
+  // for the wide launches
+  constexpr int U = RT == 64 ? 16 : 8;
   for (int k0 = 0; k0 < p.splits; k0 += U) {
     float4 a[U], b[U];
 #pragma unroll
