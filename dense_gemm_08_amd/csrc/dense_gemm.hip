@@ -15,6 +15,7 @@
 
 #include "dense_gemm.h"
 #include "gemm_kernel.h"
+#include "gemm_small_kernel.h"
 #include "plan.h"
 
 namespace dg {
@@ -69,6 +70,40 @@ dense_gemm_status device_topology(int* cus, int* xcds) {
   return st;
 }
 
+// The operands the kernels read: the caller's, or where the 16-byte chunk
+// loads cannot read one in place, its dense zero-padded copy in the
+// workspace (the repack launches are enqueued here).
+struct Operands {
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+};
+template <int LAYOUT>
+static Operands prepare_operands(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                 const void* B, int64_t ldb, const CallPlan& cp, char* ws,
+                                 hipStream_t stream) {
+  Operands o = {(const uint16_t*)A, lda, (const uint16_t*)B, ldb};
+  const int64_t K8 = (K + 7) & ~(int64_t)7, N8 = (N + 7) & ~(int64_t)7;
+  if (!cp.a_direct) {
+    uint16_t* a2 = (uint16_t*)ws;
+    hipLaunchKernelGGL(repack, dim3(repack_blocks(M * (K8 / 8))), dim3(256), 0, stream,
+                       (const uint16_t*)A, M, K, lda, a2, K8);
+    o.A = a2;
+    o.lda = K8;
+  }
+  if (!cp.b_direct) {
+    const int64_t b_rows = LAYOUT == NT ? N : K, b_cols = LAYOUT == NT ? K : N;
+    const int64_t b_dcols = LAYOUT == NT ? K8 : N8;
+    uint16_t* b2 = (uint16_t*)(ws + cp.a_bytes);
+    hipLaunchKernelGGL(repack, dim3(repack_blocks(b_rows * (b_dcols / 8))), dim3(256), 0, stream,
+                       (const uint16_t*)B, b_rows, b_cols, ldb, b2, b_dcols);
+    o.B = b2;
+    o.ldb = b_dcols;
+  }
+  return o;
+}
+
 // The launches of one call with tile width TN, given its plan and a
 // workspace of at least cp.total() bytes (256-byte aligned; null when the
 // plan needs none).
@@ -78,15 +113,16 @@ static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A,
                                  const CallPlan& cp, const DeviceInfo& info, char* ws,
                                  hipStream_t stream) {
   const int64_t* plan = cp.plan;
+  const Operands o = prepare_operands<LAYOUT>(M, N, K, A, lda, B, ldb, cp, ws, stream);
   Params p;
-  p.A = (const uint16_t*)A;
-  p.B = (const uint16_t*)B;
+  p.A = o.A;
+  p.B = o.B;
   p.D = (uint16_t*)D;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
-  p.lda = (int)lda;
-  p.ldb = (int)ldb;
+  p.lda = (int)o.lda;
+  p.ldb = (int)o.ldb;
   p.ldd = (int)ldd;
   p.tiles_m = (int)plan[3];
   p.tiles_n = (int)plan[4];
@@ -100,23 +136,6 @@ static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A,
   p.num_tasks = (int)(cp.full_tasks + cp.split_tiles * plan[8]);
   p.ws = plan[8] > 1 ? (float*)(ws + cp.a_bytes + cp.b_bytes) : nullptr;
 
-  const int64_t K8 = (K + 7) & ~(int64_t)7, N8 = (N + 7) & ~(int64_t)7;
-  if (!cp.a_direct) {
-    uint16_t* a2 = (uint16_t*)ws;
-    hipLaunchKernelGGL(repack, dim3(repack_blocks(M * (K8 / 8))), dim3(256), 0, stream,
-                       (const uint16_t*)A, M, K, lda, a2, K8);
-    p.A = a2;
-    p.lda = (int)K8;
-  }
-  if (!cp.b_direct) {
-    const int64_t b_rows = LAYOUT == NT ? N : K, b_cols = LAYOUT == NT ? K : N;
-    const int64_t b_dcols = LAYOUT == NT ? K8 : N8;
-    uint16_t* b2 = (uint16_t*)(ws + cp.a_bytes);
-    hipLaunchKernelGGL(repack, dim3(repack_blocks(b_rows * (b_dcols / 8))), dim3(256), 0, stream,
-                       (const uint16_t*)B, b_rows, b_cols, ldb, b2, b_dcols);
-    p.B = b2;
-    p.ldb = (int)b_dcols;
-  }
   const unsigned grid = (unsigned)(p.num_tasks < info.cus ? p.num_tasks : info.cus);
   if (p.splits > 1) {
     // whole tiles, then the parts of the split tiles writing FP32 partials,
@@ -137,12 +156,39 @@ static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A,
   return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
 
+// The small-output kernel's launch (A @ B.T only): one workgroup per 16 x 16
+// tile of D.
+template <typename T>
+static dense_gemm_status enqueue_small(int64_t M, int64_t N, int64_t K, const void* A,
+                                       int64_t lda, const void* B, int64_t ldb, void* D,
+                                       int64_t ldd, const CallPlan& cp, char* ws,
+                                       hipStream_t stream) {
+  const Operands o = prepare_operands<NT>(M, N, K, A, lda, B, ldb, cp, ws, stream);
+  SmallParams p;
+  p.A = o.A;
+  p.B = o.B;
+  p.D = (uint16_t*)D;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K8 = (int)((K + 7) & ~(int64_t)7);
+  p.lda = (int)o.lda;
+  p.ldb = (int)o.ldb;
+  p.ldd = (int)ldd;
+  p.tiles_n = (int)cp.plan[4];
+  p.d_vec = (((uintptr_t)D & 7) == 0 && (ldd & 3) == 0) ? 1 : 0;
+  hipLaunchKernelGGL((gemm_small<T>), dim3((unsigned)(cp.plan[3] * cp.plan[4])),
+                     dim3(SMALL_THREADS), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
+}
+
 template <typename T, int LAYOUT>
 static dense_gemm_status enqueue_width(int64_t M, int64_t N, int64_t K, const void* A,
                                        int64_t lda, const void* B, int64_t ldb, void* D,
                                        int64_t ldd, const CallPlan& cp, const DeviceInfo& info,
                                        char* ws, hipStream_t stream) {
   if constexpr (LAYOUT == NT) {
+    if (cp.small())
+      return enqueue_small<T>(M, N, K, A, lda, B, ldb, D, ldd, cp, ws, stream);
     if (cp.plan[1] == BN / 2)
       return enqueue<T, LAYOUT, BN / 2>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws, stream);
   }

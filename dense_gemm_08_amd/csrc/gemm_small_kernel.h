@@ -1,0 +1,160 @@
+// gemm_small_kernel.h -- the small-output kernel for the MI355X (gfx950):
+// D = A @ B.T for outputs of at most 128 x 128 (in FP16 or BF16), whose few
+// 256 x 128 tiles would leave almost every CU idle.
+//
+// The product is the one of gemm_kernel.h (FP32 accumulation of the K
+// blocks' partial products, one rounding to the output type; TileFoundry's
+// schedule tutorial, section 1).  What changes is the decomposition:
+//   * the output is cut into 16 x 16 tiles, one workgroup each (64 for a
+//     128 x 128 output), so that many CUs stream the operands at once;
+//   * inside a workgroup, eight waves split K: wave w takes the 64-deep K
+//     chunks w, w + 8, w + 16, ..., each wave accumulating its own 16 x 16
+//     FP32 block with v_mfma_f32_16x16x32, two accumulators (one per
+//     32-deep half of a chunk);
+//   * each wave streams its chunks through a ring of its own in LDS: the
+//     LDS-DMA loads of gemm_kernel.h (eight lanes per 128-byte row segment,
+//     the same XOR swizzle), four chunks in flight, each wave waiting only
+//     for its own loads (no barrier in the K loop).  (Fragments loaded
+//     straight into registers put 16 rows under every 16 lanes of a load:
+//     measured, that held a CU to ~37 GB/s.)
+//   * the eight waves' blocks are summed through LDS in wave order, a fixed
+//     order (results are reproducible), then rounded and stored.
+// Where 16 x 16 tiles reach past M or N, or chunks past K, the loads read
+// zeros (offsets past the buffer's range) and the stores are masked.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cdna_ops.h"
+#include "tile_config.h"
+
+namespace dg {
+
+// (SMALL_TILE, SMALL_WAVES and the planning limits: tile_config.h)
+
+struct SmallParams {
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* D;
+  int M, N;
+  int K8;    // K rounded up to 8 (the operands hold zeros in [K, K8))
+  int lda, ldb, ldd;
+  int tiles_n;
+  int d_vec;  // D rows are 8-byte aligned (4-element stores allowed)
+};
+
+// c += b-fragment rows x a-fragment columns over 32 k, through the builtin:
+// with only two accumulators live the compiler keeps them in place, and it
+// adds the wait states between the dependent MFMAs of a chain itself.
+template <typename T>
+__device__ __forceinline__ f32x4 mfma16_chain(f32x4 c, u32x4 b, u32x4 a);
+template <>
+__device__ __forceinline__ f32x4 mfma16_chain<_Float16>(f32x4 c, u32x4 b, u32x4 a) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, b),
+                                                 __builtin_bit_cast(f16x8, a), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma16_chain<__bf16>(f32x4 c, u32x4 b, u32x4 a) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b),
+                                                  __builtin_bit_cast(bf16x8, a), c, 0, 0, 0);
+}
+
+template <typename T>
+__global__ __launch_bounds__(SMALL_THREADS) void gemm_small(SmallParams p) {
+  constexpr int RING = 4;               // chunks in flight per wave
+  constexpr int SLOT = 2 * 2048;        // one chunk: the A and B tiles, 16 rows x 128 B each
+  __shared__ __attribute__((aligned(1024))) char ring[SMALL_WAVES * RING * SLOT];
+  __shared__ f32x4 part[SMALL_WAVES][64];
+
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lane = (int)threadIdx.x & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int tm = (int)blockIdx.x / p.tiles_n, tn = (int)blockIdx.x % p.tiles_n;
+  const int m0 = tm * SMALL_TILE, n0 = tn * SMALL_TILE;
+  const int vm = min(SMALL_TILE, p.M - m0), vn = min(SMALL_TILE, p.N - n0);
+
+  // Loads: descriptors over the tile's valid rows and columns [0, K8).
+  // Load instruction i (0, 1) of an operand fills rows 8 i .. 8 i + 7 of
+  // its 16 x 128 B tile: lane L takes row 8 i + L / 8 and the logical
+  // 16-byte chunk the swizzle stores at physical chunk L % 8.  Rows past M
+  // or N and chunks at or past K8 get an offset past the range: zeros.
+  const i32x4 ra = make_rsrc((uint64_t)(uintptr_t)(p.A + (int64_t)m0 * p.lda),
+                             (uint32_t)(((vm - 1) * p.lda + p.K8) * 2));
+  const i32x4 rb = make_rsrc((uint64_t)(uintptr_t)(p.B + (int64_t)n0 * p.ldb),
+                             (uint32_t)(((vn - 1) * p.ldb + p.K8) * 2));
+  uint32_t aoff[2], boff[2];
+  int kc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    kc[i] = (lane & 7) ^ swz_k(r);
+    aoff[i] = r < vm ? (uint32_t)((r * p.lda + kc[i] * 8) * 2) : OOB;
+    boff[i] = r < vn ? (uint32_t)((r * p.ldb + kc[i] * 8) * 2) : OOB;
+  }
+  const uint32_t wring = lds_addr(ring) + wave * (RING * SLOT);
+  // chunk t of this wave (K chunk wave + 8 t) into ring slot t % RING
+  auto issue = [&](int t) {
+    const int c = wave + SMALL_WAVES * t;
+    const uint32_t base = wring + (t % RING) * SLOT;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool in = c * 64 + kc[i] * 8 < p.K8;
+      dma16_at(ra, in ? aoff[i] + c * 128 : OOB, base, i * 1024);
+      dma16_at(rb, in ? boff[i] + c * 128 : OOB, base, 2048 + i * 1024);
+    }
+  };
+  // Fragment reads: lane (l16, lq) reads row l16, logical chunk 4 s + lq
+  // (half s of the chunk).
+  const int fr0 = l16 * 128 + ((lq ^ swz_k(l16)) << 4);
+  const int fr1 = l16 * 128 + (((4 + lq) ^ swz_k(l16)) << 4);
+
+  // Every wave runs the same number of chunks (chunks past K load zeros and
+  // add nothing), so that the count of loads in flight is the same at every
+  // wait: RING - 1 later chunks of 4 loads each.
+  const int chunks = (p.K8 + 63) / 64;
+  const int per_wave = (chunks + SMALL_WAVES - 1) / SMALL_WAVES;
+  f32x4 acc0 = {}, acc1 = {};
+  if (per_wave > 0) {  // (K = 0: no loads at all, D is zero)
+    for (int t = 0; t < RING; ++t) issue(t);
+    for (int t = 0; t < per_wave; ++t) {
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(4 * (RING - 1)) : "memory");
+      const char* slot = ring + (wave * RING + t % RING) * SLOT;
+      const u32x4 a0 = *(const u32x4*)(slot + fr0);
+      const u32x4 a1 = *(const u32x4*)(slot + fr1);
+      const u32x4 b0 = *(const u32x4*)(slot + 2048 + fr0);
+      const u32x4 b1 = *(const u32x4*)(slot + 2048 + fr1);
+      acc0 = mfma16_chain<T>(acc0, b0, a0);
+      acc1 = mfma16_chain<T>(acc1, b1, a1);
+      // the slot's reads are done (the MFMAs took their data): refill it
+      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+      issue(t + RING);
+    }
+    // no LDS-DMA write may land after the wave ends
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  }
+
+  // Lane (l16, lq) holds D row m0 + l16, columns n0 + 4 lq .. +3; the waves'
+  // blocks are added in wave order.
+  part[wave][lane] = acc0 + acc1;
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 s = part[0][lane];
+#pragma unroll
+  for (int w = 1; w < SMALL_WAVES; ++w) s += part[w][lane];
+  const int row = m0 + l16, col = n0 + 4 * lq;
+  if (row >= p.M || col >= p.N) return;
+  u32x2 v;
+  v[0] = pack2<T>(s[0], s[1]);
+  v[1] = pack2<T>(s[2], s[3]);
+  uint16_t* dst = p.D + (int64_t)row * p.ldd + col;
+  if (p.d_vec && col + 4 <= p.N) {
+    *(u32x2*)dst = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col + e < p.N) dst[e] = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
+  }
+}
+
+}  // namespace dg

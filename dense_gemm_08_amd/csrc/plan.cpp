@@ -100,6 +100,42 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
                                   int64_t* out) {
   if ((layout != NT && layout != NN) || M <= 0 || N <= 0 || K < 0 || num_cus <= 0 || !out)
     return DENSE_GEMM_BAD_ARG;
+  if (small_output(layout, M, N, K)) {
+    // the small-output kernel: 16 x 16 tiles, one workgroup each, K split
+    // among its eight waves (no workspace)
+    out[0] = out[1] = SMALL_TILE;
+    out[2] = BK;
+    out[3] = (M + SMALL_TILE - 1) / SMALL_TILE;
+    out[4] = (N + SMALL_TILE - 1) / SMALL_TILE;
+    out[5] = out[3] * out[4];
+    out[6] = 1;
+    out[7] = SMALL_THREADS;
+    out[8] = 1;
+    out[9] = (K + BK - 1) / BK;
+    return DENSE_GEMM_OK;
+  }
+  return tiled_plan(layout, M, N, K, num_cus, out);
+}
+
+}  // extern "C"
+
+namespace dg {
+
+// Measured on the MI355X against the tiled kernel's best plan (split-K
+// where it pays): 128 x 128 x 64 3.96 against 5.21 us, 128 x 128 x 4096 4.84
+// against 10.2, 128 x 128 x 16384 12.4 against 14.9, but 41.7 against 23.0
+// at K = 65536; 1 x 4096 x 4096 5.0 against 11.0, 128 x 1024 x 1024 5.8
+// against 13.3, and about equal at 16 x 8192 x 8192 (512 tiles).  With more
+// tiles (the same operand rows streamed by many workgroups: 64 x 4096 x
+// 4096 19.0 against 14.9) the tiled kernel is faster.
+bool small_output(int layout, int64_t M, int64_t N, int64_t K) {
+  if (layout != NT || M > SMALL_MAX || K > SMALL_K_MAX) return false;
+  const int64_t tiles = ((M + SMALL_TILE - 1) / SMALL_TILE) * ((N + SMALL_TILE - 1) / SMALL_TILE);
+  return tiles <= SMALL_MAX_TILES;
+}
+
+dense_gemm_status tiled_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t num_cus,
+                             int64_t* out) {
   const int64_t tiles_m = (M + BM - 1) / BM;
   // Tile width: 256, or for A @ B.T 128
   //   * when the output is at most 128 wide: the same single tile column,
@@ -172,10 +208,6 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
   return DENSE_GEMM_OK;
 }
 
-}  // extern "C"
-
-namespace dg {
-
 bool valid_op(int op) { return op >= DENSE_GEMM_NT_F16 && op <= DENSE_GEMM_NN_F16; }
 int op_layout(int op) { return op == DENSE_GEMM_NN_BF16 || op == DENSE_GEMM_NN_F16 ? NN : NT; }
 
@@ -185,9 +217,20 @@ dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const v
   int64_t* plan = cp->plan;
   dense_gemm_status st = dense_gemm_plan(layout, M, N, K, cus, plan);
   if (st != DENSE_GEMM_OK) return st;
+  // Any option asks for the tiled kernel, with that option applied to its
+  // plan; without one, a small output runs the small-output kernel (one
+  // workgroup per 16 x 16 tile, no split).
+  const bool options = opt != nullptr && (opt->split_k != 0 || opt->tile_n != 0);
+  if (options && cp->small()) {
+    st = tiled_plan(layout, M, N, K, cus, plan);
+    if (st != DENSE_GEMM_OK) return st;
+  }
   const int64_t nk = (K + BK - 1) / BK;
   bool forced_split = false;
-  if (opt != nullptr) {
+  if (cp->small()) {
+    cp->full_tasks = plan[5];
+    cp->split_tiles = 0;
+  } else if (opt != nullptr) {
     if (opt->tile_n != 0) {
       const int64_t want = opt->tile_n;
       if (want != BN && !(want == BN / 2 && layout == NT)) return DENSE_GEMM_BAD_ARG;
@@ -211,7 +254,9 @@ dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const v
     }
   }
   const int64_t tasks = plan[3] * plan[4];
-  if (plan[8] > 1) {
+  if (cp->small()) {
+    // (one workgroup per tile, set above)
+  } else if (plan[8] > 1) {
     cp->full_tasks = forced_split ? 0 : tasks - tasks % cus;
     cp->split_tiles = tasks - cp->full_tasks;
     plan[5] = cp->full_tasks + cp->split_tiles * plan[8];

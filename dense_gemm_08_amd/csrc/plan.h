@@ -25,7 +25,17 @@ struct CallPlan {
   size_t a_bytes, b_bytes;   // workspace of the repacked copies
   size_t split_bytes;        // workspace of the FP32 partial tiles
   size_t total() const { return a_bytes + b_bytes + split_bytes; }
+  // the small-output kernel (one workgroup per 16 x 16 tile) instead of the
+  // tiled kernel
+  bool small() const { return plan[0] == SMALL_TILE; }
 };
+
+// A @ B.T outputs the small-output kernel computes when no option asks for
+// the tiled kernel: M and N at most SMALL_MAX, K at most SMALL_K_MAX.
+bool small_output(int layout, int64_t M, int64_t N, int64_t K);
+// The tiled kernel's plan (dense_gemm_plan for the other products).
+dense_gemm_status tiled_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t num_cus,
+                             int64_t* out);
 
 bool valid_op(int op);
 int op_layout(int op);

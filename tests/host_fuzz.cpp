@@ -35,9 +35,30 @@ static int64_t sat(int64_t a, int64_t b, int64_t c = 0) {
   return (int64_t)v;
 }
 
+static void check_repack(int layout, int64_t M, int64_t N, int64_t K, const CallPlan& cp) {
+  const int64_t K8 = (K + 7) & ~(int64_t)7, N8 = (N + 7) & ~(int64_t)7;
+  if (!cp.a_direct) CHECK(cp.a_bytes >= (size_t)(M * K8 * 2) && cp.a_bytes % 256 == 0);
+  if (!cp.b_direct) CHECK(cp.b_bytes >= (size_t)((layout == NT ? N * K8 : K * N8) * 2));
+  if (cp.a_direct) CHECK(cp.a_bytes == 0);
+  if (cp.b_direct) CHECK(cp.b_bytes == 0);
+}
+
 static void check_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t cus,
                        const dense_gemm_options* opt, const CallPlan& cp) {
   const int64_t* p = cp.plan;
+  const bool options = opt && (opt->split_k != 0 || opt->tile_n != 0);
+  // the small-output kernel exactly where its rule holds and no option asks
+  // for the tiled kernel
+  CHECK(cp.small() == (small_output(layout, M, N, K) && !options));
+  if (cp.small()) {
+    CHECK(layout == NT && M <= SMALL_MAX && K <= SMALL_K_MAX);
+    CHECK(p[1] == SMALL_TILE && p[2] == BK && p[7] == SMALL_THREADS);
+    CHECK(p[3] == ceil_div(M, SMALL_TILE) && p[4] == ceil_div(N, SMALL_TILE));
+    CHECK(p[5] == p[3] * p[4] && p[5] <= SMALL_MAX_TILES && cp.full_tasks == p[5]);
+    CHECK(p[8] == 1 && cp.split_tiles == 0 && cp.split_bytes == 0);
+    check_repack(layout, M, N, K, cp);
+    return;
+  }
   CHECK(p[0] == BM && p[2] == BK && p[7] == THREADS);
   CHECK(p[1] == BN || (p[1] == BN / 2 && layout == NT));
   if (opt && opt->tile_n) CHECK(p[1] == opt->tile_n);
@@ -62,11 +83,7 @@ static void check_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t cus,
     CHECK(cp.split_tiles == 0 && cp.split_bytes == 0);
   }
   if (opt && opt->split_k == 1) CHECK(p[8] == 1);
-  const int64_t K8 = (K + 7) & ~(int64_t)7, N8 = (N + 7) & ~(int64_t)7;
-  if (!cp.a_direct) CHECK(cp.a_bytes >= (size_t)(M * K8 * 2) && cp.a_bytes % 256 == 0);
-  if (!cp.b_direct) CHECK(cp.b_bytes >= (size_t)((layout == NT ? N * K8 : K * N8) * 2));
-  if (cp.a_direct) CHECK(cp.a_bytes == 0);
-  if (cp.b_direct) CHECK(cp.b_bytes == 0);
+  check_repack(layout, M, N, K, cp);
 }
 
 int main() {

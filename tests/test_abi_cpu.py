@@ -206,11 +206,11 @@ def test_plan_for_the_workloads():
 def test_plan_split_k():
     lib = binding.load_library()
     out = (ctypes.c_int64 * 10)()
-    # one 128 x 128 tile with K = 4096 (64 steps of 64): 16 parts of 4 steps
-    assert lib.dense_gemm_plan(NT, 128, 128, 4096, 256, out) == S.OK
-    assert (out[8], out[9], out[5]) == (16, 4, 16)
+    # one 256 x 128 tile with K = 4096 (64 steps of 64): 16 parts of 4 steps
+    assert lib.dense_gemm_plan(NT, 256, 128, 4096, 256, out) == S.OK
+    assert (out[0], out[8], out[9], out[5]) == (256, 16, 4, 16)
     # K too short to split
-    assert lib.dense_gemm_plan(NT, 128, 128, 448, 256, out) == S.OK
+    assert lib.dense_gemm_plan(NT, 256, 128, 448, 256, out) == S.OK
     assert out[8] == 1
     # 128 tiles leave half of 256 CUs idle; with K = 8192 two parts pay
     assert lib.dense_gemm_plan(NN, 2048, 4096, 8192, 256, out) == S.OK
@@ -307,9 +307,10 @@ def test_plan_tile_width():
                              (1000, 130, 712, 2)]:
         assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK
         assert (out[1], out[4]) == (128, tiles_n), (M, N, K)
-    # A.B^T at most 128 wide: one 128-wide tile column, whatever the size
-    for M, N, K in [(128, 128, 64), (128, 128, 4096), (8192, 128, 8192), (8192, 64, 16384),
-                    (65536, 1, 4096)]:
+    # A.B^T at most 128 wide (and not for the small-output kernel): one
+    # 128-wide tile column, whatever the size
+    for M, N, K in [(256, 128, 64), (129, 128, 4096), (128, 128, 16392), (8192, 128, 8192),
+                    (8192, 64, 16384), (65536, 1, 4096)]:
         assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK
         assert (out[1], out[4]) == (128, 1), (M, N, K)
     # wider outputs, A.B, and operands beyond 192 MiB keep 256-wide tiles
@@ -323,6 +324,32 @@ def test_plan_tile_width():
             assert lib.dense_gemm_plan(NT, M, N, 1024, 256, out) == S.OK
             if out[1] == 128:
                 assert out[3] * out[4] <= 256
+
+
+def test_plan_small_output():
+    # A.B^T with M <= 128, K <= 16384 and at most 512 16 x 16 tiles of D: the
+    # small-output kernel, one 512-thread workgroup per tile, no split
+    lib = binding.load_library()
+    out = (ctypes.c_int64 * 10)()
+    for M, N, K in [(128, 128, 64), (128, 128, 4096), (128, 128, 16384), (100, 72, 1000),
+                    (1, 4096, 4096), (1, 8192, 1), (128, 1024, 1024), (16, 16, 0)]:
+        assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK
+        tiles_m, tiles_n = -(-M // 16), -(-N // 16)
+        assert list(out) == [16, 16, 64, tiles_m, tiles_n, tiles_m * tiles_n, 1, 512, 1,
+                             -(-K // 64)], (M, N, K)
+    # past any of the three limits, or A.B: the tiled kernel
+    for layout, M, N, K in [(NT, 129, 128, 4096), (NT, 128, 128, 16392), (NT, 1, 8208, 4096),
+                            (NT, 128, 1040, 64), (NN, 128, 128, 4096), (NN, 1, 16, 64)]:
+        assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
+        assert (out[0], out[7]) == (256, 256), (layout, M, N, K)
+    # it needs no workspace, and an option asks for the tiled kernel instead
+    assert _ws("nt", "f16", 128, 128, 4096) == (S.OK, 0)
+    assert _ws("nt", "f16", 128, 128, 4096, opts=(16, 0)) == (S.OK, 16 * 256 * 128 * 4)
+    assert _ws("nt", "f16", 128, 128, 4096, opts=(1, 0)) == (S.OK, 0)
+    # (the tiled kernel's own plan there: 128-wide, 16 parts)
+    assert _ws("nt", "f16", 128, 128, 4096, opts=(0, 128)) == (S.OK, 16 * 256 * 128 * 4)
+    # ... or repacks, like the tiled kernel, an operand it cannot read in place
+    assert _ws("nt", "f16", 128, 128, 4095) == (S.OK, 2 * 128 * 4096 * 2)
 
 
 def test_ladder_argument_checks_on_the_host():
@@ -371,8 +398,10 @@ def test_workspace_size_of_the_workloads():
     assert _ws("nn", "bf16", 8192, 17408, 5120) == (S.OK, 0)
     assert _ws("nt", "f16", 3000, 5000, 4000) == (S.OK, 0)
     assert _ws("nt", "f16", 128, 128, 64) == (S.OK, 0)
+    # one 128 x 128 output: the small-output kernel, no workspace
+    assert _ws("nt", "f16", 128, 128, 4096) == (S.OK, 0)
     # one 256 x 128 tile, 64 K steps in 16 parts: 16 FP32 partial tiles
-    assert _ws("nt", "f16", 128, 128, 4096) == (S.OK, 16 * 256 * 128 * 4)
+    assert _ws("nt", "f16", 256, 128, 4096) == (S.OK, 16 * 256 * 128 * 4)
     # K not a multiple of 8: both operands repacked with rows of K8 = 4096
     assert _ws("nt", "f16", 4096, 4096, 4095) == (S.OK, 2 * 4096 * 4096 * 2)
     # a misaligned pointer repacks that operand only

@@ -95,7 +95,8 @@ def check_against(fmt, d, s, D, what):
 @pytest.mark.parametrize("name", ["single_tile", "k_loop", "square_nt", "large_nn", "ragged_nt"])
 def test_workload_full_size_every_output(name):
     # the benchmark's call (the plain entry point, the library's own plan:
-    # 256 x 256 tiles for the three large workloads, split-K for k_loop),
+    # 256 x 256 tiles for the three large workloads, the small-output kernel
+    # for single_tile and k_loop),
     # every output against the oracle
     w = inputs.WORKLOADS[name]
     print("full size %s %dx%dx%d" % (name, w.M, w.N, w.K), flush=True)
@@ -257,6 +258,53 @@ def test_ragged_block_equals_padded_block(layout, fmt):
     assert (D1 == D2[:M, :N]).all()
 
 
+# ---------------------------------------------------- small-output kernel --
+
+SMALL = [
+    # (M, N, K) planned for the small-output kernel (A.B^T, M <= 128, K <=
+    # 16384, at most 512 tiles of 16 x 16): the longest K (32 chunks per
+    # wave), ragged tiles with K not a multiple of the 64-deep chunks, the
+    # 512-tile limit at one tile row and at eight, a K below 8 (repacked),
+    # one chunk shared by fewer than the eight waves
+    (128, 128, 16384), (100, 72, 8000), (1, 8192, 520), (128, 1024, 64), (5, 3, 7),
+    (17, 130, 1000), (128, 128, 448),
+]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", SMALL, ids=lambda v: str(v))
+def test_small_output_kernel_full_check(fmt, M, N, K):
+    import ctypes
+    from dense_gemm_08_amd import binding
+    out = (ctypes.c_int64 * 10)()
+    assert binding.load_library().dense_gemm_plan(0, M, N, K, 256, out) == 0
+    assert out[0] == 16, "planned for the tiled kernel"
+    w = inputs.Workload("x", "nt", fmt, 0, 0, 0, "uniform", 0.0, 111)
+    A, B = inputs.make_operands(w, seed=M + N + K, M=M, N=N, K=K)
+    D, st = _gpu.gemm("nt", fmt, A, B, M, N, K)
+    assert st == status().OK
+    check_full("nt", fmt, A, B, M, N, K, D)
+    # the eight waves' blocks are summed in a fixed order: a rerun is equal
+    D2, _ = _gpu.gemm("nt", fmt, A, B, M, N, K)
+    assert (D == D2).all()
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_small_output_kernel_small_integers_exact(fmt):
+    # exact integer sums up to 9K: the correctly rounded value bit for bit,
+    # equal to the tiled kernel's (an option asks for it) bit for bit
+    M, N, K = 120, 100, 3000
+    A = inputs.small_integers(fmt, (M, K), seed=33)
+    B = inputs.small_integers(fmt, (N, K), seed=34)
+    D, st = _gpu.gemm("nt", fmt, A, B, M, N, K)
+    assert st == status().OK
+    d, _ = oracle.gemm("nt", fmt, A, B)
+    assert (D == oracle.round_to(fmt, d)).all()
+    Dt, st = _gpu.gemm("nt", fmt, A, B, M, N, K, opts=(1, 0))
+    assert st == status().OK
+    assert (Dt == D).all()
+
+
 # ------------------------------------------------------------ edge paths --
 
 SWEEP = [1, 7, 8, 33, 65, 129, 255, 257]
@@ -302,7 +350,8 @@ UNALIGNED = [
     (280, 272, 200, 0, 0, 0, 0, 0, 5),
     (257, 13, 77, 2, 1, 3, 1, 2, 3),
     (300, 1001, 136, 0, 0, 0, 0, 0, 0),
-    (128, 128, 4001, 0, 0, 0, 1, 1, 1),  # + split-K
+    (128, 128, 4001, 0, 0, 0, 1, 1, 1),  # the small-output kernel
+    (256, 128, 4001, 0, 0, 0, 1, 1, 1),  # + split-K
 ]
 
 
@@ -405,10 +454,10 @@ def test_concurrent_streams_with_workspaces():
     # streams at once, give the same bits as the same calls run alone
     t = _gpu.torch()
     w = inputs.WORKLOADS["square_nt"]
-    A1, B1 = inputs.make_operands(w, seed=61, M=128, N=128, K=4096)           # split-K
+    A1, B1 = inputs.make_operands(w, seed=61, M=256, N=128, K=4096)           # split-K
     wn = inputs.WORKLOADS["large_nn"]
     A2, B2 = inputs.make_operands(wn, seed=62, M=264, N=304, K=1032)          # repacked A
-    A1d, B1d = _gpu.to_dev(A1, 128, 4096), _gpu.to_dev(B1, 128, 4096)
+    A1d, B1d = _gpu.to_dev(A1, 256, 4096), _gpu.to_dev(B1, 128, 4096)
     A2d, B2d = _gpu.to_dev(A2, 264, 1032, ld=1033), _gpu.to_dev(B2, 1032, 304)
     XA, XSA, XB, XSB = [t.from_numpy(x).cuda() for x in inputs.mx_operands(280, 300, 160, seed=63)]
     mx = binding_raw("gemm_nt_e4m3_mx")
@@ -416,13 +465,13 @@ def test_concurrent_streams_with_workspaces():
     def run(kind, D, stream):
         h = stream.cuda_stream
         if kind == 0:
-            return _gpu.call("nt", "f16", 128, 128, 4096, A1d, 4096, B1d, 4096, D, 128, stream)
+            return _gpu.call("nt", "f16", 256, 128, 4096, A1d, 4096, B1d, 4096, D, 128, stream)
         if kind == 1:
             return _gpu.call("nn", "bf16", 264, 304, 1032, A2d, 1033, B2d, 304, D, 304, stream)
         return status()(mx(280, 300, 160, XA.data_ptr(), 160, XSA.data_ptr(), 5, XB.data_ptr(), 160,
                            XSB.data_ptr(), 5, D.data_ptr(), 300, h))
 
-    shapes = [(128, 128), (264, 304), (280, 300)]
+    shapes = [(256, 128), (264, 304), (280, 300)]
     ref = []
     main = t.cuda.current_stream()
     for kind in range(3):
@@ -691,7 +740,7 @@ def _ex(layout, fmt, M, N, K, A, lda, B, ldb, D, ldd, ws_ptr, nbytes, stream=Non
 
 WS_CASES = [
     # (layout, fmt, M, N, K, lda_extra, a_off): what takes the workspace
-    ("nt", "f16", 128, 128, 4096, 0, 0),    # one tile in 16 K parts
+    ("nt", "f16", 256, 128, 4096, 0, 0),    # one 256 x 128 tile in 16 K parts
     ("nn", "bf16", 264, 304, 1032, 1, 0),   # A repacked (odd leading dimension)
     ("nt", "f16", 4252, 4088, 1000, 0, 0),  # the last wave's 16 tiles in 4 parts
     ("nt", "bf16", 280, 272, 200, 0, 3),    # A repacked (pointer off 16-byte alignment)
@@ -741,12 +790,12 @@ def test_workspace_calls_on_two_streams():
     # wait for each other, give the bits of the same calls run alone
     t = _gpu.torch()
     w = inputs.WORKLOADS["square_nt"]
-    A1, B1 = inputs.make_operands(w, seed=71, M=128, N=128, K=4096)
+    A1, B1 = inputs.make_operands(w, seed=71, M=256, N=128, K=4096)
     wn = inputs.WORKLOADS["large_nn"]
     A2, B2 = inputs.make_operands(wn, seed=72, M=264, N=304, K=1032)
-    A1d, B1d = _gpu.to_dev(A1, 128, 4096), _gpu.to_dev(B1, 128, 4096)
+    A1d, B1d = _gpu.to_dev(A1, 256, 4096), _gpu.to_dev(B1, 128, 4096)
     A2d, B2d = _gpu.to_dev(A2, 264, 1032, ld=1033), _gpu.to_dev(B2, 1032, 304)
-    cases = [("nt", "f16", 128, 128, 4096, A1d, 4096, B1d, 4096),
+    cases = [("nt", "f16", 256, 128, 4096, A1d, 4096, B1d, 4096),
              ("nn", "bf16", 264, 304, 1032, A2d, 1033, B2d, 304)]
     needs = [_need(c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], c[8]) for c in cases]
     ref = []

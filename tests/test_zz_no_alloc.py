@@ -28,7 +28,8 @@ def _noalloc(M, N, K, A, lda, B, ldb, D, ldd):
 CASES = [
     # (M, N, K, lda, what takes the scratch): a larger call, then a smaller one
     (4252, 4088, 1000, 1000, "the last wave's 16 tiles in 4 K parts (16 MiB of partials)"),
-    (128, 128, 4096, 4096, "one tile in 16 K parts (2 MiB of partials)"),
+    (256, 128, 4096, 4096, "one 256 x 128 tile in 16 K parts (2 MiB of partials)"),
+    (128, 128, 4096, 4096, "the small-output kernel (no scratch)"),
     (300, 264, 1000, 1001, "A repacked (odd leading dimension)"),
 ]
 
@@ -71,12 +72,12 @@ def test_noalloc_rejects_a_call_beyond_its_scratch():
 
 def test_noalloc_call_captured_in_a_graph():
     # the callers this entry point is for: a HIP graph captured once and
-    # replayed.  One tile in 16 K parts (two kernels, the split partials in
-    # the fixed scratch), captured, then replayed three times with new
-    # operands copied in eagerly between replays; every replay must give
-    # the plain entry point's bits for its operands
+    # replayed.  One 256 x 128 tile in 16 K parts (two kernels, the split
+    # partials in the fixed scratch), captured, then replayed three times
+    # with new operands copied in eagerly between replays; every replay must
+    # give the plain entry point's bits for its operands
     t = _gpu.torch()
-    M, N, K = 128, 128, 4096
+    M, N, K = 256, 128, 4096
     w = inputs.WORKLOADS["k_loop"]
     Ad = t.empty((M, K), dtype=t.int16, device="cuda")
     Bd = t.empty((N, K), dtype=t.int16, device="cuda")
