@@ -670,16 +670,21 @@ def main():
 
 
 def source_sha(name: str = "gemm_kernel.h") -> str:
-    """sha256 prefix of a kernel source (gemm_kernel.h, gemm_mx_kernel.h), the
-    headers it shares and the launch planning (plan.cpp), with comments and
+    """sha256 prefix of a kernel source (gemm_kernel.h with
+    gemm_small_kernel.h, or gemm_mx_kernel.h), the headers it shares and the
+    launch planning (plan.cpp), with comments and
     blank space removed: the traffic figures recorded for it stay valid
     across comment edits and other host-side changes, not across changes of
     the kernels or of which kernels a call runs."""
     import hashlib
     import re
     h = hashlib.sha256()
-    # (plan.cpp decides the tile widths and splits, i.e. which kernels run)
-    for f in (name, "cdna_ops.h", "tile_sched.h", "tile_config.h", "plan.cpp"):
+    # (plan.cpp decides the kernel, the tile widths and splits, i.e. which
+    # kernels run; FP16/BF16 products may run the small-output kernel)
+    files = [name, "cdna_ops.h", "tile_sched.h", "tile_config.h", "plan.cpp"]
+    if name == "gemm_kernel.h":
+        files.append("gemm_small_kernel.h")
+    for f in files:
         with open(os.path.join(ROOT, "dense_gemm_08_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)

@@ -13,7 +13,7 @@
 //     32-deep half of a chunk);
 //   * each wave streams its chunks through a ring of its own in LDS: the
 //     LDS-DMA loads of gemm_kernel.h (eight lanes per 128-byte row segment,
-//     the same XOR swizzle), four chunks in flight, each wave waiting only
+//     the same XOR swizzle), two chunks in flight, each wave waiting only
 //     for its own loads (no barrier in the K loop).  (Fragments loaded
 //     straight into registers put 16 rows under every 16 lanes of a load:
 //     measured, that held a CU to ~37 GB/s.)
@@ -62,7 +62,11 @@ __device__ __forceinline__ f32x4 mfma16_chain<__bf16>(f32x4 c, u32x4 b, u32x4 a)
 
 template <typename T>
 __global__ __launch_bounds__(SMALL_THREADS) void gemm_small(SmallParams p) {
-  constexpr int RING = 4;               // chunks in flight per wave
+  // Chunks in flight per wave.  Two (72 KiB of LDS per workgroup, so two
+  // workgroups fit a CU) measured faster than four (136 KiB, one per CU) on
+  // every shape tried: 4.4 against 4.9 us at 128 x 128 x 4096, 22.7 against
+  // 24.3 at 1 x 16384 x 4096, 11.6 against 12.3 at 128 x 128 x 16384.
+  constexpr int RING = 2;
   constexpr int SLOT = 2 * 2048;        // one chunk: the A and B tiles, 16 rows x 128 B each
   __shared__ __attribute__((aligned(1024))) char ring[SMALL_WAVES * RING * SLOT];
   __shared__ f32x4 part[SMALL_WAVES][64];

@@ -122,16 +122,18 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
 namespace dg {
 
 // Measured on the MI355X against the tiled kernel's best plan (split-K
-// where it pays): 128 x 128 x 64 3.96 against 5.21 us, 128 x 128 x 4096 4.84
-// against 10.2, 128 x 128 x 16384 12.4 against 14.9, but 41.7 against 23.0
-// at K = 65536; 1 x 4096 x 4096 5.0 against 11.0, 128 x 1024 x 1024 5.8
-// against 13.3, and about equal at 16 x 8192 x 8192 (512 tiles).  With more
-// tiles (the same operand rows streamed by many workgroups: 64 x 4096 x
-// 4096 19.0 against 14.9) the tiled kernel is faster.
+// where it pays), per call: 128 x 128 x 64 4.0 against 5.2 us, 128 x 128 x
+// 4096 4.4 against 10.9, 128 x 128 x 16384 11.6 against 14.9 (but with K =
+// 65536 the tiled kernel's 16-way split is faster), 128 x 1024 x 1024 4.1
+// against 13.3.  With one tile row (M <= 16) every B row is streamed once,
+// whatever N: 1 x 4096 x 4096 6.6 against 11.4, 16 x 16384 x 4096 22.7
+// against 28.6, 16 x 32768 x 4096 43.1 against 47.4.  With more tile rows
+// and more tiles (each operand row streamed by many workgroups: 64 x 4096
+// x 4096 19.0 against 14.9) the tiled kernel is faster.
 bool small_output(int layout, int64_t M, int64_t N, int64_t K) {
   if (layout != NT || M > SMALL_MAX || K > SMALL_K_MAX) return false;
   const int64_t tiles = ((M + SMALL_TILE - 1) / SMALL_TILE) * ((N + SMALL_TILE - 1) / SMALL_TILE);
-  return tiles <= SMALL_MAX_TILES;
+  return tiles <= SMALL_MAX_TILES || M <= SMALL_TILE;
 }
 
 dense_gemm_status tiled_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t num_cus,

@@ -15,9 +15,9 @@ constexpr int WAVES = 4;             // 2 x 2 waves
 constexpr int THREADS = WAVES * 64;
 
 // The small-output kernel (gemm_small_kernel.h): A @ B.T with M at most
-// SMALL_MAX, K at most SMALL_K_MAX and at most SMALL_MAX_TILES 16 x 16 tiles
-// of D (two workgroups per CU on a 256-CU device), each tile a workgroup of
-// eight waves that split K among themselves.
+// SMALL_MAX, K at most SMALL_K_MAX, and at most SMALL_MAX_TILES 16 x 16
+// tiles of D or a single tile row (M <= SMALL_TILE), each tile a workgroup
+// of eight waves that split K among themselves.
 constexpr int SMALL_TILE = 16;
 constexpr int SMALL_WAVES = 8;
 constexpr int SMALL_THREADS = SMALL_WAVES * 64;

@@ -58,6 +58,15 @@
  * unsplit results are identical.  dense_gemm_ex can force the width of
  * A @ B.T.
  *
+ * Small outputs.  D = A @ B.T with M <= 128 and K <= 16384 whose 16 x 16
+ * tiles number at most 512, or form a single tile row (M <= 16), runs a
+ * second kernel instead of the tiled one: one workgroup per 16 x 16 tile of
+ * D, whose eight waves split K among themselves and add their FP32 sums in
+ * a fixed order (reproducible; no workspace unless an operand is
+ * repacked).  Its summation order differs from the tiled kernel's, within
+ * the same rounding bound.  Any dense_gemm_options override asks for the
+ * tiled kernel instead.
+ *
  * Workspace.  A call that repacks an operand or splits K needs device
  * memory beyond A, B and D: dense_gemm_workspace_size gives the amount.
  * dense_gemm_ex takes it from the caller (the destination-passing form of
@@ -127,7 +136,8 @@ typedef enum dense_gemm_op {
 /* Overrides of the library's launch plan (a null pointer, or zeros, keep
  * its own choice).  They change the FP32 summation order of the outputs they
  * touch (split_k), or the tiling (tile_n, which keeps the order), never the
- * operation; both stay within the rounding bound.
+ * operation; both stay within the rounding bound.  Either one, non-zero,
+ * selects the tiled kernel (not the small-output kernel).
  *   split_k  0: the library's choice; 1: no split; n > 1: every tile's K
  *            steps in min(n, steps) parts of equal length (the last shorter)
  *   tile_n   0: the library's choice; 256; or 128 (D = A @ B.T only).  A
@@ -302,7 +312,9 @@ dense_gemm_status dense_gemm_tile_of_task(int64_t task, int64_t tiles_m, int64_t
  * Writes 10 values to out: BM, the tile width BN (256, or 128 as described
  * under "Tile width" above), BK, tiles_m, tiles_n, grid (workgroups of the
  * GEMM kernel), group_m, threads per workgroup, the number of K splits
- * (1: none) and the K steps (of BK) per split.  Split-K applies to the
+ * (1: none) and the K steps (of BK) per split.  For the small-output kernel
+ * ("Small outputs" above) BM = BN = 16, the grid is tiles_m * tiles_n
+ * workgroups of 512 threads, group_m 1 and no split.  Split-K applies to the
  * r = tiles mod num_cus tiles of the last, partial wave (all tiles when
  * tiles < num_cus), with K spanning at least 8 steps, at most one part per
  * CU (r * parts <= num_cus) and at least 4 steps per part.  When tiles <

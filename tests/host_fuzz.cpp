@@ -54,7 +54,8 @@ static void check_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t cus,
     CHECK(layout == NT && M <= SMALL_MAX && K <= SMALL_K_MAX);
     CHECK(p[1] == SMALL_TILE && p[2] == BK && p[7] == SMALL_THREADS);
     CHECK(p[3] == ceil_div(M, SMALL_TILE) && p[4] == ceil_div(N, SMALL_TILE));
-    CHECK(p[5] == p[3] * p[4] && p[5] <= SMALL_MAX_TILES && cp.full_tasks == p[5]);
+    CHECK(p[5] == p[3] * p[4] && cp.full_tasks == p[5]);
+    CHECK(p[5] <= SMALL_MAX_TILES || p[3] == 1);
     CHECK(p[8] == 1 && cp.split_tiles == 0 && cp.split_bytes == 0);
     check_repack(layout, M, N, K, cp);
     return;

@@ -252,8 +252,8 @@ def test_plan_split_k():
     assert lib.dense_gemm_plan(NT, 8192, 4224, 4096, 256, out) == S.OK
     assert (out[8], out[9], out[5]) == (8, 8, 256)
     # one row of tiles (M < 256): partial tiles write only their rows inside D,
-    # so the split pays sooner: 128 narrow tiles of 1 x 16384 x 4096 in 2 parts
-    assert lib.dense_gemm_plan(NT, 1, 16384, 4096, 256, out) == S.OK
+    # so the split pays sooner: 128 narrow tiles of 32 x 16384 x 4096 in 2 parts
+    assert lib.dense_gemm_plan(NT, 32, 16384, 4096, 256, out) == S.OK
     assert (out[1], out[4], out[8], out[9], out[5]) == (128, 128, 2, 32, 256)
     # ... which a full tile row would not pay for (256 rows x 128 tiles)
     assert lib.dense_gemm_plan(NT, 256, 16384, 4096, 256, out) == S.OK
@@ -327,19 +327,22 @@ def test_plan_tile_width():
 
 
 def test_plan_small_output():
-    # A.B^T with M <= 128, K <= 16384 and at most 512 16 x 16 tiles of D: the
-    # small-output kernel, one 512-thread workgroup per tile, no split
+    # A.B^T with M <= 128, K <= 16384 and at most 512 16 x 16 tiles of D, or
+    # one tile row (M <= 16) of any width: the small-output kernel, one
+    # 512-thread workgroup per tile, no split
     lib = binding.load_library()
     out = (ctypes.c_int64 * 10)()
     for M, N, K in [(128, 128, 64), (128, 128, 4096), (128, 128, 16384), (100, 72, 1000),
-                    (1, 4096, 4096), (1, 8192, 1), (128, 1024, 1024), (16, 16, 0)]:
+                    (1, 4096, 4096), (1, 8192, 1), (128, 1024, 1024), (16, 16, 0),
+                    (16, 65536, 4096), (1, 1 << 20, 64)]:
         assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK
         tiles_m, tiles_n = -(-M // 16), -(-N // 16)
         assert list(out) == [16, 16, 64, tiles_m, tiles_n, tiles_m * tiles_n, 1, 512, 1,
                              -(-K // 64)], (M, N, K)
     # past any of the three limits, or A.B: the tiled kernel
-    for layout, M, N, K in [(NT, 129, 128, 4096), (NT, 128, 128, 16392), (NT, 1, 8208, 4096),
-                            (NT, 128, 1040, 64), (NN, 128, 128, 4096), (NN, 1, 16, 64)]:
+    for layout, M, N, K in [(NT, 129, 128, 4096), (NT, 128, 128, 16392), (NT, 17, 4112, 4096),
+                            (NT, 128, 1040, 64), (NT, 1, 4096, 16392), (NN, 128, 128, 4096),
+                            (NN, 1, 16, 64)]:
         assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
         assert (out[0], out[7]) == (256, 256), (layout, M, N, K)
     # it needs no workspace, and an option asks for the tiled kernel instead

@@ -262,12 +262,13 @@ def test_ragged_block_equals_padded_block(layout, fmt):
 
 SMALL = [
     # (M, N, K) planned for the small-output kernel (A.B^T, M <= 128, K <=
-    # 16384, at most 512 tiles of 16 x 16): the longest K (32 chunks per
-    # wave), ragged tiles with K not a multiple of the 64-deep chunks, the
-    # 512-tile limit at one tile row and at eight, a K below 8 (repacked),
-    # one chunk shared by fewer than the eight waves
-    (128, 128, 16384), (100, 72, 8000), (1, 8192, 520), (128, 1024, 64), (5, 3, 7),
-    (17, 130, 1000), (128, 128, 448),
+    # 16384, at most 512 tiles of 16 x 16 or one tile row): the longest K
+    # (32 chunks per wave), ragged tiles with K not a multiple of the 64-deep
+    # chunks, the 512-tile limit at one tile row and at eight, one tile row
+    # past it, a K below 8 (repacked), one chunk shared by fewer than the
+    # eight waves
+    (128, 128, 16384), (100, 72, 8000), (1, 8192, 520), (128, 1024, 64), (16, 8200, 1000),
+    (3, 20000, 72), (5, 3, 7), (17, 130, 1000), (128, 128, 448),
 ]
 
 
