@@ -84,10 +84,23 @@ def library_path() -> str:
 
 
 def load_library():
-    """Load the HIP library once; raise if it has not been built."""
+    """Load the HIP library once; raise if it has not been built.
+
+    PyTorch is imported first when it is installed: it carries its own copy
+    of the HIP runtime (and of the HSA runtime below it) under the same
+    soname the library links against (libamdhip64.so.7), so with torch
+    loaded the dynamic linker binds the library to that copy, and tensors,
+    streams and the library's launches share one runtime.  Loaded the other
+    way round, the process would map two HIP runtimes, and the library's
+    calls would not see the device state torch set up (measured: the first
+    call then fails with DENSE_GEMM_NO_DEVICE)."""
     global _lib
     if _lib is not None:
         return _lib
+    try:
+        import torch  # noqa: F401  (the runtime the library must bind to)
+    except ImportError:
+        pass
     path = library_path()
     if not os.path.exists(path):
         raise FileNotFoundError(

@@ -497,3 +497,20 @@ def test_mx_workspace_size():
     fn = lib.gemm_nt_e4m3_mx_ex
     assert S(fn(8, 8, 40, 256, 48, 256, 2, 256, 48, 256, 2, 256, 8, 0, 0, None)) == S.BAD_ARG
     assert S(fn(8, 8, 64, 256, 64, 256, 2, 256, 64, 256, 2, 0, 8, 0, 0, None)) == S.NULL_PTR
+
+
+def test_library_binds_to_the_torch_hip_runtime():
+    # loading the library first (as a caller that imports the binding before
+    # torch would) must leave one HIP runtime in the process, torch's: the
+    # binding imports torch before it opens the library
+    import subprocess
+    import sys
+    code = ("from dense_gemm_08_amd import binding; binding.load_library(); import torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') "
+            "if 'libamdhip64' in l or 'libhsa-runtime64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=ROOT, check=True).stdout.strip()
+    import ast
+    libs = ast.literal_eval(out)
+    assert len([x for x in libs if "libamdhip64" in x]) == 1, libs
+    assert len([x for x in libs if "libhsa-runtime64" in x]) == 1, libs

@@ -10,7 +10,9 @@ below that bound, where the offsets use their full range:
 * D = A @ B, BF16, M = 16, N = 16,777,208, K = 64: a K step's B rows span
   2^31 - 1024 bytes (65,536 tiles);
 * FP8 block-scaled D = A @ B.T, M = N = 256, K = 8,388,576: a tile's rows
-  span 2^31 - 8192 bytes (65,536 K steps in one tile).
+  span 2^31 - 8192 bytes (65,536 K steps in one tile);
+* the small-output kernel (D = A @ B.T, FP16, M = N = 16, K = 200) with
+  the largest leading dimensions the check accepts (rows ~8 MiB apart).
 
 Entries are integers in {-1, 0, 1} (unit scales for FP8), so every FP32
 partial sum is an exact integer below 2^24 and each output must equal the
@@ -94,3 +96,34 @@ def test_mx_tile_span_at_the_limit():
     rows, cols = inputs.sample_indices(M, N, 256, seed=105)
     d, _ = oracle.gemm_mx_entries(A, SA, B, SB, rows, cols)
     _exact("bf16", D, d, rows, cols)
+
+
+def test_small_output_kernel_at_the_largest_leading_dimensions():
+    # the largest lda = ldb the argument check accepts for K = 200 (found on
+    # the host), one 16 x 16 tile: the small-output kernel's row offsets use
+    # the 32-bit range the check allows for a 256-row tile
+    import ctypes
+    lib = binding.load_library()
+    M, N, K = 16, 16, 200
+
+    def ok(ld):
+        return lib.dense_gemm_validate(0, M, N, K, ctypes.c_void_p(256), ld, ctypes.c_void_p(256),
+                                       ld, ctypes.c_void_p(256), N) == S.OK
+    lo, hi = K, 1 << 30
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if ok(mid) else (lo, mid)
+    ld = lo - lo % 8  # rows read in place (16-byte aligned)
+    assert ok(ld) and not ok(hi)
+    out = (ctypes.c_int64 * 10)()
+    assert lib.dense_gemm_plan(0, M, N, K, 256, out) == S.OK and out[0] == 16
+    print("small-output A.B^T FP16 %d x %d x %d, lda = ldb = %d" % (M, N, K, ld), flush=True)
+    A = inputs.small_integers("f16", (M, K), seed=106)
+    B = inputs.small_integers("f16", (N, K), seed=107)
+    Ad, Bd = _gpu.to_dev(A, M, K, ld=ld), _gpu.to_dev(B, N, K, ld=ld)
+    Dd = _gpu.empty_out(M, N)
+    assert _gpu.call("nt", "f16", M, N, K, Ad, ld, Bd, ld, Dd, N) == S.OK
+    _gpu.torch().cuda.synchronize()
+    D = _gpu.from_dev(Dd)
+    d, _ = oracle.gemm("nt", "f16", A, B)
+    assert (D == oracle.round_to("f16", d)).all()
