@@ -1,6 +1,8 @@
 // gemm_small_kernel.h -- the small-output kernel for the MI355X (gfx950):
-// D = A @ B.T for outputs of at most 128 x 128 (in FP16 or BF16), whose few
-// 256 x 128 tiles would leave almost every CU idle.
+// D = A @ B.T (FP16 or BF16) with M <= 128, such as a 128 x 128 output,
+// whose one 256 x 128 tile would leave almost every CU idle, or a single
+// row of 16 x 16 tiles (M <= 16) of any width.  (Which products run it:
+// small_output in plan.cpp.)
 //
 // The product is the one of gemm_kernel.h (FP32 accumulation of the K
 // blocks' partial products, one rounding to the output type; TileFoundry's
