@@ -59,7 +59,8 @@ def parse():
                          "gemm_nt_e4m3_mx_ex) with a workspace allocated once, before the "
                          "timed region, instead of the plain entry point (which takes its "
                          "workspace, where the call needs one, from the stream-ordered allocator "
-                         "on every call)")
+                         "on every call); with --sweep or --small-m-sweep, time that form "
+                         "beside the plain entry point")
     ap.add_argument("--split-k", type=int, default=0,
                     help="with --workspace (FP16/BF16 workloads): the plan override "
                          "dense_gemm_options.split_k (0: the library's choice, 1: no split, "
@@ -238,12 +239,29 @@ def run_sweep(args, shapes=None):
         ms = timed(ours, steps, max(3, steps // 4))
         ms_ref = timed(ref, steps, max(3, steps // 4))
         nbytes = 2.0 * (M * K + N * K + M * N)  # A, B and D once
-        print(json.dumps({"mode": "sweep", "M": M, "N": N, "K": K, "steps": steps,
-                          "kernel_ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
-                          "alg_tb_s": round(nbytes / ms / 1e9, 3),
-                          "torch_mm_ms": round(ms_ref, 5),
-                          "torch_mm_tflops": round(flops / ms_ref / 1e9, 1),
-                          "torch_mm_alg_tb_s": round(nbytes / ms_ref / 1e9, 3)}), flush=True)
+        line = {"mode": "sweep", "M": M, "N": N, "K": K, "steps": steps,
+                "kernel_ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
+                "alg_tb_s": round(nbytes / ms / 1e9, 3),
+                "torch_mm_ms": round(ms_ref, 5),
+                "torch_mm_tflops": round(flops / ms_ref / 1e9, 1),
+                "torch_mm_alg_tb_s": round(nbytes / ms_ref / 1e9, 3)}
+        if args.workspace:
+            # the same product through dense_gemm_ex, its workspace allocated
+            # once (no stream-ordered allocation per call)
+            need = binding.workspace_size("nt", "f16", M, N, K, A.data_ptr(), K, B.data_ptr(), K)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+            def ours_ws():
+                st = lib.dense_gemm_ex(binding.OPS[("nt", "f16")], M, N, K, A.data_ptr(), K,
+                                       B.data_ptr(), K, D.data_ptr(), N, None, ws.data_ptr(),
+                                       need, stream.cuda_stream)
+                if st != 0:
+                    raise binding.DenseGemmError(st, "dense_gemm_ex")
+            ms_ws = timed(ours_ws, steps, max(3, steps // 4))
+            line.update({"workspace_bytes": need, "ex_ms": round(ms_ws, 5),
+                         "ex_alg_tb_s": round(nbytes / ms_ws / 1e9, 3)})
+            del ws
+        print(json.dumps(line), flush=True)
         del A, B, D, Dt
 
 

@@ -104,10 +104,10 @@ static Operands prepare_operands(int64_t M, int64_t N, int64_t K, const void* A,
   return o;
 }
 
-// The launches of one call with tile width TN, given its plan and a
-// workspace of at least cp.total() bytes (256-byte aligned; null when the
-// plan needs none).
-template <typename T, int LAYOUT, int TN>
+// The launches of one call with tile width TN and tile rows TM, given its
+// plan and a workspace of at least cp.total() bytes (256-byte aligned; null
+// when the plan needs none).
+template <typename T, int LAYOUT, int TN, int TM>
 static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                  const void* B, int64_t ldb, void* D, int64_t ldd,
                                  const CallPlan& cp, const DeviceInfo& info, char* ws,
@@ -140,18 +140,20 @@ static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A,
   if (p.splits > 1) {
     // whole tiles, then the parts of the split tiles writing FP32 partials,
     // summed by a second kernel
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true, TN>), dim3(grid), dim3(THREADS), 0, stream, p);
-    // (one-wave workgroups where 256-thread ones would not cover the CUs)
-    const int64_t wide = p.tiles * (int64_t)reduce_blocks_per_tile<TN, 256>();
-    if (wide < info.cus)
-      hipLaunchKernelGGL((split_reduce<T, TN, 64>),
-                         dim3((unsigned)(p.tiles * reduce_blocks_per_tile<TN, 64>())), dim3(64), 0,
-                         stream, p);
-    else
-      hipLaunchKernelGGL((split_reduce<T, TN, 256>), dim3((unsigned)wide), dim3(256), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false, TN>), dim3(grid), dim3(THREADS), 0, stream,
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true, TN, TM>), dim3(grid), dim3(THREADS), 0, stream,
                        p);
+    // (one-wave workgroups where 256-thread ones would not cover the CUs)
+    const int64_t wide = p.tiles * (int64_t)reduce_blocks_per_tile<TN, 256, TM>();
+    if (wide < info.cus)
+      hipLaunchKernelGGL((split_reduce<T, TN, 64, TM>),
+                         dim3((unsigned)(p.tiles * reduce_blocks_per_tile<TN, 64, TM>())), dim3(64),
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL((split_reduce<T, TN, 256, TM>), dim3((unsigned)wide), dim3(256), 0, stream,
+                         p);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false, TN, TM>), dim3(grid), dim3(THREADS), 0,
+                       stream, p);
   }
   return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
@@ -186,13 +188,20 @@ static dense_gemm_status enqueue_width(int64_t M, int64_t N, int64_t K, const vo
                                        int64_t lda, const void* B, int64_t ldb, void* D,
                                        int64_t ldd, const CallPlan& cp, const DeviceInfo& info,
                                        char* ws, hipStream_t stream) {
+  const bool short_tiles = cp.plan[0] == BM / 2;
   if constexpr (LAYOUT == NT) {
     if (cp.small())
       return enqueue_small<T>(M, N, K, A, lda, B, ldb, D, ldd, cp, ws, stream);
     if (cp.plan[1] == BN / 2)
-      return enqueue<T, LAYOUT, BN / 2>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws, stream);
+      return short_tiles
+                 ? enqueue<T, LAYOUT, BN / 2, BM / 2>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws,
+                                                      stream)
+                 : enqueue<T, LAYOUT, BN / 2, BM>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws,
+                                                  stream);
   }
-  return enqueue<T, LAYOUT, BN>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws, stream);
+  return short_tiles
+             ? enqueue<T, LAYOUT, BN, BM / 2>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws, stream)
+             : enqueue<T, LAYOUT, BN, BM>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws, stream);
 }
 
 // A call with the caller's workspace (ws, ws_bytes): nothing is allocated.

@@ -17,7 +17,8 @@
 //     shared-memory layouts);
 //   * v_mfma_f32_16x16x32_{f16,bf16} with FP32 accumulators; four waves each
 //     own a 128 x 128 quarter of a 256 x 256 tile (128 x 64 of a 256 x 128
-//     tile for narrow A @ B.T outputs) and read the shared A and B stages
+//     tile for narrow A @ B.T outputs; 64 rows of a 128-row tile where M <=
+//     128) and read the shared A and B stages
 //     ("TIRx GEMM on Blackwell", V8/V9: larger tiles and several consumers
 //     reusing one staged operand tile);
 //   * an epilogue that rounds to the output type, stages each wave's rows in
@@ -45,16 +46,19 @@ constexpr int SLOTS3 = 3;            // LDS ring depth of the early operand (bel
 constexpr int SLOTS2 = 2;            // LDS ring depth of the other operand
 constexpr int MK = 32;               // K depth of one MFMA (16 x 16 x 32)
 constexpr int SUB = BK / MK;         // MFMA k-substeps per stage
-constexpr int WTM = 128;             // wave tile rows (columns: half the tile width)
-constexpr int MI = WTM / 16;         // 16 x 16 MFMA blocks per wave, M direction
-constexpr int A_BYTES = BM * BK * 2;           // 32 KiB: 256 rows x 128 B
-constexpr int DMA_PER_OPERAND = A_BYTES / (THREADS * 16);  // 16-byte loads per thread (A)
+// Tile rows TM: 256 (BM), or 128 for products with M <= 128 (half the
+// MFMA work of a 256-row tile that would be half padding).  A wave tile is
+// TM / 2 rows (MI 16-row MFMA blocks); the A tile of a stage is TM rows of
+// 128 B, loaded in TM / 32 16-byte loads per thread.
+template <int TM>
+constexpr int wave_rows() { return TM / 2; }
+template <int TM>
+constexpr int a_loads() { return TM * BK * 2 / (THREADS * 16); }
 // MFMA pairs of the last substep issued before its barrier: the reads of
 // that substep's fragments (issued during the previous substep) complete
 // meanwhile, so the barrier's LDS wait costs nothing
 constexpr int BAR_PAIR = 2;
 
-static_assert(DMA_PER_OPERAND == 8, "each wave fills 8 KiB of the A tile per stage");
 static_assert(BK == 64 && BM == 256 && BN == 256, "swizzles below assume these sizes");
 static_assert(SUB == 2, "the ring schedule below has two substeps per stage");
 
@@ -70,25 +74,32 @@ struct Params {
   // the rest are (tile, part) pairs over the last `tiles` tiles of the
   // order.  Task full_tasks + u is part u / tiles of tile full_tasks +
   // u % tiles; the part covers K steps [part * split_steps, min(nk, (part +
-  // 1) * split_steps)) and writes its FP32 partial tile (row-major BM x TN,
-  // TN the tile width) to ws at index part * tiles + u % tiles
+  // 1) * split_steps)) and writes its FP32 partial tile (row-major TM x TN,
+  // TM and TN the tile's rows and width) to ws at index part * tiles + u %
+  // tiles
   int full_tasks, splits, split_steps, tiles;
   float* ws;
 };
 
-template <int NB>
+template <int MA, int NB>
 struct Frags {
-  u32x4 a[MI];
+  u32x4 a[MA];
   u32x4 b[NB];
 };
 
 // Tile width TN: 256 (four 128 x 128 wave tiles), or for A @ B.T 128 (four
 // 128 x 64 wave tiles): for outputs at most 128 wide (half the work of a
 // half-padded 256-wide tile), and for twice the tiles where 256-wide ones
-// would leave half the CUs idle, at more operand traffic per FLOP.
-template <typename T, int LAYOUT, bool SPLIT, int TN>
+// would leave half the CUs idle, at more operand traffic per FLOP.  Tile
+// rows TM: 256, or 128 where M <= 128 (four 64-row wave tiles).
+template <typename T, int LAYOUT, bool SPLIT, int TN, int TM>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
   static_assert(TN == BN || (TN == BN / 2 && LAYOUT == NT), "tile widths 256, and 128 for A @ B.T");
+  static_assert(TM == BM || TM == BM / 2, "tile rows 256 or 128");
+  constexpr int WTM = wave_rows<TM>();             // wave tile rows
+  constexpr int MI = WTM / 16;                     // 16 x 16 blocks per wave, M direction
+  constexpr int A_BYTES = TM * BK * 2;             // bytes of an A tile (TM rows x 128 B)
+  constexpr int DMA_PER_OPERAND = a_loads<TM>();   // 16-byte loads per thread (A)
   constexpr int WTN = TN / 2;                      // wave tile columns
   constexpr int NI = WTN / 16;                     // 16 x 16 blocks per wave, N direction
   constexpr int PAIRS = MI * NI / 2;               // MFMA pairs per substep
@@ -105,7 +116,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
   constexpr int L_BYTES = EARLY == 0 ? B_TILE : A_BYTES;
   constexpr int RING2 = SLOTS3 * E_BYTES;            // the two-slot ring follows the other
   constexpr int LDS_BYTES = RING2 + SLOTS2 * L_BYTES;  // all 160 KiB for 256-wide tiles
-  using Frags = dg::Frags<NI>;
+  using Frags = dg::Frags<MI, NI>;
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const uint32_t lds0 = lds_addr(smem);
 
@@ -126,9 +137,9 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     // this task's K steps
     const int kbeg = split * p.split_steps;
     const int kend = part ? min(nk, kbeg + p.split_steps) : nk;
-    const int m0 = tm * BM;
+    const int m0 = tm * TM;
     const int n0 = tn * TN;
-    const int vm = min(BM, p.M - m0);  // valid rows of the A tile
+    const int vm = min(TM, p.M - m0);  // valid rows of the A tile
     const int vn = min(TN, p.N - n0);  // valid columns of D in this tile
 
     // MFMA operand layout (16 x 16 x 32): lane l holds row l % 16 of a
@@ -151,9 +162,10 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     fence();
 
     // Loader roles.  K-contiguous tiles: each wave instruction fills 1 KiB =
-    // 8 rows of 128 B; wave w's instruction i covers rows (8w + i) * 8 ...
-    // +7, lane -> row lane/8 of the group and a logical chunk by the swizzle
-    // (which depends on the row's low four bits, i.e. on i's parity).
+    // 8 rows of 128 B; wave w's instruction i of an operand with L loads per
+    // thread covers rows (L w + i) * 8 ... +7, lane -> row lane/8 of the
+    // group and a logical chunk by the swizzle (which depends on the row's
+    // low four bits, i.e. on i's parity, L being even).
     // NN B tile: each wave instruction fills 2 k rows of 512 B.
     const int nn_row_lo = lane >> 5;
 
@@ -199,7 +211,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     for (int h = 0; h < 2; ++h) kc[h] = (lane & 7) ^ swz_k(h * 8 + (lane >> 3));
 #pragma unroll
     for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-      const int r = (8 * wave + i) * 8 + (lane >> 3);
+      const int r = (DMA_PER_OPERAND * wave + i) * 8 + (lane >> 3);
       a_off[i] = r < vm ? (uint32_t)(r * p.lda * 2 + kc[i & 1] * 16) : OOB;
     }
     if (LAYOUT == NT) {
@@ -390,7 +402,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
       // FP32 partial tile, row-major 256 x 256: lane holds row l16 of each
       // 16-row block and columns j*16 + 4*lq .. +3 (16 contiguous bytes);
       // 16 x 16 blocks wholly outside D are skipped (nothing reads them)
-      float* w = p.ws + (size_t)(split * p.tiles + u % p.tiles) * (BM * TN) +
+      float* w = p.ws + (size_t)(split * p.tiles + u % p.tiles) * (TM * TN) +
                  (size_t)(wm * WTM + l16) * TN + wn * WTN + 4 * lq;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
@@ -416,7 +428,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     constexpr int RPI = 64 / CH;      // rows per wave instruction of the read-back
     constexpr int NR = 32 / RPI;      // read-back instructions per band
     char* stg = smem + wave * (32 * CH * 16);
-    const bool interior = p.d_vec && vm == BM && vn == TN;
+    const bool interior = p.d_vec && vm == TM && vn == TN;
 #pragma unroll
     for (int band = 0; band < MI / 2; ++band) {
       // lane holds row half*16 + l16 of the band, columns j*16 + 4*lq + 0..3
@@ -490,29 +502,29 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
 // part order 0, 1, ... (a fixed order: results are reproducible), rounded
 // once to the output type.  One thread per 8 consecutive columns of a row,
 // RT threads per workgroup: a workgroup covers RT / (TN / 8) rows, a split
-// tile BM * TN / (8 RT) workgroups.  The host takes RT = 64 (one wave) when
+// tile TM * TN / (8 RT) workgroups.  The host takes RT = 64 (one wave) when
 // 256-thread workgroups would be fewer than the CUs, so that the partials'
 // reads spread over more CUs (measured with 16 parts of one 128 x 128
 // output: 3.1 against 3.6 us), and RT = 256 otherwise (one-wave workgroups
 // measured up to 1% slower on the split products of the M = 8192 sweep).
-template <int TN, int RT>
-constexpr int reduce_blocks_per_tile() { return BM * TN / (8 * RT); }
-template <typename T, int TN, int RT>
+template <int TN, int RT, int TM>
+constexpr int reduce_blocks_per_tile() { return TM * TN / (8 * RT); }
+template <typename T, int TN, int RT, int TM>
 __global__ __launch_bounds__(RT) void split_reduce(Params p) {
   constexpr int TPR = TN / 8;      // threads per row
   constexpr int RPW = RT / TPR;    // rows per workgroup
-  constexpr int WPT = BM / RPW;    // workgroups per split tile
-  static_assert(RT % TPR == 0 && WPT == reduce_blocks_per_tile<TN, RT>(), "whole rows per workgroup");
+  constexpr int WPT = TM / RPW;    // workgroups per split tile
+  static_assert(RT % TPR == 0 && WPT == reduce_blocks_per_tile<TN, RT, TM>(), "whole rows per workgroup");
   const int st = blockIdx.x / WPT;      // split tile (0 .. tiles-1)
   int tm, tn;
   tile_of_task(p.full_tasks + st, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
   const int r = (blockIdx.x % WPT) * RPW + (int)threadIdx.x / TPR;
   const int c = ((int)threadIdx.x % TPR) * 8;
-  const int row = tm * BM + r;
+  const int row = tm * TM + r;
   const int col = tn * TN + c;
   if (row >= p.M || col >= p.N) return;
-  const float* w = p.ws + (size_t)st * (BM * TN) + (size_t)r * TN + c;
-  const size_t stride = (size_t)p.tiles * (BM * TN);  // between the partials of two splits
+  const float* w = p.ws + (size_t)st * (TM * TN) + (size_t)r * TN + c;
+  const size_t stride = (size_t)p.tiles * (TM * TN);  // between the partials of two splits
   float s[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = 0.0f;

@@ -138,7 +138,10 @@ bool small_output(int layout, int64_t M, int64_t N, int64_t K) {
 
 dense_gemm_status tiled_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t num_cus,
                              int64_t* out) {
-  const int64_t tiles_m = (M + BM - 1) / BM;
+  // Tile rows: 256, or 128 when M <= 128 (one tile row either way, half the
+  // MFMA work of a 256-row tile that would be half padding).
+  const int64_t tr = M <= BM / 2 ? BM / 2 : BM;
+  const int64_t tiles_m = (M + tr - 1) / tr;
   // Tile width: 256, or for A @ B.T 128
   //   * when the output is at most 128 wide: the same single tile column,
   //     with half the MFMA work and B traffic of a 256-wide tile that would
@@ -157,7 +160,7 @@ dense_gemm_status tiled_plan(int layout, int64_t M, int64_t N, int64_t K, int64_
   const int64_t tiles_n = (N + tw - 1) / tw;
   const int64_t tasks = tiles_m * tiles_n;
   const int64_t grid = tasks < num_cus ? tasks : num_cus;
-  out[0] = BM;
+  out[0] = tr;
   out[1] = tw;
   out[2] = BK;
   out[3] = tiles_m;
@@ -293,7 +296,7 @@ dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const v
   if (!cp->a_direct && !bytes_of((size_t)M, (size_t)K8, 2, &cp->a_bytes)) return DENSE_GEMM_TOO_LARGE;
   if (!cp->b_direct && !bytes_of((size_t)b_rows, (size_t)b_dcols, 2, &cp->b_bytes))
     return DENSE_GEMM_TOO_LARGE;
-  if (plan[8] > 1 && !bytes_of((size_t)plan[8] * (size_t)cp->split_tiles, (size_t)BM * plan[1],
+  if (plan[8] > 1 && !bytes_of((size_t)plan[8] * (size_t)cp->split_tiles, (size_t)plan[0] * plan[1],
                                sizeof(float), &cp->split_bytes))
     return DENSE_GEMM_TOO_LARGE;
   if (cp->a_bytes + cp->b_bytes + cp->split_bytes > cap) return DENSE_GEMM_TOO_LARGE;

@@ -50,13 +50,14 @@
  * tiles are computed whole in the same launch.  dense_gemm_ex can force a
  * number of parts, or none (dense_gemm_options).
  *
- * Tile width.  Output tiles are 256 x 256.  For D = A @ B.T they are
- * 256 x 128 instead when N <= 128 (one tile column either way, half the
+ * Tile width and rows.  Output tiles are 256 x 256.  For D = A @ B.T they
+ * are 256 x 128 instead when N <= 128 (one tile column either way, half the
  * work of a half-empty 256-wide tile), or when 256-wide tiles would occupy
  * at most half the CUs and the operands take at most 192 MiB (twice the
- * tiles, one wave).  Either width sums each output in the same order, so
- * unsplit results are identical.  dense_gemm_ex can force the width of
- * A @ B.T.
+ * tiles, one wave).  Products with M <= 128 use tiles of 128 rows (one tile
+ * row either way, half the work of a half-empty 256-row tile).  Every tile
+ * shape sums each output in the same order, so unsplit results are
+ * identical.  dense_gemm_ex can force the width of A @ B.T.
  *
  * Small outputs.  D = A @ B.T with M <= 128 and K <= 16384 whose 16 x 16
  * tiles number at most 512, or form a single tile row (M <= 16), runs a
@@ -309,8 +310,9 @@ dense_gemm_status dense_gemm_tile_of_task(int64_t task, int64_t tiles_m, int64_t
                                           int64_t group_m, int64_t* tile_m, int64_t* tile_n);
 
 /* The launch plan for a problem on a device with num_cus compute units.
- * Writes 10 values to out: BM, the tile width BN (256, or 128 as described
- * under "Tile width" above), BK, tiles_m, tiles_n, grid (workgroups of the
+ * Writes 10 values to out: the tile rows BM (256, or 128 when M <= 128),
+ * the tile width BN (256, or 128 as described under "Tile width and rows"
+ * above), BK, tiles_m, tiles_n, grid (workgroups of the
  * GEMM kernel), group_m, threads per workgroup, the number of K splits
  * (1: none) and the K steps (of BK) per split.  For the small-output kernel
  * ("Small outputs" above) BM = BN = 16, the grid is tiles_m * tiles_n

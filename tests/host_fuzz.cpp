@@ -60,10 +60,11 @@ static void check_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t cus,
     check_repack(layout, M, N, K, cp);
     return;
   }
-  CHECK(p[0] == BM && p[2] == BK && p[7] == THREADS);
+  // 128 tile rows exactly when M <= 128
+  CHECK(p[0] == (M <= BM / 2 ? BM / 2 : BM) && p[2] == BK && p[7] == THREADS);
   CHECK(p[1] == BN || (p[1] == BN / 2 && layout == NT));
   if (opt && opt->tile_n) CHECK(p[1] == opt->tile_n);
-  CHECK(p[3] == ceil_div(M, BM) && p[4] == ceil_div(N, p[1]));
+  CHECK(p[3] == ceil_div(M, p[0]) && p[4] == ceil_div(N, p[1]));
   CHECK(p[6] >= 1 && p[6] <= 8 && p[6] <= p[3]);
   const int64_t tasks = p[3] * p[4], nk = ceil_div(K, BK);
   CHECK(cp.full_tasks + cp.split_tiles == tasks);
@@ -73,7 +74,7 @@ static void check_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t cus,
     // every K step in exactly one part, no empty part
     CHECK(p[8] * p[9] >= nk && (p[8] - 1) * p[9] < nk);
     CHECK(cp.split_tiles > 0);
-    CHECK(cp.split_bytes == (size_t)p[8] * (size_t)cp.split_tiles * BM * (size_t)p[1] * 4);
+    CHECK(cp.split_bytes == (size_t)p[8] * (size_t)cp.split_tiles * (size_t)p[0] * (size_t)p[1] * 4);
     if (!(opt && opt->split_k > 1)) {
       // the library's own split: the last partial wave, at most one part per CU
       CHECK(cp.split_tiles == (tasks < cus ? tasks : tasks % cus));

@@ -326,6 +326,22 @@ def test_plan_tile_width():
                 assert out[3] * out[4] <= 256
 
 
+def test_plan_tile_rows():
+    # 128-row tiles exactly when M <= 128 (on the tiled kernel)
+    lib = binding.load_library()
+    out = (ctypes.c_int64 * 10)()
+    for layout, M, N, K, rows in [(NT, 64, 4096, 4096, 128), (NT, 128, 16384, 4096, 128),
+                                  (NN, 128, 128, 4096, 128), (NN, 1, 264, 4096, 128),
+                                  (NT, 128, 128, 20000, 128), (NT, 129, 16384, 4096, 256),
+                                  (NN, 200, 1000, 1000, 256), (NT, 4096, 4096, 4096, 256)]:
+        assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
+        assert (out[0], out[3]) == (rows, -(-M // rows)), (layout, M, N, K, list(out))
+    # split partial tiles are 128 rows then: 8 parts of 128 x 128 FP32 on 32 tiles
+    assert lib.dense_gemm_plan(NT, 64, 4096, 4096, 256, out) == S.OK
+    assert (out[1], out[4], out[8]) == (128, 32, 8)
+    assert _ws("nt", "f16", 64, 4096, 4096) == (S.OK, 8 * 32 * 128 * 128 * 4)
+
+
 def test_plan_small_output():
     # A.B^T with M <= 128, K <= 16384 and at most 512 16 x 16 tiles of D, or
     # one tile row (M <= 16) of any width: the small-output kernel, one
@@ -344,13 +360,14 @@ def test_plan_small_output():
                             (NT, 128, 1040, 64), (NT, 1, 4096, 16392), (NN, 128, 128, 4096),
                             (NN, 1, 16, 64)]:
         assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
-        assert (out[0], out[7]) == (256, 256), (layout, M, N, K)
+        # (128 tile rows where M <= 128)
+        assert (out[0], out[7]) == (128 if M <= 128 else 256, 256), (layout, M, N, K)
     # it needs no workspace, and an option asks for the tiled kernel instead
     assert _ws("nt", "f16", 128, 128, 4096) == (S.OK, 0)
-    assert _ws("nt", "f16", 128, 128, 4096, opts=(16, 0)) == (S.OK, 16 * 256 * 128 * 4)
+    assert _ws("nt", "f16", 128, 128, 4096, opts=(16, 0)) == (S.OK, 16 * 128 * 128 * 4)
     assert _ws("nt", "f16", 128, 128, 4096, opts=(1, 0)) == (S.OK, 0)
-    # (the tiled kernel's own plan there: 128-wide, 16 parts)
-    assert _ws("nt", "f16", 128, 128, 4096, opts=(0, 128)) == (S.OK, 16 * 256 * 128 * 4)
+    # (the tiled kernel's own plan there: 128 x 128 tiles, 16 parts)
+    assert _ws("nt", "f16", 128, 128, 4096, opts=(0, 128)) == (S.OK, 16 * 128 * 128 * 4)
     # ... or repacks, like the tiled kernel, an operand it cannot read in place
     assert _ws("nt", "f16", 128, 128, 4095) == (S.OK, 2 * 128 * 4096 * 2)
 

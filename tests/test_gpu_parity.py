@@ -306,6 +306,51 @@ def test_small_output_kernel_small_integers_exact(fmt):
     assert (Dt == D).all()
 
 
+# ------------------------------------------------------ 128-row tiles --
+
+TALL = [
+    # (layout, fmt, M, N, K) for the tiled kernel with 128-row tiles (M <= 128
+    # and not a small-output product: K > 16384, more than 512 tiles of 16 x
+    # 16 with M > 16, or A.B): both widths, split and unsplit, ragged edges
+    ("nt", "f16", 64, 8200, 1000), ("nt", "bf16", 100, 4200, 2000),
+    ("nt", "f16", 128, 128, 20000), ("nn", "bf16", 128, 1000, 3000), ("nn", "f16", 17, 600, 520),
+    ("nn", "bf16", 1, 264, 4096),
+]
+
+
+@pytest.mark.parametrize("layout,fmt,M,N,K", TALL, ids=lambda v: str(v))
+def test_128_row_tiles_full_check(layout, fmt, M, N, K):
+    import ctypes
+    from dense_gemm_08_amd import binding
+    out = (ctypes.c_int64 * 10)()
+    assert binding.load_library().dense_gemm_plan(0 if layout == "nt" else 1, M, N, K, 256,
+                                                  out) == 0
+    assert out[0] == 128, list(out)
+    w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 121)
+    A, B = inputs.make_operands(w, seed=M + N + K, M=M, N=N, K=K)
+    D, st = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    assert st == status().OK
+    check_full(layout, fmt, A, B, M, N, K, D)
+    D2, _ = _gpu.gemm(layout, fmt, A, B, M, N, K)
+    assert (D == D2).all()
+
+
+@pytest.mark.parametrize("layout,fmt", [("nt", "f16"), ("nn", "bf16")])
+def test_128_row_tiles_equal_256_row_tiles(layout, fmt):
+    # each output accumulates its K steps in the same order whatever the tile
+    # rows: the M = 128 product (128-row tiles) equals rows 0..127 of the
+    # M = 129 product (256-row tiles) bit for bit, split-K off
+    w = inputs.Workload("x", layout, fmt, 0, 0, 0, "uniform", 0.0, 131)
+    N, K = 1000, 1200
+    A, B = inputs.make_operands(w, M=129, N=N, K=K)
+    D129, st = _gpu.gemm(layout, fmt, A, B, 129, N, K, opts=(1, 0))
+    assert st == status().OK
+    D128, st = _gpu.gemm(layout, fmt, A[:128], B, 128, N, K, opts=(1, 0))
+    assert st == status().OK
+    assert (D128 == D129[:128]).all()
+    check_full(layout, fmt, A[:128], B, 128, N, K, D128)
+
+
 # ------------------------------------------------------------ edge paths --
 
 SWEEP = [1, 7, 8, 33, 65, 129, 255, 257]
