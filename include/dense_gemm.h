@@ -219,7 +219,10 @@ dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N, int64_t K,
  * exact in FP32; their sum is accumulated in FP32 in a fixed order.  The call
  * takes a workspace of 1 KiB per 256-row tile of A and of B per 128 K
  * values for the repacked scales (hipMallocAsync / hipFreeAsync on `stream`;
- * DENSE_GEMM_NO_MEMORY if unavailable).  The other rules (zeros for K == 0,
+ * DENSE_GEMM_NO_MEMORY if unavailable), except for small outputs (M <= 128,
+ * K <= 8192, at most 512 tiles of 16 x 16 or M <= 16), which run a
+ * small-output kernel (16 x 16 tiles, K split among eight waves, the scales
+ * staged in LDS) that needs none.  The other rules (zeros for K == 0,
  * ownership, stream order, errors) are those stated at the top of this file. */
 dense_gemm_status gemm_nt_e4m3_mx(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                   const void* SA, int64_t ldsa, const void* B, int64_t ldb,

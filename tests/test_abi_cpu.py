@@ -508,6 +508,13 @@ def test_mx_workspace_size():
     assert ws(280, 300, 160) == (S.OK, (2 + 2) * 2 * 1024)
     assert ws(256, 256, 0) == (S.OK, 2 * 1024)
     assert ws(0, 256, 64) == (S.OK, 0)
+    # the small-output kernel (M <= 128, K <= 8192, at most 512 tiles of
+    # 16 x 16 or one tile row) stages its scales in LDS: no workspace
+    assert ws(128, 128, 4096) == (S.OK, 0)
+    assert ws(16, 65536, 8192) == (S.OK, 0)
+    assert ws(64, 1100, 2080) == (S.OK, 0)
+    assert ws(128, 128, 8224) == (S.OK, (1 + 1) * 65 * 1024)
+    assert ws(17, 8200, 512) == (S.OK, (1 + 33) * 4 * 1024)
     assert ws(8, 8, 40)[0] == S.BAD_ARG
     assert ws(-1, 8, 32)[0] == S.INVALID_DIM
     assert S(lib.gemm_nt_e4m3_mx_workspace_size(8, 8, 32, None)) == S.BAD_ARG

@@ -293,3 +293,84 @@ def test_mx_scale_range_ends(case):
     else:
         # only the rows built to overflow are exempt; the rest pass the bound
         assert checked >= (M - 16) * N and 0 < exempt <= 16 * N
+
+
+# ------------------------------------------------ the small-output kernel --
+
+MX_SMALL = [
+    # (M, N, K) for the small-output kernel (M <= 128, K <= 8192, at most
+    # 512 tiles of 16 x 16 or one tile row): K mod 128 = 0, 32, 64, 96, the
+    # longest K, one tile row past 512 tiles, ragged tiles, one block
+    (128, 128, 4096), (100, 72, 8192), (1, 4096, 1024), (16, 8200, 480), (128, 1024, 96),
+    (5, 300, 224), (33, 17, 32),
+]
+
+
+def _mx_small(M, N, K):
+    import ctypes
+    from dense_gemm_08_amd import binding
+    need = ctypes.c_size_t(1)
+    assert binding.load_library().gemm_nt_e4m3_mx_workspace_size(M, N, K, ctypes.byref(need)) == 0
+    return need.value == 0
+
+
+@pytest.mark.parametrize("kind", ["quantised", "codes"])
+@pytest.mark.parametrize("M,N,K", MX_SMALL, ids=lambda v: str(v))
+def test_mx_small_output_full_parity(kind, M, N, K):
+    assert _mx_small(M, N, K), "planned for the tiled kernel"
+    A, SA, B, SB = inputs.mx_operands(M, N, K, seed=M + 7 * N + K + 1, kind=kind)
+    D, st = run_mx(A, SA, B, SB)
+    assert st == status().OK
+    check_full(A, SA, B, SB, D)
+    # the eight waves' sums are added in a fixed order: a rerun is equal
+    D2, _ = run_mx(A, SA, B, SB)
+    assert np.array_equal(D, D2)
+
+
+def test_mx_small_output_small_integers_bit_exact_and_leading_dimensions():
+    M, N, K = 120, 200, 2048
+    assert _mx_small(M, N, K)
+    A, SA, B, SB = inputs.mx_small_integers(M, N, K, seed=K + 1)
+    d, _ = oracle.gemm_mx(A, SA, B, SB)
+    want = oracle.round_to("bf16", d)
+    D, st = run_mx(A, SA, B, SB)
+    assert st == status().OK
+    assert np.array_equal(D, want), np.argwhere(D != want)[:5]
+    # padded rows (NaN codes in the padding) and an odd-sized D row: the
+    # kernel reads only [0, K) of each row and [0, K/32) of each scale row
+    D, st = run_mx(A, SA, B, SB, lda=K + 48, ldb=K + 16, ldsa=K // 32 + 3, ldsb=K // 32 + 1,
+                   ldd=N + 3)
+    assert st == status().OK
+    assert np.array_equal(D[:, :N], want)
+    assert (D[:, N:] == _gpu.CANARY).all()
+
+
+def test_mx_small_output_nan_propagates_like_the_oracle():
+    M, N, K = 64, 80, 256
+    assert _mx_small(M, N, K)
+    A, SA, B, SB = inputs.mx_operands(M, N, K, seed=16)
+    SA[3, 1] = 255   # E8M0 NaN: row 3 of D is NaN
+    SB[7, 6] = 255   # column 7 of D is NaN
+    A[5, 100] = 0x7F  # E4M3 NaN: row 5 of D is NaN
+    D, st = run_mx(A, SA, B, SB)
+    assert st == status().OK
+    d, s = oracle.gemm_mx(A, SA, B, SB)
+    g = oracle.decode("bf16", D)
+    assert np.array_equal(np.isnan(g), np.isnan(d))
+    ok = ~np.isnan(d)
+    res = oracle.check("bf16", d[ok], s[ok], D[ok])
+    assert res.ok, res
+
+
+@pytest.mark.parametrize("case", ["compensated", "top", "bottom_subnormal", "overflow_rows"])
+def test_mx_small_output_scale_range_ends(case):
+    M, N, K = 64, 272, 512
+    assert _mx_small(M, N, K)
+    A, SA, B, SB = _range_operands(case, M, N, K, seed=len(case) + 1)
+    D, st = run_mx(A, SA, B, SB)
+    assert st == status().OK
+    checked, exempt, nonfinite = _check_in_fp32_range(A, SA, B, SB, D)
+    if case == "overflow_rows":
+        assert checked >= (M - 16) * N and 0 < exempt <= 16 * N
+    else:
+        assert exempt == 0 and checked == M * N
