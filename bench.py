@@ -529,7 +529,8 @@ def main():
         if args.workspace:
             import ctypes
             need = ctypes.c_size_t()
-            assert lib.gemm_nt_e4m3_mx_workspace_size(w.M, w.N, w.K, ctypes.byref(need)) == 0
+            assert lib.gemm_nt_e4m3_mx_workspace_size(w.M, w.N, w.K, 0,
+                                                      ctypes.byref(need)) == 0
             ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
 
             def step():
@@ -689,17 +690,20 @@ def main():
 
 def source_sha(name: str = "gemm_kernel.h") -> str:
     """sha256 prefix of a kernel source (gemm_kernel.h with
-    gemm_small_kernel.h, or gemm_mx_kernel.h), the headers it shares and the
-    launch planning (plan.cpp), with comments and
-    blank space removed: the traffic figures recorded for it stay valid
-    across comment edits and other host-side changes, not across changes of
-    the kernels or of which kernels a call runs."""
+    gemm_small_kernel.h, or gemm_mx_kernel.h), the headers it shares (the
+    split-K reduction's included) and the launch planning (plan.cpp,
+    plan.h), with comments and blank space removed: the traffic figures
+    recorded for it stay valid across comment edits and other host-side
+    changes, not across changes of the kernels or of which kernels a call
+    runs."""
     import hashlib
     import re
     h = hashlib.sha256()
-    # (plan.cpp decides the kernel, the tile widths and splits, i.e. which
-    # kernels run; FP16/BF16 products may run the small-output kernel)
-    files = [name, "cdna_ops.h", "tile_sched.h", "tile_config.h", "plan.cpp"]
+    # (plan.cpp and plan.h decide the kernel, the tile shapes and splits,
+    # i.e. which kernels run; FP16/BF16 products may run the small-output
+    # kernel)
+    files = [name, "cdna_ops.h", "tile_sched.h", "tile_config.h", "split_reduce.h", "plan.cpp",
+             "plan.h"]
     if name == "gemm_kernel.h":
         files.append("gemm_small_kernel.h")
     for f in files:

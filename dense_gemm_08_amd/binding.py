@@ -73,7 +73,9 @@ SIGNATURES = {
     "dense_gemm_ex": ([_i32] + _GEMM_ARGS[:-1] + [ctypes.POINTER(Options), _vp, ctypes.c_size_t,
                                                  _vp], _i32),
     "gemm_nt_f16_noalloc": (_GEMM_ARGS, _i32),
-    "gemm_nt_e4m3_mx_workspace_size": ([_i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)], _i32),
+    "gemm_nt_e4m3_mx_workspace_size": ([_i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)],
+                                       _i32),
+    "gemm_nt_e4m3_mx_plan": ([_i64, _i64, _i64, _i64, ctypes.POINTER(_i64)], _i32),
     "gemm_nt_e4m3_mx_ex": ([_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                             _i64, _vp, ctypes.c_size_t, _vp], _i32),
 }

@@ -17,6 +17,7 @@
 #include "gemm_kernel.h"
 #include "gemm_small_kernel.h"
 #include "plan.h"
+#include "split_reduce.h"
 
 namespace dg {
 
@@ -142,15 +143,9 @@ static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A,
     // summed by a second kernel
     hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true, TN, TM>), dim3(grid), dim3(THREADS), 0, stream,
                        p);
-    // (one-wave workgroups where 256-thread ones would not cover the CUs)
-    const int64_t wide = p.tiles * (int64_t)reduce_blocks_per_tile<TN, 256, TM>();
-    if (wide < info.cus)
-      hipLaunchKernelGGL((split_reduce<T, TN, 64, TM>),
-                         dim3((unsigned)(p.tiles * reduce_blocks_per_tile<TN, 64, TM>())), dim3(64),
-                         0, stream, p);
-    else
-      hipLaunchKernelGGL((split_reduce<T, TN, 256, TM>), dim3((unsigned)wide), dim3(256), 0, stream,
-                         p);
+    const ReduceParams r = {p.D, p.ws, p.M, p.N, p.ldd, p.tiles_m, p.tiles_n, p.group_m,
+                            p.full_tasks, p.splits, p.tiles, p.d_vec};
+    enqueue_split_reduce<T, TN, TM>(r, info.cus, stream);
   } else {
     hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false, TN, TM>), dim3(grid), dim3(THREADS), 0,
                        stream, p);

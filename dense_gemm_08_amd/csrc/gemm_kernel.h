@@ -1,5 +1,6 @@
 // gemm_kernel.h -- the FP16/BF16 tiled GEMM kernels for the MI355X (gfx950):
-// the persistent GEMM kernel, the split-K reduction and the operand repack.
+// the persistent GEMM kernel and the operand repack (the split-K reduction
+// is in split_reduce.h).
 //
 // Kernel structure (one persistent workgroup per CU):
 //   * a persistent loop over output tiles in the grouped, XCD-aware order of
@@ -27,9 +28,9 @@
 //   * ragged M, N and K handled by masking: out-of-range loads read zeros
 //     through the buffer descriptor's range check, out-of-range stores are
 //     skipped (the pages' shapes all divide the tiles; this is our reading);
-//   * split-K for the last, partial wave of tiles, and a repack of operands
-//     the 16-byte loads cannot read in place (chosen by the host side,
-//     dense_gemm.hip).
+//   * split-K for the last, partial wave of tiles (the parts' FP32 tiles
+//     summed by split_reduce.h), and a repack of operands the 16-byte loads
+//     cannot read in place (chosen by the host side, dense_gemm.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -495,72 +496,6 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Params p) {
     // staging reads done before the next tile refills the ring; the stores
     // drain while the next tile's first loads are in flight
     wait_lds_barrier();
-  }
-}
-
-// Sum of the split-K partials of every output element of the split tiles in
-// part order 0, 1, ... (a fixed order: results are reproducible), rounded
-// once to the output type.  One thread per 8 consecutive columns of a row,
-// RT threads per workgroup: a workgroup covers RT / (TN / 8) rows, a split
-// tile TM * TN / (8 RT) workgroups.  The host takes RT = 64 (one wave) when
-// 256-thread workgroups would be fewer than the CUs, so that the partials'
-// reads spread over more CUs (measured with 16 parts of one 128 x 128
-// output: 3.1 against 3.6 us), and RT = 256 otherwise (one-wave workgroups
-// measured up to 1% slower on the split products of the M = 8192 sweep).
-template <int TN, int RT, int TM>
-constexpr int reduce_blocks_per_tile() { return TM * TN / (8 * RT); }
-template <typename T, int TN, int RT, int TM>
-__global__ __launch_bounds__(RT) void split_reduce(Params p) {
-  constexpr int TPR = TN / 8;      // threads per row
-  constexpr int RPW = RT / TPR;    // rows per workgroup
-  constexpr int WPT = TM / RPW;    // workgroups per split tile
-  static_assert(RT % TPR == 0 && WPT == reduce_blocks_per_tile<TN, RT, TM>(), "whole rows per workgroup");
-  const int st = blockIdx.x / WPT;      // split tile (0 .. tiles-1)
-  int tm, tn;
-  tile_of_task(p.full_tasks + st, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
-  const int r = (blockIdx.x % WPT) * RPW + (int)threadIdx.x / TPR;
-  const int c = ((int)threadIdx.x % TPR) * 8;
-  const int row = tm * TM + r;
-  const int col = tn * TN + c;
-  if (row >= p.M || col >= p.N) return;
-  const float* w = p.ws + (size_t)st * (TM * TN) + (size_t)r * TN + c;
-  const size_t stride = (size_t)p.tiles * (TM * TN);  // between the partials of two splits
-  float s[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] = 0.0f;
-  // U splits' loads in flight at once, then added in split order: 16 for the
-  // few one-wave workgroups, 8 (half the registers, so more waves per SIMD)
-  // for the wide launches
-  constexpr int U = RT == 64 ? 16 : 8;
-  for (int k0 = 0; k0 < p.splits; k0 += U) {
-    float4 a[U], b[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (k0 + u < p.splits) {
-        a[u] = *(const float4*)(w + (k0 + u) * stride);
-        b[u] = *(const float4*)(w + (k0 + u) * stride + 4);
-      } else {
-        a[u] = b[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (k0 + u < p.splits) {
-        s[0] += a[u].x; s[1] += a[u].y; s[2] += a[u].z; s[3] += a[u].w;
-        s[4] += b[u].x; s[5] += b[u].y; s[6] += b[u].z; s[7] += b[u].w;
-      }
-    }
-  }
-  u32x4 v;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = pack2<T>(s[2 * e], s[2 * e + 1]);
-  uint16_t* dst = p.D + (int64_t)row * p.ldd + col;
-  if (p.d_vec && col + 8 <= p.N) {
-    __builtin_nontemporal_store(v, (u32x4*)dst);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (col + e < p.N) dst[e] = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
   }
 }
 

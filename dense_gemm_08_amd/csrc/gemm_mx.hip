@@ -1,11 +1,14 @@
 // gemm_mx.hip -- host side of the FP8 block-scaled GEMM for the MI355X
-// (gfx950): argument checks, workspace and the C ABI.  The operation and
-// the kernel design are described in gemm_mx_kernel.h.
+// (gfx950): argument checks, the launches and the C ABI.  The operation and
+// the kernel design are described in gemm_mx_kernel.h, the plan (kernel,
+// split-K, workspace) is made in plan.cpp.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "dense_gemm.h"
 #include "gemm_mx_kernel.h"
+#include "plan.h"
+#include "split_reduce.h"
 
 namespace dg {
 
@@ -40,35 +43,15 @@ static dense_gemm_status validate(int64_t M, int64_t N, int64_t K, const void* A
   return DENSE_GEMM_OK;
 }
 
-// Products the small-output kernel computes (gemm_mx_small): M <= 128, K
-// <= MX_SMALL_K_MAX, at most SMALL_MAX_TILES tiles of 16 x 16 or one tile
-// row.  Measured per call against the tiled kernel (its scale packing and
-// workspace included), one box: 128 x 128 x 4096 6.2 against 45.3 us,
-// 1 x 4096 x 4096 6.2 against 44.5, 16 x 16384 x 4096 21.3 against 48.3,
-// 128 x 1024 x 8192 12.3 against 75.6, 128 x 128 x 64 4.5 against 23.1.
-static bool small_output(int64_t M, int64_t N, int64_t K) {
-  if (M > SMALL_MAX || K > MX_SMALL_K_MAX) return false;
-  const int64_t tiles = ((M + SMALL_TILE - 1) / SMALL_TILE) * ((N + SMALL_TILE - 1) / SMALL_TILE);
-  return tiles <= SMALL_MAX_TILES || M <= SMALL_TILE;
-}
-
-// Workspace of a call: the packed scale panels, 1 KiB per 256-row tile of A
-// and of B per 128-deep K stage (at least one stage); none for the
-// small-output kernel, which stages the scales in LDS itself.
-static size_t workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || small_output(M, N, K)) return 0;
-  const int64_t tiles = (M + BM - 1) / BM + (N + BN - 1) / BN;
-  const int64_t nks = (K + BKE - 1) / BKE;
-  return (size_t)tiles * (size_t)(nks > 0 ? nks : 1) * SC_BYTES;
-}
-
 // The launches of a validated call with M, N > 0 into a workspace of at
-// least workspace_bytes(M, N, K).
+// least mp.total() bytes (256-byte aligned; null when that is 0).
 static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                  const void* SA, int64_t ldsa, const void* B, int64_t ldb,
-                                 const void* SB, int64_t ldsb, void* D, int64_t ldd, uint8_t* ws,
-                                 int cus, int xcds, hipStream_t stream) {
-  if (small_output(M, N, K)) {
+                                 const void* SB, int64_t ldsb, void* D, int64_t ldd,
+                                 const MxPlan& mp, uint8_t* ws, int cus, int xcds,
+                                 hipStream_t stream) {
+  const int64_t* plan = mp.plan;
+  if (mp.small()) {
     MxSmallParams q;
     q.A = (const uint8_t*)A;
     q.B = (const uint8_t*)B;
@@ -83,10 +66,10 @@ static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A,
     q.ldsa = (int)ldsa;
     q.ldsb = (int)ldsb;
     q.ldd = (int)ldd;
-    q.tiles_n = (int)((N + SMALL_TILE - 1) / SMALL_TILE);
+    q.tiles_n = (int)plan[4];
     q.d_vec = (((uintptr_t)D & 7) == 0 && (ldd & 3) == 0) ? 1 : 0;
-    const int64_t tiles = ((M + SMALL_TILE - 1) / SMALL_TILE) * q.tiles_n;
-    hipLaunchKernelGGL(gemm_mx_small, dim3((unsigned)tiles), dim3(SMALL_THREADS), 0, stream, q);
+    hipLaunchKernelGGL(gemm_mx_small, dim3((unsigned)(plan[3] * plan[4])), dim3(SMALL_THREADS), 0,
+                       stream, q);
     return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
   }
   MxParams p;
@@ -99,17 +82,21 @@ static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A,
   p.lda = (int)lda;
   p.ldb = (int)ldb;
   p.ldd = (int)ldd;
-  p.tiles_m = (int)((M + BM - 1) / BM);
-  p.tiles_n = (int)((N + BN - 1) / BN);
-  p.group_m = p.tiles_m < 8 ? p.tiles_m : 8;
-  p.num_tasks = p.tiles_m * p.tiles_n;
+  p.tiles_m = (int)plan[3];
+  p.tiles_n = (int)plan[4];
+  p.group_m = (int)plan[6];
   p.num_xcds = xcds;
   p.d_vec = (((uintptr_t)D & 15) == 0 && (ldd & 7) == 0) ? 1 : 0;
   p.nks = (int)((K + BKE - 1) / BKE);
   p.koff = (int)((BKE - K % BKE) % BKE);
-  const size_t pa = (size_t)p.tiles_m * (p.nks > 0 ? p.nks : 1) * SC_BYTES;
   p.PSA = ws;
-  p.PSB = ws + pa;
+  p.PSB = ws + mp.panel_bytes[0];
+  p.full_tasks = (int)mp.full_tasks;
+  p.tiles = (int)mp.split_tiles;
+  p.splits = (int)plan[8];
+  p.split_steps = (int)plan[9];
+  p.num_tasks = (int)(mp.full_tasks + mp.split_tiles * plan[8]);
+  p.ws = plan[8] > 1 ? (float*)(ws + mp.panel_bytes[0] + mp.panel_bytes[1]) : nullptr;
   if (p.nks > 0) {
     PackArgs pk{{(const uint8_t*)SA, (const uint8_t*)SB}, {p.M, p.N}, {(int)ldsa, (int)ldsb},
                 {p.tiles_m, p.tiles_n}};
@@ -118,8 +105,17 @@ static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A,
                             (unsigned)((p.nks + PACK_STAGES - 1) / PACK_STAGES)),
                        dim3(256), 0, stream, pk, (int)(K / GROUP), p.nks, p.koff, ws);
   }
-  hipLaunchKernelGGL(gemm_mx_kernel, dim3((unsigned)(p.num_tasks < cus ? p.num_tasks : cus)),
-                     dim3(THREADS), 0, stream, p);
+  const unsigned grid = (unsigned)(p.num_tasks < cus ? p.num_tasks : cus);
+  if (p.splits > 1) {
+    // whole tiles, then the parts of the split tiles writing FP32 partials,
+    // summed in part order and rounded to BF16 by the reduction
+    hipLaunchKernelGGL(gemm_mx_kernel<true>, dim3(grid), dim3(THREADS), 0, stream, p);
+    const ReduceParams r = {p.D, p.ws, p.M, p.N, p.ldd, p.tiles_m, p.tiles_n, p.group_m,
+                            p.full_tasks, p.splits, p.tiles, p.d_vec};
+    enqueue_split_reduce<__bf16, BN, BM>(r, cus, stream);
+  } else {
+    hipLaunchKernelGGL(gemm_mx_kernel<false>, dim3(grid), dim3(THREADS), 0, stream, p);
+  }
   return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
 
@@ -130,14 +126,25 @@ using namespace dg;
 
 extern "C" {
 
-dense_gemm_status gemm_nt_e4m3_mx_workspace_size(int64_t M, int64_t N, int64_t K, size_t* bytes) {
-  if (bytes == nullptr) return DENSE_GEMM_BAD_ARG;
+dense_gemm_status gemm_nt_e4m3_mx_workspace_size(int64_t M, int64_t N, int64_t K,
+                                                  int64_t num_cus, size_t* bytes) {
+  if (bytes == nullptr || num_cus < 0) return DENSE_GEMM_BAD_ARG;
   if (M < 0 || N < 0 || K < 0) return DENSE_GEMM_INVALID_DIM;
   if (K % mx::GROUP != 0) return DENSE_GEMM_BAD_ARG;
   const int64_t lim = (int64_t)1 << 31;
   if (M >= lim || N >= lim || K >= lim) return DENSE_GEMM_TOO_LARGE;
-  *bytes = mx::workspace_bytes(M, N, K);
-  return DENSE_GEMM_OK;
+  *bytes = 0;
+  if (M == 0 || N == 0) return DENSE_GEMM_OK;
+  if (num_cus == 0) {
+    int cus = 0, xcds = 1;
+    const dense_gemm_status st = device_topology(&cus, &xcds);
+    if (st != DENSE_GEMM_OK) return st;
+    num_cus = cus;
+  }
+  MxPlan mp;
+  const dense_gemm_status st = mx_plan_call(M, N, K, num_cus, &mp);
+  if (st == DENSE_GEMM_OK) *bytes = mp.total();
+  return st;
 }
 
 dense_gemm_status gemm_nt_e4m3_mx_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -150,12 +157,15 @@ dense_gemm_status gemm_nt_e4m3_mx_ex(int64_t M, int64_t N, int64_t K, const void
   int cus = 0, xcds = 1;
   st = device_topology(&cus, &xcds);
   if (st != DENSE_GEMM_OK) return st;
-  const size_t need = mx::workspace_bytes(M, N, K);
+  MxPlan mp;
+  st = mx_plan_call(M, N, K, cus, &mp);
+  if (st != DENSE_GEMM_OK) return st;
+  const size_t need = mp.total();
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return DENSE_GEMM_WORKSPACE_TOO_SMALL;
     if (((uintptr_t)workspace & 255) != 0) return DENSE_GEMM_MISALIGNED;
   }
-  return mx::enqueue(M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, D, ldd, (uint8_t*)workspace,
+  return mx::enqueue(M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, D, ldd, mp, (uint8_t*)workspace,
                      cus, xcds, stream);
 }
 
@@ -168,14 +178,18 @@ dense_gemm_status gemm_nt_e4m3_mx(int64_t M, int64_t N, int64_t K, const void* A
   int cus = 0, xcds = 1;
   st = device_topology(&cus, &xcds);
   if (st != DENSE_GEMM_OK) return st;
-  // packed scale panels, stream-ordered workspace (none for small outputs)
-  const size_t need = mx::workspace_bytes(M, N, K);
+  MxPlan mp;
+  st = mx_plan_call(M, N, K, cus, &mp);
+  if (st != DENSE_GEMM_OK) return st;
+  // packed scale panels and split-K partials, stream-ordered workspace (none
+  // for small outputs)
+  const size_t need = mp.total();
   uint8_t* ws = nullptr;
   if (need > 0 && (hipMallocAsync((void**)&ws, need, stream) != hipSuccess || ws == nullptr)) {
     (void)hipGetLastError();
     return DENSE_GEMM_NO_MEMORY;
   }
-  st = mx::enqueue(M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, D, ldd, ws, cus, xcds, stream);
+  st = mx::enqueue(M, N, K, A, lda, SA, ldsa, B, ldb, SB, ldsb, D, ldd, mp, ws, cus, xcds, stream);
   if (ws != nullptr) (void)hipFreeAsync(ws, stream);
   return st;
 }

@@ -28,7 +28,11 @@
 //   * each stage runs as two halves of 32 MFMAs (A fragments 0-3, then
 //     4-7), so that all fragments fit in 128 VGPRs: the first half reads A
 //     fragments 4-7, the second half (after the stage barrier) reads the next
-//     stage's A fragments 0-3, scales and, as each frees, B fragments.
+//     stage's A fragments 0-3, scales and, as each frees, B fragments;
+//   * split-K, as in the FP16 kernel, for the tiles of a last, partial wave
+//     (all tiles when there are fewer than CUs): parts over ranges of K
+//     stages write FP32 partial tiles that split_reduce.h sums in part order
+//     and rounds to BF16.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -46,14 +50,11 @@ namespace mx {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 256, BN = 256;
-constexpr int BKE = 128;                   // K elements (= bytes) per stage
-constexpr int GROUP = 32;                  // K elements per scale
+// (BM, BN, BKE, GROUP, SC_BYTES and MX_SMALL_K_MAX: tile_config.h)
 constexpr int THREADS = 256;
 constexpr int WT = 128;                    // wave tile
 constexpr int MI = 8, NI = 8;              // 16 x 16 blocks per wave
 constexpr int OP_BYTES = BM * BKE;         // 32 KiB per operand per stage
-constexpr int SC_BYTES = 1024;             // scale panel per operand per stage
 constexpr int SLOT = 2 * OP_BYTES + 2 * SC_BYTES;
 constexpr int LDS = 2 * SLOT;              // 132 KiB
 constexpr int DMA = OP_BYTES / (THREADS * 16);  // 8 loads per thread per operand
@@ -75,6 +76,14 @@ struct MxParams {
   int d_vec;
   int nks;   // K stages
   int koff;  // leading pad of the first stage (K elements)
+  // split-K (the SPLIT kernel): tasks below full_tasks are whole tiles; the
+  // rest are (tile, part) pairs over the last `tiles` tiles of the order.
+  // Task full_tasks + u is part u / tiles of tile full_tasks + u % tiles; the
+  // part covers K stages [part * split_steps, min(nks, (part + 1) *
+  // split_steps)) and writes its FP32 partial tile (row-major 256 x 256) to
+  // ws at index part * tiles + u % tiles (split_reduce.h sums them)
+  int full_tasks, splits, split_steps, tiles;
+  float* ws;
 };
 
 // Panel layout: byte ((w*2 + h)*64 + s*16 + l16)*4 + b holds the scale of
@@ -216,6 +225,7 @@ __device__ __forceinline__ void mfma_mx(f32x4 (&acc)[MI][NI], const i32x8& bf, c
 template <int T>
 constexpr int snake_i() { return ((T / 4) & 1) ? 3 - T % 4 : T % 4; }
 
+template <bool SPLIT>
 __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   const uint32_t lds0 = lds_addr(smem);
@@ -227,7 +237,14 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
 
   for (int task = slot0; task < p.num_tasks; task += gridDim.x) {
     int tm, tn;
-    tile_of_task(task, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    const bool part = SPLIT && task >= p.full_tasks;
+    const int u = task - p.full_tasks;
+    const int split = part ? u / p.tiles : 0;
+    tile_of_task(part ? p.full_tasks + u % p.tiles : task, p.tiles_m, p.tiles_n, p.group_m, &tm,
+                 &tn);
+    // this task's K stages (ring slots count from kbeg)
+    const int kbeg = split * p.split_steps;
+    const int kend = part ? min(nk, kbeg + p.split_steps) : nk;
     const int m0 = tm * BM, n0 = tn * BN;
     const int vm = min(BM, p.M - m0), vn = min(BN, p.N - n0);
 
@@ -273,7 +290,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
     auto stage_setup = [&](int ks, int slot) {
       Stage st;
       const int k0 = ks * BKE - p.koff;
-      const bool live = ks < nk;
+      const bool live = ks < kend;
       st.k0 = k0;
       st.base = lds0 + slot * SLOT;
       st.wbase = st.base + (8 * wave) * 1024;
@@ -316,7 +333,7 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
     };
     auto read_s = [&](int slot, int off) { return *(const uint32_t*)(smem + slot * SLOT + off); };
 
-    // Ring: stage ks in slot ks % 2; entering step ks, stage ks has landed,
+    // Ring: stage ks in slot (ks - kbeg) % 2; entering step ks, stage ks has landed,
     // stage ks+1 is in flight, and F.lo, F.b, sa[0], sb hold stage ks.  Each
     // scale word (four fragments' scales) is read straight into the register
     // the MFMAs use, after that register's last use by the stage before: no
@@ -347,10 +364,10 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
       fence();
     };
     {
-      const Stage s0 = stage_setup(0, 0);
+      const Stage s0 = stage_setup(kbeg, 0);
 #pragma unroll
       for (int i = 0; i < 2 * DMA + 1; ++i) load(s0, i, true);
-      const Stage s1 = stage_setup(1, 1);
+      const Stage s1 = stage_setup(kbeg + 1, 1);
 #pragma unroll
       for (int i = 0; i < DMA; ++i) load(s1, i, true);
       load(s1, 2 * DMA, true);
@@ -359,8 +376,8 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
       for (int step = 0; step < 15; ++step) read_next(0, step);
     }
 
-    for (int ks = 0; ks < nk; ++ks) {
-      const int slot = ks & 1;
+    for (int ks = kbeg; ks < kend; ++ks) {
+      const int slot = (ks - kbeg) & 1;
       // stage ks+1's B tile, into the other slot (free since the last
       // barrier): issued over the first half's first DMA pairs
       const Stage sn1 = stage_setup(ks + 1, slot ^ 1);
@@ -417,6 +434,28 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
     // wait states between the last MFMAs and the reads of their results
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     fence();
+
+    if constexpr (SPLIT) {
+      if (part) {
+        // FP32 partial tile, row-major 256 x 256: lane holds row l16 of each
+        // 16-row block and columns j*16 + 4*lq .. +3 (16 contiguous bytes);
+        // 16 x 16 blocks wholly outside D are skipped (nothing reads them)
+        float* w = p.ws + (size_t)(split * p.tiles + u % p.tiles) * (BM * BN) +
+                   (size_t)(wm * WT + l16) * BN + wn * WT + 4 * lq;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          if (wm * WT + i * 16 >= vm) break;
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            if (wn * WT + j * 16 >= vn) break;
+            *(float4*)(w + i * 16 * BN + j * 16) =
+                make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        continue;
+      }
+    }
 
     // Epilogue (the FP16 kernel's): per 32-row band, round to BF16, stage the
     // band's 32 x 128 outputs of this wave in LDS, store 16-byte row chunks.
@@ -479,8 +518,6 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
 // K / 32 each) are staged in LDS once, before the K loop, read as they are
 // stored (any leading dimension; scale 1 outside the rows and blocks).  The
 // waves' FP32 blocks are added in wave order, rounded to BF16 and stored.
-constexpr int MX_SMALL_K_MAX = 8192;
-
 struct MxSmallParams {
   const uint8_t* A;
   const uint8_t* B;

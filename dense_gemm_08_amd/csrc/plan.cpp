@@ -1,6 +1,7 @@
-// plan.cpp -- host-side planning of the FP16/BF16 GEMM calls: the argument
-// check, the persistent tile scheduler's helpers, the launch plan (tile
-// width, split-K) and the workspace a call needs.  Plain C++ with no device
+// plan.cpp -- host-side planning of the GEMM calls: the FP16/BF16 argument
+// check, the persistent tile scheduler's helpers, the launch plans (kernel,
+// tile shape, split-K) of the FP16/BF16 and FP8 products and the workspace
+// a call needs.  Plain C++ with no device
 // code, so it also builds with the host sanitizers (tests/host_fuzz.cpp).
 #include "plan.h"
 
@@ -136,6 +137,47 @@ bool small_output(int layout, int64_t M, int64_t N, int64_t K) {
   return tiles <= SMALL_MAX_TILES || M <= SMALL_TILE;
 }
 
+// Split-K for the tiles of the last, partial wave (all tiles when there
+// are fewer than CUs), at most one part per idle CU and at least 4 K steps
+// per part.
+//   * Fewer tiles than CUs: the split (if any) with the least estimated
+//     time, from a model fitted to measured times on the MI355X (in units
+//     of 0.01 us): step_cost per K step of a tile, fixed_cost for a split
+//     call's extra work (the reduce launch, the workspace), and part_cost
+//     per partial tile for its FP32 write and read back, scaled by
+//     blocks16 / 16, the share of the tile's 16 16-row blocks inside D.
+//   * After full waves: split when the last wave would leave at least
+//     three quarters of the CUs idle (measured: splitting a half-full last
+//     wave gains nothing), into as many parts as fit.
+void choose_split(int64_t tasks, int64_t nk, int64_t num_cus, int64_t step_cost,
+                  int64_t fixed_cost, int64_t part_cost, int64_t blocks16, int64_t* splits_out,
+                  int64_t* steps_out) {
+  const int64_t rem = tasks % num_cus;
+  int64_t splits = 1, steps = nk;
+  if (rem > 0 && nk >= 8) {
+    const int64_t by_cus = num_cus / rem, by_k = nk / 4;
+    const int64_t most = by_cus < by_k ? by_cus : by_k;
+    if (tasks < num_cus) {
+      // (in 1/16 of the units above)
+      int64_t best = nk * 16 * step_cost;
+      for (int64_t sp = 2; sp <= most; ++sp) {
+        const int64_t st = (nk + sp - 1) / sp, parts = (nk + st - 1) / st;
+        const int64_t t = st * 16 * step_cost + 16 * fixed_cost + part_cost * blocks16 * parts * rem;
+        if (t < best) {
+          best = t;
+          steps = st;
+          splits = parts;
+        }
+      }
+    } else if (rem * 4 <= num_cus && most >= 2) {
+      steps = (nk + most - 1) / most;
+      splits = (nk + steps - 1) / steps;
+    }
+  }
+  *splits_out = splits;
+  *steps_out = steps;
+}
+
 dense_gemm_status tiled_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t num_cus,
                              int64_t* out) {
   // Tile rows: 256, or 128 when M <= 128 (one tile row either way, half the
@@ -168,45 +210,16 @@ dense_gemm_status tiled_plan(int layout, int64_t M, int64_t N, int64_t K, int64_
   out[5] = grid;
   out[6] = choose_group_m(tiles_m);
   out[7] = THREADS;
-  // Split-K for the tiles of the last, partial wave (all tiles when there
-  // are fewer than CUs), at most one part per idle CU and at least 4 K steps
-  // per part.
-  //   * Fewer tiles than CUs: the split (if any) with the least estimated
-  //     time, from a model fitted to measured times on the MI355X (in units
-  //     of 0.01 us): a K step of a 256-wide tile 105 (128-wide: 70), a split
-  //     call's fixed cost (the reduce launch, the workspace) 1200 plus 12 per
-  //     256-wide partial tile (6 per 128-wide one) for its FP32 write and
-  //     read back.  A partial tile writes and the reduction reads only its
-  //     16-row blocks inside D, so with one tile row (M < 256) that last
-  //     term shrinks to its share of those blocks.
-  //   * After full waves: split when the last wave would leave at least
-  //     three quarters of the CUs idle (measured: splitting a half-full last
-  //     wave gains nothing), into as many parts as fit.
+  // Split-K: the model of choose_split with the FP16 kernel's costs (a K
+  // step of a 256-wide tile 105, of a 128-wide one 70; a split call 1200; a
+  // partial tile 12 or 6); a partial tile writes and the reduction reads
+  // only its 16-row blocks inside D, so with one tile row that cost shrinks
+  // to their share.
   const int64_t nk = (K + BK - 1) / BK;
-  const int64_t rem = tasks % num_cus;
+  const int64_t blocks16 = tiles_m == 1 ? (M + 15) / 16 : BM / 16;
   int64_t splits = 1, steps = nk;
-  if (rem > 0 && nk >= 8) {
-    const int64_t by_cus = num_cus / rem, by_k = nk / 4;
-    const int64_t most = by_cus < by_k ? by_cus : by_k;
-    if (tasks < num_cus) {
-      // (in 1/16 of the units above: the partial tiles' share of 16-row blocks)
-      const int64_t step_cost = 16 * (tw == BN ? 105 : 70), part_cost = tw == BN ? 12 : 6;
-      const int64_t blocks16 = tiles_m == 1 ? (M + 15) / 16 : BM / 16;
-      int64_t best = nk * step_cost;
-      for (int64_t sp = 2; sp <= most; ++sp) {
-        const int64_t st = (nk + sp - 1) / sp, parts = (nk + st - 1) / st;
-        const int64_t t = st * step_cost + 16 * 1200 + part_cost * blocks16 * parts * rem;
-        if (t < best) {
-          best = t;
-          steps = st;
-          splits = parts;
-        }
-      }
-    } else if (rem * 4 <= num_cus && most >= 2) {
-      steps = (nk + most - 1) / most;
-      splits = (nk + steps - 1) / steps;
-    }
-  }
+  choose_split(tasks, nk, num_cus, tw == BN ? 105 : 70, 1200, tw == BN ? 12 : 6, blocks16, &splits,
+               &steps);
   out[8] = splits;
   out[9] = steps;
   if (splits > 1 && tasks < num_cus) out[5] = tasks * splits;
@@ -303,4 +316,95 @@ dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const v
   return DENSE_GEMM_OK;
 }
 
+// Products the FP8 small-output kernel computes (gemm_mx_small): M <= 128,
+// K <= MX_SMALL_K_MAX, at most SMALL_MAX_TILES tiles of 16 x 16 or one tile
+// row.  Measured per call against the tiled kernel (its scale packing and
+// workspace included), one box: 128 x 128 x 4096 6.2 against 45.3 us,
+// 1 x 4096 x 4096 6.2 against 44.5, 16 x 16384 x 4096 21.3 against 48.3,
+// 128 x 1024 x 8192 12.3 against 75.6, 128 x 128 x 64 4.5 against 23.1.
+bool mx_small_output(int64_t M, int64_t N, int64_t K) {
+  if (M > SMALL_MAX || K > mx::MX_SMALL_K_MAX) return false;
+  const int64_t tiles = ((M + SMALL_TILE - 1) / SMALL_TILE) * ((N + SMALL_TILE - 1) / SMALL_TILE);
+  return tiles <= SMALL_MAX_TILES || M <= SMALL_TILE;
+}
+
+dense_gemm_status mx_plan_call(int64_t M, int64_t N, int64_t K, int64_t num_cus, MxPlan* mp) {
+  if (M <= 0 || N <= 0 || K < 0 || K % mx::GROUP != 0 || num_cus <= 0 || mp == nullptr ||
+      M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return DENSE_GEMM_BAD_ARG;
+  int64_t* out = mp->plan;
+  const int64_t nks = (K + mx::BKE - 1) / mx::BKE;
+  mp->panel_bytes[0] = mp->panel_bytes[1] = mp->split_bytes = 0;
+  if (mx_small_output(M, N, K)) {
+    // 16 x 16 tiles, one workgroup each, the scales staged in LDS: no
+    // workspace
+    out[0] = out[1] = SMALL_TILE;
+    out[2] = mx::BKE;
+    out[3] = (M + SMALL_TILE - 1) / SMALL_TILE;
+    out[4] = (N + SMALL_TILE - 1) / SMALL_TILE;
+    out[5] = out[3] * out[4];
+    out[6] = 1;
+    out[7] = SMALL_THREADS;
+    out[8] = 1;
+    out[9] = nks;
+    mp->full_tasks = out[5];
+    mp->split_tiles = 0;
+    return DENSE_GEMM_OK;
+  }
+  const int64_t tiles_m = (M + mx::BM - 1) / mx::BM, tiles_n = (N + mx::BN - 1) / mx::BN;
+  const int64_t tasks = tiles_m * tiles_n;
+  if (tasks >= kMaxDim) return DENSE_GEMM_TOO_LARGE;
+  // Split-K: the model of choose_split with the FP8 kernel's costs (a
+  // 128-deep K stage of a tile 100, a split call 1000, a partial tile 5),
+  // fitted to the workspace-passing call's times on the MI355X over 18
+  // products of fewer tiles than CUs (256 x 256 x 16384 to 8192 x 1024 x
+  // 16384), each at 6-9 part counts: the model's pick was the fastest
+  // measured on 13 of them and within 10% on all (1% on the geometric
+  // mean), 1.55 times as fast as the unsplit call on the geometric mean;
+  // the FP16 kernel's split and partial-tile costs (1200, 12) picked up to
+  // 14% slower.  (The partial tiles of these products, at most 64 MiB, stay
+  // in the 256 MB Infinity Cache between their write and the reduction's
+  // read.)
+  const int64_t blocks16 = tiles_m == 1 ? (M + 15) / 16 : mx::BM / 16;
+  int64_t splits = 1, steps = nks;
+  choose_split(tasks, nks, num_cus, MX_STEP_COST, MX_SPLIT_COST, MX_PART_COST, blocks16, &splits,
+               &steps);
+  out[0] = mx::BM;
+  out[1] = mx::BN;
+  out[2] = mx::BKE;
+  out[3] = tiles_m;
+  out[4] = tiles_n;
+  out[6] = choose_group_m(tiles_m);
+  out[7] = THREADS;
+  out[8] = splits;
+  out[9] = steps;
+  mp->full_tasks = splits > 1 ? tasks - tasks % num_cus : tasks;
+  mp->split_tiles = tasks - mp->full_tasks;
+  const int64_t all = mp->full_tasks + mp->split_tiles * splits;
+  out[5] = all < num_cus ? all : num_cus;
+  // packed scale panels (at least one stage), then the FP32 partial tiles
+  const size_t stages = (size_t)(nks > 0 ? nks : 1);
+  mp->panel_bytes[0] = (size_t)tiles_m * stages * mx::SC_BYTES;
+  mp->panel_bytes[1] = (size_t)tiles_n * stages * mx::SC_BYTES;
+  if (splits > 1) {
+    size_t n;
+    if (__builtin_mul_overflow((size_t)splits * (size_t)mp->split_tiles,
+                               (size_t)mx::BM * mx::BN * sizeof(float), &n) ||
+        n > ((size_t)1 << 62))
+      return DENSE_GEMM_TOO_LARGE;
+    mp->split_bytes = n;
+  }
+  return DENSE_GEMM_OK;
+}
+
 }  // namespace dg
+
+extern "C" dense_gemm_status gemm_nt_e4m3_mx_plan(int64_t M, int64_t N, int64_t K,
+                                                  int64_t num_cus, int64_t* out) {
+  if (out == nullptr) return DENSE_GEMM_BAD_ARG;
+  dg::MxPlan mp;
+  const dense_gemm_status st = dg::mx_plan_call(M, N, K, num_cus, &mp);
+  if (st == DENSE_GEMM_OK)
+    for (int i = 0; i < 10; ++i) out[i] = mp.plan[i];
+  return st;
+}

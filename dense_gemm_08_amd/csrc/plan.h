@@ -1,5 +1,5 @@
-// plan.h -- host-side planning of the FP16/BF16 GEMM calls (plain C++, no
-// device code): the argument check, the launch plan with the caller's
+// plan.h -- host-side planning of the GEMM calls (plain C++, no device
+// code): the FP16/BF16 argument check, the launch plans with the caller's
 // options, and the workspace a call needs.  Implemented in plan.cpp.
 #pragma once
 
@@ -37,6 +37,12 @@ bool small_output(int layout, int64_t M, int64_t N, int64_t K);
 dense_gemm_status tiled_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t num_cus,
                              int64_t* out);
 
+// Split-K of the last, partial wave of `tasks` tiles over nk K steps on
+// num_cus CUs (the cost model in plan.cpp): parts and K steps per part.
+void choose_split(int64_t tasks, int64_t nk, int64_t num_cus, int64_t step_cost,
+                  int64_t fixed_cost, int64_t part_cost, int64_t blocks16, int64_t* splits,
+                  int64_t* steps);
+
 bool valid_op(int op);
 int op_layout(int op);
 
@@ -46,5 +52,33 @@ int op_layout(int op);
 dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const void* A,
                             int64_t lda, const void* B, int64_t ldb, int64_t cus,
                             const dense_gemm_options* opt, CallPlan* cp);
+
+// ---- the FP8 block-scaled product ----
+
+// The FP8 costs of the split model (0.01 us): one 128-deep K stage of a
+// 256 x 256 tile, a split call's extra work, one partial tile.
+constexpr int64_t MX_STEP_COST = 100;
+constexpr int64_t MX_SPLIT_COST = 1000;
+constexpr int64_t MX_PART_COST = 5;
+
+// Everything an FP8 call launches.  plan: as gemm_nt_e4m3_mx_plan (16 x 16
+// tiles for the small-output kernel, else 256 x 256 tiles with `splits`
+// parts of `steps` stages on the split tiles).  The workspace holds A's
+// and B's packed scale panels, then the FP32 partial tiles.
+struct MxPlan {
+  int64_t plan[10];
+  int64_t full_tasks, split_tiles;
+  size_t panel_bytes[2];  // A's, B's (multiples of 1 KiB)
+  size_t split_bytes;
+  size_t total() const { return panel_bytes[0] + panel_bytes[1] + split_bytes; }
+  bool small() const { return plan[0] == SMALL_TILE; }
+};
+
+// The FP8 small-output kernel's products (M <= 128, K <= MX_SMALL_K_MAX,
+// at most SMALL_MAX_TILES 16 x 16 tiles or one tile row).
+bool mx_small_output(int64_t M, int64_t N, int64_t K);
+// The plan of an FP8 call with M, N > 0 and K a multiple of 32 on a device
+// with num_cus CUs.
+dense_gemm_status mx_plan_call(int64_t M, int64_t N, int64_t K, int64_t num_cus, MxPlan* mp);
 
 }  // namespace dg

@@ -1,6 +1,7 @@
-// tile_config.h -- the FP16/BF16 GEMM's tile configuration, shared by the
-// kernels (gemm_kernel.h) and the host-side planning (plan.cpp, which is
-// plain C++ and builds without HIP).
+// tile_config.h -- the tile configurations of the FP16/BF16 GEMM and of the
+// FP8 block-scaled GEMM, shared by the kernels (gemm_kernel.h,
+// gemm_small_kernel.h, gemm_mx_kernel.h) and the host-side planning
+// (plan.cpp, which is plain C++ and builds without HIP).
 #pragma once
 
 namespace dg {
@@ -24,5 +25,17 @@ constexpr int SMALL_THREADS = SMALL_WAVES * 64;
 constexpr int SMALL_MAX = 128;
 constexpr int SMALL_K_MAX = 16384;
 constexpr int SMALL_MAX_TILES = 512;
+
+// The FP8 block-scaled GEMM (gemm_mx_kernel.h): 256 x 256 tiles, 128-deep
+// K stages (128 bytes per row), one E8M0 scale per GROUP K values; its
+// small-output kernel takes the small-output decomposition above for K up
+// to MX_SMALL_K_MAX.
+namespace mx {
+constexpr int BM = 256, BN = 256;
+constexpr int BKE = 128;                   // K elements (= bytes) per stage
+constexpr int GROUP = 32;                  // K elements per scale
+constexpr int SC_BYTES = 1024;             // packed scale panel per operand per stage
+constexpr int MX_SMALL_K_MAX = 8192;
+}  // namespace mx
 
 }  // namespace dg

@@ -216,14 +216,20 @@ dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N, int64_t K,
  * K must be a multiple of 32 (DENSE_GEMM_BAD_ARG otherwise); A and B must be
  * 16-byte aligned with lda and ldb multiples of 16 (DENSE_GEMM_MISALIGNED);
  * D needs 2-byte alignment.  M, N and K/128 may be ragged.  The products are
- * exact in FP32; their sum is accumulated in FP32 in a fixed order.  The call
- * takes a workspace of 1 KiB per 256-row tile of A and of B per 128 K
- * values for the repacked scales (hipMallocAsync / hipFreeAsync on `stream`;
- * DENSE_GEMM_NO_MEMORY if unavailable), except for small outputs (M <= 128,
- * K <= 8192, at most 512 tiles of 16 x 16 or M <= 16), which run a
- * small-output kernel (16 x 16 tiles, K split among eight waves, the scales
- * staged in LDS) that needs none.  The other rules (zeros for K == 0,
- * ownership, stream order, errors) are those stated at the top of this file. */
+ * exact in FP32; their sum is accumulated in FP32 in a fixed order (results
+ * are reproducible on a device; the order depends on the plan, hence on the
+ * CU count).  Small outputs (M <= 128, K <= 8192, at most 512 tiles of
+ * 16 x 16 or M <= 16) run a small-output kernel (16 x 16 tiles, K split
+ * among eight waves, the scales staged in LDS) that needs no workspace.
+ * Other products run a tiled kernel (256 x 256 tiles) that takes a
+ * workspace (hipMallocAsync / hipFreeAsync on `stream`;
+ * DENSE_GEMM_NO_MEMORY if unavailable) of 1 KiB per 256-row tile of A and
+ * of B per 128 K values for the repacked scales, plus, where the plan
+ * splits K (gemm_nt_e4m3_mx_plan: the tiles of a last, partial wave, or all
+ * tiles when there are fewer than CUs), 256 KiB per part of each split tile
+ * for its FP32 partial sums, which a second kernel adds in part order and
+ * rounds to BF16.  The other rules (zeros for K == 0, ownership, stream
+ * order, errors) are those stated at the top of this file. */
 dense_gemm_status gemm_nt_e4m3_mx(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                   const void* SA, int64_t ldsa, const void* B, int64_t ldb,
                                   const void* SB, int64_t ldsb, void* D, int64_t ldd,
@@ -280,10 +286,15 @@ dense_gemm_status gemm_nt_f16_noalloc(int64_t M, int64_t N, int64_t K, const voi
                                       int64_t lda, const void* B, int64_t ldb, void* D,
                                       int64_t ldd, hipStream_t stream);
 
-/* Bytes of workspace gemm_nt_e4m3_mx_ex needs: the repacked scale panels,
- * 1 KiB per 256-row tile of A and of B per 128 K values (0 when M or N is
- * 0).  DENSE_GEMM_BAD_ARG for K not a multiple of 32 or a null `bytes`. */
-dense_gemm_status gemm_nt_e4m3_mx_workspace_size(int64_t M, int64_t N, int64_t K, size_t* bytes);
+/* Bytes of workspace gemm_nt_e4m3_mx_ex needs on a device with num_cus
+ * compute units (0: query the current device): the repacked scale panels,
+ * 1 KiB per 256-row tile of A and of B per 128 K values, and the FP32
+ * partial tiles of a split-K plan, 256 KiB per part of each split tile (0
+ * when M or N is 0, and for the small-output kernel).  DENSE_GEMM_BAD_ARG
+ * for K not a multiple of 32, a negative num_cus or a null `bytes`,
+ * DENSE_GEMM_NO_DEVICE if num_cus is 0 and no gfx950 is current. */
+dense_gemm_status gemm_nt_e4m3_mx_workspace_size(int64_t M, int64_t N, int64_t K,
+                                                  int64_t num_cus, size_t* bytes);
 
 /* gemm_nt_e4m3_mx with the caller's workspace. */
 dense_gemm_status gemm_nt_e4m3_mx_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -333,6 +344,19 @@ dense_gemm_status dense_gemm_tile_of_task(int64_t task, int64_t tiles_m, int64_t
  * then r * parts when tiles < num_cus, else num_cus. */
 dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K,
                                   int64_t num_cus, int64_t* out);
+
+/* The launch plan of gemm_nt_e4m3_mx for M, N > 0 and K a multiple of 32
+ * on a device with num_cus compute units, as 10 values in the format of
+ * dense_gemm_plan: tile rows and columns (16 and 16 for the small-output
+ * kernel, else 256 and 256), the K depth of a stage (128), tiles_m,
+ * tiles_n, grid, group_m, threads per workgroup, the number of K parts and
+ * the stages per part.  The split rule is dense_gemm_plan's for 256-wide
+ * tiles with the FP8 kernel's costs: the estimate ceil(stages / p) * 100 +
+ * 1000 + 5 * f * p * r against stages * 100 unsplit.
+ * DENSE_GEMM_BAD_ARG on a bad argument, DENSE_GEMM_TOO_LARGE when the
+ * tiles overflow 32-bit task numbers. */
+dense_gemm_status gemm_nt_e4m3_mx_plan(int64_t M, int64_t N, int64_t K, int64_t num_cus,
+                                       int64_t* out);
 
 /* The workgroup-to-task permutation of the persistent grid: workgroup b
  * (dispatched to XCD b mod num_xcds) takes slot dense_gemm_xcd_slot(...) of

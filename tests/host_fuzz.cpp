@@ -1,7 +1,8 @@
 // host_fuzz.cpp -- exercises the host-side planning code of the library
 // (dense_gemm_08_amd/csrc/plan.cpp: the argument check, the tile scheduler
-// helpers, the launch plan with options, the workspace sizes) over edge and
-// random arguments, and checks the plan's invariants.  tests/test_sanitizers.py
+// helpers, the FP16/BF16 launch plan with options, the FP8 plan, the
+// workspace sizes) over edge and random arguments, and checks the plans'
+// invariants.  tests/test_sanitizers.py
 // builds it with -fsanitize=address,undefined, so an out-of-bounds access,
 // a signed overflow or any other undefined behaviour also ends the run.
 // Prints "ok" and exits 0 on success.
@@ -88,6 +89,38 @@ static void check_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t cus,
   check_repack(layout, M, N, K, cp);
 }
 
+// The FP8 plan's invariants (mx_plan_call succeeded for M, N > 0).
+static void check_mx_plan(int64_t M, int64_t N, int64_t K, int64_t cus, const MxPlan& mp) {
+  const int64_t* p = mp.plan;
+  const int64_t nks = ceil_div(K, mx::BKE);
+  CHECK(mp.small() == mx_small_output(M, N, K));
+  CHECK(p[2] == mx::BKE && p[9] >= 0);
+  if (mp.small()) {
+    CHECK(M <= SMALL_MAX && K <= mx::MX_SMALL_K_MAX && p[1] == SMALL_TILE);
+    CHECK(p[3] == ceil_div(M, SMALL_TILE) && p[4] == ceil_div(N, SMALL_TILE));
+    CHECK(p[5] == p[3] * p[4] && (p[5] <= SMALL_MAX_TILES || p[3] == 1));
+    CHECK(p[7] == SMALL_THREADS && p[8] == 1 && mp.total() == 0);
+    return;
+  }
+  CHECK(p[0] == mx::BM && p[1] == mx::BN && p[7] == THREADS);
+  CHECK(p[3] == ceil_div(M, mx::BM) && p[4] == ceil_div(N, mx::BN));
+  CHECK(p[6] >= 1 && p[6] <= 8 && p[6] <= p[3]);
+  const int64_t tasks = p[3] * p[4];
+  CHECK(mp.full_tasks + mp.split_tiles == tasks);
+  CHECK(p[5] >= 1 && p[5] <= cus);
+  const size_t stages = (size_t)(nks > 0 ? nks : 1);
+  CHECK(mp.panel_bytes[0] == (size_t)p[3] * stages * mx::SC_BYTES);
+  CHECK(mp.panel_bytes[1] == (size_t)p[4] * stages * mx::SC_BYTES);
+  if (p[8] > 1) {
+    CHECK(p[8] * p[9] >= nks && (p[8] - 1) * p[9] < nks && p[9] >= 4);
+    CHECK(mp.split_tiles == (tasks < cus ? tasks : tasks % cus) && mp.split_tiles > 0);
+    CHECK(mp.split_tiles * p[8] <= cus);
+    CHECK(mp.split_bytes == (size_t)p[8] * (size_t)mp.split_tiles * mx::BM * mx::BN * 4);
+  } else {
+    CHECK(p[9] == nks && mp.split_tiles == 0 && mp.split_bytes == 0);
+  }
+}
+
 int main() {
   std::mt19937_64 rng(20261202);
   auto pick = [&](const std::vector<int64_t>& v) { return v[rng() % v.size()]; };
@@ -140,6 +173,29 @@ int main() {
       CHECK(out[8] == cp.plan[8]);
     }
   }
+  // the FP8 plan
+  long mx_planned = 0;
+  for (long it = 0; it < 200000; ++it) {
+    int64_t M = pick(dims), N = pick(dims), K = pick(dims);
+    if (rng() % 2) M = (int64_t)(rng() % 9000);
+    if (rng() % 2) N = (int64_t)(rng() % 20000);
+    if (rng() % 2) K = 32 * (int64_t)(rng() % 700);
+    const int64_t cus = rng() % 8 == 0 ? (int64_t)(rng() % 4) - 1 : pick(cus_list);
+    MxPlan mp;
+    const dense_gemm_status st = mx_plan_call(M, N, K, cus, &mp);
+    const bool args_ok = M > 0 && N > 0 && K >= 0 && K % 32 == 0 && cus > 0 && M < kMaxDim &&
+                         N < kMaxDim && K < kMaxDim;
+    if (!args_ok) {
+      CHECK(st == DENSE_GEMM_BAD_ARG);
+      continue;
+    }
+    const bool many_tiles = ceil_div(M, mx::BM) * ceil_div(N, mx::BN) >= kMaxDim;
+    CHECK(st == (many_tiles && !mx_small_output(M, N, K) ? DENSE_GEMM_TOO_LARGE : DENSE_GEMM_OK));
+    if (st != DENSE_GEMM_OK) continue;
+    check_mx_plan(M, N, K, cus, mp);
+    ++mx_planned;
+  }
+  CHECK(mx_planned > 1000);
   // the public planner's own argument check
   int64_t out[10];
   CHECK(dense_gemm_plan(2, 8, 8, 8, 256, out) == DENSE_GEMM_BAD_ARG);

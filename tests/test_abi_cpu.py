@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from dense_gemm_08_amd import binding
@@ -267,6 +268,100 @@ def test_plan_split_k():
             assert out[5] == tiles * sp
 
 
+def _split_choice(tasks, nk, cus, step_cost, fixed_cost, part_cost, blocks16):
+    """The split rule as the header states it (dense_gemm_plan), written out
+    for the host-logic check below: (parts, steps per part)."""
+    rem = tasks % cus
+    splits, steps = 1, nk
+    if rem > 0 and nk >= 8:
+        most = min(cus // rem, nk // 4)
+        if tasks < cus:
+            best = nk * step_cost * 16
+            for sp in range(2, most + 1):
+                st = -(-nk // sp)
+                parts = -(-nk // st)
+                t = st * step_cost * 16 + 16 * fixed_cost + part_cost * blocks16 * parts * rem
+                if t < best:
+                    best, steps, splits = t, st, parts
+        elif rem * 4 <= cus and most >= 2:
+            steps = -(-nk // most)
+            splits = -(-nk // steps)
+    return splits, steps
+
+
+def test_mx_plan():
+    lib = binding.load_library()
+    out = (ctypes.c_int64 * 10)()
+
+    def plan(M, N, K, cus=256):
+        assert lib.gemm_nt_e4m3_mx_plan(M, N, K, cus, out) == S.OK
+        return list(out)
+
+    # small outputs: 16 x 16 tiles, one 512-thread workgroup each, no split
+    assert plan(128, 128, 4096) == [16, 16, 128, 8, 8, 64, 1, 512, 1, 32]
+    assert plan(1, 40000, 256)[:6] == [16, 16, 128, 1, 2500, 2500]
+    # the page workloads: whole waves, no split
+    assert plan(8192, 8192, 8192) == [256, 256, 128, 32, 32, 256, 8, 256, 1, 64]
+    assert plan(8192, 17408, 5120) == [256, 256, 128, 32, 68, 256, 8, 256, 1, 40]
+    # one tile, K = 16384 (128 stages): 32 parts of 4 stages
+    # (4 * 100 + 1000 + 5 * 32 = 1560 against 128 * 100 = 12800)
+    assert plan(256, 256, 16384) == [256, 256, 128, 1, 1, 32, 1, 256, 32, 4]
+    # 16 tiles over 64 stages: 8 parts of 8 (800 + 1000 + 5 * 8 * 16 = 2440,
+    # against 11 parts of 6 2480 and 6 parts of 11 2580)
+    assert plan(1024, 1024, 8192) == [256, 256, 128, 4, 4, 128, 4, 256, 8, 8]
+    # 64 tiles over 32 stages: 3 parts of 11 (1100 + 1000 + 960 = 3060
+    # against 4 parts of 8 3080 and 3200 unsplit)
+    assert plan(2048, 2048, 4096)[5:] == [192, 8, 256, 3, 11]
+    # M <= 128 past the small kernel's K: one tile row, 8 of 16 row blocks
+    assert plan(128, 128, 8224)[8:] == [13, 5]
+    # two waves plus 32 tiles: the last wave in 8 parts of 4 stages
+    assert plan(8192, 4224, 4096)[5:] == [256, 8, 256, 8, 4]
+    # a half-full last wave and K too short to split stay whole
+    assert plan(8192, 1024, 4096)[8] == 1
+    assert plan(280, 300, 160)[8] == 1
+    # the rule as documented, on many shapes and CU counts
+    rng = np.random.default_rng(5)
+    for _ in range(400):
+        M, N = (int(v) for v in rng.integers(129, 9000, 2))
+        K = 32 * int(rng.integers(0, 700))
+        cus = int(rng.choice([256, 240, 128, 80, 32]))
+        p = plan(M, N, K, cus)
+        tm, tn = -(-M // 256), -(-N // 256)
+        nk = -(-K // 128)
+        sp, st = _split_choice(tm * tn, nk, cus, 100, 1000, 5, -(-M // 16) if tm == 1 else 16)
+        assert p[:5] == [256, 256, 128, tm, tn] and p[6:10] == [min(tm, 8), 256, sp, st], (M, N, K, cus)
+        full = tm * tn - (tm * tn) % cus if sp > 1 else tm * tn
+        assert p[5] == min(full + (tm * tn - full) * sp, cus)
+        if sp > 1:
+            assert (sp - 1) * st < nk <= sp * st and st >= 4
+    for bad in ((0, 8, 32, 256), (8, 8, 40, 256), (8, 8, 32, 0), (8, -1, 32, 256)):
+        assert lib.gemm_nt_e4m3_mx_plan(*bad, out) == S.BAD_ARG
+    assert lib.gemm_nt_e4m3_mx_plan(8, 8, 32, 256, None) == S.BAD_ARG
+
+
+def test_plan_split_rule_as_documented():
+    # dense_gemm_plan's split against the rule written out above (256-wide
+    # tiles 105 and 12, 128-wide 70 and 6) on shapes the tiled kernel takes
+    lib = binding.load_library()
+    out = (ctypes.c_int64 * 10)()
+    rng = np.random.default_rng(6)
+    for _ in range(400):
+        layout = int(rng.integers(0, 2))
+        M = int(rng.integers(1, 9000))
+        N = int(rng.integers(1, 9000))
+        K = int(rng.integers(0, 40000))
+        cus = int(rng.choice([256, 240, 128, 32]))
+        assert lib.dense_gemm_plan(layout, M, N, K, cus, out) == S.OK
+        if out[0] == 16:
+            continue  # the small-output kernel: no split
+        tr, tw, tm, tn = out[0], out[1], out[3], out[4]
+        nk = -(-K // 64)
+        cost = (105, 12) if tw == 256 else (70, 6)
+        sp, st = _split_choice(tm * tn, nk, cus, cost[0], 1200, cost[1],
+                               -(-M // 16) if tm == 1 else 16)
+        assert (out[8], out[9]) == (sp, st), (layout, M, N, K, cus)
+
+
 def _mx(M, N, K, A=64, lda=None, SA=64, ldsa=None, B=64, ldb=None, SB=64, ldsb=None, D=64,
         ldd=None):
     """gemm_nt_e4m3_mx on fake addresses: every case here is rejected (or
@@ -498,8 +593,8 @@ def test_mx_workspace_size():
     lib = binding.load_library()
     out = ctypes.c_size_t()
 
-    def ws(M, N, K):
-        st = S(lib.gemm_nt_e4m3_mx_workspace_size(M, N, K, ctypes.byref(out)))
+    def ws(M, N, K, cus=256):
+        st = S(lib.gemm_nt_e4m3_mx_workspace_size(M, N, K, cus, ctypes.byref(out)))
         return st, out.value
 
     # 1 KiB per 256-row tile of A and of B per 128-deep K stage
@@ -513,11 +608,23 @@ def test_mx_workspace_size():
     assert ws(128, 128, 4096) == (S.OK, 0)
     assert ws(16, 65536, 8192) == (S.OK, 0)
     assert ws(64, 1100, 2080) == (S.OK, 0)
-    assert ws(128, 128, 8224) == (S.OK, (1 + 1) * 65 * 1024)
     assert ws(17, 8200, 512) == (S.OK, (1 + 33) * 4 * 1024)
+    # split-K adds 256 KiB (a 256 x 256 FP32 tile) per part of each split
+    # tile: 128 x 128 x 8224 is one tile in 13 parts, 256 x 256 x 16384 one
+    # in 32, 8192 x 4224 x 4096 has 32 tiles after two full waves, in 8 parts
+    assert ws(128, 128, 8224) == (S.OK, (1 + 1) * 65 * 1024 + 13 * 262144)
+    assert ws(256, 256, 16384) == (S.OK, (1 + 1) * 128 * 1024 + 32 * 262144)
+    assert ws(8192, 4224, 4096) == (S.OK, (32 + 17) * 32 * 1024 + 8 * 32 * 262144)
+    # ... which follows the plan for the CU count given
+    plan = (ctypes.c_int64 * 10)()
+    for cus in (256, 64, 8):
+        assert lib.gemm_nt_e4m3_mx_plan(1024, 1024, 8192, cus, plan) == S.OK
+        tiles = 16 % cus if plan[8] > 1 else 0
+        assert ws(1024, 1024, 8192, cus) == (S.OK, (4 + 4) * 64 * 1024 + plan[8] * tiles * 262144)
     assert ws(8, 8, 40)[0] == S.BAD_ARG
     assert ws(-1, 8, 32)[0] == S.INVALID_DIM
-    assert S(lib.gemm_nt_e4m3_mx_workspace_size(8, 8, 32, None)) == S.BAD_ARG
+    assert ws(8, 8, 32, cus=-1)[0] == S.BAD_ARG
+    assert S(lib.gemm_nt_e4m3_mx_workspace_size(8, 8, 32, 256, None)) == S.BAD_ARG
     fn = lib.gemm_nt_e4m3_mx_ex
     assert S(fn(8, 8, 40, 256, 48, 256, 2, 256, 48, 256, 2, 256, 8, 0, 0, None)) == S.BAD_ARG
     assert S(fn(8, 8, 64, 256, 64, 256, 2, 256, 64, 256, 2, 0, 8, 0, 0, None)) == S.NULL_PTR

@@ -297,6 +297,89 @@ def test_mx_scale_range_ends(case):
 
 # ------------------------------------------------ the small-output kernel --
 
+MX_SPLIT = [
+    # (M, N, K) planned with split-K on a 256-CU device: one tile in 16
+    # parts, ragged tiles with K mod 128 = 32 (the leading pad of the first
+    # stage falls in part 0 only), one tile row (partial tiles with row
+    # blocks outside D), M <= 128 past the small kernel's K, and a last wave
+    # of 33 tiles after a full one
+    (256, 256, 8192), (300, 200, 4128), (129, 520, 2080), (100, 72, 8224), (4097, 4097, 1024),
+    (600, 520, 3104),
+]
+
+
+def _mx_plan(M, N, K):
+    import ctypes
+    from dense_gemm_08_amd import binding
+    t = _gpu.torch()
+    cus = t.cuda.get_device_properties(0).multi_processor_count
+    out = (ctypes.c_int64 * 10)()
+    assert binding.load_library().gemm_nt_e4m3_mx_plan(M, N, K, cus, out) == 0
+    return list(out)
+
+
+@pytest.mark.parametrize("kind", ["quantised", "codes"])
+@pytest.mark.parametrize("M,N,K", MX_SPLIT, ids=lambda v: str(v))
+def test_mx_split_k_full_parity(kind, M, N, K):
+    plan = _mx_plan(M, N, K)
+    if plan[8] == 1:
+        pytest.skip("not split on a device with this CU count")
+    A, SA, B, SB = inputs.mx_operands(M, N, K, seed=M + 5 * N + K, kind=kind)
+    D, st = run_mx(A, SA, B, SB)
+    assert st == status().OK
+    check_full(A, SA, B, SB, D)
+    # the parts are added in a fixed order: a rerun is equal
+    D2, _ = run_mx(A, SA, B, SB)
+    assert np.array_equal(D, D2)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 8192), (300, 200, 4128), (4097, 4097, 1024)],
+                         ids=lambda v: str(v))
+def test_mx_split_k_small_integers_bit_exact(M, N, K):
+    # exact FP32 sums in any order: the split gives the correctly rounded value
+    if _mx_plan(M, N, K)[8] == 1:
+        pytest.skip("not split on a device with this CU count")
+    A, SA, B, SB = inputs.mx_small_integers(M, N, K, seed=K + 1)
+    D, st = run_mx(A, SA, B, SB, ldd=N + 3)
+    assert st == status().OK
+    assert (D[:, N:] == _gpu.CANARY).all()
+    d, _ = oracle.gemm_mx(A, SA, B, SB)
+    want = oracle.round_to("bf16", d)
+    assert np.array_equal(D[:, :N], want), np.argwhere(D[:, :N] != want)[:5]
+
+
+def test_mx_split_k_workspace_call_equals_plain_call():
+    import ctypes
+    from dense_gemm_08_amd import binding
+    t = _gpu.torch()
+    lib = binding.load_library()
+    M, N, K = 300, 200, 4128
+    if _mx_plan(M, N, K)[8] == 1:
+        pytest.skip("not split on a device with this CU count")
+    XA, XSA, XB, XSB = [t.from_numpy(x).cuda() for x in inputs.mx_operands(M, N, K, seed=74)]
+    nb = K // 32
+    need = ctypes.c_size_t()
+    assert lib.gemm_nt_e4m3_mx_workspace_size(M, N, K, 0, ctypes.byref(need)) == 0
+    panels = (2 + 1) * 33 * 1024
+    assert need.value > panels  # the partial tiles follow the scale panels
+    ws = _gpu.workspace(need.value)
+    h = t.cuda.current_stream().cuda_stream
+    args = (M, N, K, XA.data_ptr(), K, XSA.data_ptr(), nb, XB.data_ptr(), K, XSB.data_ptr(), nb)
+    D1, D2, D3, D4 = (_gpu.empty_out(M, N) for _ in range(4))
+    assert lib.gemm_nt_e4m3_mx(*args, D1.data_ptr(), N, h) == 0
+    assert lib.gemm_nt_e4m3_mx_ex(*args, D2.data_ptr(), N, ws.data_ptr(), need.value, h) == 0
+    # a workspace with room for the panels only is refused before any launch
+    assert status()(lib.gemm_nt_e4m3_mx_ex(*args, D3.data_ptr(), N, ws.data_ptr(), panels,
+                                           h)) == status().WORKSPACE_TOO_SMALL
+    # the workspace's old contents do not matter: a second call over the
+    # first call's partials gives the same result
+    assert lib.gemm_nt_e4m3_mx_ex(*args, D4.data_ptr(), N, ws.data_ptr(), need.value, h) == 0
+    t.cuda.synchronize()
+    assert (_gpu.from_dev(D1) == _gpu.from_dev(D2)).all()
+    assert (_gpu.from_dev(D1) == _gpu.from_dev(D4)).all()
+    assert (_gpu.from_dev(D3) == _gpu.CANARY).all()
+
+
 MX_SMALL = [
     # (M, N, K) for the small-output kernel (M <= 128, K <= 8192, at most
     # 512 tiles of 16 x 16 or one tile row): K mod 128 = 0, 32, 64, 96, the
@@ -310,7 +393,8 @@ def _mx_small(M, N, K):
     import ctypes
     from dense_gemm_08_amd import binding
     need = ctypes.c_size_t(1)
-    assert binding.load_library().gemm_nt_e4m3_mx_workspace_size(M, N, K, ctypes.byref(need)) == 0
+    assert binding.load_library().gemm_nt_e4m3_mx_workspace_size(M, N, K, 0,
+                                                                 ctypes.byref(need)) == 0
     return need.value == 0
 
 

@@ -882,7 +882,7 @@ def test_mx_workspace_call_equals_plain_call():
     XA, XSA, XB, XSB = [t.from_numpy(x).cuda() for x in inputs.mx_operands(M, N, K, seed=73)]
     nb = K // 32
     need = ctypes.c_size_t()
-    assert lib.gemm_nt_e4m3_mx_workspace_size(M, N, K, ctypes.byref(need)) == 0
+    assert lib.gemm_nt_e4m3_mx_workspace_size(M, N, K, 0, ctypes.byref(need)) == 0
     ws = _gpu.workspace(need.value)
     h = t.cuda.current_stream().cuda_stream
     args = (M, N, K, XA.data_ptr(), K, XSA.data_ptr(), nb, XB.data_ptr(), K, XSB.data_ptr(), nb)
