@@ -85,6 +85,9 @@ def parse():
                     help="instead of one workload, time D = A @ B.T (FP16) at small M (1 to 512) "
                          "against N, K of 4096 to 16384, torch.mm timed beside it (shapes outside "
                          "the pages' workloads: where the 256-row tile computes mostly padding)")
+    ap.add_argument("--small-m-sweep-nn", action="store_true",
+                    help="the same for D = A @ B (BF16, B row-major K x N) at M of 1 to 128, "
+                         "where the small-output kernel and the tiled one divide the shapes")
     ap.add_argument("--seed", type=int, default=8192)
     ap.add_argument("--ladder", action="store_true",
                     help="instead of one workload, time each optimisation-step kernel "
@@ -192,16 +195,27 @@ def run_ladder(args):
 
 SMALL_M = [(m, n, k) for m in (1, 16, 64, 128, 256, 512)
            for n, k in ((4096, 4096), (8192, 8192), (16384, 4096))]
+SMALL_M_NN = [(m, n, k) for m in (1, 16, 64, 128)
+              for n, k in ((128, 4096), (1024, 1024), (1024, 4096), (4096, 4096), (8192, 8192),
+                           (16384, 4096))]
 
 
-def run_sweep(args, shapes=None):
-    """Per shape: N(0,1)/8 FP16 operands from torch's seeded device generator
-    (timing only; tests check these shapes against the oracle on sampled
-    entries), warm-up, then HIP events around about 50 ms of back-to-back
-    calls on the launch stream."""
+def run_sweep(args, shapes=None, layout="nt"):
+    """Per shape: N(0,1)/8 operands (FP16 for D = A @ B.T, BF16 for D = A @ B)
+    from torch's seeded device generator (timing only; tests check these
+    shapes' paths against the oracle), warm-up, then HIP events around about
+    50 ms of back-to-back calls on the launch stream, torch.mm's beside them.
+    Each line names the kernel the library's plan runs (small-output or
+    tiled)."""
+    import ctypes
     import torch
     from dense_gemm_08_amd import binding
     lib = binding.load_library()
+    fmt = "f16" if layout == "nt" else "bf16"
+    dtype = torch.half if layout == "nt" else torch.bfloat16
+    entry = lib.gemm_nt_f16 if layout == "nt" else lib.gemm_nn_bf16
+    plan = (ctypes.c_int64 * 10)()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(args.seed)
@@ -220,26 +234,32 @@ def run_sweep(args, shapes=None):
         return e0.elapsed_time(e1) / steps
 
     for M, N, K in (shapes or sweep_shapes()):
-        A = (torch.randn(M, K, device=dev, generator=gen) * 0.125).half()
-        B = (torch.randn(N, K, device=dev, generator=gen) * 0.125).half()
-        D = torch.empty(M, N, dtype=torch.half, device=dev)
-        Dt = torch.empty(M, N, dtype=torch.half, device=dev)
+        A = (torch.randn(M, K, device=dev, generator=gen) * 0.125).to(dtype)
+        B = (torch.randn(*((N, K) if layout == "nt" else (K, N)), device=dev, generator=gen)
+             * 0.125).to(dtype)
+        ldb = K if layout == "nt" else N
+        D = torch.empty(M, N, dtype=dtype, device=dev)
+        Dt = torch.empty(M, N, dtype=dtype, device=dev)
         flops = 2.0 * M * N * K
         steps = max(5, min(200, int(0.05 / (flops / 1.2e15))))
+        if lib.dense_gemm_plan(0 if layout == "nt" else 1, M, N, K, cus, plan) != 0:
+            raise RuntimeError("no plan for %d x %d x %d" % (M, N, K))
 
         def ours():
-            st = lib.gemm_nt_f16(M, N, K, A.data_ptr(), K, B.data_ptr(), K, D.data_ptr(), N,
-                                 stream.cuda_stream)
+            st = entry(M, N, K, A.data_ptr(), K, B.data_ptr(), ldb, D.data_ptr(), N,
+                       stream.cuda_stream)
             if st != 0:
-                raise binding.DenseGemmError(st, "gemm_nt_f16")
+                raise binding.DenseGemmError(st, "gemm_%s_%s" % (layout, fmt))
 
         def ref():
-            torch.mm(A, B.t(), out=Dt)
+            torch.mm(A, B.t() if layout == "nt" else B, out=Dt)
 
         ms = timed(ours, steps, max(3, steps // 4))
         ms_ref = timed(ref, steps, max(3, steps // 4))
         nbytes = 2.0 * (M * K + N * K + M * N)  # A, B and D once
-        line = {"mode": "sweep", "M": M, "N": N, "K": K, "steps": steps,
+        line = {"mode": "sweep", "layout": layout, "dtype": fmt, "M": M, "N": N, "K": K,
+                "kernel": "small" if plan[0] == 16 else "tiled", "splits": int(plan[8]),
+                "steps": steps,
                 "kernel_ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
                 "alg_tb_s": round(nbytes / ms / 1e9, 3),
                 "torch_mm_ms": round(ms_ref, 5),
@@ -248,12 +268,13 @@ def run_sweep(args, shapes=None):
         if args.workspace:
             # the same product through dense_gemm_ex, its workspace allocated
             # once (no stream-ordered allocation per call)
-            need = binding.workspace_size("nt", "f16", M, N, K, A.data_ptr(), K, B.data_ptr(), K)
+            need = binding.workspace_size(layout, fmt, M, N, K, A.data_ptr(), K, B.data_ptr(),
+                                          ldb)
             ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
             def ours_ws():
-                st = lib.dense_gemm_ex(binding.OPS[("nt", "f16")], M, N, K, A.data_ptr(), K,
-                                       B.data_ptr(), K, D.data_ptr(), N, None, ws.data_ptr(),
+                st = lib.dense_gemm_ex(binding.OPS[(layout, fmt)], M, N, K, A.data_ptr(), K,
+                                       B.data_ptr(), ldb, D.data_ptr(), N, None, ws.data_ptr(),
                                        need, stream.cuda_stream)
                 if st != 0:
                     raise binding.DenseGemmError(st, "dense_gemm_ex")
@@ -478,6 +499,9 @@ def main():
         return
     if args.small_m_sweep:
         run_sweep(args, SMALL_M)
+        return
+    if args.small_m_sweep_nn:
+        run_sweep(args, SMALL_M_NN, layout="nn")
         return
     if args.ladder:
         run_ladder(args)

@@ -153,27 +153,29 @@ static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A,
   return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
 
-// The small-output kernel's launch (A @ B.T only): one workgroup per 16 x 16
-// tile of D.
-template <typename T>
+// The small-output kernel's launch: one workgroup per 16 x 16 tile of D.
+template <typename T, int LAYOUT>
 static dense_gemm_status enqueue_small(int64_t M, int64_t N, int64_t K, const void* A,
                                        int64_t lda, const void* B, int64_t ldb, void* D,
-                                       int64_t ldd, const CallPlan& cp, char* ws,
-                                       hipStream_t stream) {
-  const Operands o = prepare_operands<NT>(M, N, K, A, lda, B, ldb, cp, ws, stream);
+                                       int64_t ldd, const CallPlan& cp, const DeviceInfo& info,
+                                       char* ws, hipStream_t stream) {
+  const Operands o = prepare_operands<LAYOUT>(M, N, K, A, lda, B, ldb, cp, ws, stream);
   SmallParams p;
   p.A = o.A;
   p.B = o.B;
   p.D = (uint16_t*)D;
   p.M = (int)M;
   p.N = (int)N;
+  p.K = (int)K;
   p.K8 = (int)((K + 7) & ~(int64_t)7);
+  p.N8 = (int)((N + 7) & ~(int64_t)7);
   p.lda = (int)o.lda;
   p.ldb = (int)o.ldb;
   p.ldd = (int)ldd;
   p.tiles_n = (int)cp.plan[4];
+  p.num_xcds = info.xcds;
   p.d_vec = (((uintptr_t)D & 7) == 0 && (ldd & 3) == 0) ? 1 : 0;
-  hipLaunchKernelGGL((gemm_small<T>), dim3((unsigned)(cp.plan[3] * cp.plan[4])),
+  hipLaunchKernelGGL((gemm_small<T, LAYOUT>), dim3((unsigned)(cp.plan[3] * cp.plan[4])),
                      dim3(SMALL_THREADS), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
@@ -184,9 +186,9 @@ static dense_gemm_status enqueue_width(int64_t M, int64_t N, int64_t K, const vo
                                        int64_t ldd, const CallPlan& cp, const DeviceInfo& info,
                                        char* ws, hipStream_t stream) {
   const bool short_tiles = cp.plan[0] == BM / 2;
+  if (cp.small())
+    return enqueue_small<T, LAYOUT>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws, stream);
   if constexpr (LAYOUT == NT) {
-    if (cp.small())
-      return enqueue_small<T>(M, N, K, A, lda, B, ldb, D, ldd, cp, ws, stream);
     if (cp.plan[1] == BN / 2)
       return short_tiles
                  ? enqueue<T, LAYOUT, BN / 2, BM / 2>(M, N, K, A, lda, B, ldb, D, ldd, cp, info, ws,

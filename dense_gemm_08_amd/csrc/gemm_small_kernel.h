@@ -1,8 +1,8 @@
 // gemm_small_kernel.h -- the small-output kernel for the MI355X (gfx950):
-// D = A @ B.T (FP16 or BF16) with M <= 128, such as a 128 x 128 output,
-// whose one 256 x 128 tile would leave almost every CU idle, or a single
-// row of 16 x 16 tiles (M <= 16) of any width.  (Which products run it:
-// small_output in plan.cpp.)
+// D = A @ B.T or D = A @ B (FP16 or BF16) with M <= 128, such as a 128 x
+// 128 output, whose one 256 x 128 tile would leave almost every CU idle, or
+// a single row of 16 x 16 tiles (M <= 16) of any width.  (Which products
+// run it: small_output in plan.cpp.)
 //
 // The product is the one of gemm_kernel.h (FP32 accumulation of the K
 // blocks' partial products, one rounding to the output type; TileFoundry's
@@ -23,6 +23,13 @@
 //     order (results are reproducible), then rounded and stored.
 // Where 16 x 16 tiles reach past M or N, or chunks past K, the loads read
 // zeros (offsets past the buffer's range) and the stores are masked.
+//
+// A @ B (B row-major K x N): a chunk's B tile is 64 k rows of 32 bytes (the
+// tile's 16 columns), still two 16-byte loads per lane, read into MFMA
+// fragments (eight consecutive k of one column per lane) by transposing LDS
+// reads, as the tiled kernel's A @ B does.  Four tiles side by side share
+// B's 128-byte lines, so the tiles are laid out XCD by XCD (tile_sched.h's
+// xcd_slot): tiles that share lines run on one XCD and share its L2.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,6 +37,7 @@
 
 #include "cdna_ops.h"
 #include "tile_config.h"
+#include "tile_sched.h"
 
 namespace dg {
 
@@ -40,11 +48,20 @@ struct SmallParams {
   const uint16_t* B;
   uint16_t* D;
   int M, N;
-  int K8;    // K rounded up to 8 (the operands hold zeros in [K, K8))
+  int K;     // (A @ B: rows of B)
+  int K8;    // K rounded up to 8 (A, and B for A @ B.T, hold zeros in [K, K8))
+  int N8;    // (A @ B) N rounded up to 8: B's columns that may be read
   int lda, ldb, ldd;
   int tiles_n;
-  int d_vec;  // D rows are 8-byte aligned (4-element stores allowed)
+  int num_xcds;  // (A @ B) XCDs of the device, for the tile order
+  int d_vec;     // D rows are 8-byte aligned (4-element stores allowed)
 };
+
+// LDS position of row k of a chunk's A @ B tile (64 rows of 32 bytes): the
+// 128-byte half flips where bit 3 of k is set, so that the transposing
+// reads of the two 16-lane blocks of a half-wave (rows 8 apart) fall in
+// different banks.
+__device__ __forceinline__ int nn_row_pos(int k) { return (32 * k) ^ (((k >> 3) & 1) << 7); }
 
 // c += b-fragment rows x a-fragment columns over 32 k, through the builtin:
 // with only two accumulators live the compiler keeps them in place, and it
@@ -62,7 +79,7 @@ __device__ __forceinline__ f32x4 mfma16_chain<__bf16>(f32x4 c, u32x4 b, u32x4 a)
                                                   __builtin_bit_cast(bf16x8, a), c, 0, 0, 0);
 }
 
-template <typename T>
+template <typename T, int LAYOUT>
 __global__ __launch_bounds__(SMALL_THREADS) void gemm_small(SmallParams p) {
   // Chunks in flight per wave.  Two (72 KiB of LDS per workgroup, so two
   // workgroups fit a CU) measured faster than four (136 KiB, one per CU) on
@@ -76,7 +93,9 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_small(SmallParams p) {
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = (int)threadIdx.x & 63;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int tm = (int)blockIdx.x / p.tiles_n, tn = (int)blockIdx.x % p.tiles_n;
+  const int tile = LAYOUT == NN ? xcd_slot((int)blockIdx.x, (int)gridDim.x, p.num_xcds)
+                                : (int)blockIdx.x;
+  const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
   const int m0 = tm * SMALL_TILE, n0 = tn * SMALL_TILE;
   const int vm = min(SMALL_TILE, p.M - m0), vn = min(SMALL_TILE, p.N - n0);
 
@@ -98,22 +117,61 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_small(SmallParams p) {
     aoff[i] = r < vm ? (uint32_t)((r * p.lda + kc[i] * 8) * 2) : OOB;
     boff[i] = r < vn ? (uint32_t)((r * p.ldb + kc[i] * 8) * 2) : OOB;
   }
+  // A @ B: load i of the B tile fills LDS bytes 1024 i .. +1023 of it; lane
+  // L's 16 bytes there hold row kn[i] (nn_row_pos inverted), column chunk
+  // L % 2 of the tile (columns n0 + 8 (L % 2) .. +7); chunks at or past N8
+  // read zeros.  The offsets are relative to the chunk's first row (the
+  // descriptor is rebased per chunk, so they stay small).
+  int kn[2];
+  uint32_t bnoff[2];
+  const bool ncol = n0 + 8 * (lane & 1) < p.N8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int b = 1024 * i + 16 * lane;
+    kn[i] = (b >> 5) ^ (((b >> 8) & 1) << 2);
+    bnoff[i] = ncol ? (uint32_t)((kn[i] * p.ldb + 8 * (lane & 1)) * 2) : OOB;
+  }
   const uint32_t wring = lds_addr(ring) + wave * (RING * SLOT);
   // chunk t of this wave (K chunk wave + 8 t) into ring slot t % RING
   auto issue = [&](int t) {
     const int c = wave + SMALL_WAVES * t;
     const uint32_t base = wring + (t % RING) * SLOT;
+    if constexpr (LAYOUT == NT) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool in = c * 64 + kc[i] * 8 < p.K8;
-      dma16_at(ra, in ? aoff[i] + c * 128 : OOB, base, i * 1024);
-      dma16_at(rb, in ? boff[i] + c * 128 : OOB, base, 2048 + i * 1024);
+      for (int i = 0; i < 2; ++i) {
+        const bool in = c * 64 + kc[i] * 8 < p.K8;
+        dma16_at(ra, in ? aoff[i] + c * 128 : OOB, base, i * 1024);
+        dma16_at(rb, in ? boff[i] + c * 128 : OOB, base, 2048 + i * 1024);
+      }
+    } else {
+      // B rows c*64 .. of the tile's columns, the range ending with the
+      // last row of B (none for chunks past K); the descriptor is
+      // wave-uniform: readfirstlane keeps it in the scalar registers the
+      // load takes
+      const int k0 = c * 64;
+      const int rows = min(64, p.K - k0);
+      const uint64_t a = (uint64_t)(uintptr_t)(p.B + (int64_t)k0 * p.ldb + n0);
+      i32x4 rbn = make_rsrc(a, rows > 0 ? (uint32_t)(((rows - 1) * p.ldb + (p.N8 - n0)) * 2) : 0u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rbn[e] = __builtin_amdgcn_readfirstlane(rbn[e]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const bool in = c * 64 + kc[i] * 8 < p.K8;
+        dma16_at(ra, in ? aoff[i] + c * 128 : OOB, base, i * 1024);
+        dma16_at(rbn, kn[i] < rows ? bnoff[i] : OOB, base, 2048 + i * 1024);
+      }
     }
   };
   // Fragment reads: lane (l16, lq) reads row l16, logical chunk 4 s + lq
   // (half s of the chunk).
   const int fr0 = l16 * 128 + ((lq ^ swz_k(l16)) << 4);
   const int fr1 = l16 * 128 + (((4 + lq) ^ swz_k(l16)) << 4);
+  // A @ B, transposing reads: for half s and read h, lane (l16, lq) supplies
+  // row 32 s + 8 lq + l16 / 4 + 4 h, columns 4 (l16 % 4) .. +3, and receives
+  // column l16 at four consecutive k (8 lq + 4 h .. +3 of the half)
+  int ft[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) ft[h] = nn_row_pos(8 * lq + (l16 >> 2) + 4 * h) + 8 * (l16 & 3);
 
   // Every wave runs the same number of chunks (chunks past K load zeros and
   // add nothing), so that the count of loads in flight is the same at every
@@ -128,8 +186,20 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_small(SmallParams p) {
       const char* slot = ring + (wave * RING + t % RING) * SLOT;
       const u32x4 a0 = *(const u32x4*)(slot + fr0);
       const u32x4 a1 = *(const u32x4*)(slot + fr1);
-      const u32x4 b0 = *(const u32x4*)(slot + 2048 + fr0);
-      const u32x4 b1 = *(const u32x4*)(slot + 2048 + fr1);
+      u32x4 b0, b1;
+      if constexpr (LAYOUT == NT) {
+        b0 = *(const u32x4*)(slot + 2048 + fr0);
+        b1 = *(const u32x4*)(slot + 2048 + fr1);
+      } else {
+        // (row 32 s + k of the tile: nn_row_pos adds 1024 s, bit 3 of k
+        // unchanged)
+        const u32x2 x0 = read_tr(slot + 2048 + ft[0]);
+        const u32x2 x1 = read_tr(slot + 2048 + ft[1]);
+        const u32x2 y0 = read_tr(slot + 2048 + 1024 + ft[0]);
+        const u32x2 y1 = read_tr(slot + 2048 + 1024 + ft[1]);
+        b0 = (u32x4){x0[0], x0[1], x1[0], x1[1]};
+        b1 = (u32x4){y0[0], y0[1], y1[0], y1[1]};
+      }
       acc0 = mfma16_chain<T>(acc0, b0, a0);
       acc1 = mfma16_chain<T>(acc1, b1, a1);
       // the slot's reads are done (the MFMAs took their data): refill it

@@ -131,10 +131,29 @@ namespace dg {
 // against 28.6, 16 x 32768 x 4096 43.1 against 47.4.  With more tile rows
 // and more tiles (each operand row streamed by many workgroups: 64 x 4096
 // x 4096 19.0 against 14.9) the tiled kernel is faster.
+//
+// A @ B: a 16 x 16 tile reads B in 32-byte row segments, four tiles to a
+// 128-byte line (the lines are fetched once: the tiles that share them run
+// on one XCD), which takes four times the L2 requests of A @ B.T (measured at
+// 1 x 8192 x 8192: 4.3 against 1.1 million): a CU streams its tiles at
+// about 40 GB/s, against about 90 for A @ B.T.  So A @ B runs the
+// small-output kernel only where K is at most SMALL_NN_K_MAX = 4096 and the
+// B elements its tiles stream, tile rows x N x K, are at most SMALL_NN_ELEMS
+// = 21 * 2^20.  Measured against the tiled kernel with its workspace passed
+// (with the workspace allocated per call, the tiled kernel's split costs
+// about 4 us more): 1 x 4096 x 4096 8.6 against 10.9 us, 16 x 4096 x 4096
+// 10.5 against 12.0, 32 x 1024 x 4096 5.7 against 10.4, 100 x 1000 x 3000
+// 13.6 against 14.4, 128 x 128 x 4096 5.3 against 10.9; beyond the limits
+// 1 x 6144 x 4096 18.3 against 14.7 (384 tiles: more than one per CU),
+// 1 x 8192 x 4096 17.3 against 16.4, 64 x 2048 x 4096 19.5 against 14.4,
+// 1 x 8192 x 8192 31.4 against 25.4, 128 x 1024 x 8192 35.8 against 19.6,
+// 1 x 2048 x 16384 30.3 against 17.6.
 bool small_output(int layout, int64_t M, int64_t N, int64_t K) {
-  if (layout != NT || M > SMALL_MAX || K > SMALL_K_MAX) return false;
-  const int64_t tiles = ((M + SMALL_TILE - 1) / SMALL_TILE) * ((N + SMALL_TILE - 1) / SMALL_TILE);
-  return tiles <= SMALL_MAX_TILES || M <= SMALL_TILE;
+  if ((layout != NT && layout != NN) || M > SMALL_MAX || K > SMALL_K_MAX) return false;
+  const int64_t tiles_m = (M + SMALL_TILE - 1) / SMALL_TILE;
+  const int64_t tiles = tiles_m * ((N + SMALL_TILE - 1) / SMALL_TILE);
+  if (tiles > SMALL_MAX_TILES && M > SMALL_TILE) return false;
+  return layout == NT || (K <= SMALL_NN_K_MAX && tiles_m * N * K <= SMALL_NN_ELEMS);
 }
 
 // Split-K for the tiles of the last, partial wave (all tiles when there

@@ -30,8 +30,10 @@ struct CallPlan {
   bool small() const { return plan[0] == SMALL_TILE; }
 };
 
-// A @ B.T outputs the small-output kernel computes when no option asks for
-// the tiled kernel: M and N at most SMALL_MAX, K at most SMALL_K_MAX.
+// Products the small-output kernel computes when no option asks for the
+// tiled kernel: M at most SMALL_MAX, K at most SMALL_K_MAX, at most
+// SMALL_MAX_TILES 16 x 16 tiles or one tile row, and for A @ B K at most
+// SMALL_NN_K_MAX and tile rows x N x K at most SMALL_NN_ELEMS.
 bool small_output(int layout, int64_t M, int64_t N, int64_t K);
 // The tiled kernel's plan (dense_gemm_plan for the other products).
 dense_gemm_status tiled_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t num_cus,

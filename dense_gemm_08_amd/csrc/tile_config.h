@@ -25,6 +25,10 @@ constexpr int SMALL_THREADS = SMALL_WAVES * 64;
 constexpr int SMALL_MAX = 128;
 constexpr int SMALL_K_MAX = 16384;
 constexpr int SMALL_MAX_TILES = 512;
+// A @ B also needs K at most SMALL_NN_K_MAX and tile rows x N x K, the B
+// elements its tiles stream, at most SMALL_NN_ELEMS (plan.cpp: small_output).
+constexpr int SMALL_NN_K_MAX = 4096;
+constexpr long long SMALL_NN_ELEMS = 21LL << 20;
 
 // The FP8 block-scaled GEMM (gemm_mx_kernel.h): 256 x 256 tiles, 128-deep
 // K stages (128 bytes per row), one E8M0 scale per GROUP K values; its

@@ -59,14 +59,18 @@
  * shape sums each output in the same order, so unsplit results are
  * identical.  dense_gemm_ex can force the width of A @ B.T.
  *
- * Small outputs.  D = A @ B.T with M <= 128 and K <= 16384 whose 16 x 16
+ * Small outputs.  A product with M <= 128 and K <= 16384 whose 16 x 16
  * tiles number at most 512, or form a single tile row (M <= 16), runs a
  * second kernel instead of the tiled one: one workgroup per 16 x 16 tile of
  * D, whose eight waves split K among themselves and add their FP32 sums in
  * a fixed order (reproducible; no workspace unless an operand is
- * repacked).  Its summation order differs from the tiled kernel's, within
- * the same rounding bound.  Any dense_gemm_options override asks for the
- * tiled kernel instead.
+ * repacked).  For D = A @ B it also needs K <= 4096 and at most 21 * 2^20
+ * B elements streamed by its tiles, ceil(M / 16) * N * K (its tiles read B
+ * in 32-byte row segments; past that the tiled kernel is faster); A @ B
+ * and A @ B.T on the same operands then give the same result bit for bit.
+ * Its summation order differs from the tiled kernel's, within the same
+ * rounding bound.  Any dense_gemm_options override asks for the tiled
+ * kernel instead.
  *
  * Workspace.  A call that repacks an operand or splits K needs device
  * memory beyond A, B and D: dense_gemm_workspace_size gives the amount.

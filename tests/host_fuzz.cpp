@@ -52,7 +52,8 @@ static void check_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t cus,
   // for the tiled kernel
   CHECK(cp.small() == (small_output(layout, M, N, K) && !options));
   if (cp.small()) {
-    CHECK(layout == NT && M <= SMALL_MAX && K <= SMALL_K_MAX);
+    CHECK(M <= SMALL_MAX && K <= SMALL_K_MAX);
+    CHECK(layout == NT || (K <= SMALL_NN_K_MAX && ceil_div(M, SMALL_TILE) * N * K <= SMALL_NN_ELEMS));
     CHECK(p[1] == SMALL_TILE && p[2] == BK && p[7] == SMALL_THREADS);
     CHECK(p[3] == ceil_div(M, SMALL_TILE) && p[4] == ceil_div(N, SMALL_TILE));
     CHECK(p[5] == p[3] * p[4] && cp.full_tasks == p[5]);

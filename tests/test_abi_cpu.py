@@ -410,7 +410,7 @@ def test_plan_tile_width():
         assert (out[1], out[4]) == (128, 1), (M, N, K)
     # wider outputs, A.B, and operands beyond 192 MiB keep 256-wide tiles
     for layout, M, N, K in [(NT, 8192, 2048, 1024), (NT, 4096, 4096, 4096), (NT, 3000, 5000, 4000),
-                            (NN, 128, 128, 4096), (NN, 8192, 1024, 2048), (NT, 8192, 1024, 16384)]:
+                            (NN, 128, 4096, 4096), (NN, 8192, 1024, 2048), (NT, 8192, 1024, 16384)]:
         assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
         assert out[1] == 256, (layout, M, N, K)
     # one wave either way: 128-wide tiles never exceed the CUs
@@ -426,7 +426,7 @@ def test_plan_tile_rows():
     lib = binding.load_library()
     out = (ctypes.c_int64 * 10)()
     for layout, M, N, K, rows in [(NT, 64, 4096, 4096, 128), (NT, 128, 16384, 4096, 128),
-                                  (NN, 128, 128, 4096, 128), (NN, 1, 264, 4096, 128),
+                                  (NN, 128, 2048, 4096, 128), (NN, 1, 8192, 8192, 128),
                                   (NT, 128, 128, 20000, 128), (NT, 129, 16384, 4096, 256),
                                   (NN, 200, 1000, 1000, 256), (NT, 4096, 4096, 4096, 256)]:
         assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
@@ -438,22 +438,29 @@ def test_plan_tile_rows():
 
 
 def test_plan_small_output():
-    # A.B^T with M <= 128, K <= 16384 and at most 512 16 x 16 tiles of D, or
-    # one tile row (M <= 16) of any width: the small-output kernel, one
+    # M <= 128, K <= 16384 and at most 512 16 x 16 tiles of D, or one tile
+    # row (M <= 16) of any width, and for A.B K <= 4096 and at most 21 * 2^20
+    # B elements streamed (tile rows x N x K): the small-output kernel, one
     # 512-thread workgroup per tile, no split
     lib = binding.load_library()
     out = (ctypes.c_int64 * 10)()
-    for M, N, K in [(128, 128, 64), (128, 128, 4096), (128, 128, 16384), (100, 72, 1000),
-                    (1, 4096, 4096), (1, 8192, 1), (128, 1024, 1024), (16, 16, 0),
-                    (16, 65536, 4096), (1, 1 << 20, 64)]:
-        assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK
+    for layout, M, N, K in [(NT, 128, 128, 64), (NT, 128, 128, 4096), (NT, 128, 128, 16384),
+                            (NT, 100, 72, 1000), (NT, 1, 4096, 4096), (NT, 1, 8192, 1),
+                            (NT, 128, 1024, 1024), (NT, 16, 16, 0), (NT, 16, 65536, 4096),
+                            (NT, 1, 1 << 20, 64), (NN, 128, 128, 4096), (NN, 1, 4096, 4096),
+                            (NN, 16, 4096, 4096), (NN, 100, 1000, 3000), (NN, 32, 1024, 4096),
+                            (NN, 1, 16, 64), (NN, 1, 5376, 4096), (NN, 3, 16, 4096)]:
+        assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
         tiles_m, tiles_n = -(-M // 16), -(-N // 16)
         assert list(out) == [16, 16, 64, tiles_m, tiles_n, tiles_m * tiles_n, 1, 512, 1,
-                             -(-K // 64)], (M, N, K)
-    # past any of the three limits, or A.B: the tiled kernel
+                             -(-K // 64)], (layout, M, N, K)
+    # past any of the limits: the tiled kernel (A.B: 1 x 8192 x 4096 and
+    # 64 x 2048 x 4096 stream 2^25 B elements, 1 x 5392 x 4096 one 16-column
+    # tile more than 21 * 2^20; K above 4096)
     for layout, M, N, K in [(NT, 129, 128, 4096), (NT, 128, 128, 16392), (NT, 17, 4112, 4096),
-                            (NT, 128, 1040, 64), (NT, 1, 4096, 16392), (NN, 128, 128, 4096),
-                            (NN, 1, 16, 64)]:
+                            (NT, 128, 1040, 64), (NT, 1, 4096, 16392), (NN, 1, 8192, 4096),
+                            (NN, 64, 2048, 4096), (NN, 1, 5392, 4096), (NN, 128, 1024, 8192),
+                            (NN, 1, 2048, 16384), (NN, 1, 16, 4104), (NN, 128, 128, 16384)]:
         assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
         # (128 tile rows where M <= 128)
         assert (out[0], out[7]) == (128 if M <= 128 else 256, 256), (layout, M, N, K)

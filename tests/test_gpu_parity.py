@@ -306,15 +306,91 @@ def test_small_output_kernel_small_integers_exact(fmt):
     assert (Dt == D).all()
 
 
+SMALL_NN = [
+    # (M, N, K) of A.B planned for the small-output kernel (also K <= 4096
+    # and at most 21 * 2^20 B elements streamed): the longest K, ragged tiles
+    # with K not a multiple of the 64-deep chunks, the streamed-elements
+    # limit exactly, one tile row past 512 tiles, N not a multiple of 8 (B
+    # repacked) at several widths, a K below 8 (A repacked), one chunk
+    # shared by fewer than the eight waves
+    (128, 128, 4096), (100, 72, 4000), (1, 5376, 4096), (16, 8200, 1000), (3, 20000, 72),
+    (5, 3, 7), (17, 130, 1000), (128, 1024, 64), (33, 266, 448),
+]
+
+
+def _nn_small(M, N, K):
+    import ctypes
+    from dense_gemm_08_amd import binding
+    out = (ctypes.c_int64 * 10)()
+    assert binding.load_library().dense_gemm_plan(1, M, N, K, 256, out) == 0
+    return out[0] == 16
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+@pytest.mark.parametrize("M,N,K", SMALL_NN, ids=lambda v: str(v))
+def test_small_output_kernel_nn_full_check(fmt, M, N, K):
+    assert _nn_small(M, N, K), "planned for the tiled kernel"
+    w = inputs.Workload("x", "nn", fmt, 0, 0, 0, "uniform", 0.0, 113)
+    A, B = inputs.make_operands(w, seed=M + 3 * N + K, M=M, N=N, K=K)
+    D, st = _gpu.gemm("nn", fmt, A, B, M, N, K)
+    assert st == status().OK
+    check_full("nn", fmt, A, B, M, N, K, D)
+    D2, _ = _gpu.gemm("nn", fmt, A, B, M, N, K)
+    assert (D == D2).all()
+    # the same chunks, fragments and MFMA order as A @ B.T with B transposed
+    # (its B fragments come from LDS rows instead of transposing reads): the
+    # two products are equal bit for bit
+    Bt = np.ascontiguousarray(B.reshape(K, N).T)
+    Dt, st = _gpu.gemm("nt", fmt, A, Bt, M, N, K)
+    assert st == status().OK
+    assert (Dt == D).all()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_small_output_kernel_nn_small_integers_exact(fmt):
+    # exact integer sums: the correctly rounded value bit for bit, equal to
+    # the tiled kernel's (an option asks for it)
+    M, N, K = 120, 104, 3000
+    assert _nn_small(M, N, K)
+    A = inputs.small_integers(fmt, (M, K), seed=35)
+    B = inputs.small_integers(fmt, (K, N), seed=36)
+    D, st = _gpu.gemm("nn", fmt, A, B, M, N, K)
+    assert st == status().OK
+    d, _ = oracle.gemm("nn", fmt, A, B)
+    assert (D == oracle.round_to(fmt, d)).all()
+    Dt, st = _gpu.gemm("nn", fmt, A, B, M, N, K, opts=(1, 0))
+    assert st == status().OK
+    assert (Dt == D).all()
+
+
+def test_small_output_kernel_nn_leading_dimensions_and_offsets():
+    # padded rows (B read in place: N and ldb multiples of 8), then pointers
+    # off 16-byte alignment (both operands repacked); D's padding untouched
+    M, N, K = 40, 520, 1000
+    assert _nn_small(M, N, K)
+    w = inputs.Workload("x", "nn", "bf16", 0, 0, 0, "uniform", 0.0, 117)
+    A, B = inputs.make_operands(w, seed=9, M=M, N=N, K=K)
+    D, st = _gpu.gemm("nn", "bf16", A, B, M, N, K, lda=K + 24, ldb=N + 40, ldd=N + 3)
+    assert st == status().OK
+    assert (D[:, N:] == _gpu.CANARY).all()
+    check_full("nn", "bf16", A, B, M, N, K, D[:, :N])
+    D2, st = _gpu.gemm("nn", "bf16", A, B, M, N, K, lda=K + 1, ldb=N + 5, ldd=N, a_off=1, b_off=3,
+                       d_off=1)
+    assert st == status().OK
+    assert (D2 == D[:, :N]).all()
+
+
 # ------------------------------------------------------ 128-row tiles --
 
 TALL = [
     # (layout, fmt, M, N, K) for the tiled kernel with 128-row tiles (M <= 128
     # and not a small-output product: K > 16384, more than 512 tiles of 16 x
-    # 16 with M > 16, or A.B): both widths, split and unsplit, ragged edges
+    # 16 with M > 16, or A.B with K > 4096 or streaming more than 21 * 2^20 B
+    # elements through 16 x 16 tiles): both widths, split and unsplit, ragged
+    # edges
     ("nt", "f16", 64, 8200, 1000), ("nt", "bf16", 100, 4200, 2000),
-    ("nt", "f16", 128, 128, 20000), ("nn", "bf16", 128, 1000, 3000), ("nn", "f16", 17, 600, 520),
-    ("nn", "bf16", 1, 264, 4096),
+    ("nt", "f16", 128, 128, 20000), ("nn", "bf16", 128, 1000, 4000), ("nn", "f16", 17, 2600, 5000),
+    ("nn", "bf16", 1, 6200, 4100),
 ]
 
 
