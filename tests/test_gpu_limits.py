@@ -12,7 +12,11 @@ below that bound, where the offsets use their full range:
 * FP8 block-scaled D = A @ B.T, M = N = 256, K = 8,388,576: a tile's rows
   span 2^31 - 8192 bytes (65,536 K steps in one tile);
 * the small-output kernel (D = A @ B.T, FP16, M = N = 16, K = 200) with
-  the largest leading dimensions the check accepts (rows ~8 MiB apart).
+  the largest leading dimensions the check accepts (rows ~8 MiB apart);
+* the small-output kernel on D = A @ B (BF16, M = N = 16, K = 128) with the
+  largest ldb the check accepts: a chunk's 64 rows of B span 2^31 - 96
+  bytes from its descriptor's base, and the second chunk's base lies 2 GiB
+  past B's start.
 
 Entries are integers in {-1, 0, 1} (unit scales for FP8), so every FP32
 partial sum is an exact integer below 2^24 and each output must equal the
@@ -127,3 +131,31 @@ def test_small_output_kernel_at_the_largest_leading_dimensions():
     D = _gpu.from_dev(Dd)
     d, _ = oracle.gemm("nt", "f16", A, B)
     assert (D == oracle.round_to("f16", d)).all()
+
+
+def test_small_output_kernel_nn_at_the_largest_ldb():
+    import ctypes
+    lib = binding.load_library()
+    M, N, K = 16, 16, 128
+
+    def ok(ld):
+        return lib.dense_gemm_validate(1, M, N, K, ctypes.c_void_p(256), K, ctypes.c_void_p(256),
+                                       ld, ctypes.c_void_p(256), N) == S.OK
+    lo, hi = N, 1 << 30
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if ok(mid) else (lo, mid)
+    ld = lo - lo % 8  # B read in place (16-byte aligned rows)
+    assert ok(ld) and not ok(hi)
+    out = (ctypes.c_int64 * 10)()
+    assert lib.dense_gemm_plan(1, M, N, K, 256, out) == S.OK and out[0] == 16
+    print("small-output A.B BF16 %d x %d x %d, ldb = %d" % (M, N, K, ld), flush=True)
+    A = inputs.small_integers("bf16", (M, K), seed=108)
+    B = inputs.small_integers("bf16", (K, N), seed=109)
+    Ad, Bd = _gpu.to_dev(A, M, K), _gpu.to_dev(B, K, N, ld=ld)
+    Dd = _gpu.empty_out(M, N)
+    assert _gpu.call("nn", "bf16", M, N, K, Ad, K, Bd, ld, Dd, N) == S.OK
+    _gpu.torch().cuda.synchronize()
+    D = _gpu.from_dev(Dd)
+    d, _ = oracle.gemm("nn", "bf16", A, B)
+    assert (D == oracle.round_to("bf16", d)).all()
