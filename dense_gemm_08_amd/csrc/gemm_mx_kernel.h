@@ -586,34 +586,33 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_mx_small(MxSmallParams p) 
   if (per_wave > 0)
     for (int t = 0; t < RING; ++t) issue(t);
 
-  // The tile's scales, while the first chunks load: each thread's share (at
-  // most PER bytes) is loaded first, every load unconditional (an address
-  // inside the matrix, the value replaced by scale 1 outside the rows and
-  // blocks), so that all of them are in flight at once, then stored.  (With
-  // K = 0 there are none, and the scale pointers may be null.)
+  // The tile's scales, while the first chunks load.  Thread t takes operand
+  // t / 256 (A, then B), row (t / 16) % 16 of the tile and blocks t % 16 +
+  // 16 j: its PER bytes are loaded first, every load unconditional (from an
+  // address inside the matrix: row 0 of the tile for rows past M or N,
+  // block 0 for blocks past K / 32), so that all of them are in flight at
+  // once, then stored (scale 1 for rows past M or N; blocks past K / 32 are
+  // never read).  The shares follow from shifts of t: index arithmetic with
+  // K / 32 as divisor measured ~1.5 us per call.  (With K = 0 there are no
+  // scales, and the scale pointers may be null.)
+  static_assert(SMALL_THREADS == 2 * SMALL_TILE * 16 && NBMAX % 16 == 0, "one thread per 16 blocks");
   if (nb > 0) {
-    constexpr int PER = 2 * SMALL_TILE * NBMAX / SMALL_THREADS;
-    const int total = 2 * SMALL_TILE * nb;
+    constexpr int PER = NBMAX / 16;
+    const int t = (int)threadIdx.x;
+    const int op = t >> 8, row = (t >> 4) & 15, b0 = t & 15;
+    const bool rin = row < (op ? vn : vm);
+    const uint8_t* src = op ? p.SB + (int64_t)(n0 + (rin ? row : 0)) * p.ldsb
+                            : p.SA + (int64_t)(m0 + (rin ? row : 0)) * p.ldsa;
     int v[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int idx = (int)threadIdx.x + j * SMALL_THREADS;
-      const int op = idx >= SMALL_TILE * nb ? 1 : 0;
-      const int rem = idx - op * SMALL_TILE * nb;
-      const int row = nb > 0 ? rem / nb : 0, b = nb > 0 ? rem % nb : 0;
-      const bool in = idx < total && row < (op ? vn : vm);
-      const uint8_t* src = op ? p.SB + (int64_t)(n0 + (in ? row : 0)) * p.ldsb
-                              : p.SA + (int64_t)(m0 + (in ? row : 0)) * p.ldsa;
-      v[j] = in ? (int)src[in ? b : 0] : 127;  // 127: scale 1
+      const int b = b0 + 16 * j;
+      v[j] = src[b < nb ? b : 0];
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int idx = (int)threadIdx.x + j * SMALL_THREADS;
-      if (idx < total) {
-        const int op = idx >= SMALL_TILE * nb ? 1 : 0;
-        const int rem = idx - op * SMALL_TILE * nb;
-        scales[op][rem / nb][rem % nb] = (uint8_t)v[j];
-      }
+      const int b = b0 + 16 * j;
+      if (b < nb) scales[op][row][b] = (uint8_t)(rin ? v[j] : 127);  // 127: scale 1
     }
   }
   __syncthreads();

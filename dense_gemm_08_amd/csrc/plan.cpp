@@ -337,10 +337,12 @@ dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const v
 
 // Products the FP8 small-output kernel computes (gemm_mx_small): M <= 128,
 // K <= MX_SMALL_K_MAX, at most SMALL_MAX_TILES tiles of 16 x 16 or one tile
-// row.  Measured per call against the tiled kernel (its scale packing and
-// workspace included), one box: 128 x 128 x 4096 6.2 against 45.3 us,
-// 1 x 4096 x 4096 6.2 against 44.5, 16 x 16384 x 4096 21.3 against 48.3,
-// 128 x 1024 x 8192 12.3 against 75.6, 128 x 128 x 64 4.5 against 23.1.
+// row.  Measured per call against the tiled kernel before its split-K (its
+// scale packing and workspace included), one box: 128 x 128 x 4096 6.2
+// against 45.3 us, 1 x 4096 x 4096 6.2 against 44.5, 16 x 16384 x 4096 21.3
+// against 48.3, 128 x 1024 x 8192 12.3 against 75.6, 128 x 128 x 64 4.5
+// against 23.1 (since the scale staging lost its divisions: 4.55, 5.2,
+// 21.3, 10.3 and 4.05 us).
 bool mx_small_output(int64_t M, int64_t N, int64_t K) {
   if (M > SMALL_MAX || K > mx::MX_SMALL_K_MAX) return false;
   const int64_t tiles = ((M + SMALL_TILE - 1) / SMALL_TILE) * ((N + SMALL_TILE - 1) / SMALL_TILE);
