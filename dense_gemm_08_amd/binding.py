@@ -250,11 +250,23 @@ def raw(name: str):
     return getattr(load_library(), name)
 
 
-def gemm_nt_e4m3_mx(A, SA, B, SB, D=None, stream=None):
+def mx_workspace_size(M: int, N: int, K: int, num_cus: int = 0) -> int:
+    """Bytes of workspace gemm_nt_e4m3_mx_ex needs (gemm_nt_e4m3_mx_workspace_size;
+    num_cus 0: the current device's)."""
+    out = ctypes.c_size_t()
+    st = load_library().gemm_nt_e4m3_mx_workspace_size(M, N, K, num_cus, ctypes.byref(out))
+    if st != Status.OK:
+        raise DenseGemmError(st, "gemm_nt_e4m3_mx_workspace_size")
+    return out.value
+
+
+def gemm_nt_e4m3_mx(A, SA, B, SB, D=None, stream=None, workspace=None):
     """D = A @ B.T with E4M3 A (M x K), B (N x K) and E8M0 block scales SA
     (M x K/32), SB (N x K/32), FP32 accumulation, BF16 out.  A and B are
     uint8 or float8_e4m3fn device tensors, SA and SB uint8 device tensors,
-    all 2-D with unit column stride."""
+    all 2-D with unit column stride.  With ``workspace`` (a device tensor, or
+    True to take one from torch's allocator), the call goes through
+    gemm_nt_e4m3_mx_ex with that workspace."""
     import torch
     lib = load_library()
     for t, what in ((A, "A"), (SA, "SA"), (B, "B"), (SB, "SB")):
@@ -272,10 +284,22 @@ def gemm_nt_e4m3_mx(A, SA, B, SB, D=None, stream=None):
         if D.shape[0] != M or D.shape[1] != N:
             raise ValueError("D has shape %s, expected (%d, %d)" % (tuple(D.shape), M, N))
     dev = _same_device(A, SA, B, SB, D)
+    name = "gemm_nt_e4m3_mx"
     with torch.cuda.device(dev):
-        st = lib.gemm_nt_e4m3_mx(M, N, K, A.data_ptr(), _ld(A), SA.data_ptr(), _ld(SA),
-                                 B.data_ptr(), _ld(B), SB.data_ptr(), _ld(SB),
-                                 D.data_ptr(), _ld(D), _stream_handle(stream, dev))
+        args = (M, N, K, A.data_ptr(), _ld(A), SA.data_ptr(), _ld(SA), B.data_ptr(), _ld(B),
+                SB.data_ptr(), _ld(SB), D.data_ptr(), _ld(D))
+        if workspace is None:
+            st = lib.gemm_nt_e4m3_mx(*args, _stream_handle(stream, dev))
+        else:
+            if workspace is True:
+                workspace = torch.empty(max(mx_workspace_size(M, N, K), 1), dtype=torch.uint8,
+                                        device=dev)
+            if not workspace.is_cuda or workspace.device != dev:
+                raise ValueError("workspace must be a device tensor on %s" % dev)
+            st = lib.gemm_nt_e4m3_mx_ex(*args, workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream_handle(stream, dev))
+            name = "gemm_nt_e4m3_mx_ex"
     if st != Status.OK:
-        raise DenseGemmError(st, "gemm_nt_e4m3_mx")
+        raise DenseGemmError(st, name)
     return D

@@ -184,6 +184,14 @@ def test_mx_python_binding_takes_float8_tensors():
     t.cuda.synchronize()
     assert D.dtype == t.bfloat16 and tuple(D.shape) == (M, N)
     check_full(A, SA, B, SB, D.cpu().view(t.int16).numpy().view(np.uint16))
+    # the workspace-passing form, with a workspace taken by the binding and
+    # with the caller's: the same bits
+    D2 = dg.gemm_nt_e4m3_mx(dev(A), dev(SA), dev(B), dev(SB), workspace=True)
+    from dense_gemm_08_amd import binding
+    ws = t.empty(max(binding.mx_workspace_size(M, N, K), 1), dtype=t.uint8, device="cuda")
+    D3 = dg.gemm_nt_e4m3_mx(dev(A), dev(SA), dev(B), dev(SB), workspace=ws)
+    t.cuda.synchronize()
+    assert t.equal(D.view(t.int16), D2.view(t.int16)) and t.equal(D.view(t.int16), D3.view(t.int16))
 
 
 @pytest.mark.timeout(900)
