@@ -506,8 +506,9 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
 }
 
 // ---- the small-output kernel ---------------------------------------------
-// D = A @ B.T for M <= 128 and K <= MX_SMALL_K_MAX with at most
-// SMALL_MAX_TILES 16 x 16 tiles of D, or one tile row (M <= 16): the FP16
+// D = A @ B.T for M <= 128 and K <= MX_SMALL_K_MAX with one tile row (M <=
+// 16) or at most MX_SMALL_MAX_TILES 16 x 16 tiles of D (tiles x K at most
+// MX_SMALL_TILES_K): the FP16
 // small-output kernel's decomposition (gemm_small_kernel.h) with FP8 data.
 // One workgroup of eight waves per 16 x 16 tile; wave w takes the 128-deep
 // K chunks w, w + 8, ... (128 bytes per row, the FP16 kernel's 64-deep LDS

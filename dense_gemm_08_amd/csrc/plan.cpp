@@ -336,8 +336,18 @@ dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const v
 }
 
 // Products the FP8 small-output kernel computes (gemm_mx_small): M <= 128,
-// K <= MX_SMALL_K_MAX, at most SMALL_MAX_TILES tiles of 16 x 16 or one tile
-// row.  Measured per call against the tiled kernel before its split-K (its
+// K <= MX_SMALL_K_MAX = 8192, and one tile row (M <= 16) or at most
+// MX_SMALL_MAX_TILES = 2048 tiles of 16 x 16 with tiles x K at most
+// MX_SMALL_TILES_K = 2^23.  The tiled FP8 kernel has no 128-row tile, so
+// against it the small kernel pays at more tiles than the FP16 rule allows:
+// measured per call on one box (small against tiled with its split-K),
+// 64 x 4096 x 4096 13.5 against 25.8 us, 128 x 4096 x 4096 24.4 against
+// 30.1, 128 x 2048 x 8192 19.2 against 30.0, 32 x 16384 x 2048 18.5 against
+// 26.2, 128 x 1536 x 8192 15.9 against 28.3, 32 x 8192 x 8192 (tiles x K =
+// 2^23) 27.4 against 31.2; past the limits 128 x 4096 x 8192 36.0 against
+// 30.5, 48 x 8192 x 8192 38.9 against 32.3, 64 x 16384 x 2048 34.8 against
+// 31.4, 128 x 16384 x 1024 49.9 against 24.3.  Within the former limit of
+// 512 tiles, against the tiled kernel before its split-K (its
 // scale packing and workspace included), one box: 128 x 128 x 4096 6.2
 // against 45.3 us, 1 x 4096 x 4096 6.2 against 44.5, 16 x 16384 x 4096 21.3
 // against 48.3, 128 x 1024 x 8192 12.3 against 75.6, 128 x 128 x 64 4.5
@@ -345,8 +355,9 @@ dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const v
 // 21.3, 10.3 and 4.05 us).
 bool mx_small_output(int64_t M, int64_t N, int64_t K) {
   if (M > SMALL_MAX || K > mx::MX_SMALL_K_MAX) return false;
+  if (M <= SMALL_TILE) return true;
   const int64_t tiles = ((M + SMALL_TILE - 1) / SMALL_TILE) * ((N + SMALL_TILE - 1) / SMALL_TILE);
-  return tiles <= SMALL_MAX_TILES || M <= SMALL_TILE;
+  return tiles <= mx::MX_SMALL_MAX_TILES && tiles * K <= mx::MX_SMALL_TILES_K;
 }
 
 dense_gemm_status mx_plan_call(int64_t M, int64_t N, int64_t K, int64_t num_cus, MxPlan* mp) {

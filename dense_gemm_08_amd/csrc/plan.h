@@ -77,7 +77,8 @@ struct MxPlan {
 };
 
 // The FP8 small-output kernel's products (M <= 128, K <= MX_SMALL_K_MAX,
-// at most SMALL_MAX_TILES 16 x 16 tiles or one tile row).
+// one tile row or at most MX_SMALL_MAX_TILES 16 x 16 tiles with tiles x K
+// at most MX_SMALL_TILES_K).
 bool mx_small_output(int64_t M, int64_t N, int64_t K);
 // The plan of an FP8 call with M, N > 0 and K a multiple of 32 on a device
 // with num_cus CUs.

@@ -33,13 +33,17 @@ constexpr long long SMALL_NN_ELEMS = 21LL << 20;
 // The FP8 block-scaled GEMM (gemm_mx_kernel.h): 256 x 256 tiles, 128-deep
 // K stages (128 bytes per row), one E8M0 scale per GROUP K values; its
 // small-output kernel takes the small-output decomposition above for K up
-// to MX_SMALL_K_MAX.
+// to MX_SMALL_K_MAX and at most MX_SMALL_MAX_TILES 16 x 16 tiles with tiles
+// x K at most MX_SMALL_TILES_K, or one tile row (plan.cpp:
+// mx_small_output).
 namespace mx {
 constexpr int BM = 256, BN = 256;
 constexpr int BKE = 128;                   // K elements (= bytes) per stage
 constexpr int GROUP = 32;                  // K elements per scale
 constexpr int SC_BYTES = 1024;             // packed scale panel per operand per stage
 constexpr int MX_SMALL_K_MAX = 8192;
+constexpr int MX_SMALL_MAX_TILES = 2048;
+constexpr long long MX_SMALL_TILES_K = 1LL << 23;
 }  // namespace mx
 
 }  // namespace dg

@@ -222,9 +222,10 @@ dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N, int64_t K,
  * D needs 2-byte alignment.  M, N and K/128 may be ragged.  The products are
  * exact in FP32; their sum is accumulated in FP32 in a fixed order (results
  * are reproducible on a device; the order depends on the plan, hence on the
- * CU count).  Small outputs (M <= 128, K <= 8192, at most 512 tiles of
- * 16 x 16 or M <= 16) run a small-output kernel (16 x 16 tiles, K split
- * among eight waves, the scales staged in LDS) that needs no workspace.
+ * CU count).  Small outputs (M <= 128, K <= 8192, and M <= 16 or at most
+ * 2048 tiles of 16 x 16 with tiles * K <= 2^23) run a small-output kernel
+ * (16 x 16 tiles, K split among eight waves, the scales staged in LDS) that
+ * needs no workspace.
  * Other products run a tiled kernel (256 x 256 tiles) that takes a
  * workspace (hipMallocAsync / hipFreeAsync on `stream`;
  * DENSE_GEMM_NO_MEMORY if unavailable) of 1 KiB per 256-row tile of A and

@@ -99,7 +99,8 @@ static void check_mx_plan(int64_t M, int64_t N, int64_t K, int64_t cus, const Mx
   if (mp.small()) {
     CHECK(M <= SMALL_MAX && K <= mx::MX_SMALL_K_MAX && p[1] == SMALL_TILE);
     CHECK(p[3] == ceil_div(M, SMALL_TILE) && p[4] == ceil_div(N, SMALL_TILE));
-    CHECK(p[5] == p[3] * p[4] && (p[5] <= SMALL_MAX_TILES || p[3] == 1));
+    CHECK(p[5] == p[3] * p[4] &&
+          (p[3] == 1 || (p[5] <= mx::MX_SMALL_MAX_TILES && p[5] * K <= mx::MX_SMALL_TILES_K)));
     CHECK(p[7] == SMALL_THREADS && p[8] == 1 && mp.total() == 0);
     return;
   }

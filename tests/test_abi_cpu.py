@@ -300,6 +300,11 @@ def test_mx_plan():
     # small outputs: 16 x 16 tiles, one 512-thread workgroup each, no split
     assert plan(128, 128, 4096) == [16, 16, 128, 8, 8, 64, 1, 512, 1, 32]
     assert plan(1, 40000, 256)[:6] == [16, 16, 128, 1, 2500, 2500]
+    # ... up to 2048 tiles with tiles x K <= 2^23 (exactly, at 2048 x 4096)
+    assert plan(128, 4096, 4096) == [16, 16, 128, 8, 256, 2048, 1, 512, 1, 32]
+    assert plan(32, 8192, 8192)[:6] == [16, 16, 128, 2, 512, 1024]
+    for M, N, K in [(128, 4096, 4128), (128, 4112, 1024), (48, 8192, 8192), (128, 128, 8224)]:
+        assert plan(M, N, K)[:3] == [256, 256, 128], (M, N, K)
     # the page workloads: whole waves, no split
     assert plan(8192, 8192, 8192) == [256, 256, 128, 32, 32, 256, 8, 256, 1, 64]
     assert plan(8192, 17408, 5120) == [256, 256, 128, 32, 68, 256, 8, 256, 1, 40]
@@ -610,12 +615,14 @@ def test_mx_workspace_size():
     assert ws(280, 300, 160) == (S.OK, (2 + 2) * 2 * 1024)
     assert ws(256, 256, 0) == (S.OK, 2 * 1024)
     assert ws(0, 256, 64) == (S.OK, 0)
-    # the small-output kernel (M <= 128, K <= 8192, at most 512 tiles of
-    # 16 x 16 or one tile row) stages its scales in LDS: no workspace
+    # the small-output kernel (M <= 128, K <= 8192, and one tile row or at
+    # most 2048 tiles of 16 x 16 with tiles x K <= 2^23) stages its scales
+    # in LDS: no workspace
     assert ws(128, 128, 4096) == (S.OK, 0)
     assert ws(16, 65536, 8192) == (S.OK, 0)
     assert ws(64, 1100, 2080) == (S.OK, 0)
-    assert ws(17, 8200, 512) == (S.OK, (1 + 33) * 4 * 1024)
+    assert ws(17, 8200, 512) == (S.OK, 0)  # 1026 tiles
+    assert ws(17, 16400, 512) == (S.OK, (1 + 65) * 4 * 1024)  # 2050 tiles: the tiled kernel
     # split-K adds 256 KiB (a 256 x 256 FP32 tile) per part of each split
     # tile: 128 x 128 x 8224 is one tile in 13 parts, 256 x 256 x 16384 one
     # in 32, 8192 x 4224 x 4096 has 32 tiles after two full waves, in 8 parts

@@ -389,11 +389,12 @@ def test_mx_split_k_workspace_call_equals_plain_call():
 
 
 MX_SMALL = [
-    # (M, N, K) for the small-output kernel (M <= 128, K <= 8192, at most
-    # 512 tiles of 16 x 16 or one tile row): K mod 128 = 0, 32, 64, 96, the
-    # longest K, one tile row past 512 tiles, ragged tiles, one block
+    # (M, N, K) for the small-output kernel (M <= 128, K <= 8192, and one
+    # tile row or at most 2048 tiles of 16 x 16 with tiles x K <= 2^23): K
+    # mod 128 = 0, 32, 64, 96, the longest K, one tile row past 512 tiles,
+    # several tile rows past 512 tiles, ragged tiles, one block
     (128, 128, 4096), (100, 72, 8192), (1, 4096, 1024), (16, 8200, 480), (128, 1024, 96),
-    (5, 300, 224), (33, 17, 32),
+    (5, 300, 224), (33, 17, 32), (64, 2200, 1056), (120, 1536, 4096),
 ]
 
 
