@@ -610,10 +610,14 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_mx_small(MxSmallParams p) 
       const int b = b0 + 16 * j;
       v[j] = src[b < nb ? b : 0];
     }
+    // Every loaded value is stored (blocks past K / 32 with scale 1; they
+    // are never read): a load whose value went unused would stay pending,
+    // as far as the compiler knows, into the K loop, where it would then
+    // wait for all loads in flight (the ring's included) at every chunk.
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int b = b0 + 16 * j;
-      if (b < nb) scales[op][row][b] = (uint8_t)(rin ? v[j] : 127);  // 127: scale 1
+      scales[op][row][b] = (uint8_t)(rin && b < nb ? v[j] : 127);  // 127: scale 1
     }
   }
   __syncthreads();
