@@ -69,6 +69,15 @@ __device__ __forceinline__ void dma16_at(i32x4 rsrc, uint32_t off, uint32_t base
                : "v"(off), "s"(rsrc), "s"(base), "i"(imm)
                : "memory", "m0", "scc");
 }
+// 4-byte global -> LDS copy for every lane of the wave: lane L's 4 bytes at
+// buffer offset `off` land at LDS address base + imm + 4 L (offsets at or
+// past the descriptor's range write zeros).
+__device__ __forceinline__ void dma4_at(i32x4 rsrc, uint32_t off, uint32_t base, int imm) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(base), "i"(imm)
+               : "memory", "m0", "scc");
+}
 #pragma clang diagnostic pop
 
 // Scheduling fence: the compiler may move no instruction across it.

@@ -584,12 +584,44 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_mx_small(MxSmallParams p) 
   };
   const int chunks = (p.K + BKE - 1) / BKE;
   const int per_wave = (chunks + SMALL_WAVES - 1) / SMALL_WAVES;
+
+  // The tile's scales by LDS-DMA where every scale row starts 4-byte aligned,
+  // K / 32 is a multiple of 4 and a tile's rows span less than 2^31 bytes:
+  // waves 0-3 copy A's 16 rows, waves 4-7 B's, one 256-byte row of
+  // `scales` per instruction (lane L: blocks 4 L .. 4 L + 3; rows past M or
+  // N and blocks past K / 32 read zeros, whose data is zero too).  Issued
+  // before the ring's first chunks, so that each wave then waits for these
+  // loads only.
+  const int64_t sld = p.ldsa > p.ldsb ? p.ldsa : p.ldsb;
+  const bool sdma = nb > 0 && (nb & 3) == 0 &&
+                    ((((uintptr_t)p.SA | (uintptr_t)p.SB) & 3) == 0) &&
+                    (((p.ldsa | p.ldsb) & 3) == 0) &&
+                    (SMALL_TILE - 1) * sld + nb < ((int64_t)1 << 31);
+  if (sdma) {
+    const int op = wave >> 2;
+    const int vr = op ? vn : vm;
+    const int ld = op ? p.ldsb : p.ldsa;
+    i32x4 rs = make_rsrc((uint64_t)(uintptr_t)(op ? p.SB + (int64_t)n0 * p.ldsb
+                                                  : p.SA + (int64_t)m0 * p.ldsa),
+                         (uint32_t)((vr - 1) * ld + nb));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs[i] = __builtin_amdgcn_readfirstlane(rs[i]);
+    const int r0 = 4 * (wave & 3);
+    const uint32_t sbase = lds_addr(&scales[op][r0][0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + i;
+      dma4_at(rs, row < vr && 4 * lane < nb ? (uint32_t)(row * ld + 4 * lane) : OOB, sbase,
+              i * NBMAX);
+    }
+  }
   if (per_wave > 0)
     for (int t = 0; t < RING; ++t) issue(t);
 
-  // The tile's scales, while the first chunks load.  Thread t takes operand
-  // t / 256 (A, then B), row (t / 16) % 16 of the tile and blocks t % 16 +
-  // 16 j: its PER bytes are loaded first, every load unconditional (from an
+  // Otherwise the tile's scales are loaded as bytes, while the first chunks
+  // load.  Thread t takes operand t / 256 (A, then B), row (t / 16) % 16 of
+  // the tile and blocks t % 16 + 16 j: its PER bytes are loaded first (the
+  // wait for them also waits for the first chunks), every load unconditional (from an
   // address inside the matrix: row 0 of the tile for rows past M or N,
   // block 0 for blocks past K / 32), so that all of them are in flight at
   // once, then stored (scale 1 for rows past M or N; blocks past K / 32 are
@@ -597,7 +629,11 @@ __global__ __launch_bounds__(SMALL_THREADS) void gemm_mx_small(MxSmallParams p) 
   // K / 32 as divisor measured ~1.5 us per call.  (With K = 0 there are no
   // scales, and the scale pointers may be null.)
   static_assert(SMALL_THREADS == 2 * SMALL_TILE * 16 && NBMAX % 16 == 0, "one thread per 16 blocks");
-  if (nb > 0) {
+  if (sdma) {
+    // this wave's scale rows have landed; the ring's first two chunks (8
+    // loads) may still be in flight
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(4 * RING) : "memory");
+  } else if (nb > 0) {
     constexpr int PER = NBMAX / 16;
     const int t = (int)threadIdx.x;
     const int op = t >> 8, row = (t >> 4) & 15, b0 = t & 15;
