@@ -15,6 +15,13 @@ edges included):
 
 counting ``s_nop N`` as N + 1 slots.  A synthetic listing with one planted
 violation of each kind checks the checker.
+
+The kernels' LDS rings count their loads themselves (the loads are inline
+asm, which the compiler does not track, so each wait is the kernel's own
+``s_waitcnt vmcnt(N)``).  A vector-memory wait the compiler adds inside a
+loop (for loads of its own it believes still pending) waits for every load
+in flight, the ring's prefetches included: a further check finds none in
+any loop of the GEMM kernels (a synthetic listing checks it too).
 """
 import os
 import re
@@ -241,3 +248,97 @@ def test_library_kernels_keep_mfma_operands_apart(src, tmp_path):
     assert n_mfma > 0
     bad = check(asm)
     assert not bad, "\n".join(bad[:20])
+
+
+# ------------------------------------------- compiler waits in the rings --
+
+def gemm_functions(asm: str):
+    """{function name: [(label or None, instruction, from inline asm)]} for
+    every function whose name contains "gemm" (the tiled and small-output
+    kernels)."""
+    out, cur, in_asm = {}, None, False
+    for line in asm.split("\n"):
+        if ";;#ASMSTART" in line:
+            in_asm = True
+            continue
+        if ";;#ASMEND" in line:
+            in_asm = False
+            continue
+        s = line.split(";")[0].rstrip()
+        m = re.match(r"^(_Z\S*gemm\S*):", s)
+        if m:
+            cur = out.setdefault(m.group(1), [])
+            continue
+        if cur is None:
+            continue
+        t = s.strip()
+        if t.startswith(".Lfunc_end"):
+            cur = None
+            continue
+        if t.startswith(".LBB") and t.endswith(":"):
+            cur.append((t[:-1], None, False))
+            continue
+        if not t or t.startswith(".") or t.endswith(":"):
+            continue
+        cur.append((None, t, in_asm))
+    return out
+
+
+def compiler_waits_in_loops(asm: str):
+    """The compiler's own vector-memory waits in blocks on a cycle."""
+    found = []
+    for name, items in gemm_functions(asm).items():
+        blocks, succ, _ = cfg([(label, ins) for label, ins, _ in items])
+        # the inline-asm flag of each block's instructions (cfg keeps the
+        # instructions in order)
+        flags = [a for label, _, a in items if label is None]
+        block_flags, k = [], 0
+        for ins_list in blocks:
+            block_flags.append(flags[k:k + len(ins_list)])
+            k += len(ins_list)
+
+        def reaches(b):
+            seen, st = set(), list(succ[b])
+            while st:
+                x = st.pop()
+                if x not in seen:
+                    seen.add(x)
+                    st.extend(succ[x])
+            return seen
+        for b, ins_list in enumerate(blocks):
+            if b not in reaches(b):
+                continue
+            for ins, a in zip(ins_list, block_flags[b]):
+                if not a and ins.startswith("s_waitcnt") and "vmcnt" in ins:
+                    found.append("%s: %s" % (name, ins))
+    return found
+
+
+def test_loop_wait_checker_finds_a_compiler_wait():
+    asm = """_Z4gemmv:
+	s_mov_b32 s0, 4
+.LBB0_1:
+	;;#ASMSTART
+	s_waitcnt vmcnt(4)
+	;;#ASMEND
+	s_waitcnt vmcnt(0)
+	v_mov_b32_e32 v0, v1
+	s_add_i32 s0, s0, -1
+	s_cmp_eq_u32 s0, 0
+	s_cbranch_scc0 .LBB0_1
+	s_waitcnt vmcnt(0)
+	s_endpgm
+.Lfunc_end0:
+"""
+    found = compiler_waits_in_loops(asm)
+    # the loop's compiler wait only: the kernel's own wait and the one after
+    # the loop are not reported
+    assert found == ["_Z4gemmv: s_waitcnt vmcnt(0)"], found
+
+
+@pytest.mark.parametrize("src", ["dense_gemm.hip", "gemm_mx.hip"])
+def test_ring_loops_hold_no_compiler_memory_waits(src, tmp_path):
+    asm = compile_asm(src, str(tmp_path / (src + ".s")))
+    assert gemm_functions(asm), "no GEMM kernels found in the generated code"
+    found = compiler_waits_in_loops(asm)
+    assert not found, "\n".join(found[:20])
