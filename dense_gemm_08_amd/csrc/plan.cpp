@@ -346,7 +346,11 @@ dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const v
 // 26.2, 128 x 1536 x 8192 15.9 against 28.3, 32 x 8192 x 8192 (tiles x K =
 // 2^23) 27.4 against 31.2; past the limits 128 x 4096 x 8192 36.0 against
 // 30.5, 48 x 8192 x 8192 38.9 against 32.3, 64 x 16384 x 2048 34.8 against
-// 31.4, 128 x 16384 x 1024 49.9 against 24.3.  Within the former limit of
+// 31.4, 128 x 16384 x 1024 49.9 against 24.3.  Re-measured after the
+// small kernel's scale staging got faster: past the limits it ties the
+// tiled kernel within 3% (64 x 16384 x 2048, 96 x 8192 x 4096, 128 x 8192 x
+// 1024) or loses (128 x 8192 x 4096 by 23%, 64 x 8192 x 8192 by 40%, 128 x
+// 16384 x 1024 by 86%), so the limits stay.  Within the former limit of
 // 512 tiles, against the tiled kernel before its split-K (its
 // scale packing and workspace included), one box: 128 x 128 x 4096 6.2
 // against 45.3 us, 1 x 4096 x 4096 6.2 against 44.5, 16 x 16384 x 4096 21.3
