@@ -388,6 +388,55 @@ def test_mx_split_k_workspace_call_equals_plain_call():
     assert (_gpu.from_dev(D3) == _gpu.CANARY).all()
 
 
+def test_mx_workspace_calls_on_two_streams():
+    # split-K calls (and one with scale panels only), each given its own
+    # workspace, issued back to back on two streams that do not wait for
+    # each other: the bits of the same calls run alone
+    import ctypes
+    from dense_gemm_08_amd import binding
+    t = _gpu.torch()
+    lib = binding.load_library()
+    shapes = [(300, 200, 4128), (256, 256, 8192), (520, 300, 416)]
+    cases = []
+    for i, (M, N, K) in enumerate(shapes):
+        ops = [t.from_numpy(x).cuda() for x in inputs.mx_operands(M, N, K, seed=90 + i)]
+        need = ctypes.c_size_t()
+        assert lib.gemm_nt_e4m3_mx_workspace_size(M, N, K, 0, ctypes.byref(need)) == 0
+        assert need.value > 0
+        cases.append((M, N, K, ops, need.value))
+
+    def call(c, D, ws, stream):
+        M, N, K, (A, SA, B, SB), need = c
+        nb = K // 32
+        return lib.gemm_nt_e4m3_mx_ex(M, N, K, A.data_ptr(), K, SA.data_ptr(), nb, B.data_ptr(), K,
+                                      SB.data_ptr(), nb, D.data_ptr(), N, ws.data_ptr(), need,
+                                      stream.cuda_stream)
+    main = t.cuda.current_stream()
+    ref = []
+    for c in cases:
+        D = _gpu.empty_out(c[0], c[1])
+        assert call(c, D, _gpu.workspace(c[4]), main) == 0
+        t.cuda.synchronize()
+        ref.append(_gpu.from_dev(D))
+    streams = [t.cuda.Stream(), t.cuda.Stream()]
+    jobs = []
+    for it in range(12):
+        for si in range(2):
+            k = (it + si) % len(cases)
+            jobs.append((k, si, _gpu.empty_out(cases[k][0], cases[k][1]),
+                         _gpu.workspace(cases[k][4])))
+    for st in streams:
+        st.wait_stream(main)
+    for k, si, D, ws in jobs:
+        with t.cuda.stream(streams[si]):
+            assert call(cases[k], D, ws, streams[si]) == 0
+    for st in streams:
+        main.wait_stream(st)
+    t.cuda.synchronize()
+    for k, _, D, _ in jobs:
+        assert (_gpu.from_dev(D) == ref[k]).all(), k
+
+
 MX_SMALL = [
     # (M, N, K) for the small-output kernel (M <= 128, K <= 8192, and one
     # tile row or at most 2048 tiles of 16 x 16 with tiles x K <= 2^23): K
