@@ -88,6 +88,9 @@ def parse():
     ap.add_argument("--small-m-sweep-nn", action="store_true",
                     help="the same for D = A @ B (BF16, B row-major K x N) at M of 1 to 128, "
                          "where the small-output kernel and the tiled one divide the shapes")
+    ap.add_argument("--small-m-sweep-mx", action="store_true",
+                    help="the same for the FP8 block-scaled D = A @ B.T at M of 1 to 128, "
+                         "torch._scaled_mm timed beside it")
     ap.add_argument("--seed", type=int, default=8192)
     ap.add_argument("--ladder", action="store_true",
                     help="instead of one workload, time each optimisation-step kernel "
@@ -372,13 +375,21 @@ def _event_timer(stream):
     return timed
 
 
-def run_mx_sweep(args):
-    """The FP8 block-scaled product over the M = 8192 sweep shapes: random
-    finite E4M3 codes and E8M0 scales from torch's seeded device generator
-    (timing only; tests check the product against the oracle), HIP events
-    around about 50 ms of back-to-back calls.  Beside it, torch._scaled_mm
-    with the same 1 x 32 block scales and, where it runs, with one scale per
-    tensor (the library products of this PyTorch build)."""
+SMALL_M_MX = [(m, n, k) for m in (1, 16, 64, 128)
+              for n, k in ((1024, 1024), (1024, 4096), (4096, 4096), (4096, 8192),
+                           (8192, 8192), (16384, 4096))]
+
+
+def run_mx_sweep(args, shapes=None):
+    """The FP8 block-scaled product over the M = 8192 sweep shapes (or the
+    given ones): random finite E4M3 codes and E8M0 scales from torch's seeded
+    device generator (timing only; tests check the product against the
+    oracle), HIP events around about 50 ms of back-to-back calls.  Beside it,
+    torch._scaled_mm with the same 1 x 32 block scales and, where it runs,
+    with one scale per tensor (the library products of this PyTorch build).
+    Each line names the kernel the library's plan runs (small-output or
+    tiled) and its K parts."""
+    import ctypes
     import torch
     from dense_gemm_08_amd import binding
     lib = binding.load_library()
@@ -387,7 +398,9 @@ def run_mx_sweep(args):
     gen.manual_seed(args.seed)
     stream = torch.cuda.current_stream()
     timed = _event_timer(stream)
-    for M, N, K in sweep_shapes(k_extra=32):
+    plan = (ctypes.c_int64 * 10)()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for M, N, K in (shapes or sweep_shapes(k_extra=32)):
         A = torch.randint(0, 255, (M, K), device=dev, generator=gen, dtype=torch.uint8)
         B = torch.randint(0, 255, (N, K), device=dev, generator=gen, dtype=torch.uint8)
         A[(A & 0x7F) == 0x7F] = 0
@@ -405,9 +418,30 @@ def run_mx_sweep(args):
             if st != 0:
                 raise binding.DenseGemmError(st, "gemm_nt_e4m3_mx")
 
-        rec = {"mode": "mx_sweep", "M": M, "N": N, "K": K, "steps": steps}
+        if lib.gemm_nt_e4m3_mx_plan(M, N, K, cus, plan) != 0:
+            raise RuntimeError("no plan for %d x %d x %d" % (M, N, K))
+        nbytes = M * K + N * K + (M + N) * (K // 32) + 2.0 * M * N  # A, B, scales, D once
+        rec = {"mode": "mx_sweep", "M": M, "N": N, "K": K, "steps": steps,
+               "kernel": "small" if plan[0] == 16 else "tiled", "splits": int(plan[8])}
         ms = timed(ours, steps, max(3, steps // 4))
-        rec.update(kernel_ms=round(ms, 5), tflops=round(flops / ms / 1e9, 1))
+        rec.update(kernel_ms=round(ms, 5), tflops=round(flops / ms / 1e9, 1),
+                   alg_tb_s=round(nbytes / ms / 1e9, 3))
+        if args.workspace:
+            # the same product through gemm_nt_e4m3_mx_ex, its workspace
+            # allocated once (no stream-ordered allocation per call)
+            need = binding.mx_workspace_size(M, N, K)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+            def ours_ws():
+                st = lib.gemm_nt_e4m3_mx_ex(M, N, K, A.data_ptr(), K, SA.data_ptr(), K // 32,
+                                            B.data_ptr(), K, SB.data_ptr(), K // 32, D.data_ptr(),
+                                            N, ws.data_ptr(), need, stream.cuda_stream)
+                if st != 0:
+                    raise binding.DenseGemmError(st, "gemm_nt_e4m3_mx_ex")
+            ms_ws = timed(ours_ws, steps, max(3, steps // 4))
+            rec.update(workspace_bytes=need, ex_ms=round(ms_ws, 5),
+                       ex_alg_tb_s=round(nbytes / ms_ws / 1e9, 3))
+            del ws
         a8, b8 = A.view(torch.float8_e4m3fn), B.view(torch.float8_e4m3fn)
         refs = {
             "scaled_mm_mx": lambda: torch._scaled_mm(
@@ -420,6 +454,7 @@ def run_mx_sweep(args):
         for name, fn in refs.items():
             try:
                 ms_ref = timed(fn, steps, max(3, steps // 4))
+                rec[name + "_ms"] = round(ms_ref, 5)
                 rec[name + "_tflops"] = round(flops / ms_ref / 1e9, 1)
             except (RuntimeError, TypeError, AttributeError) as ex:
                 rec[name + "_tflops"] = None
@@ -508,6 +543,9 @@ def main():
         return
     if args.mx_sweep:
         run_mx_sweep(args)
+        return
+    if args.small_m_sweep_mx:
+        run_mx_sweep(args, SMALL_M_MX)
         return
     if args.wave_fill:
         run_wave_fill(args)

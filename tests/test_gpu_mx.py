@@ -469,6 +469,22 @@ def test_mx_small_output_full_parity(kind, M, N, K):
     assert np.array_equal(D, D2)
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("M,N,K,small", [
+    # the ends of the benchmark's small-M FP8 sweep: one row at the widest N,
+    # the longest K at M <= 16, the small kernel's tiles x K limit exactly
+    # (1024 tiles x 8192), and the tiled kernel split at M = 128
+    (1, 16384, 4096, True), (16, 8192, 8192, True), (64, 4096, 8192, True),
+    (128, 16384, 4096, False)], ids=lambda v: str(v))
+def test_mx_small_m_sweep_shapes_every_output(M, N, K, small):
+    assert _mx_small(M, N, K) == small
+    print("small-M sweep shape %dx%dx%d" % (M, N, K), flush=True)
+    A, SA, B, SB = inputs.mx_operands(M, N, K, seed=M + N + K, kind="quantised")
+    D, st = run_mx(A, SA, B, SB)
+    assert st == status().OK
+    check_full(A, SA, B, SB, D)
+
+
 def test_mx_small_output_small_integers_bit_exact_and_leading_dimensions():
     M, N, K = 120, 200, 2048
     assert _mx_small(M, N, K)
