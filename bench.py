@@ -422,7 +422,8 @@ def run_mx_sweep(args, shapes=None):
             raise RuntimeError("no plan for %d x %d x %d" % (M, N, K))
         nbytes = M * K + N * K + (M + N) * (K // 32) + 2.0 * M * N  # A, B, scales, D once
         rec = {"mode": "mx_sweep", "M": M, "N": N, "K": K, "steps": steps,
-               "kernel": "small" if plan[0] == 16 else "tiled", "splits": int(plan[8])}
+               "kernel": "small" if plan[0] < 256 else "tiled", "tile": [int(plan[0]), int(plan[1])],
+               "splits": int(plan[8])}
         ms = timed(ours, steps, max(3, steps // 4))
         rec.update(kernel_ms=round(ms, 5), tflops=round(flops / ms / 1e9, 1),
                    alg_tb_s=round(nbytes / ms / 1e9, 3))
@@ -752,7 +753,8 @@ def main():
 
 def source_sha(name: str = "gemm_kernel.h") -> str:
     """sha256 prefix of a kernel source (gemm_kernel.h with
-    gemm_small_kernel.h, or gemm_mx_kernel.h), the headers it shares (the
+    gemm_small_kernel.h, or gemm_mx_kernel.h with gemm_mx_small_kernel.h),
+    the headers it shares (the
     split-K reduction's included) and the launch planning (plan.cpp,
     plan.h), with comments and blank space removed: the traffic figures
     recorded for it stay valid across comment edits and other host-side
@@ -768,6 +770,8 @@ def source_sha(name: str = "gemm_kernel.h") -> str:
              "plan.h"]
     if name == "gemm_kernel.h":
         files.append("gemm_small_kernel.h")
+    elif name == "gemm_mx_kernel.h":
+        files.append("gemm_mx_small_kernel.h")
     for f in files:
         with open(os.path.join(ROOT, "dense_gemm_08_amd", "csrc", f)) as fh:
             text = fh.read()

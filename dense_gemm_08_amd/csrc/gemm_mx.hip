@@ -7,6 +7,7 @@
 
 #include "dense_gemm.h"
 #include "gemm_mx_kernel.h"
+#include "gemm_mx_small_kernel.h"
 #include "plan.h"
 #include "split_reduce.h"
 
@@ -66,10 +67,17 @@ static dense_gemm_status enqueue(int64_t M, int64_t N, int64_t K, const void* A,
     q.ldsa = (int)ldsa;
     q.ldsb = (int)ldsb;
     q.ldd = (int)ldd;
+    q.tiles_m = (int)plan[3];
     q.tiles_n = (int)plan[4];
+    q.num_xcds = xcds;
     q.d_vec = (((uintptr_t)D & 7) == 0 && (ldd & 3) == 0) ? 1 : 0;
-    hipLaunchKernelGGL(gemm_mx_small, dim3((unsigned)(plan[3] * plan[4])), dim3(SMALL_THREADS), 0,
-                       stream, q);
+    const dim3 grid((unsigned)(plan[3] * plan[4])), block(SMALL_THREADS);
+    if (plan[0] == 2 * SMALL_TILE && plan[1] == 2 * SMALL_TILE)
+      hipLaunchKernelGGL((gemm_mx_small<2, 2>), grid, block, 0, stream, q);
+    else if (plan[0] == 2 * SMALL_TILE)
+      hipLaunchKernelGGL((gemm_mx_small<2, 1>), grid, block, 0, stream, q);
+    else
+      hipLaunchKernelGGL((gemm_mx_small<1, 1>), grid, block, 0, stream, q);
     return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
   }
   MxParams p;

@@ -505,211 +505,5 @@ __global__ __launch_bounds__(THREADS) void gemm_mx_kernel(MxParams p) {
   }
 }
 
-// ---- the small-output kernel ---------------------------------------------
-// D = A @ B.T for M <= 128 and K <= MX_SMALL_K_MAX with one tile row (M <=
-// 16) or at most MX_SMALL_MAX_TILES 16 x 16 tiles of D (tiles x K at most
-// MX_SMALL_TILES_K): the FP16
-// small-output kernel's decomposition (gemm_small_kernel.h) with FP8 data.
-// One workgroup of eight waves per 16 x 16 tile; wave w takes the 128-deep
-// K chunks w, w + 8, ... (128 bytes per row, the FP16 kernel's 64-deep LDS
-// row and swizzle), streamed through a two-slot LDS ring of its own; one
-// scaled MFMA per chunk (lane group q holds 32 bytes of its row, logical
-// 16-byte chunks q and q + 4, and the scale of the chunk's block q, as in
-// the tiled kernel above).  The tile's scale bytes (16 rows of A and of B,
-// K / 32 each) are staged in LDS once, before the K loop, read as they are
-// stored (any leading dimension; scale 1 outside the rows and blocks).  The
-// waves' FP32 blocks are added in wave order, rounded to BF16 and stored.
-struct MxSmallParams {
-  const uint8_t* A;
-  const uint8_t* B;
-  const uint8_t* SA;
-  const uint8_t* SB;
-  uint16_t* D;
-  int M, N, K;  // K a multiple of 32, at most MX_SMALL_K_MAX
-  int lda, ldb, ldsa, ldsb, ldd;
-  int tiles_n;
-  int d_vec;  // D rows are 8-byte aligned (4-element stores allowed)
-};
-
-__global__ __launch_bounds__(SMALL_THREADS) void gemm_mx_small(MxSmallParams p) {
-  constexpr int RING = 2;              // chunks in flight per wave
-  constexpr int SLOT = 2 * 2048;       // one chunk: the A and B tiles, 16 rows x 128 B each
-  constexpr int NBMAX = MX_SMALL_K_MAX / GROUP;
-  __shared__ __attribute__((aligned(1024))) char ring[SMALL_WAVES * RING * SLOT];
-  __shared__ f32x4 part[SMALL_WAVES][64];
-  __shared__ uint8_t scales[2][SMALL_TILE][NBMAX];
-
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int lane = (int)threadIdx.x & 63;
-  const int l16 = lane & 15, lq = lane >> 4;
-  const int tm = (int)blockIdx.x / p.tiles_n, tn = (int)blockIdx.x % p.tiles_n;
-  const int m0 = tm * SMALL_TILE, n0 = tn * SMALL_TILE;
-  const int vm = min(SMALL_TILE, p.M - m0), vn = min(SMALL_TILE, p.N - n0);
-  const int nb = p.K / GROUP;
-
-  // Loads (as in the FP16 small-output kernel, in bytes): instruction i of
-  // an operand fills rows 8 i .. 8 i + 7 of its 16 x 128 B chunk tile, lane
-  // L row 8 i + L / 8 and the logical 16-byte chunk the swizzle stores at
-  // physical chunk L % 8; rows past M or N and bytes past K read zeros.
-  // (the descriptors are workgroup-uniform: read through readfirstlane so
-  // that the compiler keeps them in the scalar registers the loads take)
-  i32x4 ra = make_rsrc((uint64_t)(uintptr_t)(p.A + (int64_t)m0 * p.lda),
-                       (uint32_t)((vm - 1) * p.lda + p.K));
-  i32x4 rb = make_rsrc((uint64_t)(uintptr_t)(p.B + (int64_t)n0 * p.ldb),
-                       (uint32_t)((vn - 1) * p.ldb + p.K));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = __builtin_amdgcn_readfirstlane(ra[i]);
-    rb[i] = __builtin_amdgcn_readfirstlane(rb[i]);
-  }
-  uint32_t aoff[2], boff[2];
-  int kc[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 8 * i + (lane >> 3);
-    kc[i] = (lane & 7) ^ swz_k(r);
-    aoff[i] = r < vm ? (uint32_t)(r * p.lda + kc[i] * 16) : OOB;
-    boff[i] = r < vn ? (uint32_t)(r * p.ldb + kc[i] * 16) : OOB;
-  }
-  const uint32_t wring = lds_addr(ring) + wave * (RING * SLOT);
-  auto issue = [&](int t) {
-    const int c = wave + SMALL_WAVES * t;
-    const uint32_t base = wring + (t % RING) * SLOT;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool in = c * BKE + kc[i] * 16 < p.K;
-      dma16_at(ra, in ? aoff[i] + c * BKE : OOB, base, i * 1024);
-      dma16_at(rb, in ? boff[i] + c * BKE : OOB, base, 2048 + i * 1024);
-    }
-  };
-  const int chunks = (p.K + BKE - 1) / BKE;
-  const int per_wave = (chunks + SMALL_WAVES - 1) / SMALL_WAVES;
-
-  // The tile's scales by LDS-DMA where every scale row starts 4-byte aligned,
-  // K / 32 is a multiple of 4 and a tile's rows span less than 2^31 bytes:
-  // waves 0-3 copy A's 16 rows, waves 4-7 B's, one 256-byte row of
-  // `scales` per instruction (lane L: blocks 4 L .. 4 L + 3; rows past M or
-  // N and blocks past K / 32 read zeros, whose data is zero too).  Issued
-  // before the ring's first chunks, so that each wave then waits for these
-  // loads only.
-  const int64_t sld = p.ldsa > p.ldsb ? p.ldsa : p.ldsb;
-  const bool sdma = nb > 0 && (nb & 3) == 0 &&
-                    ((((uintptr_t)p.SA | (uintptr_t)p.SB) & 3) == 0) &&
-                    (((p.ldsa | p.ldsb) & 3) == 0) &&
-                    (SMALL_TILE - 1) * sld + nb < ((int64_t)1 << 31);
-  if (sdma) {
-    const int op = wave >> 2;
-    const int vr = op ? vn : vm;
-    const int ld = op ? p.ldsb : p.ldsa;
-    i32x4 rs = make_rsrc((uint64_t)(uintptr_t)(op ? p.SB + (int64_t)n0 * p.ldsb
-                                                  : p.SA + (int64_t)m0 * p.ldsa),
-                         (uint32_t)((vr - 1) * ld + nb));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rs[i] = __builtin_amdgcn_readfirstlane(rs[i]);
-    const int r0 = 4 * (wave & 3);
-    const uint32_t sbase = lds_addr(&scales[op][r0][0]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = r0 + i;
-      dma4_at(rs, row < vr && 4 * lane < nb ? (uint32_t)(row * ld + 4 * lane) : OOB, sbase,
-              i * NBMAX);
-    }
-  }
-  if (per_wave > 0)
-    for (int t = 0; t < RING; ++t) issue(t);
-
-  // Otherwise the tile's scales are loaded as bytes, while the first chunks
-  // load.  Thread t takes operand t / 256 (A, then B), row (t / 16) % 16 of
-  // the tile and blocks t % 16 + 16 j: its PER bytes are loaded first (the
-  // wait for them also waits for the first chunks), every load unconditional (from an
-  // address inside the matrix: row 0 of the tile for rows past M or N,
-  // block 0 for blocks past K / 32), so that all of them are in flight at
-  // once, then stored (scale 1 for rows past M or N; blocks past K / 32 are
-  // never read).  The shares follow from shifts of t: index arithmetic with
-  // K / 32 as divisor measured ~1.5 us per call.  (With K = 0 there are no
-  // scales, and the scale pointers may be null.)
-  static_assert(SMALL_THREADS == 2 * SMALL_TILE * 16 && NBMAX % 16 == 0, "one thread per 16 blocks");
-  if (sdma) {
-    // this wave's scale rows have landed; the ring's first two chunks (8
-    // loads) may still be in flight
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(4 * RING) : "memory");
-  } else if (nb > 0) {
-    constexpr int PER = NBMAX / 16;
-    const int t = (int)threadIdx.x;
-    const int op = t >> 8, row = (t >> 4) & 15, b0 = t & 15;
-    const bool rin = row < (op ? vn : vm);
-    const uint8_t* src = op ? p.SB + (int64_t)(n0 + (rin ? row : 0)) * p.ldsb
-                            : p.SA + (int64_t)(m0 + (rin ? row : 0)) * p.ldsa;
-    int v[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int b = b0 + 16 * j;
-      v[j] = src[b < nb ? b : 0];
-    }
-    // Every loaded value is stored (blocks past K / 32 with scale 1; they
-    // are never read): a load whose value went unused would stay pending,
-    // as far as the compiler knows, into the K loop, where it would then
-    // wait for all loads in flight (the ring's included) at every chunk.
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int b = b0 + 16 * j;
-      scales[op][row][b] = (uint8_t)(rin && b < nb ? v[j] : 127);  // 127: scale 1
-    }
-  }
-  __syncthreads();
-
-  // Fragment reads: lane (l16, lq) reads row l16, logical chunks lq, lq + 4.
-  const int sw = swz_k(l16);
-  const int fr0 = l16 * 128 + ((lq ^ sw) << 4);
-  const int fr1 = l16 * 128 + (((lq + 4) ^ sw) << 4);
-  f32x4 acc = {};
-  if (per_wave > 0) {
-    for (int t = 0; t < per_wave; ++t) {
-      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(4 * (RING - 1)) : "memory");
-      const char* slot = ring + (wave * RING + t % RING) * SLOT;
-      const u32x4 a0 = *(const u32x4*)(slot + fr0);
-      const u32x4 a1 = *(const u32x4*)(slot + fr1);
-      const u32x4 b0 = *(const u32x4*)(slot + 2048 + fr0);
-      const u32x4 b1 = *(const u32x4*)(slot + 2048 + fr1);
-      const int blk = (wave + SMALL_WAVES * t) * (BKE / GROUP) + lq;
-      const int sa = blk < nb ? scales[0][l16][blk] : 127;
-      const int sb = blk < nb ? scales[1][l16][blk] : 127;
-      const i32x8 af = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                        (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-      const i32x8 bf = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
-                        (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-      // srcA the B fragment (its scale sb), srcB the A fragment (sa): each
-      // lane ends up holding one row of D, four columns; E4M3 operands
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, acc, 0, 0, 0, sb, 0, sa);
-      // the slot's reads are done (the MFMA took their data): refill it
-      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-      issue(t + RING);
-    }
-    // no LDS-DMA write may land after the wave ends
-    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-  }
-
-  // lane (l16, lq): D row m0 + l16, columns n0 + 4 lq .. +3; waves in order
-  part[wave][lane] = acc;
-  __syncthreads();
-  if (wave != 0) return;
-  f32x4 s = part[0][lane];
-#pragma unroll
-  for (int w = 1; w < SMALL_WAVES; ++w) s += part[w][lane];
-  const int row = m0 + l16, col = n0 + 4 * lq;
-  if (row >= p.M || col >= p.N) return;
-  u32x2 v;
-  v[0] = pack2<__bf16>(s[0], s[1]);
-  v[1] = pack2<__bf16>(s[2], s[3]);
-  uint16_t* dst = p.D + (int64_t)row * p.ldd + col;
-  if (p.d_vec && col + 4 <= p.N) {
-    *(u32x2*)dst = v;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (col + e < p.N) dst[e] = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
-  }
-}
-
 }  // namespace mx
 }  // namespace dg

@@ -336,32 +336,49 @@ dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const v
 }
 
 // Products the FP8 small-output kernel computes (gemm_mx_small): M <= 128,
-// K <= MX_SMALL_K_MAX = 8192, and one tile row (M <= 16) or at most
-// MX_SMALL_MAX_TILES = 2048 tiles of 16 x 16 with tiles x K at most
-// MX_SMALL_TILES_K = 2^23.  The tiled FP8 kernel has no 128-row tile, so
-// against it the small kernel pays at more tiles than the FP16 rule allows:
-// measured per call on one box (small against tiled with its split-K),
-// 64 x 4096 x 4096 13.5 against 25.8 us, 128 x 4096 x 4096 24.4 against
-// 30.1, 128 x 2048 x 8192 19.2 against 30.0, 32 x 16384 x 2048 18.5 against
-// 26.2, 128 x 1536 x 8192 15.9 against 28.3, 32 x 8192 x 8192 (tiles x K =
-// 2^23) 27.4 against 31.2; past the limits 128 x 4096 x 8192 36.0 against
-// 30.5, 48 x 8192 x 8192 38.9 against 32.3, 64 x 16384 x 2048 34.8 against
-// 31.4, 128 x 16384 x 1024 49.9 against 24.3.  Re-measured after the
-// small kernel's scale staging got faster: past the limits it ties the
-// tiled kernel within 3% (64 x 16384 x 2048, 96 x 8192 x 4096, 128 x 8192 x
-// 1024) or loses (128 x 8192 x 4096 by 23%, 64 x 8192 x 8192 by 40%, 128 x
-// 16384 x 1024 by 86%), so the limits stay.  Within the former limit of
-// 512 tiles, against the tiled kernel before its split-K (its
-// scale packing and workspace included), one box: 128 x 128 x 4096 6.2
-// against 45.3 us, 1 x 4096 x 4096 6.2 against 44.5, 16 x 16384 x 4096 21.3
-// against 48.3, 128 x 1024 x 8192 12.3 against 75.6, 128 x 128 x 64 4.5
-// against 23.1 (since the scale staging lost its divisions: 4.55, 5.2,
-// 21.3, 10.3 and 4.05 us).
+// K <= MX_SMALL_K_MAX = 8192 (its scales are staged in LDS), and one 16-row
+// tile row, or at most MX_SMALL_T32 = 1024 tiles of 32 x 32 in D, or at most
+// MX_SMALL_T32_MAX = 1536 of them with tiles x K at most MX_SMALL_T32_K =
+// 2^23.  The tiled FP8 kernel has no 128-row tile and, at these M, splits K
+// into FP32 partial tiles; the small kernel's cost is each tile row's pass
+// over B, which its 32-row tiles halve and its XCD-grouped tile order
+// serves from L2.  Measured per call on one box over the 23 products of M
+// = 24 ... 128, N = 2048 ... 16384 and K = 2048 ... 8192 that the former
+// rule (at most 2048 tiles of 16 x 16 with tiles x K <= 2^23) left to the
+// tiled kernel, the small kernel (its tile as mx_small_tile picks) against
+// the tiled one through the plain entry point (which allocates the split's
+// workspace per call; with a preallocated workspace, about 3 us less): up
+// to 1024 tiles of 32 x 32 1.17-2.31x as fast (e.g. 64 x 8192 x 8192 17.3
+// against 32.2 us, 128 x 8192 x 8192 30.9 against 36.0);
+// at 1536 tiles (96 x 16384) 1.26x and 1.10x at K = 2048 and 4096, 0.99x at
+// 8192 (tiles x K 3 2^20, 3 2^21 and 3 2^22); at 2048 tiles (128 x 16384)
+// 0.98x and 0.88x at K = 2048 and 4096.  Products inside the former rule
+// run the small kernel as before, its new tiles no slower (one tile row:
+// 16 x 16 as before; more rows: measured 1.0-1.9x as fast).
 bool mx_small_output(int64_t M, int64_t N, int64_t K) {
   if (M > SMALL_MAX || K > mx::MX_SMALL_K_MAX) return false;
   if (M <= SMALL_TILE) return true;
-  const int64_t tiles = ((M + SMALL_TILE - 1) / SMALL_TILE) * ((N + SMALL_TILE - 1) / SMALL_TILE);
-  return tiles <= mx::MX_SMALL_MAX_TILES && tiles * K <= mx::MX_SMALL_TILES_K;
+  const int64_t t32 = ((M + 31) / 32) * ((N + 31) / 32);
+  return t32 <= mx::MX_SMALL_T32 || (t32 <= mx::MX_SMALL_T32_MAX && t32 * K <= mx::MX_SMALL_T32_K);
+}
+
+// The largest tile whose grid still covers the CUs: more columns per tile
+// read each chunk of A once for more blocks, more rows each chunk of B, but
+// fewer tiles leave CUs idle (measured, one box: 64 x 1024 x 4096 4.3 us in
+// 16 x 16 tiles, 256 of them, against 5.1 in 32 x 16 and 6.0 in 32 x 32;
+// 128 x 1024 x 4096 5.2 us in 32 x 16, 256 tiles, against 6.2 in 16 x 16
+// and 32 x 32).  One 16-row tile row keeps 16 x 16 tiles: there a taller
+// tile only computes padding (16 x 8192 x 8192 13.5 us against 16.0 in
+// 32 x 16).
+void mx_small_tile(int64_t M, int64_t N, int64_t num_cus, int64_t* rows, int64_t* cols) {
+  *rows = *cols = SMALL_TILE;
+  if (M <= SMALL_TILE) return;
+  const int64_t tm = (M + 31) / 32;
+  if (tm * ((N + 31) / 32) >= num_cus) {
+    *rows = *cols = 32;
+  } else if (tm * ((N + 15) / 16) >= num_cus) {
+    *rows = 32;
+  }
 }
 
 dense_gemm_status mx_plan_call(int64_t M, int64_t N, int64_t K, int64_t num_cus, MxPlan* mp) {
@@ -372,12 +389,11 @@ dense_gemm_status mx_plan_call(int64_t M, int64_t N, int64_t K, int64_t num_cus,
   const int64_t nks = (K + mx::BKE - 1) / mx::BKE;
   mp->panel_bytes[0] = mp->panel_bytes[1] = mp->split_bytes = 0;
   if (mx_small_output(M, N, K)) {
-    // 16 x 16 tiles, one workgroup each, the scales staged in LDS: no
-    // workspace
-    out[0] = out[1] = SMALL_TILE;
+    // one workgroup per tile, the scales staged in LDS: no workspace
+    mx_small_tile(M, N, num_cus, &out[0], &out[1]);
     out[2] = mx::BKE;
-    out[3] = (M + SMALL_TILE - 1) / SMALL_TILE;
-    out[4] = (N + SMALL_TILE - 1) / SMALL_TILE;
+    out[3] = (M + out[0] - 1) / out[0];
+    out[4] = (N + out[1] - 1) / out[1];
     out[5] = out[3] * out[4];
     out[6] = 1;
     out[7] = SMALL_THREADS;

@@ -63,23 +63,28 @@ constexpr int64_t MX_STEP_COST = 100;
 constexpr int64_t MX_SPLIT_COST = 1000;
 constexpr int64_t MX_PART_COST = 5;
 
-// Everything an FP8 call launches.  plan: as gemm_nt_e4m3_mx_plan (16 x 16
-// tiles for the small-output kernel, else 256 x 256 tiles with `splits`
-// parts of `steps` stages on the split tiles).  The workspace holds A's
-// and B's packed scale panels, then the FP32 partial tiles.
+// Everything an FP8 call launches.  plan: as gemm_nt_e4m3_mx_plan (tiles of
+// 16 x 16, 32 x 16 or 32 x 32 for the small-output kernel, else 256 x 256
+// tiles with `splits` parts of `steps` stages on the split tiles).  The
+// workspace holds A's and B's packed scale panels, then the FP32 partial
+// tiles.
 struct MxPlan {
   int64_t plan[10];
   int64_t full_tasks, split_tiles;
   size_t panel_bytes[2];  // A's, B's (multiples of 1 KiB)
   size_t split_bytes;
   size_t total() const { return panel_bytes[0] + panel_bytes[1] + split_bytes; }
-  bool small() const { return plan[0] == SMALL_TILE; }
+  bool small() const { return plan[0] != mx::BM; }
 };
 
 // The FP8 small-output kernel's products (M <= 128, K <= MX_SMALL_K_MAX,
-// one tile row or at most MX_SMALL_MAX_TILES 16 x 16 tiles with tiles x K
-// at most MX_SMALL_TILES_K).
+// and one 16-row tile row, or at most MX_SMALL_T32 tiles of 32 x 32, or at
+// most MX_SMALL_T32_MAX of them with tiles x K at most MX_SMALL_T32_K).
 bool mx_small_output(int64_t M, int64_t N, int64_t K);
+// The small-output kernel's tile rows and columns for such a product on a
+// device with num_cus CUs: 16 x 16 where M <= 16, else 32 x 32 where those
+// tiles number at least num_cus, else 32 x 16 where those do, else 16 x 16.
+void mx_small_tile(int64_t M, int64_t N, int64_t num_cus, int64_t* rows, int64_t* cols);
 // The plan of an FP8 call with M, N > 0 and K a multiple of 32 on a device
 // with num_cus CUs.
 dense_gemm_status mx_plan_call(int64_t M, int64_t N, int64_t K, int64_t num_cus, MxPlan* mp);

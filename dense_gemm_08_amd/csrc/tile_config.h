@@ -1,6 +1,7 @@
 // tile_config.h -- the tile configurations of the FP16/BF16 GEMM and of the
 // FP8 block-scaled GEMM, shared by the kernels (gemm_kernel.h,
-// gemm_small_kernel.h, gemm_mx_kernel.h) and the host-side planning
+// gemm_small_kernel.h, gemm_mx_kernel.h, gemm_mx_small_kernel.h) and the
+// host-side planning
 // (plan.cpp, which is plain C++ and builds without HIP).
 #pragma once
 
@@ -31,19 +32,21 @@ constexpr int SMALL_NN_K_MAX = 4096;
 constexpr long long SMALL_NN_ELEMS = 21LL << 20;
 
 // The FP8 block-scaled GEMM (gemm_mx_kernel.h): 256 x 256 tiles, 128-deep
-// K stages (128 bytes per row), one E8M0 scale per GROUP K values; its
-// small-output kernel takes the small-output decomposition above for K up
-// to MX_SMALL_K_MAX and at most MX_SMALL_MAX_TILES 16 x 16 tiles with tiles
-// x K at most MX_SMALL_TILES_K, or one tile row (plan.cpp:
-// mx_small_output).
+// K stages (128 bytes per row), one E8M0 scale per GROUP K values.  Its
+// small-output kernel (gemm_mx_small_kernel.h: tiles of 16 x 16, 32 x 16 or
+// 32 x 32) takes products with M up to SMALL_MAX and K up to
+// MX_SMALL_K_MAX with one 16-row tile row, or at most MX_SMALL_T32 tiles of
+// 32 x 32 in D, or at most MX_SMALL_T32_MAX such tiles with tiles x K at
+// most MX_SMALL_T32_K (plan.cpp: mx_small_output).
 namespace mx {
 constexpr int BM = 256, BN = 256;
 constexpr int BKE = 128;                   // K elements (= bytes) per stage
 constexpr int GROUP = 32;                  // K elements per scale
 constexpr int SC_BYTES = 1024;             // packed scale panel per operand per stage
 constexpr int MX_SMALL_K_MAX = 8192;
-constexpr int MX_SMALL_MAX_TILES = 2048;
-constexpr long long MX_SMALL_TILES_K = 1LL << 23;
+constexpr int MX_SMALL_T32 = 1024;
+constexpr int MX_SMALL_T32_MAX = 1536;
+constexpr long long MX_SMALL_T32_K = 1LL << 23;
 }  // namespace mx
 
 }  // namespace dg

@@ -222,10 +222,11 @@ dense_gemm_status gemm_nt_f16_ladder(int level, int64_t M, int64_t N, int64_t K,
  * D needs 2-byte alignment.  M, N and K/128 may be ragged.  The products are
  * exact in FP32; their sum is accumulated in FP32 in a fixed order (results
  * are reproducible on a device; the order depends on the plan, hence on the
- * CU count).  Small outputs (M <= 128, K <= 8192, and M <= 16 or at most
- * 2048 tiles of 16 x 16 with tiles * K <= 2^23) run a small-output kernel
- * (16 x 16 tiles, K split among eight waves, the scales staged in LDS) that
- * needs no workspace.
+ * CU count).  Small outputs (M <= 128, K <= 8192, and M <= 16, or at most
+ * 1024 tiles of 32 x 32 in D, or at most 1536 with tiles * K <= 2^23) run a
+ * small-output kernel (tiles of 16 x 16, 32 x 16 or 32 x 32 as
+ * gemm_nt_e4m3_mx_plan gives, K split among eight waves, the scales staged
+ * in LDS; every tile shape gives the same bits) that needs no workspace.
  * Other products run a tiled kernel (256 x 256 tiles) that takes a
  * workspace (hipMallocAsync / hipFreeAsync on `stream`;
  * DENSE_GEMM_NO_MEMORY if unavailable) of 1 KiB per 256-row tile of A and
@@ -352,10 +353,13 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K,
 
 /* The launch plan of gemm_nt_e4m3_mx for M, N > 0 and K a multiple of 32
  * on a device with num_cus compute units, as 10 values in the format of
- * dense_gemm_plan: tile rows and columns (16 and 16 for the small-output
- * kernel, else 256 and 256), the K depth of a stage (128), tiles_m,
- * tiles_n, grid, group_m, threads per workgroup, the number of K parts and
- * the stages per part.  The split rule is dense_gemm_plan's for 256-wide
+ * dense_gemm_plan: tile rows and columns, the K depth of a stage (128),
+ * tiles_m, tiles_n, grid, group_m, threads per workgroup, the number of K
+ * parts and the stages per part.  The small-output kernel (a grid of
+ * tiles_m * tiles_n workgroups of 512 threads, group_m 1, no split) takes
+ * 16 x 16 tiles where M <= 16, else 32 x 32 where those number at least
+ * num_cus, else 32 x 16 where those do, else 16 x 16; the tiled kernel
+ * 256 x 256 tiles.  The split rule is dense_gemm_plan's for 256-wide
  * tiles with the FP8 kernel's costs: the estimate ceil(stages / p) * 100 +
  * 1000 + 5 * f * p * r against stages * 100 unsplit.
  * DENSE_GEMM_BAD_ARG on a bad argument, DENSE_GEMM_TOO_LARGE when the

@@ -97,11 +97,25 @@ static void check_mx_plan(int64_t M, int64_t N, int64_t K, int64_t cus, const Mx
   CHECK(mp.small() == mx_small_output(M, N, K));
   CHECK(p[2] == mx::BKE && p[9] >= 0);
   if (mp.small()) {
-    CHECK(M <= SMALL_MAX && K <= mx::MX_SMALL_K_MAX && p[1] == SMALL_TILE);
-    CHECK(p[3] == ceil_div(M, SMALL_TILE) && p[4] == ceil_div(N, SMALL_TILE));
-    CHECK(p[5] == p[3] * p[4] &&
-          (p[3] == 1 || (p[5] <= mx::MX_SMALL_MAX_TILES && p[5] * K <= mx::MX_SMALL_TILES_K)));
-    CHECK(p[7] == SMALL_THREADS && p[8] == 1 && mp.total() == 0);
+    CHECK(M <= SMALL_MAX && K <= mx::MX_SMALL_K_MAX);
+    const int64_t t32 = ceil_div(M, 32) * ceil_div(N, 32);
+    CHECK(M <= SMALL_TILE || t32 <= mx::MX_SMALL_T32 ||
+          (t32 <= mx::MX_SMALL_T32_MAX && t32 * K <= mx::MX_SMALL_T32_K));
+    // tiles of 16 x 16, 32 x 16 or 32 x 32: the largest whose grid covers
+    // the CUs, 16 x 16 for one 16-row tile row
+    const int64_t tr = p[0], tc = p[1];
+    CHECK((tr == 16 && tc == 16) || (tr == 32 && (tc == 16 || tc == 32)));
+    CHECK(p[3] == ceil_div(M, tr) && p[4] == ceil_div(N, tc) && p[5] == p[3] * p[4]);
+    if (M <= SMALL_TILE) {
+      CHECK(tr == 16);
+    } else if (tc == 32) {
+      CHECK(p[5] >= cus);
+    } else if (tr == 32) {
+      CHECK(p[5] >= cus && t32 < cus);
+    } else {
+      CHECK(ceil_div(M, 32) * ceil_div(N, 16) < cus);
+    }
+    CHECK(p[6] == 1 && p[7] == SMALL_THREADS && p[8] == 1 && p[9] == nks && mp.total() == 0);
     return;
   }
   CHECK(p[0] == mx::BM && p[1] == mx::BN && p[7] == THREADS);

@@ -297,13 +297,27 @@ def test_mx_plan():
         assert lib.gemm_nt_e4m3_mx_plan(M, N, K, cus, out) == S.OK
         return list(out)
 
-    # small outputs: 16 x 16 tiles, one 512-thread workgroup each, no split
+    # small outputs: one 512-thread workgroup per tile, no split; 16 x 16
+    # tiles where 32 x 16 ones would not cover the CUs
     assert plan(128, 128, 4096) == [16, 16, 128, 8, 8, 64, 1, 512, 1, 32]
+    assert plan(64, 1024, 4096)[:6] == [16, 16, 128, 4, 64, 256]
+    # one 16-row tile row: 16 x 16 tiles, any N
     assert plan(1, 40000, 256)[:6] == [16, 16, 128, 1, 2500, 2500]
-    # ... up to 2048 tiles with tiles x K <= 2^23 (exactly, at 2048 x 4096)
-    assert plan(128, 4096, 4096) == [16, 16, 128, 8, 256, 2048, 1, 512, 1, 32]
-    assert plan(32, 8192, 8192)[:6] == [16, 16, 128, 2, 512, 1024]
-    for M, N, K in [(128, 4096, 4128), (128, 4112, 1024), (48, 8192, 8192), (128, 128, 8224)]:
+    assert plan(16, 8192, 8192)[:6] == [16, 16, 128, 1, 512, 512]
+    # 32 x 16 where those cover the CUs and 32 x 32 would not
+    assert plan(128, 1024, 4096)[:6] == [32, 16, 128, 4, 64, 256]
+    # 32 x 32 where those cover the CUs
+    assert plan(128, 4096, 4096) == [32, 32, 128, 4, 128, 512, 1, 512, 1, 32]
+    assert plan(32, 8192, 8192)[:6] == [32, 32, 128, 1, 256, 256]
+    assert plan(128, 4096, 4096, cus=1024)[:6] == [32, 16, 128, 4, 256, 1024]
+    # up to 1024 tiles of 32 x 32 (exactly, at 64 x 16384), and up to 1536
+    # with tiles x K <= 2^23
+    assert plan(64, 16384, 8192)[:6] == [32, 32, 128, 2, 512, 1024]
+    assert plan(96, 16384, 4096)[:6] == [32, 32, 128, 3, 512, 1536]
+    # past the limits: K > 8192, M > 128, more than 1536 tiles, or more than
+    # 1024 with tiles x K > 2^23
+    for M, N, K in [(128, 128, 8224), (129, 100, 64), (128, 16384, 1024), (96, 16384, 8192),
+                    (64, 16416, 8192)]:
         assert plan(M, N, K)[:3] == [256, 256, 128], (M, N, K)
     # the page workloads: whole waves, no split
     assert plan(8192, 8192, 8192) == [256, 256, 128, 32, 32, 256, 8, 256, 1, 64]
@@ -339,6 +353,29 @@ def test_mx_plan():
         assert p[5] == min(full + (tm * tn - full) * sp, cus)
         if sp > 1:
             assert (sp - 1) * st < nk <= sp * st and st >= 4
+    # the small-output rule and its tile as documented, on many shapes with
+    # M <= 128 and CU counts
+    for _ in range(400):
+        M = int(rng.integers(1, 129))
+        N = int(rng.choice([int(rng.integers(1, 600)), int(rng.integers(600, 40000))]))
+        K = 32 * int(rng.integers(0, 300))
+        cus = int(rng.choice([256, 240, 128, 80, 32]))
+        p = plan(M, N, K, cus)
+        t32 = -(-M // 32) * -(-N // 32)
+        small = K <= 8192 and (M <= 16 or t32 <= 1024 or (t32 <= 1536 and t32 * K <= 1 << 23))
+        if not small:
+            assert p[:3] == [256, 256, 128], (M, N, K, cus)
+            continue
+        if M <= 16:
+            tile = (16, 16)
+        elif t32 >= cus:
+            tile = (32, 32)
+        elif -(-M // 32) * -(-N // 16) >= cus:
+            tile = (32, 16)
+        else:
+            tile = (16, 16)
+        tm, tn = -(-M // tile[0]), -(-N // tile[1])
+        assert p == [tile[0], tile[1], 128, tm, tn, tm * tn, 1, 512, 1, -(-K // 128)], (M, N, K, cus)
     for bad in ((0, 8, 32, 256), (8, 8, 40, 256), (8, 8, 32, 0), (8, -1, 32, 256)):
         assert lib.gemm_nt_e4m3_mx_plan(*bad, out) == S.BAD_ARG
     assert lib.gemm_nt_e4m3_mx_plan(8, 8, 32, 256, None) == S.BAD_ARG
@@ -615,14 +652,15 @@ def test_mx_workspace_size():
     assert ws(280, 300, 160) == (S.OK, (2 + 2) * 2 * 1024)
     assert ws(256, 256, 0) == (S.OK, 2 * 1024)
     assert ws(0, 256, 64) == (S.OK, 0)
-    # the small-output kernel (M <= 128, K <= 8192, and one tile row or at
-    # most 2048 tiles of 16 x 16 with tiles x K <= 2^23) stages its scales
-    # in LDS: no workspace
+    # the small-output kernel (M <= 128, K <= 8192, and one 16-row tile row,
+    # or at most 1024 tiles of 32 x 32, or 1536 with tiles x K <= 2^23)
+    # stages its scales in LDS: no workspace
     assert ws(128, 128, 4096) == (S.OK, 0)
     assert ws(16, 65536, 8192) == (S.OK, 0)
     assert ws(64, 1100, 2080) == (S.OK, 0)
-    assert ws(17, 8200, 512) == (S.OK, 0)  # 1026 tiles
-    assert ws(17, 16400, 512) == (S.OK, (1 + 65) * 4 * 1024)  # 2050 tiles: the tiled kernel
+    assert ws(17, 16400, 512) == (S.OK, 0)  # 513 tiles of 32 x 32
+    assert ws(17, 49152, 512) == (S.OK, 0)  # 1536 tiles, tiles x K = 3 * 2^18
+    assert ws(17, 49184, 512) == (S.OK, (1 + 193) * 4 * 1024)  # 1537: the tiled kernel
     # split-K adds 256 KiB (a 256 x 256 FP32 tile) per part of each split
     # tile: 128 x 128 x 8224 is one tile in 13 parts, 256 x 256 x 16384 one
     # in 32, 8192 x 4224 x 4096 has 32 tiles after two full waves, in 8 parts

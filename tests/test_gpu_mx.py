@@ -439,11 +439,16 @@ def test_mx_workspace_calls_on_two_streams():
 
 MX_SMALL = [
     # (M, N, K) for the small-output kernel (M <= 128, K <= 8192, and one
-    # tile row or at most 2048 tiles of 16 x 16 with tiles x K <= 2^23): K
-    # mod 128 = 0, 32, 64, 96, the longest K, one tile row past 512 tiles,
-    # several tile rows past 512 tiles, ragged tiles, one block
-    (128, 128, 4096), (100, 72, 8192), (1, 4096, 1024), (16, 8200, 480), (128, 1024, 96),
-    (5, 300, 224), (33, 17, 32), (64, 2200, 1056), (120, 1536, 4096),
+    # 16-row tile row, or at most 1024 tiles of 32 x 32, or 1536 with tiles x
+    # K <= 2^23): K mod 128 = 0, 32, 64, 96, the longest K, one tile row past
+    # 512 tiles, ragged tiles, one block; on 256 CUs, 16 x 16 tiles for the
+    # first seven, 32 x 16 for (128, 1024, 96), (64, 2200, 1056), (120,
+    # 1536, 4096) and (128, 1100, 1056), 32 x 32 for the last four (ragged
+    # in M, N and K; the 1536-tile band)
+    (128, 128, 4096), (100, 72, 8192), (1, 4096, 1024), (16, 8200, 480), (5, 300, 224),
+    (33, 17, 32), (64, 1000, 2080), (128, 1024, 96), (64, 2200, 1056), (120, 1536, 4096),
+    (128, 1100, 1056), (33, 8200, 1056), (100, 2600, 2144), (128, 4096, 8192),
+    (96, 16384, 4096),
 ]
 
 
@@ -472,9 +477,9 @@ def test_mx_small_output_full_parity(kind, M, N, K):
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("M,N,K,small", [
     # the ends of the benchmark's small-M FP8 sweep: one row at the widest N,
-    # the longest K at M <= 16, the small kernel's tiles x K limit exactly
-    # (1024 tiles x 8192), and the tiled kernel split at M = 128
-    (1, 16384, 4096, True), (16, 8192, 8192, True), (64, 4096, 8192, True),
+    # the longest K at M <= 16, the small kernel's 1024 tiles of 32 x 32 at
+    # the longest K, and the tiled kernel split at M = 128 past 1536 tiles
+    (1, 16384, 4096, True), (16, 8192, 8192, True), (64, 16384, 8192, True),
     (128, 16384, 4096, False)], ids=lambda v: str(v))
 def test_mx_small_m_sweep_shapes_every_output(M, N, K, small):
     assert _mx_small(M, N, K) == small
@@ -485,8 +490,27 @@ def test_mx_small_m_sweep_shapes_every_output(M, N, K, small):
     check_full(A, SA, B, SB, D)
 
 
-def test_mx_small_output_small_integers_bit_exact_and_leading_dimensions():
-    M, N, K = 120, 200, 2048
+def test_mx_small_output_tile_shapes_give_the_same_bits():
+    # every output's sum is the same sequence of MFMAs in 16 x 16, 32 x 16
+    # and 32 x 32 tiles: the products of A with the first rows of one B agree
+    # bit for bit on their common columns, whichever tile each runs in
+    for M, K, widths in [(64, 1056, (1000, 4200)), (128, 2080, (300, 1100, 4200))]:
+        A, SA, B, SB = inputs.mx_operands(M, max(widths), K, seed=M + K)
+        tiles = {tuple(_mx_plan(M, n, K)[:2]) for n in widths}
+        assert len(tiles) == len(widths), tiles  # distinct shapes (on 256 CUs: all three)
+        outs = []
+        for n in widths:
+            D, st = run_mx(A, SA, B[:n], SB[:n])
+            assert st == status().OK
+            outs.append(D)
+        for D in outs[1:]:
+            assert np.array_equal(D[:, :widths[0]], outs[0]), (M, K)
+        check_full(A, SA, B[:widths[0]], SB[:widths[0]], outs[0])
+
+
+@pytest.mark.parametrize("M,N,K", [(120, 200, 2048), (100, 8200, 2080)], ids=lambda v: str(v))
+def test_mx_small_output_small_integers_bit_exact_and_leading_dimensions(M, N, K):
+    # 16 x 16 tiles, and 32 x 32 (ragged in M, N and K) on 256 CUs
     assert _mx_small(M, N, K)
     A, SA, B, SB = inputs.mx_small_integers(M, N, K, seed=K + 1)
     d, _ = oracle.gemm_mx(A, SA, B, SB)
@@ -503,8 +527,9 @@ def test_mx_small_output_small_integers_bit_exact_and_leading_dimensions():
     assert (D[:, N:] == _gpu.CANARY).all()
 
 
-def test_mx_small_output_nan_propagates_like_the_oracle():
-    M, N, K = 64, 80, 256
+@pytest.mark.parametrize("M,N,K", [(64, 80, 256), (64, 4200, 256)], ids=lambda v: str(v))
+def test_mx_small_output_nan_propagates_like_the_oracle(M, N, K):
+    # 16 x 16 tiles, and 32 x 32 on 256 CUs
     assert _mx_small(M, N, K)
     A, SA, B, SB = inputs.mx_operands(M, N, K, seed=16)
     SA[3, 1] = 255   # E8M0 NaN: row 3 of D is NaN
@@ -520,9 +545,11 @@ def test_mx_small_output_nan_propagates_like_the_oracle():
     assert res.ok, res
 
 
+@pytest.mark.parametrize("N", [272, 8200])
 @pytest.mark.parametrize("case", ["compensated", "top", "bottom_subnormal", "overflow_rows"])
-def test_mx_small_output_scale_range_ends(case):
-    M, N, K = 64, 272, 512
+def test_mx_small_output_scale_range_ends(case, N):
+    # 16 x 16 tiles, and 32 x 32 on 256 CUs
+    M, K = 64, 512
     assert _mx_small(M, N, K)
     A, SA, B, SB = _range_operands(case, M, N, K, seed=len(case) + 1)
     D, st = run_mx(A, SA, B, SB)
