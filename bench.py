@@ -261,7 +261,8 @@ def run_sweep(args, shapes=None, layout="nt"):
         ms_ref = timed(ref, steps, max(3, steps // 4))
         nbytes = 2.0 * (M * K + N * K + M * N)  # A, B and D once
         line = {"mode": "sweep", "layout": layout, "dtype": fmt, "M": M, "N": N, "K": K,
-                "kernel": "small" if plan[0] == 16 else "tiled", "splits": int(plan[8]),
+                "kernel": "small" if plan[7] == 512 else "tiled",
+                "tile": [int(plan[0]), int(plan[1])], "splits": int(plan[8]),
                 "steps": steps,
                 "kernel_ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
                 "alg_tb_s": round(nbytes / ms / 1e9, 3),
@@ -422,7 +423,7 @@ def run_mx_sweep(args, shapes=None):
             raise RuntimeError("no plan for %d x %d x %d" % (M, N, K))
         nbytes = M * K + N * K + (M + N) * (K // 32) + 2.0 * M * N  # A, B, scales, D once
         rec = {"mode": "mx_sweep", "M": M, "N": N, "K": K, "steps": steps,
-               "kernel": "small" if plan[0] < 256 else "tiled", "tile": [int(plan[0]), int(plan[1])],
+               "kernel": "small" if plan[7] == 512 else "tiled", "tile": [int(plan[0]), int(plan[1])],
                "splits": int(plan[8])}
         ms = timed(ours, steps, max(3, steps // 4))
         rec.update(kernel_ms=round(ms, 5), tflops=round(flops / ms / 1e9, 1),

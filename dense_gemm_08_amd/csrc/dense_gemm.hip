@@ -172,11 +172,22 @@ static dense_gemm_status enqueue_small(int64_t M, int64_t N, int64_t K, const vo
   p.lda = (int)o.lda;
   p.ldb = (int)o.ldb;
   p.ldd = (int)ldd;
+  p.tiles_m = (int)cp.plan[3];
   p.tiles_n = (int)cp.plan[4];
   p.num_xcds = info.xcds;
   p.d_vec = (((uintptr_t)D & 7) == 0 && (ldd & 3) == 0) ? 1 : 0;
-  hipLaunchKernelGGL((gemm_small<T, LAYOUT>), dim3((unsigned)(cp.plan[3] * cp.plan[4])),
-                     dim3(SMALL_THREADS), 0, stream, p);
+  const dim3 grid((unsigned)(cp.plan[3] * cp.plan[4])), block(SMALL_THREADS);
+  if constexpr (LAYOUT == NT) {
+    if (cp.plan[0] == 2 * SMALL_TILE && cp.plan[1] == 2 * SMALL_TILE) {
+      hipLaunchKernelGGL((gemm_small<T, LAYOUT, 2, 2>), grid, block, 0, stream, p);
+      return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
+    }
+    if (cp.plan[0] == 2 * SMALL_TILE) {
+      hipLaunchKernelGGL((gemm_small<T, LAYOUT, 2, 1>), grid, block, 0, stream, p);
+      return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
+    }
+  }
+  hipLaunchKernelGGL((gemm_small<T, LAYOUT, 1, 1>), grid, block, 0, stream, p);
   return hipGetLastError() == hipSuccess ? DENSE_GEMM_OK : DENSE_GEMM_LAUNCH_FAILED;
 }
 

@@ -102,12 +102,13 @@ dense_gemm_status dense_gemm_plan(int layout, int64_t M, int64_t N, int64_t K, i
   if ((layout != NT && layout != NN) || M <= 0 || N <= 0 || K < 0 || num_cus <= 0 || !out)
     return DENSE_GEMM_BAD_ARG;
   if (small_output(layout, M, N, K)) {
-    // the small-output kernel: 16 x 16 tiles, one workgroup each, K split
-    // among its eight waves (no workspace)
+    // the small-output kernel: one workgroup per tile, K split among its
+    // eight waves (no workspace); A @ B in 16 x 16 tiles
     out[0] = out[1] = SMALL_TILE;
+    if (layout == NT) small_tile(M, N, num_cus, &out[0], &out[1]);
     out[2] = BK;
-    out[3] = (M + SMALL_TILE - 1) / SMALL_TILE;
-    out[4] = (N + SMALL_TILE - 1) / SMALL_TILE;
+    out[3] = (M + out[0] - 1) / out[0];
+    out[4] = (N + out[1] - 1) / out[1];
     out[5] = out[3] * out[4];
     out[6] = 1;
     out[7] = SMALL_THREADS;
@@ -148,12 +149,47 @@ namespace dg {
 // 1 x 8192 x 4096 17.3 against 16.4, 64 x 2048 x 4096 19.5 against 14.4,
 // 1 x 8192 x 8192 31.4 against 25.4, 128 x 1024 x 8192 35.8 against 19.6,
 // 1 x 2048 x 16384 30.3 against 17.6.
+//
+// A @ B.T also takes products of more tiles where tiles of 32 x 32 times K
+// are at most SMALL_T32_K = 2^21: its 32-row tiles (small_tile) and
+// XCD-grouped tile order cut each tile row's pass over B to about half and
+// serve it from L2.  Measured per call on one box against the tiled kernel
+// (128-row tiles, split-K, workspace passed): 32 x 8192 x 8192 21.2
+// against 25.4 us, 64 x 4096 x 4096 8.9 against 13.6, 128 x 2048 x 8192
+// 13.8 against 16.2, 48 x 8192 x 4096 16.5 against 17.6, 128 x 4096 x 4096
+// 15.5 against 16.4 (all at 2^20 or 2^21); past the limit 96 x 4096 x 8192
+// 25.5 against 19.3 (3 2^20), 64 x 8192 x 8192 28.2 against 26.9 (2^22),
+// 128 x 8192 x 8192 49.9 against 29.6 (2^23).
 bool small_output(int layout, int64_t M, int64_t N, int64_t K) {
   if ((layout != NT && layout != NN) || M > SMALL_MAX || K > SMALL_K_MAX) return false;
   const int64_t tiles_m = (M + SMALL_TILE - 1) / SMALL_TILE;
   const int64_t tiles = tiles_m * ((N + SMALL_TILE - 1) / SMALL_TILE);
+  if (layout == NT) {
+    const int64_t t32 = ((M + 31) / 32) * ((N + 31) / 32);
+    return M <= SMALL_TILE || tiles <= SMALL_MAX_TILES || t32 * K <= SMALL_T32_K;
+  }
   if (tiles > SMALL_MAX_TILES && M > SMALL_TILE) return false;
-  return layout == NT || (K <= SMALL_NN_K_MAX && tiles_m * N * K <= SMALL_NN_ELEMS);
+  return K <= SMALL_NN_K_MAX && tiles_m * N * K <= SMALL_NN_ELEMS;
+}
+
+// The largest tile whose grid still covers the CUs: more columns per tile
+// read each chunk of A once for more blocks, more rows each chunk of B, but
+// fewer tiles leave CUs idle.  Measured on one box, FP8: 64 x 1024 x 4096
+// 4.3 us in 16 x 16 tiles (256 of them) against 5.1 in 32 x 16 and 6.0 in
+// 32 x 32; 128 x 1024 x 4096 5.2 us in 32 x 16 (256 tiles) against 6.2 in
+// the others; FP16 A @ B.T alike (64 x 1024 x 4096 4.9 in 16 x 16 against
+// 5.7 and 6.8; 128 x 1024 x 4096 6.4 in 32 x 16 against 7.6 and 6.9).  One
+// 16-row tile row keeps 16 x 16 tiles: there a taller tile only computes
+// padding (FP8 16 x 8192 x 8192 13.5 us against 16.0 in 32 x 16).
+void small_tile(int64_t M, int64_t N, int64_t num_cus, int64_t* rows, int64_t* cols) {
+  *rows = *cols = SMALL_TILE;
+  if (M <= SMALL_TILE) return;
+  const int64_t tm = (M + 31) / 32;
+  if (tm * ((N + 31) / 32) >= num_cus) {
+    *rows = *cols = 32;
+  } else if (tm * ((N + 15) / 16) >= num_cus) {
+    *rows = 32;
+  }
 }
 
 // Split-K for the tiles of the last, partial wave (all tiles when there
@@ -345,7 +381,7 @@ dense_gemm_status plan_call(int layout, int64_t M, int64_t N, int64_t K, const v
 // serves from L2.  Measured per call on one box over the 23 products of M
 // = 24 ... 128, N = 2048 ... 16384 and K = 2048 ... 8192 that the former
 // rule (at most 2048 tiles of 16 x 16 with tiles x K <= 2^23) left to the
-// tiled kernel, the small kernel (its tile as mx_small_tile picks) against
+// tiled kernel, the small kernel (its tile as small_tile picks) against
 // the tiled one through the plain entry point (which allocates the split's
 // workspace per call; with a preallocated workspace, about 3 us less): up
 // to 1024 tiles of 32 x 32 1.17-2.31x as fast (e.g. 64 x 8192 x 8192 17.3
@@ -362,25 +398,6 @@ bool mx_small_output(int64_t M, int64_t N, int64_t K) {
   return t32 <= mx::MX_SMALL_T32 || (t32 <= mx::MX_SMALL_T32_MAX && t32 * K <= mx::MX_SMALL_T32_K);
 }
 
-// The largest tile whose grid still covers the CUs: more columns per tile
-// read each chunk of A once for more blocks, more rows each chunk of B, but
-// fewer tiles leave CUs idle (measured, one box: 64 x 1024 x 4096 4.3 us in
-// 16 x 16 tiles, 256 of them, against 5.1 in 32 x 16 and 6.0 in 32 x 32;
-// 128 x 1024 x 4096 5.2 us in 32 x 16, 256 tiles, against 6.2 in 16 x 16
-// and 32 x 32).  One 16-row tile row keeps 16 x 16 tiles: there a taller
-// tile only computes padding (16 x 8192 x 8192 13.5 us against 16.0 in
-// 32 x 16).
-void mx_small_tile(int64_t M, int64_t N, int64_t num_cus, int64_t* rows, int64_t* cols) {
-  *rows = *cols = SMALL_TILE;
-  if (M <= SMALL_TILE) return;
-  const int64_t tm = (M + 31) / 32;
-  if (tm * ((N + 31) / 32) >= num_cus) {
-    *rows = *cols = 32;
-  } else if (tm * ((N + 15) / 16) >= num_cus) {
-    *rows = 32;
-  }
-}
-
 dense_gemm_status mx_plan_call(int64_t M, int64_t N, int64_t K, int64_t num_cus, MxPlan* mp) {
   if (M <= 0 || N <= 0 || K < 0 || K % mx::GROUP != 0 || num_cus <= 0 || mp == nullptr ||
       M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
@@ -390,7 +407,7 @@ dense_gemm_status mx_plan_call(int64_t M, int64_t N, int64_t K, int64_t num_cus,
   mp->panel_bytes[0] = mp->panel_bytes[1] = mp->split_bytes = 0;
   if (mx_small_output(M, N, K)) {
     // one workgroup per tile, the scales staged in LDS: no workspace
-    mx_small_tile(M, N, num_cus, &out[0], &out[1]);
+    small_tile(M, N, num_cus, &out[0], &out[1]);
     out[2] = mx::BKE;
     out[3] = (M + out[0] - 1) / out[0];
     out[4] = (N + out[1] - 1) / out[1];

@@ -25,16 +25,22 @@ struct CallPlan {
   size_t a_bytes, b_bytes;   // workspace of the repacked copies
   size_t split_bytes;        // workspace of the FP32 partial tiles
   size_t total() const { return a_bytes + b_bytes + split_bytes; }
-  // the small-output kernel (one workgroup per 16 x 16 tile) instead of the
-  // tiled kernel
-  bool small() const { return plan[0] == SMALL_TILE; }
+  // the small-output kernel (one 512-thread workgroup per tile) instead of
+  // the tiled kernel
+  bool small() const { return plan[7] == SMALL_THREADS; }
 };
 
 // Products the small-output kernel computes when no option asks for the
-// tiled kernel: M at most SMALL_MAX, K at most SMALL_K_MAX, at most
-// SMALL_MAX_TILES 16 x 16 tiles or one tile row, and for A @ B K at most
-// SMALL_NN_K_MAX and tile rows x N x K at most SMALL_NN_ELEMS.
+// tiled kernel: M at most SMALL_MAX, K at most SMALL_K_MAX, and one tile
+// row or at most SMALL_MAX_TILES 16 x 16 tiles, or for A @ B.T tiles of
+// 32 x 32 x K at most SMALL_T32_K; for A @ B also K at most SMALL_NN_K_MAX
+// and tile rows x N x K at most SMALL_NN_ELEMS.
 bool small_output(int layout, int64_t M, int64_t N, int64_t K);
+// The small-output kernel's tile rows and columns for a product with M
+// rows and N columns on a device with num_cus CUs: 16 x 16 where M <= 16,
+// else 32 x 32 where those tiles number at least num_cus, else 32 x 16
+// where those do, else 16 x 16.  (A @ B takes 16 x 16 tiles.)
+void small_tile(int64_t M, int64_t N, int64_t num_cus, int64_t* rows, int64_t* cols);
 // The tiled kernel's plan (dense_gemm_plan for the other products).
 dense_gemm_status tiled_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t num_cus,
                              int64_t* out);
@@ -74,17 +80,14 @@ struct MxPlan {
   size_t panel_bytes[2];  // A's, B's (multiples of 1 KiB)
   size_t split_bytes;
   size_t total() const { return panel_bytes[0] + panel_bytes[1] + split_bytes; }
-  bool small() const { return plan[0] != mx::BM; }
+  bool small() const { return plan[7] == SMALL_THREADS; }
 };
 
 // The FP8 small-output kernel's products (M <= 128, K <= MX_SMALL_K_MAX,
 // and one 16-row tile row, or at most MX_SMALL_T32 tiles of 32 x 32, or at
 // most MX_SMALL_T32_MAX of them with tiles x K at most MX_SMALL_T32_K).
 bool mx_small_output(int64_t M, int64_t N, int64_t K);
-// The small-output kernel's tile rows and columns for such a product on a
-// device with num_cus CUs: 16 x 16 where M <= 16, else 32 x 32 where those
-// tiles number at least num_cus, else 32 x 16 where those do, else 16 x 16.
-void mx_small_tile(int64_t M, int64_t N, int64_t num_cus, int64_t* rows, int64_t* cols);
+// (Its tile: small_tile, as for FP16 A @ B.T.)
 // The plan of an FP8 call with M, N > 0 and K a multiple of 32 on a device
 // with num_cus CUs.
 dense_gemm_status mx_plan_call(int64_t M, int64_t N, int64_t K, int64_t num_cus, MxPlan* mp);

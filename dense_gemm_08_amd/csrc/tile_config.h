@@ -17,15 +17,17 @@ constexpr int WAVES = 4;             // 2 x 2 waves
 constexpr int THREADS = WAVES * 64;
 
 // The small-output kernel (gemm_small_kernel.h): A @ B.T with M at most
-// SMALL_MAX, K at most SMALL_K_MAX, and at most SMALL_MAX_TILES 16 x 16
-// tiles of D or a single tile row (M <= SMALL_TILE), each tile a workgroup
-// of eight waves that split K among themselves.
+// SMALL_MAX, K at most SMALL_K_MAX, and a single tile row (M <= SMALL_TILE),
+// or at most SMALL_MAX_TILES 16 x 16 tiles of D, or tiles of 32 x 32 x K at
+// most SMALL_T32_K; each tile (16 x 16, 32 x 16 or 32 x 32) a workgroup of
+// eight waves that split K among themselves.
 constexpr int SMALL_TILE = 16;
 constexpr int SMALL_WAVES = 8;
 constexpr int SMALL_THREADS = SMALL_WAVES * 64;
 constexpr int SMALL_MAX = 128;
 constexpr int SMALL_K_MAX = 16384;
 constexpr int SMALL_MAX_TILES = 512;
+constexpr long long SMALL_T32_K = 1LL << 21;
 // A @ B also needs K at most SMALL_NN_K_MAX and tile rows x N x K, the B
 // elements its tiles stream, at most SMALL_NN_ELEMS (plan.cpp: small_output).
 constexpr int SMALL_NN_K_MAX = 4096;

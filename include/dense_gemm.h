@@ -60,14 +60,17 @@
  * identical.  dense_gemm_ex can force the width of A @ B.T.
  *
  * Small outputs.  A product with M <= 128 and K <= 16384 whose 16 x 16
- * tiles number at most 512, or form a single tile row (M <= 16), runs a
- * second kernel instead of the tiled one: one workgroup per 16 x 16 tile of
- * D, whose eight waves split K among themselves and add their FP32 sums in
- * a fixed order (reproducible; no workspace unless an operand is
- * repacked).  For D = A @ B it also needs K <= 4096 and at most 21 * 2^20
- * B elements streamed by its tiles, ceil(M / 16) * N * K (its tiles read B
- * in 32-byte row segments; past that the tiled kernel is faster); A @ B
- * and A @ B.T on the same operands then give the same result bit for bit.
+ * tiles number at most 512, or form a single tile row (M <= 16), or (A @
+ * B.T) whose 32 x 32 tiles times K are at most 2^21, runs a second kernel
+ * instead of the tiled one: one workgroup per tile of D (16 x 16; for
+ * A @ B.T 32 x 16 or 32 x 32 where dense_gemm_plan gives them), whose eight
+ * waves split K among themselves and add their FP32 sums in a fixed order
+ * (reproducible, and the same bits whatever the tile shape; no workspace
+ * unless an operand is repacked).  For D = A @ B it also needs K <= 4096
+ * and at most 21 * 2^20 B elements streamed by its tiles, ceil(M / 16) * N
+ * * K (its tiles read B in 32-byte row segments; past that the tiled
+ * kernel is faster); A @ B and A @ B.T on the same operands then give the
+ * same result bit for bit.
  * Its summation order differs from the tiled kernel's, within the same
  * rounding bound.  Any dense_gemm_options override asks for the tiled
  * kernel instead.
@@ -335,8 +338,10 @@ dense_gemm_status dense_gemm_tile_of_task(int64_t task, int64_t tiles_m, int64_t
  * above), BK, tiles_m, tiles_n, grid (workgroups of the
  * GEMM kernel), group_m, threads per workgroup, the number of K splits
  * (1: none) and the K steps (of BK) per split.  For the small-output kernel
- * ("Small outputs" above) BM = BN = 16, the grid is tiles_m * tiles_n
- * workgroups of 512 threads, group_m 1 and no split.  Split-K applies to the
+ * ("Small outputs" above) the grid is tiles_m * tiles_n workgroups of 512
+ * threads, group_m 1 and no split; its tiles are 16 x 16 for A @ B and for
+ * M <= 16, else 32 x 32 where those number at least num_cus, else 32 x 16
+ * where those do, else 16 x 16.  Split-K applies to the
  * r = tiles mod num_cus tiles of the last, partial wave (all tiles when
  * tiles < num_cus), with K spanning at least 8 steps, at most one part per
  * CU (r * parts <= num_cus) and at least 4 steps per part.  When tiles <

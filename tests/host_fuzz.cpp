@@ -54,10 +54,20 @@ static void check_plan(int layout, int64_t M, int64_t N, int64_t K, int64_t cus,
   if (cp.small()) {
     CHECK(M <= SMALL_MAX && K <= SMALL_K_MAX);
     CHECK(layout == NT || (K <= SMALL_NN_K_MAX && ceil_div(M, SMALL_TILE) * N * K <= SMALL_NN_ELEMS));
-    CHECK(p[1] == SMALL_TILE && p[2] == BK && p[7] == SMALL_THREADS);
-    CHECK(p[3] == ceil_div(M, SMALL_TILE) && p[4] == ceil_div(N, SMALL_TILE));
+    // A @ B.T: the tile small_tile gives (16 x 16 for one 16-row tile row,
+    // else the largest whose grid covers the CUs); A @ B: 16 x 16
+    const int64_t tr = p[0], tc = p[1];
+    int64_t er = SMALL_TILE, ec = SMALL_TILE;
+    if (layout == NT) small_tile(M, N, cus, &er, &ec);
+    CHECK(tr == er && tc == ec);
+    CHECK((tr == 16 && tc == 16) || (tr == 32 && (tc == 16 || tc == 32)));
+    if (tc == 32) CHECK(ceil_div(M, 32) * ceil_div(N, 32) >= cus);
+    if (tr == 32 && tc == 16) CHECK(ceil_div(M, 32) * ceil_div(N, 16) >= cus);
+    CHECK(p[2] == BK && p[7] == SMALL_THREADS);
+    CHECK(p[3] == ceil_div(M, tr) && p[4] == ceil_div(N, tc));
     CHECK(p[5] == p[3] * p[4] && cp.full_tasks == p[5]);
-    CHECK(p[5] <= SMALL_MAX_TILES || p[3] == 1);
+    const int64_t t16 = ceil_div(M, 16) * ceil_div(N, 16), t32 = ceil_div(M, 32) * ceil_div(N, 32);
+    CHECK(M <= SMALL_TILE || t16 <= SMALL_MAX_TILES || (layout == NT && t32 * K <= SMALL_T32_K));
     CHECK(p[8] == 1 && cp.split_tiles == 0 && cp.split_bytes == 0);
     check_repack(layout, M, N, K, cp);
     return;
@@ -104,6 +114,9 @@ static void check_mx_plan(int64_t M, int64_t N, int64_t K, int64_t cus, const Mx
     // tiles of 16 x 16, 32 x 16 or 32 x 32: the largest whose grid covers
     // the CUs, 16 x 16 for one 16-row tile row
     const int64_t tr = p[0], tc = p[1];
+    int64_t er, ec;
+    small_tile(M, N, cus, &er, &ec);
+    CHECK(tr == er && tc == ec);
     CHECK((tr == 16 && tc == 16) || (tr == 32 && (tc == 16 || tc == 32)));
     CHECK(p[3] == ceil_div(M, tr) && p[4] == ceil_div(N, tc) && p[5] == p[3] * p[4]);
     if (M <= SMALL_TILE) {

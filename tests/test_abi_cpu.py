@@ -253,8 +253,8 @@ def test_plan_split_k():
     assert lib.dense_gemm_plan(NT, 8192, 4224, 4096, 256, out) == S.OK
     assert (out[8], out[9], out[5]) == (8, 8, 256)
     # one row of tiles (M < 256): partial tiles write only their rows inside D,
-    # so the split pays sooner: 128 narrow tiles of 32 x 16384 x 4096 in 2 parts
-    assert lib.dense_gemm_plan(NT, 32, 16384, 4096, 256, out) == S.OK
+    # so the split pays sooner: 128 narrow tiles of 48 x 16384 x 4096 in 2 parts
+    assert lib.dense_gemm_plan(NT, 48, 16384, 4096, 256, out) == S.OK
     assert (out[1], out[4], out[8], out[9], out[5]) == (128, 128, 2, 32, 256)
     # ... which a full tile row would not pay for (256 rows x 128 tiles)
     assert lib.dense_gemm_plan(NT, 256, 16384, 4096, 256, out) == S.OK
@@ -394,7 +394,7 @@ def test_plan_split_rule_as_documented():
         K = int(rng.integers(0, 40000))
         cus = int(rng.choice([256, 240, 128, 32]))
         assert lib.dense_gemm_plan(layout, M, N, K, cus, out) == S.OK
-        if out[0] == 16:
+        if out[7] == 512:
             continue  # the small-output kernel: no split
         tr, tw, tm, tn = out[0], out[1], out[3], out[4]
         nk = -(-K // 64)
@@ -467,40 +467,63 @@ def test_plan_tile_rows():
     # 128-row tiles exactly when M <= 128 (on the tiled kernel)
     lib = binding.load_library()
     out = (ctypes.c_int64 * 10)()
-    for layout, M, N, K, rows in [(NT, 64, 4096, 4096, 128), (NT, 128, 16384, 4096, 128),
+    for layout, M, N, K, rows in [(NT, 96, 4096, 8192, 128), (NT, 128, 16384, 4096, 128),
                                   (NN, 128, 2048, 4096, 128), (NN, 1, 8192, 8192, 128),
                                   (NT, 128, 128, 20000, 128), (NT, 129, 16384, 4096, 256),
                                   (NN, 200, 1000, 1000, 256), (NT, 4096, 4096, 4096, 256)]:
         assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
         assert (out[0], out[3]) == (rows, -(-M // rows)), (layout, M, N, K, list(out))
     # split partial tiles are 128 rows then: 8 parts of 128 x 128 FP32 on 32 tiles
-    assert lib.dense_gemm_plan(NT, 64, 4096, 4096, 256, out) == S.OK
+    assert lib.dense_gemm_plan(NT, 96, 4096, 8192, 256, out) == S.OK
     assert (out[1], out[4], out[8]) == (128, 32, 8)
-    assert _ws("nt", "f16", 64, 4096, 4096) == (S.OK, 8 * 32 * 128 * 128 * 4)
+    assert _ws("nt", "f16", 96, 4096, 8192) == (S.OK, 8 * 32 * 128 * 128 * 4)
+
+
+def _small_tile(M, N, cus):
+    # the small-output kernel's tile (as dense_gemm_plan documents it): 16 x
+    # 16 for one 16-row tile row, else the largest of 32 x 32 and 32 x 16
+    # whose tiles number at least the CUs, else 16 x 16
+    if M <= 16:
+        return 16, 16
+    if -(-M // 32) * -(-N // 32) >= cus:
+        return 32, 32
+    if -(-M // 32) * -(-N // 16) >= cus:
+        return 32, 16
+    return 16, 16
 
 
 def test_plan_small_output():
-    # M <= 128, K <= 16384 and at most 512 16 x 16 tiles of D, or one tile
-    # row (M <= 16) of any width, and for A.B K <= 4096 and at most 21 * 2^20
-    # B elements streamed (tile rows x N x K): the small-output kernel, one
-    # 512-thread workgroup per tile, no split
+    # M <= 128, K <= 16384 and one tile row (M <= 16) of any width, or at
+    # most 512 16 x 16 tiles of D, or for A.B^T tiles of 32 x 32 x K at most
+    # 2^21; for A.B at most 512 tiles or one tile row, K <= 4096 and at most
+    # 21 * 2^20 B elements streamed (tile rows x N x K): the small-output
+    # kernel, one 512-thread workgroup per tile, no split
     lib = binding.load_library()
     out = (ctypes.c_int64 * 10)()
     for layout, M, N, K in [(NT, 128, 128, 64), (NT, 128, 128, 4096), (NT, 128, 128, 16384),
                             (NT, 100, 72, 1000), (NT, 1, 4096, 4096), (NT, 1, 8192, 1),
                             (NT, 128, 1024, 1024), (NT, 16, 16, 0), (NT, 16, 65536, 4096),
-                            (NT, 1, 1 << 20, 64), (NN, 128, 128, 4096), (NN, 1, 4096, 4096),
+                            (NT, 1, 1 << 20, 64), (NT, 17, 4112, 4096), (NT, 128, 1040, 64),
+                            (NT, 32, 8192, 8192), (NT, 128, 4096, 4096), (NT, 64, 4096, 4096),
+                            (NN, 128, 128, 4096), (NN, 1, 4096, 4096),
                             (NN, 16, 4096, 4096), (NN, 100, 1000, 3000), (NN, 32, 1024, 4096),
                             (NN, 1, 16, 64), (NN, 1, 5376, 4096), (NN, 3, 16, 4096)]:
         assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
-        tiles_m, tiles_n = -(-M // 16), -(-N // 16)
-        assert list(out) == [16, 16, 64, tiles_m, tiles_n, tiles_m * tiles_n, 1, 512, 1,
+        tr, tc = _small_tile(M, N, 256) if layout == NT else (16, 16)
+        tiles_m, tiles_n = -(-M // tr), -(-N // tc)
+        assert list(out) == [tr, tc, 64, tiles_m, tiles_n, tiles_m * tiles_n, 1, 512, 1,
                              -(-K // 64)], (layout, M, N, K)
-    # past any of the limits: the tiled kernel (A.B: 1 x 8192 x 4096 and
-    # 64 x 2048 x 4096 stream 2^25 B elements, 1 x 5392 x 4096 one 16-column
-    # tile more than 21 * 2^20; K above 4096)
-    for layout, M, N, K in [(NT, 129, 128, 4096), (NT, 128, 128, 16392), (NT, 17, 4112, 4096),
-                            (NT, 128, 1040, 64), (NT, 1, 4096, 16392), (NN, 1, 8192, 4096),
+    # the three tile shapes of A.B^T on 256 CUs
+    for M, N, K, tile in [(128, 128, 4096, [16, 16]), (128, 1024, 1024, [32, 16]),
+                          (128, 4096, 4096, [32, 32]), (16, 65536, 4096, [16, 16])]:
+        assert lib.dense_gemm_plan(NT, M, N, K, 256, out) == S.OK
+        assert list(out[:2]) == tile, (M, N, K)
+    # past any of the limits: the tiled kernel (A.B^T: 32 x 32 tiles x K
+    # above 2^21; A.B: 1 x 8192 x 4096 and 64 x 2048 x 4096 stream 2^25 B
+    # elements, 1 x 5392 x 4096 one 16-column tile more than 21 * 2^20; K
+    # above 4096)
+    for layout, M, N, K in [(NT, 129, 128, 4096), (NT, 128, 128, 16392), (NT, 17, 16400, 8192),
+                            (NT, 128, 4112, 4096), (NT, 1, 4096, 16392), (NN, 1, 8192, 4096),
                             (NN, 64, 2048, 4096), (NN, 1, 5392, 4096), (NN, 128, 1024, 8192),
                             (NN, 1, 2048, 16384), (NN, 1, 16, 4104), (NN, 128, 128, 16384)]:
         assert lib.dense_gemm_plan(layout, M, N, K, 256, out) == S.OK
@@ -514,6 +537,26 @@ def test_plan_small_output():
     assert _ws("nt", "f16", 128, 128, 4096, opts=(0, 128)) == (S.OK, 16 * 128 * 128 * 4)
     # ... or repacks, like the tiled kernel, an operand it cannot read in place
     assert _ws("nt", "f16", 128, 128, 4095) == (S.OK, 2 * 128 * 4096 * 2)
+    # the rule and the tile as documented, on many shapes with M <= 128 and
+    # CU counts
+    rng = np.random.default_rng(8)
+    for _ in range(600):
+        layout = int(rng.integers(0, 2))
+        M = int(rng.integers(1, 129))
+        N = int(rng.choice([int(rng.integers(1, 600)), int(rng.integers(600, 40000))]))
+        K = int(rng.choice([int(rng.integers(0, 300)), int(rng.integers(300, 20000))]))
+        cus = int(rng.choice([256, 240, 128, 80, 32]))
+        assert lib.dense_gemm_plan(layout, M, N, K, cus, out) == S.OK
+        tiles = -(-M // 16) * -(-N // 16)
+        if layout == NT:
+            small = K <= 16384 and (M <= 16 or tiles <= 512 or
+                                    -(-M // 32) * -(-N // 32) * K <= 1 << 21)
+        else:
+            small = (K <= 4096 and (M <= 16 or tiles <= 512) and -(-M // 16) * N * K <= 21 << 20)
+        assert (out[7] == 512) == small, (layout, M, N, K, cus, list(out))
+        if small:
+            tr, tc = _small_tile(M, N, cus) if layout == NT else (16, 16)
+            assert list(out[:2]) == [tr, tc] and out[5] == -(-M // tr) * -(-N // tc)
 
 
 def test_ladder_argument_checks_on_the_host():

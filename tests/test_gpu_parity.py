@@ -262,13 +262,17 @@ def test_ragged_block_equals_padded_block(layout, fmt):
 
 SMALL = [
     # (M, N, K) planned for the small-output kernel (A.B^T, M <= 128, K <=
-    # 16384, at most 512 tiles of 16 x 16 or one tile row): the longest K
-    # (32 chunks per wave), ragged tiles with K not a multiple of the 64-deep
-    # chunks, the 512-tile limit at one tile row and at eight, one tile row
-    # past it, a K below 8 (repacked), one chunk shared by fewer than the
-    # eight waves
+    # 16384, and one tile row, or at most 512 tiles of 16 x 16, or 32 x 32
+    # tiles x K at most 2^21): the longest K (32 chunks per wave), ragged
+    # tiles with K not a multiple of the 64-deep chunks, the 512-tile limit
+    # at one tile row and at eight, one tile row past it, a K below 8
+    # (repacked), one chunk shared by fewer than the eight waves; on 256
+    # CUs 32 x 16 tiles for (128, 1024, 64), (128, 1100, 1000) and (17, 4112,
+    # 4096) (17 of 32 rows), 32 x 32 for the last three (ragged in M, N and
+    # K; 32 x 32 tiles x K = 2^21 exactly)
     (128, 128, 16384), (100, 72, 8000), (1, 8192, 520), (128, 1024, 64), (16, 8200, 1000),
-    (3, 20000, 72), (5, 3, 7), (17, 130, 1000), (128, 128, 448),
+    (3, 20000, 72), (5, 3, 7), (17, 130, 1000), (128, 128, 448), (128, 1100, 1000),
+    (17, 4112, 4096), (100, 2600, 1000), (64, 4096, 4096), (48, 8192, 4096),
 ]
 
 
@@ -279,7 +283,7 @@ def test_small_output_kernel_full_check(fmt, M, N, K):
     from dense_gemm_08_amd import binding
     out = (ctypes.c_int64 * 10)()
     assert binding.load_library().dense_gemm_plan(0, M, N, K, 256, out) == 0
-    assert out[0] == 16, "planned for the tiled kernel"
+    assert out[7] == 512, "planned for the tiled kernel"
     w = inputs.Workload("x", "nt", fmt, 0, 0, 0, "uniform", 0.0, 111)
     A, B = inputs.make_operands(w, seed=M + N + K, M=M, N=N, K=K)
     D, st = _gpu.gemm("nt", fmt, A, B, M, N, K)
@@ -288,6 +292,34 @@ def test_small_output_kernel_full_check(fmt, M, N, K):
     # the eight waves' blocks are summed in a fixed order: a rerun is equal
     D2, _ = _gpu.gemm("nt", fmt, A, B, M, N, K)
     assert (D == D2).all()
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_small_output_kernel_tile_shapes_give_the_same_bits(fmt):
+    # every output's sum is the same sequence of MFMAs in 16 x 16, 32 x 16
+    # and 32 x 32 tiles: the products of A with the first rows of one B
+    # agree bit for bit on their common columns, whichever tile each runs in
+    import ctypes
+    from dense_gemm_08_amd import binding
+    lib = binding.load_library()
+    cus = _gpu.torch().cuda.get_device_properties(0).multi_processor_count
+    out = (ctypes.c_int64 * 10)()
+    w = inputs.Workload("x", "nt", fmt, 0, 0, 0, "uniform", 0.0, 141)
+    for M, K, widths in [(64, 1000, (1000, 4200)), (128, 1000, (300, 1100, 4200))]:
+        A, B = inputs.make_operands(w, seed=M + K, M=M, N=max(widths), K=K)
+        tiles = set()
+        for n in widths:
+            assert lib.dense_gemm_plan(0, M, n, K, cus, out) == 0 and out[7] == 512
+            tiles.add((out[0], out[1]))
+        assert len(tiles) == len(widths), tiles  # distinct shapes (on 256 CUs: all three)
+        outs = []
+        for n in widths:
+            D, st = _gpu.gemm("nt", fmt, A, B[:n], M, n, K)
+            assert st == status().OK
+            outs.append(D)
+        for D in outs[1:]:
+            assert (D[:, :widths[0]] == outs[0]).all(), (M, K)
+        check_full("nt", fmt, A, B[:widths[0]], M, widths[0], K, outs[0])
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
@@ -323,7 +355,7 @@ def _nn_small(M, N, K):
     from dense_gemm_08_amd import binding
     out = (ctypes.c_int64 * 10)()
     assert binding.load_library().dense_gemm_plan(1, M, N, K, 256, out) == 0
-    return out[0] == 16
+    return out[7] == 512
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
@@ -384,11 +416,11 @@ def test_small_output_kernel_nn_leading_dimensions_and_offsets():
 
 TALL = [
     # (layout, fmt, M, N, K) for the tiled kernel with 128-row tiles (M <= 128
-    # and not a small-output product: K > 16384, more than 512 tiles of 16 x
-    # 16 with M > 16, or A.B with K > 4096 or streaming more than 21 * 2^20 B
-    # elements through 16 x 16 tiles): both widths, split and unsplit, ragged
-    # edges
-    ("nt", "f16", 64, 8200, 1000), ("nt", "bf16", 100, 4200, 2000),
+    # and not a small-output product: K > 16384, or more than 512 tiles of
+    # 16 x 16 with M > 16 and, for A.B^T, 32 x 32 tiles x K above 2^21, or
+    # A.B with K > 4096 or streaming more than 21 * 2^20 B elements through
+    # 16 x 16 tiles): both widths, split and unsplit, ragged edges
+    ("nt", "f16", 64, 8200, 8200), ("nt", "bf16", 100, 4200, 6000),
     ("nt", "f16", 128, 128, 20000), ("nn", "bf16", 128, 1000, 4000), ("nn", "f16", 17, 2600, 5000),
     ("nn", "bf16", 1, 6200, 4100),
 ]
