@@ -46,8 +46,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="square_nt",
-                    help="a workload of dense_gemm_08_amd/inputs.py: WORKLOADS (FP16/BF16) or "
-                         "MX_WORKLOADS (FP8 block-scaled)")
+                    help="a workload of dense_gemm_08_amd/inputs.py: WORKLOADS (FP16/BF16), "
+                         "SHARD_WORKLOADS (one GPU's share of the large A @ B product split "
+                         "over 2, 4 or 8 GPUs) or MX_WORKLOADS (FP8 block-scaled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-ms", type=float, default=150.0,
                     help="before the warm-up steps, run untimed calls back to back for this many "
@@ -615,7 +616,7 @@ def main():
                   "scales": "e8m0 per 32 K values of a row", "out": "bf16",
                   "recipe": w.kind, "seed": w.seed}
     else:
-        w = inputs.WORKLOADS[args.workload]
+        w = {**inputs.WORKLOADS, **inputs.SHARD_WORKLOADS}[args.workload]
         entry = getattr(lib, {("nt", "f16"): "gemm_nt_f16", ("nn", "bf16"): "gemm_nn_bf16",
                               ("nt", "bf16"): "gemm_nt_bf16", ("nn", "f16"): "gemm_nn_f16"}
                         [(w.layout, w.fmt)])

@@ -53,6 +53,19 @@ WORKLOADS = {
     "ragged_nt": Workload("ragged_nt", "nt", "f16", 3000, 5000, 4000, "uniform", 0.0, 5),
 }
 
+# One GPU's share of the 8192 x 17408 x 5120 BF16 A @ B product when it is
+# split over g GPUs with no exchange between them (output tiles are
+# independent): "rows<g>" takes M / g rows of A and D and all of B;
+# "cols<g>" takes N / g columns of B and D and all of A.  Same distribution
+# as the whole product, a seed of its own per shard.
+SHARD_WORKLOADS = {
+    "large_nn_%s%d" % (how, g): Workload(
+        "large_nn_%s%d" % (how, g), "nn", "bf16", 8192 // g if how == "rows" else 8192,
+        17408 // g if how == "cols" else 17408, 5120, "normal", 0.02,
+        40 + g + (10 if how == "cols" else 0))
+    for how in ("rows", "cols") for g in (2, 4, 8)
+}
+
 
 def f16_bits(x: np.ndarray) -> np.ndarray:
     """Round float64 values to FP16 (numpy's RNE cast) and return the bits."""
