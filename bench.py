@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of one workload, time D = A @ B.T (FP16) at M = 8192 over a grid "
                          "of N and K (one JSON line per shape, torch.mm timed beside it)")
+    ap.add_argument("--shapes", default="",
+                    help="with --sweep: a comma-separated list of MxNxK shapes to time instead "
+                         "of the grid (e.g. 4096x4096x4096,8192x16384x16384)")
     ap.add_argument("--small-m-sweep", action="store_true",
                     help="instead of one workload, time D = A @ B.T (FP16) at small M (1 to 512) "
                          "against N, K of 4096 to 16384, torch.mm timed beside it (shapes outside "
@@ -533,7 +536,10 @@ def main():
     from dense_gemm_08_amd import binding, inputs
 
     if args.sweep:
-        run_sweep(args)
+        shapes = [tuple(int(v) for v in x.split("x")) for x in args.shapes.split(",") if x]
+        if any(len(t) != 3 or min(t) < 1 for t in shapes):
+            raise SystemExit("--shapes takes MxNxK triples of positive sizes")
+        run_sweep(args, shapes or None)
         return
     if args.small_m_sweep:
         run_sweep(args, SMALL_M)
