@@ -204,6 +204,26 @@ def test_plan_for_the_workloads():
     assert lib.dense_gemm_plan(NT, 0, 5, 5, 256, out) == S.BAD_ARG
 
 
+def test_split_tail_of_the_shard_shapes_is_an_even_k_partition():
+    # One GPU's share of the 8192 x 17408 x 5120 A.B product (row or column
+    # split over 2, 4, 8 GPUs): whole waves of 256 x 256 tiles, then the
+    # leftover tiles' K steps dealt out so that every CU of the last pass
+    # gets the same number of them -- the tail partition of a stream-K
+    # schedule, whose equal shares here fall on tile-part boundaries
+    from dense_gemm_08_amd import inputs
+    lib = binding.load_library()
+    out = (ctypes.c_int64 * 10)()
+    for name, w in inputs.SHARD_WORKLOADS.items():
+        assert lib.dense_gemm_plan(NN, w.M, w.N, w.K, 256, out) == S.OK
+        BM, BN, BK, tm, tn, grid, gm, threads, splits, steps = list(out)
+        tiles, nk = tm * tn, -(-w.K // BK)
+        left = tiles % grid
+        assert (BM, BN, grid) == (256, 256, 256) and left > 0, name
+        assert splits * steps == nk, name              # parts tile the K range
+        assert left * splits == grid, name             # one part per CU
+        assert left * nk // grid == steps, name        # the even share of the tail
+
+
 def test_plan_split_k():
     lib = binding.load_library()
     out = (ctypes.c_int64 * 10)()
