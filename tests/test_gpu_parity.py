@@ -126,12 +126,14 @@ def test_two_tiles_per_workgroup_every_output(layout, fmt, M, N, K):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["large_nn_rows8", "large_nn_cols8", "large_nn_rows4"])
+@pytest.mark.parametrize("name", ["large_nn_rows8", "large_nn_cols8", "large_nn_rows4",
+                                  "large_nn_cols4", "large_nn_rows2", "large_nn_cols2"])
 def test_shard_of_large_nn_every_output(name):
-    # one GPU's share of the 8192 x 17408 x 5120 A.B product split over 8
-    # (4) GPUs, as the benchmark times it: 1024 rows (272 tiles on 256
-    # workgroups, the last 16 split in K), 2176 columns (288 tiles, 32
-    # split), 2048 rows (544 tiles); every output
+    # one GPU's share of the 8192 x 17408 x 5120 A.B product split over 8,
+    # 4 or 2 GPUs, as the benchmark times it: e.g. 1024 rows (272 tiles on
+    # 256 workgroups, the last 16 split 16 ways in K), 2176 columns (288
+    # tiles, 32 split 8 ways), 4096 rows (1088 tiles, 64 split 4 ways);
+    # every output
     w = inputs.SHARD_WORKLOADS[name]
     print("shard %s %dx%dx%d" % (name, w.M, w.N, w.K), flush=True)
     A, B = inputs.make_operands(w)
