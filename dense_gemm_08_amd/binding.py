@@ -138,6 +138,27 @@ def _stream_handle(stream, device) -> int:
     return stream.cuda_stream
 
 
+def _stream_object(stream, device):
+    """The torch stream object of a launch stream given as a torch stream or
+    a raw HIP stream handle."""
+    import torch
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream, device=device)
+    return stream
+
+
+def _used_by(t, stream, device):
+    """Mark a tensor from torch's caching allocator as in use by the launch
+    stream when that is not the current stream (an explicit ``stream``):
+    torch ties each block to the stream it was allocated on, so without the
+    mark a block dropped (or freed by the caller) while the call's kernels
+    still run on the other stream could be handed to a new allocation on
+    the current stream and overwritten under them."""
+    if stream is not None:
+        t.record_stream(_stream_object(stream, device))
+    return t
+
+
 def _ld(t) -> int:
     """Leading dimension (elements between rows) of a 2-D tensor with unit
     column stride.  A single row may carry any row stride (a transposed
@@ -180,7 +201,11 @@ def workspace_size(layout: str, fmt: str, M: int, N: int, K: int, A_ptr: int, ld
 def _call(name: str, layout: str, fmt: str, A, B, D=None, stream=None, workspace=None):
     """D = A @ B.T (layout "nt", B is N x K) or D = A @ B ("nn", B is K x N).
     With ``workspace`` (a device tensor, or True to take one from torch's
-    allocator), the call goes through dense_gemm_ex with that workspace."""
+    allocator), the call goes through dense_gemm_ex with that workspace.
+    The call is asynchronous on ``stream`` (None: the current stream).  A
+    workspace or D passed in stays the caller's to keep alive until the
+    call's kernels finish; the ones this function allocates are marked as in
+    use by ``stream``."""
     import torch
     lib = load_library()
     _check_tensor(A, fmt, "A")
@@ -192,13 +217,16 @@ def _call(name: str, layout: str, fmt: str, A, B, D=None, stream=None, workspace
         Kb, N = B.shape
     if Kb != K:
         raise ValueError("inner dimensions differ: A is %s, B is %s" % (tuple(A.shape), tuple(B.shape)))
-    if D is None:
+    own_d = D is None
+    if own_d:
         D = torch.empty((M, N), dtype=A.dtype, device=A.device)
     else:
         _check_tensor(D, fmt, "D")
         if D.shape[0] != M or D.shape[1] != N:
             raise ValueError("D has shape %s, expected (%d, %d)" % (tuple(D.shape), M, N))
     dev = _same_device(A, B, D)
+    if own_d:
+        _used_by(D, stream, dev)
     # the library launches on the current device
     with torch.cuda.device(dev):
         if workspace is None:
@@ -208,7 +236,8 @@ def _call(name: str, layout: str, fmt: str, A, B, D=None, stream=None, workspace
             if workspace is True:
                 need = workspace_size(layout, fmt, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(),
                                       _ld(B))
-                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+                workspace = _used_by(torch.empty(max(need, 1), dtype=torch.uint8, device=dev),
+                                     stream, dev)
             if not workspace.is_cuda or workspace.device != dev:
                 raise ValueError("workspace must be a device tensor on %s" % dev)
             st = lib.dense_gemm_ex(OPS[(layout, fmt)], M, N, K, A.data_ptr(), _ld(A),
@@ -277,13 +306,16 @@ def gemm_nt_e4m3_mx(A, SA, B, SB, D=None, stream=None, workspace=None):
     if B.shape[1] != K or tuple(SA.shape) != (M, K // 32) or tuple(SB.shape) != (N, K // 32):
         raise ValueError("inconsistent shapes: A %s, SA %s, B %s, SB %s"
                          % (tuple(A.shape), tuple(SA.shape), tuple(B.shape), tuple(SB.shape)))
-    if D is None:
+    own_d = D is None
+    if own_d:
         D = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     else:
         _check_tensor(D, "bf16", "D")
         if D.shape[0] != M or D.shape[1] != N:
             raise ValueError("D has shape %s, expected (%d, %d)" % (tuple(D.shape), M, N))
     dev = _same_device(A, SA, B, SB, D)
+    if own_d:
+        _used_by(D, stream, dev)
     name = "gemm_nt_e4m3_mx"
     with torch.cuda.device(dev):
         args = (M, N, K, A.data_ptr(), _ld(A), SA.data_ptr(), _ld(SA), B.data_ptr(), _ld(B),
@@ -292,8 +324,8 @@ def gemm_nt_e4m3_mx(A, SA, B, SB, D=None, stream=None, workspace=None):
             st = lib.gemm_nt_e4m3_mx(*args, _stream_handle(stream, dev))
         else:
             if workspace is True:
-                workspace = torch.empty(max(mx_workspace_size(M, N, K), 1), dtype=torch.uint8,
-                                        device=dev)
+                workspace = _used_by(torch.empty(max(mx_workspace_size(M, N, K), 1),
+                                                 dtype=torch.uint8, device=dev), stream, dev)
             if not workspace.is_cuda or workspace.device != dev:
                 raise ValueError("workspace must be a device tensor on %s" % dev)
             st = lib.gemm_nt_e4m3_mx_ex(*args, workspace.data_ptr(),

@@ -1019,3 +1019,33 @@ def test_mx_workspace_call_equals_plain_call():
     t.cuda.synchronize()
     assert (_gpu.from_dev(D1) == _gpu.from_dev(D2)).all()
     assert (_gpu.from_dev(D3) == _gpu.CANARY).all()
+
+
+def test_binding_call_on_another_stream_with_its_own_workspace_and_output():
+    # the Python binding on a stream other than the current one, taking its
+    # workspace (split-K partials) and D from torch's allocator: both are
+    # marked as in use by that stream, so the allocations the current stream
+    # makes right after the call (filled at once) cannot land on them while
+    # the call's kernels run
+    import dense_gemm_08_amd as dg
+    t = _gpu.torch()
+    w = inputs.WORKLOADS["k_loop"]
+    M, N, K = 256, 128, 4096  # one 256 x 128 tile: the plan splits K 16 ways
+    A, B = inputs.make_operands(w, seed=91, M=M, N=N, K=K)
+    Ad = t.from_numpy(A.view(np.int16)).cuda().view(t.float16)
+    Bd = t.from_numpy(B.view(np.int16)).cuda().view(t.float16)
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    outs = []
+    for rep in range(8):
+        outs.append(dg.gemm_nt_f16(Ad, Bd, stream=side, workspace=True))
+        outs.append(dg.gemm_nt_f16(Ad, Bd, stream=side.cuda_stream, workspace=True))
+        junk = [t.full((1 << 20,), -1.0, dtype=t.float32, device="cuda") for _ in range(4)]
+        del junk
+    t.cuda.synchronize()
+    d, s = oracle.gemm("nt", "f16", A, B, M=M, N=N, K=K)
+    first = _gpu.from_dev(outs[0].view(t.int16))
+    for D in outs:
+        got = _gpu.from_dev(D.view(t.int16))
+        assert (got == first).all()
+    check_against("f16", d, s, first, "side stream")
