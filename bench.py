@@ -526,19 +526,30 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this GEMM has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
+              "(run with --gpus 1; one GPU's share of the large A @ B product split over "
+              "2, 4 or 8 GPUs runs as --workload large_nn_rows<g> or large_nn_cols<g>)",
+              file=sys.stderr)
         sys.exit(2)
 
     if (args.split_k or args.tile_n) and not args.workspace:
         raise SystemExit("--split-k and --tile-n are options of dense_gemm_ex: add --workspace")
 
+    from dense_gemm_08_amd import inputs
+    known = set(inputs.WORKLOADS) | set(inputs.SHARD_WORKLOADS) | set(inputs.MX_WORKLOADS)
+    if args.workload not in known:
+        raise SystemExit("unknown workload %r (one of: %s)" % (args.workload,
+                                                               ", ".join(sorted(known))))
+    try:
+        shapes = [tuple(int(v) for v in x.split("x")) for x in args.shapes.split(",") if x]
+    except ValueError:
+        shapes = [()]
+    if any(len(t) != 3 or min(t) < 1 for t in shapes):
+        raise SystemExit("--shapes takes MxNxK triples of positive sizes")
+
     import torch
-    from dense_gemm_08_amd import binding, inputs
+    from dense_gemm_08_amd import binding
 
     if args.sweep:
-        shapes = [tuple(int(v) for v in x.split("x")) for x in args.shapes.split(",") if x]
-        if any(len(t) != 3 or min(t) < 1 for t in shapes):
-            raise SystemExit("--shapes takes MxNxK triples of positive sizes")
         run_sweep(args, shapes or None)
         return
     if args.small_m_sweep:
@@ -658,6 +669,10 @@ def main():
                     raise binding.DenseGemmError(st, "gemm")
         config = {"workload": w.name, "layout": w.layout, "M": w.M, "N": w.N, "K": w.K,
                   "lda": lda, "ldb": ldb, "ldd": ldd, "dist": w.dist, "seed": w.seed}
+        if w.name in inputs.SHARD_WORKLOADS:
+            g = int(w.name[-1])
+            config["share_of"] = {"workload": "large_nn", "gpus": g,
+                                  "split": "M" if "_rows" in w.name else "N"}
         if args.split_k or args.tile_n:
             config["options"] = {"split_k": args.split_k, "tile_n": args.tile_n}
     config["entry"] = ("dense_gemm_ex" if src == "gemm_kernel.h" else "gemm_nt_e4m3_mx_ex") \
